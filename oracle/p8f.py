@@ -1,0 +1,525 @@
+"""CPU oracle for the Pingala-8 hot path, format P8F v1 (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product (the `qgemv_amd` package,
+its HIP kernels or its C-ABI library) may import, call, link or execute this
+module.  Only the test suite, `__graft_entry__.smoke()` and the CPU-baseline
+leg of `bench.py` use it.  It shares no code with the library: every rule
+below is written out again here from the method's description.
+
+Sources.  The pages describe Pingala-8 in words only:
+  [P1] "Pingala-8" landing page (ja), section 仕組み ("How it works"), with the
+       same text in the zh landing page, section 原理: an Ungerboeck 8-state
+       trellis code encodes groups of four weights in order; a small state
+       carried from one group to the next picks the value set the next group
+       may use; a random Hadamard rotation spreads out large weights before
+       encoding; LDLQ rounding is used by the compressor.
+  [P1-name] same page, section 名前の由来 ("Where the name comes from"): eight
+       states over short three-syllable patterns, trellis labels after
+       Ungerboeck.
+  [P1-paper] same page, section 論文 ("Paper"): the title calls it small-state
+       *coset* trellis coding.
+  [P4] article "8 open models, 77-85% smaller: what 2-bit quantization costs
+       and what it keeps", section "What 2-bit keeps": files carry per-block
+       scales; batch-1 generation is dominated by reading the weights once per
+       token.
+The pages give no bit layout, codebook, block length or Hadamard size.  This
+oracle follows format P8F v1, whose every choice is the plainest reading the
+pages support (listed, with reasons, among the readings of the pages in the
+design notes):
+  * rotation: per 128-block, x~ = 2^-3.5 * H_128 * diag(sigma) * x, with H in
+    Sylvester order and sigma the random signs of the input site;
+  * a block is 128 consecutive rotated weights of one row = 32 groups of 4,
+    with one fp16 scale (u16 bits); the trellis state is 0 at each block start;
+  * state s in 0..7 is the three most recent branch bits, s' = ((s<<1)|u) & 7,
+    u = bit 0 of the code byte;
+  * z0(s) = bit 1 of s picks the value set A0 = {-7,-3,1,5} or
+    A1 = {-5,-1,3,7} (units of the scale) for all four weights of the group;
+    z1 = u ^ bit0(s) ^ bit2(s) picks the parity coset;
+  * byte bits 1..3 are b0..b2, b3 = z1 ^ b0 ^ b1 ^ b2, bits 4..7 are e0..e3,
+    p_j = 2 e_j + b_j and level_j = 4 p_j + 2 z0 - 7; weight = scale * level.
+Products are plain fp64 sums.  The encoder is a Viterbi search for the
+minimum-squared-error code sequence (LDLQ with an identity Hessian), with
+fixed tie-breaks so that its output is unique.
+
+Parity pins: every function here is checked in tests/test_oracle_*.py against
+something other than itself (worked examples derived by hand, closed forms,
+brute force on tiny inputs, invariants).  The one part the pages cannot pin
+is coding quality (MSE); that is "parity unpinned" and only reported.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 128          # weights per scale block and per Hadamard block
+GROUP = 4            # weights per trellis group (one code byte)
+GROUPS_PER_BLOCK = BLOCK // GROUP
+SCALE_C = 0.29       # encoder scale rule: s = fp16(c * rms(block))
+FP16_MAX = 65504.0
+
+
+# ---------------------------------------------------------------- rotation
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """H[i, j] = (-1)^popcount(i & j), the Sylvester-ordered Hadamard matrix.
+
+    Written entry by entry from its definition (no recursion, no FWHT)."""
+    idx = np.arange(n)
+    andm = idx[:, None] & idx[None, :]
+    pop = np.zeros_like(andm)
+    for bit in range(int(n).bit_length()):
+        pop += (andm >> bit) & 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
+def signs_from_bits(sign_bits: np.ndarray, k: int) -> np.ndarray:
+    """sigma_k = -1 where bit (k & 7) of byte (k >> 3) is set, else +1."""
+    sign_bits = np.asarray(sign_bits, dtype=np.uint8)
+    kk = np.arange(k)
+    bits = (sign_bits[kk >> 3] >> (kk & 7)) & 1
+    return np.where(bits == 1, -1.0, 1.0)
+
+
+def rotation_block_matrix(sigma_block: np.ndarray) -> np.ndarray:
+    """R_b = 2^-3.5 * H_128 * diag(sigma_b) for one 128-block ([P1] random
+    Hadamard rotation; the normalisation makes R_b orthogonal)."""
+    h = sylvester_hadamard(BLOCK)
+    return (2.0 ** -3.5) * h * np.asarray(sigma_block, dtype=np.float64)[None, :]
+
+
+def rotate(x: np.ndarray, sign_bits: np.ndarray) -> np.ndarray:
+    """Apply the blockwise random-sign Hadamard rotation to the last axis.
+
+    Used both for activations (x~ = R x) and for weight rows (w~_n = R w_n,
+    i.e. W~ = W R^T), so that W~ x~ = W x.  Explicit 128x128 products in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    k = x.shape[-1]
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    sigma = signs_from_bits(sign_bits, k)
+    out = np.empty_like(x)
+    for b in range(k // BLOCK):
+        rb = rotation_block_matrix(sigma[b * BLOCK:(b + 1) * BLOCK])
+        out[..., b * BLOCK:(b + 1) * BLOCK] = x[..., b * BLOCK:(b + 1) * BLOCK] @ rb.T
+    return out
+
+
+# ------------------------------------------------------------ fp16 helpers
+def fp16_rne(x) -> np.ndarray:
+    """Round to IEEE binary16, round-to-nearest-even, back to fp64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def fp16_bits_to_float(u16: np.ndarray) -> np.ndarray:
+    return np.asarray(u16, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def float_to_fp16_bits(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def bf16_rne_bits(x) -> np.ndarray:
+    """fp32 -> bf16 bits with round-to-nearest-even (finite inputs)."""
+    f = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (f + 0x7FFF + ((f >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_float(u16: np.ndarray) -> np.ndarray:
+    return (np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------- the trellis
+def next_state(s: int, u: int) -> int:
+    """State = last three branch bits ([P1-name]: 8 states over 3-symbol
+    patterns); the newest bit enters at bit 0."""
+    return ((s << 1) | u) & 7
+
+
+def z0_of_state(s: int) -> int:
+    """Value set selected by the carried state ([P1]): A_{z0}."""
+    return (s >> 1) & 1
+
+
+def z1_of_branch(s: int, u: int) -> int:
+    """Parity coset of the branch: z1 = u ^ bit0(s) ^ bit2(s)."""
+    return u ^ (s & 1) ^ ((s >> 2) & 1)
+
+
+def decode_group(byte: int, s: int) -> list[int]:
+    """Four integer levels (units of the block scale) of one code byte read
+    in state s."""
+    u = byte & 1
+    z0 = z0_of_state(s)
+    z1 = z1_of_branch(s, u)
+    b = [(byte >> 1) & 1, (byte >> 2) & 1, (byte >> 3) & 1]
+    b.append(z1 ^ b[0] ^ b[1] ^ b[2])
+    levels = []
+    for j in range(4):
+        e = (byte >> (4 + j)) & 1
+        p = 2 * e + b[j]
+        levels.append(4 * p + 2 * z0 - 7)
+    return levels
+
+
+def decode_block_levels(codes) -> list[int]:
+    """Walk the trellis over one block's code bytes from state 0 and return
+    all levels, group after group (scalar, serial: the definition)."""
+    s = 0
+    out: list[int] = []
+    for byte in codes:
+        byte = int(byte)
+        out.extend(decode_group(byte, s))
+        s = next_state(s, byte & 1)
+    return out
+
+
+def codebook_table() -> np.ndarray:
+    """T[s][byte] = the four levels of `byte` read in state s (int8)."""
+    t = np.zeros((8, 256, 4), dtype=np.int8)
+    for s in range(8):
+        for byte in range(256):
+            t[s, byte] = decode_group(byte, s)
+    return t
+
+
+def decode_levels(codes: np.ndarray) -> np.ndarray:
+    """Vectorised form of decode_block_levels for codes [..., K/4] (uint8).
+
+    Pinned against the scalar walk in the tests.  Returns int8 [..., K]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lead = c.shape[:-1]
+    g = c.shape[-1]
+    if g % GROUPS_PER_BLOCK:
+        raise ValueError("K/4 must be a multiple of 32")
+    c = c.reshape(lead + (g // GROUPS_PER_BLOCK, GROUPS_PER_BLOCK)).astype(np.int32)
+    u = c & 1
+
+    def prev(a, d):
+        out = np.zeros_like(a)
+        out[..., d:] = a[..., :-d]
+        return out
+
+    u1, u2, u3 = prev(u, 1), prev(u, 2), prev(u, 3)
+    z0 = u2
+    z1 = u ^ u1 ^ u3
+    b0, b1, b2 = (c >> 1) & 1, (c >> 2) & 1, (c >> 3) & 1
+    b3 = z1 ^ b0 ^ b1 ^ b2
+    bs = [b0, b1, b2, b3]
+    lv = np.empty(c.shape + (4,), dtype=np.int8)
+    for j in range(4):
+        e = (c >> (4 + j)) & 1
+        lv[..., j] = 4 * (2 * e + bs[j]) + 2 * z0 - 7
+    return lv.reshape(lead + (g * 4,))
+
+
+def decode_weights(codes: np.ndarray, scales_u16: np.ndarray) -> np.ndarray:
+    """Rotated-domain weights s * level as fp64 [..., K] (each value is exact
+    in fp32 as well: an 11-bit scale times |level| <= 7)."""
+    lv = decode_levels(codes).astype(np.float64)
+    s = fp16_bits_to_float(scales_u16)
+    k = lv.shape[-1]
+    return (lv.reshape(lv.shape[:-1] + (k // BLOCK, BLOCK)) * s[..., None]).reshape(lv.shape)
+
+
+def levels_trellis_valid(levels: np.ndarray) -> bool:
+    """Check that a level sequence (one block, 4*G values) is a trellis path:
+    recover (z0, z1) of each group from its point, rebuild the branch bits and
+    require the value set of every group to be the one its state allows."""
+    lv = np.asarray(levels, dtype=np.int64).reshape(-1, 4)
+    if not np.all(np.isin(lv, [-7, -5, -3, -1, 1, 3, 5, 7])):
+        return False
+    u_hist: list[int] = []
+    for grp in lv:
+        z0 = int(((grp[0] + 7) // 2) % 2)
+        if not all(((v + 7) // 2) % 2 == z0 for v in grp):
+            return False            # all four weights must share one value set
+        p = (grp + 7 - 2 * z0) // 4
+        z1 = int(np.sum(p % 2) % 2)
+        um1 = u_hist[-1] if len(u_hist) >= 1 else 0
+        um2 = u_hist[-2] if len(u_hist) >= 2 else 0
+        um3 = u_hist[-3] if len(u_hist) >= 3 else 0
+        if z0 != um2:
+            return False
+        u_hist.append(z1 ^ um1 ^ um3)
+    return True
+
+
+# ----------------------------------------------------------- scale rule
+def block_scale_bits(w_rot_blocks: np.ndarray, c: float = SCALE_C) -> np.ndarray:
+    """fp16 scale per block: s = fp16_RNE(min(c * rms, 65504)); 0 if rms is 0.
+
+    The sum of squares runs sequentially over the 128 entries (a fixed order,
+    so that every implementation of the rule rounds the same value)."""
+    w = np.asarray(w_rot_blocks, dtype=np.float64)
+    acc = np.zeros(w.shape[:-1], dtype=np.float64)
+    for j in range(w.shape[-1]):
+        acc = acc + w[..., j] * w[..., j]
+    rms = np.sqrt(acc / w.shape[-1])
+    val = np.minimum(c * rms, FP16_MAX)
+    return float_to_fp16_bits(val)
+
+
+# ------------------------------------------------------- Viterbi encoder
+def _point_tables():
+    """For each (z0, z1): the 128 bytes of that coset in increasing order and
+    their 4-D level points.  The byte <-> point map of a state depends only
+    on (z0, z1), so states sharing them share the table."""
+    tabs = {}
+    for z0 in (0, 1):
+        for z1 in (0, 1):
+            # any state with these (z0, z1) for branch u: pick s with
+            # bit1 = z0, and u chosen so that z1 matches with bit0 = bit2 = 0
+            s = z0 << 1
+            u = z1
+            bytes_ = np.array([b for b in range(256) if (b & 1) == u], dtype=np.int64)
+            pts = np.array([decode_group(int(b), s) for b in bytes_], dtype=np.float64)
+            tabs[(z0, z1)] = (bytes_, pts)
+    return tabs
+
+
+_TABS = None
+
+
+def _tabs():
+    global _TABS
+    if _TABS is None:
+        _TABS = _point_tables()
+    return _TABS
+
+
+def branch_metrics(w_groups: np.ndarray, s_val: np.ndarray):
+    """Distortion of the nearest point of every coset for every group.
+
+    w_groups [nb, G, 4] fp64, s_val [nb].  Returns dict (z0, z1) ->
+    (metric [nb, G], byte [nb, G]).  Brute force over all 128 points of the
+    coset, each distortion evaluated as ((d0^2 + d1^2) + d2^2) + d3^2 with
+    d_j = w_j - s * level_j; the smallest byte wins ties (first minimum in
+    ascending byte order)."""
+    out = {}
+    for key, (bytes_, pts) in _tabs().items():
+        # pts [128, 4] in ascending byte order; distortion per point
+        d = w_groups[:, :, None, :] - s_val[:, None, None, None] * pts[None, None, :, :]
+        sq = d * d
+        m = ((sq[..., 0] + sq[..., 1]) + sq[..., 2]) + sq[..., 3]     # [nb, G, 128]
+        arg = np.argmin(m, axis=2)                                    # first minimum
+        best = np.take_along_axis(m, arg[..., None], axis=2)[..., 0]
+        out[key] = (best, bytes_[arg])
+    return out
+
+
+def viterbi_encode(w_rot: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Minimum-squared-error trellis path for each block.
+
+    w_rot [nb, 4G] fp64 rotated weights, scale_bits [nb] u16.  G is free (32
+    for real blocks; tests use short blocks).  Start in state 0, free end
+    state.  Tie-breaks (strict < in ascending order): predecessor s'>>1 over
+    (s'>>1)|4, smaller byte among equally near points, smaller end state.
+    A zero scale codes every group as byte 0."""
+    w = np.asarray(w_rot, dtype=np.float64)
+    nb = w.shape[0]
+    g = w.shape[1] // 4
+    wg = w.reshape(nb, g, 4)
+    s_val = fp16_bits_to_float(scale_bits)
+    bm = branch_metrics(wg, s_val)
+    inf = np.inf
+    metric = np.full((nb, 8), inf)
+    metric[:, 0] = 0.0
+    back_prev = np.zeros((nb, g, 8), dtype=np.int8)     # predecessor state
+    back_byte = np.zeros((nb, g, 8), dtype=np.int16)    # byte on that branch
+    for t in range(g):
+        new = np.full((nb, 8), inf)
+        for sn in range(8):
+            u = sn & 1
+            for cand in (sn >> 1, (sn >> 1) | 4):
+                key = (z0_of_state(cand), z1_of_branch(cand, u))
+                m_b, byte_b = bm[key]
+                tot = metric[:, cand] + m_b[:, t]
+                better = tot < new[:, sn]
+                new[:, sn] = np.where(better, tot, new[:, sn])
+                back_prev[:, t, sn] = np.where(better, cand, back_prev[:, t, sn])
+                # the coset table's bytes carry bit 0 = z1; on this branch the
+                # byte's bit 0 is the branch bit u (bits 1..7 pick the point)
+                byte_u = (byte_b[:, t] & 0xFE) | u
+                back_byte[:, t, sn] = np.where(better, byte_u, back_byte[:, t, sn])
+        metric = new
+    end = np.argmin(metric, axis=1)        # first minimum = smaller state on ties
+    codes = np.zeros((nb, g), dtype=np.uint8)
+    st = end.copy()
+    rows = np.arange(nb)
+    for t in range(g - 1, -1, -1):
+        codes[:, t] = back_byte[rows, t, st].astype(np.uint8)
+        st = back_prev[rows, t, st].astype(np.int64)
+    codes[s_val == 0] = 0
+    return codes
+
+
+def block_distortion(w_rot: np.ndarray, codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Squared error of each block's decoded path (fp64)."""
+    lv = np.stack([np.array(decode_block_levels(c), dtype=np.float64) for c in codes])
+    s = fp16_bits_to_float(scale_bits)[:, None]
+    d = np.asarray(w_rot, dtype=np.float64) - s * lv
+    return np.sum(d * d, axis=1)
+
+
+def exhaustive_encode_bytes(w_rot_row: np.ndarray, scale_bits: int):
+    """All 256^G byte strings of a short block (G <= 3), each decoded through
+    the state table (state = last three branch bits, 0 at the start).
+    Returns (min distortion, first minimising string in lexicographic order,
+    group 0 most significant)."""
+    w = np.asarray(w_rot_row, dtype=np.float64)
+    g = len(w) // 4
+    if g > 3:
+        raise ValueError("exhaustive byte search is for G <= 3")
+    s = float(fp16_bits_to_float(np.array([scale_bits]))[0])
+    table = codebook_table().astype(np.float64)           # [8, 256, 4]
+    tail = g - 1
+    rest = np.arange(256 ** tail, dtype=np.int64)
+    rest_bytes = [(rest >> (8 * (tail - 1 - t))) & 0xFF for t in range(tail)]
+    best, best_codes = np.inf, None
+    for b0 in range(256):                                  # lexicographic order
+        bytes_ = [np.full(rest.shape, b0, dtype=np.int64)] + rest_bytes
+        st = np.zeros(rest.shape, dtype=np.int64)
+        acc = np.zeros(rest.shape)
+        for t in range(g):
+            lv = table[st, bytes_[t]]                      # [n, 4]
+            d = w[4 * t:4 * t + 4][None, :] - s * lv
+            sq = d * d
+            acc = acc + (((sq[:, 0] + sq[:, 1]) + sq[:, 2]) + sq[:, 3])
+            st = ((st << 1) | (bytes_[t] & 1)) & 7
+        i = int(np.argmin(acc))
+        if acc[i] < best:
+            best = float(acc[i])
+            best_codes = [int(bytes_[t][i]) for t in range(g)]
+    return best, best_codes
+
+
+def exhaustive_encode_paths(w_rot_row: np.ndarray, scale_bits: int) -> float:
+    """Minimum distortion over all 2^G branch paths, each group taking the
+    nearest point of its coset by brute force (G <= 12)."""
+    w = np.asarray(w_rot_row, dtype=np.float64)
+    g = len(w) // 4
+    s = float(fp16_bits_to_float(np.array([scale_bits]))[0])
+    tabs = _tabs()
+    # nearest-point distortion per group per coset
+    near = {}
+    for key, (_, pts) in tabs.items():
+        d = w.reshape(g, 1, 4) - s * pts[None, :, :]
+        near[key] = np.min(np.sum(d * d, axis=2), axis=1)
+    best = np.inf
+    for path in range(1 << g):
+        st = 0
+        acc = 0.0
+        for t in range(g):
+            u = (path >> t) & 1
+            acc += near[(z0_of_state(st), z1_of_branch(st, u))][t]
+            st = next_state(st, u)
+        best = min(best, acc)
+    return best
+
+
+_CLIB = None
+
+
+def _c_lib():
+    """The oracle's plain-C twin of viterbi_encode (oracle/viterbi_ref.c)."""
+    global _CLIB
+    if _CLIB is None:
+        import ctypes
+        import os
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboracle_p8f.so")
+        if not os.path.exists(path):
+            from . import build_oracle
+            build_oracle.build()
+        lib = ctypes.CDLL(path)
+        lib.p8f_oracle_viterbi.restype = ctypes.c_int
+        lib.p8f_oracle_viterbi.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int, ctypes.c_void_p]
+        _CLIB = lib
+    return _CLIB
+
+
+def viterbi_encode_c(w_rot: np.ndarray, scale_bits: np.ndarray, threads: int = 0) -> np.ndarray:
+    """Same search as viterbi_encode, run by the C twin (bit-identical
+    metrics: same brute force, same evaluation order, no fused multiply-add).
+    Blocks are split over `threads` Python threads (ctypes drops the GIL)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    w = np.ascontiguousarray(w_rot, dtype=np.float64)
+    sb = np.ascontiguousarray(scale_bits, dtype=np.uint16)
+    nb, g4 = w.shape
+    g = g4 // 4
+    codes = np.zeros((nb, g), dtype=np.uint8)
+    lib = _c_lib()
+    nt = threads or min(16, os.cpu_count() or 1)
+    bounds = np.linspace(0, nb, nt + 1).astype(np.int64)
+
+    def run(i):
+        a, b = int(bounds[i]), int(bounds[i + 1])
+        if b > a:
+            rc = lib.p8f_oracle_viterbi(w[a:b].ctypes.data, sb[a:b].ctypes.data, b - a, g,
+                                        codes[a:b].ctypes.data)
+            if rc != 0:
+                raise RuntimeError("oracle viterbi failed")
+
+    with ThreadPoolExecutor(nt) as ex:
+        list(ex.map(run, range(nt)))
+    return codes
+
+
+def encode_matrix(w: np.ndarray, sign_bits: np.ndarray, c: float = SCALE_C,
+                  chunk_blocks: int = 2048, use_c: bool = True):
+    """Offline compression of W [N][K] (fp32 values, original domain):
+    rotate each row, set each block's fp16 scale, Viterbi-encode.
+    Returns codes u8 [N][K/4] and scale bits u16 [N][K/128]."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    n, k = w.shape
+    nbk = k // BLOCK
+    codes = np.empty((n, k // 4), dtype=np.uint8)
+    scales = np.empty((n, nbk), dtype=np.uint16)
+    if use_c:
+        chunk_blocks = max(chunk_blocks, 65536)
+    rows_per_chunk = max(1, chunk_blocks // nbk)
+    for r0 in range(0, n, rows_per_chunk):
+        r1 = min(n, r0 + rows_per_chunk)
+        wr = rotate(w[r0:r1], sign_bits).reshape(-1, BLOCK)
+        sb = block_scale_bits(wr, c)
+        cb = viterbi_encode_c(wr, sb) if use_c else viterbi_encode(wr, sb)
+        codes[r0:r1] = cb.reshape(r1 - r0, k // 4)
+        scales[r0:r1] = sb.reshape(r1 - r0, nbk)
+    return codes, scales
+
+
+# -------------------------------------------------------------- products
+def gemv_ref(codes: np.ndarray, scales_u16: np.ndarray, x_rot: np.ndarray) -> np.ndarray:
+    """y[b][n] = sum_blk s[n][blk] * sum_{k in blk} level[n][k] * x~[b][k], fp64.
+
+    x_rot [B][K] (any float dtype; taken exactly).  Returns fp64 [B][N]."""
+    lv = decode_levels(codes).astype(np.float64)              # [N, K]
+    n, k = lv.shape
+    x = np.asarray(x_rot, dtype=np.float64).reshape(-1, k)
+    s = fp16_bits_to_float(scales_u16)                          # [N, nb]
+    part = np.einsum("nbk,mbk->mnb", lv.reshape(n, k // BLOCK, BLOCK),
+                     x.reshape(x.shape[0], k // BLOCK, BLOCK))  # per-block dots
+    return np.einsum("mnb,nb->mn", part, s)
+
+
+def gemm_ref(codes, scales_u16, x_rot):
+    """Same product for M activation rows (prompt processing): Y [M][N]."""
+    return gemv_ref(codes, scales_u16, x_rot)
+
+
+def gemv_rows_ref(codes_rows, scales_rows, x_rot):
+    """gemv_ref restricted to selected rows (for sampled checks at full size)."""
+    return gemv_ref(codes_rows, scales_rows, x_rot)
+
+
+# ------------------------------------------------------- activation chain
+def rmsnorm16(v: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """fp16_RNE(v / sqrt(mean(v^2) + eps)) over the last axis (fp64 math).
+
+    The normalisation that keeps activations in fp16 range between the
+    layers of a synthetic linear stack (the pages' decoder layers feed each
+    matrix's output onward; norm layers sit between them)."""
+    v = np.asarray(v, dtype=np.float64)
+    r = np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+    return fp16_rne(v / r)
