@@ -1,0 +1,163 @@
+"""Benchmark of the Pingala-8 hot path on one MI355X.
+
+Default workload: the 36-layer Qwen3-4B-shaped linear stack at batch 1
+(uniform random trellis bitstreams, fp16 U(0.005, 0.05) scales, fp16 N(0,1)
+input fed layer to layer; 965,099,520 coded bytes per token).  One step is
+one token through the whole stack: per layer four activation rotations
+(three with the fused RMS normalisation) and four qgemv launches (qkv and
+gate/up merged).  Inputs are resident in HBM before timing starts.
+
+Printed: one JSON line with the whole-job compressed-weight GB/s
+(bytes per token x tokens per second), tokens per second, the qgemv
+kernel-sum roofline (HIP events around every qgemv launch of a separate
+pass over the same tokens) and the oracle's CPU throughput on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "qgemv compressed-weight GB/s (% HBM peak) + linear-stack tok/s at batch 1"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(seconds: float = 12.0):
+    """The oracle (numpy fp64 decode + product), as it stands, on a bounded
+    sample of the stack: layer-0 launch groups of the Qwen3-4B-shaped stack,
+    repeated until `seconds` have passed.  numpy runs these ops on one
+    thread."""
+    import numpy as np
+
+    from oracle import p8f
+    from qgemv_amd import synth
+
+    merged = synth.random_layer_merged(0, synth.qwen3_4b_shapes())
+    x = {s: synth.activations_f32(1, merged[s][0].shape[1] * 4) for s in merged}
+    done_bytes, t0, mats = 0, time.perf_counter(), 0
+    while True:
+        for site in ("o", "qkv", "down", "gu"):
+            codes, scales = merged[site]
+            p8f.gemv_ref(codes, scales, x[site])
+            done_bytes += codes.nbytes + scales.nbytes
+            mats += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{mats} launch-group products of layer 0 (decode + fp64 GEMV, batch 1) in {dt:.1f} s; "
+                      f"{done_bytes} coded bytes"}
+
+
+def run_stack(args):
+    import torch
+
+    import qgemv_amd as q
+    from qgemv_amd import synth
+    from qgemv_amd.stack import ORDER, Stack
+
+    shapes = synth.qwen3_4b_shapes() if args.workload == "qwen36" else synth.llama31_8b_shapes()
+    layers = 36 if args.workload == "qwen36" else 32
+    log(f"building {args.workload}: {layers} layers")
+    st = Stack(shapes, layers, batch=1, x_dtype=q.PG_F32)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        st.token()
+    torch.cuda.synchronize()
+    log("warmup done")
+    # timed region: exactly `steps` tokens
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        st.token()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_tok = max(gpu_ms, wall * 1e3) / args.steps
+    log(f"timed {args.steps} tokens: {gpu_ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
+
+    # qgemv kernel durations: events around every qgemv launch of a second pass
+    qg_ms, qg_bytes, launches = 0.0, 0, 0
+    evs = []
+    for _ in range(args.steps):
+        for layer in range(layers):
+            for site in ORDER:
+                n, k = st.shapes[site]
+                src = st.h0 if (site == "qkv" and layer == 0) else st.out["down" if site == "qkv" else
+                                                                          {"o": "qkv", "gu": "o", "down": "gu"}[site]]
+                dt_in = q.PG_F16 if (site == "qkv" and layer == 0) else q.PG_F32
+                flags = 0 if (site == "qkv" and layer == 0) else q.PG_FLAG_RMSNORM
+                q.pg_fwht_rotate(src, dt_in, st.xrot, st.x_dtype, st.signs[layer][site], 1, k, flags)
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                q.pg_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.xrot, st.x_dtype, 1,
+                           st.out[site])
+                b.record(stream)
+                evs.append((a, b))
+                qg_bytes += st.codes[layer][site].numel() + 2 * st.scales[layer][site].numel()
+                launches += 1
+    torch.cuda.synchronize()
+    for a, b in evs:
+        qg_ms += a.elapsed_time(b)
+    achieved = qg_bytes / (qg_ms * 1e-3) / 1e9
+    tok_s = 1e3 / ms_per_tok
+    value = st.bytes_per_token * tok_s / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_tok, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{'Qwen3-4B' if args.workload == 'qwen36' else 'Llama-3.1-8B'}-shaped "
+                               f"{layers}-layer linear stack, batch 1, random trellis bitstreams",
+                   "layers": layers, "batch": 1, "bytes_per_token": st.bytes_per_token,
+                   "tok_per_s": round(tok_s, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "hip_graphs": False, "launches_per_token": 8 * layers},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "qgemv", "launches": launches, "avg_launch_us": round(1e3 * qg_ms / launches, 3)},
+    }
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen36", choices=["qwen36", "llama32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "
+              "(see the sharding notes in the design document); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    res = run_stack(args)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

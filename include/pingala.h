@@ -1,0 +1,158 @@
+/* libpingala: Pingala-8 trellis-coded 2-bit weights on AMD Instinct MI355X
+ * (gfx950).  C ABI; every call returns an int status.
+ *
+ * What the method is (the pages describe it in words only):
+ *   - "Pingala-8" landing page, section "How it works": an Ungerboeck 8-state
+ *     trellis code encodes groups of 4 weights in order; a small state carried
+ *     from one group to the next picks the value set the next group can use;
+ *     before coding, a random Hadamard rotation spreads out the few very large
+ *     weights; LDLQ rounding is used by the compressor.
+ *   - same page, section "Where the name comes from": 8 states over short
+ *     three-symbol patterns, trellis labels after Ungerboeck.
+ *   - same page, section "Paper": the paper title calls it small-state coset
+ *     trellis coding.
+ *   - article "8 open models, 77-85% smaller: what 2-bit quantization costs
+ *     and what it keeps", section "What 2-bit keeps": files keep per-block
+ *     scales; one-user generation is mostly reading every weight once per
+ *     token.
+ *
+ * Format P8F v1 (the pages give no bit layout; these are the plainest
+ * choices they support):
+ *   codes   u8 [n][k/4], row-major, one byte per group of 4 weights.
+ *   scales  u16 [n][k/128], row-major, IEEE binary16 bits, one per block of
+ *           128 weights (32 code bytes) of a row.  k % 128 == 0.
+ *   state   s in 0..7 = the last three branch bits; s = 0 at every block
+ *           start; after byte c: s = ((s << 1) | (c & 1)) & 7.
+ *   decode  of byte c read in state s:
+ *             z0 = (s >> 1) & 1                  value set A0 = {-7,-3,1,5},
+ *                                                 A1 = {-5,-1,3,7}
+ *             z1 = (c & 1) ^ (s & 1) ^ (s >> 2)   parity coset
+ *             b_j = bit (1+j) of c for j < 3;  b_3 = z1 ^ b_0 ^ b_1 ^ b_2
+ *             e_j = bit (4+j) of c
+ *             level_j = 4 * (2 e_j + b_j) + 2 z0 - 7      (odd, -7..7)
+ *             weight_j = scale * level_j   (rotated domain; exact in fp32)
+ *   rotation per 128-block b of the input dimension:
+ *             (R v)_i = 2^-3.5 * sum_j (-1)^popcount(i & j) sigma_j v_j
+ *           sigma = the input site's random signs, sign_bits u8 [k/8], bit
+ *           (k & 7) of byte (k >> 3), 1 meaning -1.  Rows of W are stored
+ *           rotated (w~ = R w); activations are rotated at run time (x~ = R x)
+ *           so that W~ x~ = W x.
+ *   footprint: n*k/4 + 2*n*k/128 bytes = 2.125 bits per weight.
+ *
+ * Conventions.
+ *   - Device pointers are device memory (e.g. torch tensors' data_ptr());
+ *     host pointers are ordinary host memory.  All buffers are caller-owned;
+ *     no call allocates, keeps or frees a caller buffer.
+ *   - Device calls are asynchronous on the caller's hipStream_t (0 = the null
+ *     stream) and validate all arguments on the host before any launch; on an
+ *     invalid argument nothing is launched.  pg_encode_ref is synchronous.
+ *   - codes, x, y and w pointers must be 16-byte aligned; scales and
+ *     sign_bits 2-byte and 1-byte aligned.
+ *   - Errors: PG_OK = 0; negative codes below.  pg_last_error() returns a
+ *     per-thread message for the last failing call of that thread.
+ *   - Results of pg_decode are bit-exact; products accumulate in fp32.
+ */
+#ifndef PINGALA_H
+#define PINGALA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* pg_stream_t; /* a hipStream_t */
+
+enum {
+    PG_OK = 0,
+    PG_ERR_INVALID_ARG = -1,  /* bad size, null or misaligned pointer, bad dtype */
+    PG_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
+    PG_ERR_HIP = -3           /* a HIP runtime call or launch failed */
+};
+
+enum { PG_F32 = 0, PG_F16 = 1, PG_BF16 = 2 };   /* element types of x / y */
+
+enum { PG_FLAG_RMSNORM = 1u };                   /* pg_fwht_rotate flags */
+
+#define PG_FORMAT_VERSION 1
+#define PG_LIB_VERSION 1
+
+/* (format_version << 16) | lib_version. */
+int pg_version(void);
+
+/* Bytes of codes + scales for an n x k matrix: n*k/4 + n*(k/128)*2.
+ * Returns 0 if n < 1 or k is not a positive multiple of 128. */
+size_t pg_footprint_bytes(int64_t n, int64_t k);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* pg_last_error(void);
+
+/* Test hook: the decode table the kernels use, out[s][c][j] = level_j of
+ * byte c read in state s (int8 [8][256][4], host memory). */
+int pg_codebook_table(int8_t* out);
+
+/* Host (CPU) reference encoder, synchronous.  Follows the "How it works"
+ * description (rotation, then sequential trellis coding; the LDLQ Hessian is
+ * the identity, i.e. plain minimum squared error):
+ *   w          host fp32 [n][k], original (unrotated) weights
+ *   sign_bits  host u8 [k/8], the input site's random signs
+ *   codes      host u8 [n][k/4] out
+ *   scales     host u16 [n][k/128] out (fp16 bits)
+ *   n_threads  worker threads (<= 0: hardware concurrency)
+ * Per row: rotate each 128-block in fp64; scale = fp16_RNE(min(0.29 * rms,
+ * 65504)) with the squares summed in index order (0 if the block is zero);
+ * Viterbi over the 32 groups from state 0 with a free end state, the branch
+ * metric being the nearest of the 128 points of the branch's coset
+ * (distortion ((d0^2 + d1^2) + d2^2) + d3^2); ties go to the predecessor
+ * s'>>1, then the smaller byte, then the smaller end state; a zero scale
+ * codes every group as byte 0. */
+int pg_encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits,
+                  uint8_t* codes, uint16_t* scales, int n_threads);
+
+/* Decode to rotated-domain fp32 weights (bit-exact: scale * level in fp32).
+ *   codes device u8 [n][k/4], scales device u16 [n][k/128],
+ *   w_rot device f32 [n][k] out. */
+int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+              float* w_rot, pg_stream_t stream);
+
+/* Run-time activation rotation ("How it works": the random Hadamard
+ * rotation; the activations take the same rotation as the weight rows):
+ *   x        device [rows][k] of in_dtype (PG_F32 / PG_F16 / PG_BF16)
+ *   y        device [rows][k] of out_dtype (PG_F32 / PG_F16 / PG_BF16)
+ *   sign_bits device u8 [k/8]
+ *   flags    PG_FLAG_RMSNORM: first replace each row v by
+ *            fp16_RNE(v / sqrt(mean(v^2) + 1e-6)) (fp32 math), as the
+ *            normalisation between the layers of a linear stack.
+ * x and y may not overlap.  fp32 arithmetic; fp16/bf16 outputs round to
+ * nearest even. */
+int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype,
+                   const uint8_t* sign_bits, int64_t rows, int64_t k, uint32_t flags,
+                   pg_stream_t stream);
+
+/* Batch-1..8 product over the compressed weights (the generation path,
+ * article "8 open models...", section "What 2-bit keeps": one pass over all
+ * weights per token):
+ *   y[b][i] = sum_blk scale[i][blk] * sum_{k in blk} level[i][k] * x_rot[b][k]
+ *   codes device u8 [n][k/4], scales device u16 [n][k/128]
+ *   x_rot device [batch][k], PG_F32 or PG_F16, already rotated
+ *   batch 1..8, y device f32 [batch][n] out.
+ * fp32 accumulation; summation order is fixed, so repeated calls are
+ * bitwise identical. */
+int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+             const void* x_rot, int x_dtype, int batch, float* y, pg_stream_t stream);
+
+/* Prompt-processing product for m activation rows (landing page, section
+ * "Results": prompt reading is the mat-mat path):
+ *   Y[r][i] = sum_blk scale[i][blk] * sum_{k in blk} level[i][k] * X[r][k]
+ *   x_rot_bf16 device u16 [m][k] (bf16 bits, already rotated), y device f32
+ *   [m][n] out.  Levels enter the matrix cores as exact bf16 values; each
+ *   128-block's partial product is scaled in fp32. */
+int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+             const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PINGALA_H */

@@ -1,0 +1,123 @@
+// The C ABI of libpingala (declared in include/pingala.h): argument
+// validation on the host, then dispatch to the HIP launchers.  No call
+// launches anything when an argument is invalid.
+#include <cstdint>
+
+#include "pg_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_nk(int64_t n, int64_t k) {
+    if (n < 1) return pg::fail(PG_ERR_INVALID_ARG, "n must be >= 1 (got %lld)", (long long)n);
+    if (k < 128 || k % 128 != 0)
+        return pg::fail(PG_ERR_INVALID_ARG, "k must be a positive multiple of 128 (got %lld)", (long long)k);
+    // device kernels index rows and columns with 32-bit offsets per row
+    if (k > (int64_t)1 << 24 || n > (int64_t)1 << 30)
+        return pg::fail(PG_ERR_UNSUPPORTED, "n or k too large (n=%lld k=%lld)", (long long)n, (long long)k);
+    return PG_OK;
+}
+
+int check_ptr(const void* p, uintptr_t align, const char* name) {
+    if (!p) return pg::fail(PG_ERR_INVALID_ARG, "%s is null", name);
+    if (!aligned(p, align)) return pg::fail(PG_ERR_INVALID_ARG, "%s is not %u-byte aligned", name, (unsigned)align);
+    return PG_OK;
+}
+
+int check_dtype(int dt, const char* name, bool allow_bf16) {
+    if (dt == PG_F32 || dt == PG_F16 || (allow_bf16 && dt == PG_BF16)) return PG_OK;
+    return pg::fail(PG_ERR_INVALID_ARG, "%s: unsupported dtype %d", name, dt);
+}
+
+}  // namespace
+
+#define PG_TRY(expr)                 \
+    do {                             \
+        int _rc = (expr);            \
+        if (_rc != PG_OK) return _rc; \
+    } while (0)
+
+extern "C" {
+
+int pg_version(void) { return (PG_FORMAT_VERSION << 16) | PG_LIB_VERSION; }
+
+size_t pg_footprint_bytes(int64_t n, int64_t k) {
+    if (n < 1 || k < 128 || k % 128 != 0) return 0;
+    return (size_t)(n * (k / 4) + n * (k / 128) * 2);
+}
+
+const char* pg_last_error(void) { return pg::last_error(); }
+
+int pg_codebook_table(int8_t* out) {
+    pg::clear_error();
+    PG_TRY(check_ptr(out, 1, "out"));
+    pg::build_codebook(out);
+    return PG_OK;
+}
+
+int pg_encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
+                  uint16_t* scales, int n_threads) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    PG_TRY(check_ptr(w, 4, "w"));
+    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    PG_TRY(check_ptr(codes, 1, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    return pg::encode_ref(w, n, k, sign_bits, codes, scales, n_threads);
+}
+
+int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w_rot,
+              pg_stream_t stream) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    PG_TRY(check_ptr(w_rot, 16, "w_rot"));
+    return pg::launch_decode(codes, scales, n, k, w_rot, stream);
+}
+
+int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype, const uint8_t* sign_bits,
+                   int64_t rows, int64_t k, uint32_t flags, pg_stream_t stream) {
+    pg::clear_error();
+    if (rows < 1) return pg::fail(PG_ERR_INVALID_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
+    PG_TRY(check_nk(rows, k));
+    PG_TRY(check_dtype(in_dtype, "in_dtype", true));
+    PG_TRY(check_dtype(out_dtype, "out_dtype", true));
+    PG_TRY(check_ptr(x, 16, "x"));
+    PG_TRY(check_ptr(y, 16, "y"));
+    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    if (flags & ~PG_FLAG_RMSNORM) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    const size_t in_b = (size_t)rows * k * (in_dtype == PG_F32 ? 4 : 2);
+    const size_t out_b = (size_t)rows * k * (out_dtype == PG_F32 ? 4 : 2);
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+    if (xa < ya + out_b && ya < xa + in_b) return pg::fail(PG_ERR_INVALID_ARG, "x and y overlap");
+    return pg::launch_fwht(x, in_dtype, y, out_dtype, sign_bits, rows, k, flags, stream);
+}
+
+int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x_rot,
+             int x_dtype, int batch, float* y, pg_stream_t stream) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    if (batch < 1 || batch > 8) return pg::fail(PG_ERR_INVALID_ARG, "batch must be 1..8 (got %d)", batch);
+    PG_TRY(check_dtype(x_dtype, "x_dtype", false));
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    PG_TRY(check_ptr(x_rot, 16, "x_rot"));
+    PG_TRY(check_ptr(y, 16, "y"));
+    return pg::launch_qgemv(codes, scales, n, k, x_rot, x_dtype, batch, y, stream);
+}
+
+int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,
+             int64_t m, float* y, pg_stream_t stream) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    if (m < 1 || m > ((int64_t)1 << 30)) return pg::fail(PG_ERR_INVALID_ARG, "m must be >= 1 (got %lld)", (long long)m);
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    PG_TRY(check_ptr(x_rot_bf16, 16, "x_rot_bf16"));
+    PG_TRY(check_ptr(y, 16, "y"));
+    return pg::launch_qgemm(codes, scales, n, k, x_rot_bf16, m, y, stream);
+}
+
+}  // extern "C"

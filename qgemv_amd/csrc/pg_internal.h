@@ -1,0 +1,35 @@
+// Internal declarations shared by the host C++ and the HIP launchers of
+// libpingala.  Not part of the public C ABI (include/pingala.h).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/pingala.h"
+
+namespace pg {
+
+// error plumbing (pg_host.cpp)
+int fail(int code, const char* fmt, ...);
+void clear_error();
+const char* last_error();
+
+// format helpers (pg_host.cpp)
+void group_levels(int s, int c, int out[4]);
+void build_codebook(int8_t* out /* [8][256][4] */);
+uint16_t double_to_half_rne(double v);
+double half_to_double(uint16_t h);
+int encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
+               uint16_t* scales, int n_threads);
+
+// HIP launchers (pg_kernels.hip); arguments are already validated.
+// Each returns PG_OK or PG_ERR_HIP (message set).
+int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w,
+                  pg_stream_t s);
+int launch_fwht(const void* x, int in_dt, void* y, int out_dt, const uint8_t* sign_bits,
+                int64_t rows, int64_t k, uint32_t flags, pg_stream_t s);
+int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                 const void* x, int x_dt, int batch, float* y, pg_stream_t s);
+int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                 const uint16_t* x, int64_t m, float* y, pg_stream_t s);
+
+}  // namespace pg

@@ -1,0 +1,81 @@
+"""Per-token driver for a synthetic linear stack (Qwen3-4B- or
+Llama-3.1-8B-shaped layers) on one GPU.
+
+Orchestration only: device buffers come from torch, every step is a
+libpingala call (pg_fwht_rotate, pg_qgemv) on one stream.  Per layer, the
+four launch groups that share an input are chained as
+    x~ = R_qkv h        -> [q k v] = W~qkv x~
+    x~ = R_o n16(q)     -> o        = W~o x~
+    x~ = R_gu n16(o)    -> [g u]    = W~gu x~
+    x~ = R_down n16(g)  -> d        = W~down x~ ,   h' = d
+where n16 is the RMS normalisation with fp16 rounding fused into the
+rotation (PG_FLAG_RMSNORM); the first layer's input is fp16 and is not
+normalised.  k, v and u are computed and stored but not consumed.
+"""
+from __future__ import annotations
+
+from . import _lib as L
+from . import synth
+
+ORDER = ("qkv", "o", "gu", "down")
+
+
+class Stack:
+    def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_F32):
+        import torch
+        self.shapes = synth.merged_shapes(shapes)
+        self.raw_shapes = shapes
+        self.layers = layers
+        self.batch = batch
+        self.x_dtype = x_dtype
+        self.codes, self.scales, self.signs = [], [], []
+        self.bytes_per_token = 0
+        for layer in range(layers):
+            merged = synth.random_layer_merged(layer, shapes)
+            c, s, g = {}, {}, {}
+            for t, site in enumerate(ORDER):
+                codes, scales = merged[site]
+                c[site] = torch.from_numpy(codes).to(device)
+                s[site] = torch.from_numpy(scales).to(device)
+                g[site] = torch.from_numpy(synth.site_sign_bits(layer, t, self.shapes[site][1])).to(device)
+                self.bytes_per_token += codes.nbytes + scales.nbytes
+            self.codes.append(c)
+            self.scales.append(s)
+            self.signs.append(g)
+        b = batch
+        kmax = max(k for _, k in self.shapes.values())
+        xt = torch.float32 if x_dtype == L.PG_F32 else torch.float16
+        self.xrot = torch.empty((b, kmax), dtype=xt, device=device)
+        self.out = {site: torch.empty((b, n), dtype=torch.float32, device=device)
+                    for site, (n, _) in self.shapes.items()}
+        h = shapes["q"][1]
+        self.h0 = torch.from_numpy(synth.activations_fp16(b, h)).to(device)
+
+    def token(self, stream=None, h_in=None):
+        """Run one token through all layers; returns the last layer's d."""
+        if self.batch != 1:
+            raise NotImplementedError("the chained driver runs batch 1 (per-matrix batch products are separate)")
+        for layer in range(self.layers):
+            for site in ORDER:
+                n, k = self.shapes[site]
+                if site == "qkv":
+                    if layer == 0:
+                        src, src_dt, flags = (h_in if h_in is not None else self.h0), L.PG_F16, 0
+                    else:
+                        src, src_dt, flags = self.out["down"], L.PG_F32, L.PG_FLAG_RMSNORM
+                else:
+                    prev = {"o": "qkv", "gu": "o", "down": "gu"}[site]
+                    src, src_dt, flags = self.out[prev], L.PG_F32, L.PG_FLAG_RMSNORM
+                # batch 1: the first k columns of the previous output are the input
+                L.pg_fwht_rotate(src, src_dt, self.xrot, self.x_dtype, self.signs[layer][site], 1, k, flags,
+                                 stream)
+                L.pg_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.xrot, self.x_dtype,
+                           1, self.out[site], stream)
+        return self.out["down"]
+
+    def host_arrays(self, layer):
+        """Numpy copies of one layer's codes, scales and signs (for checks)."""
+        return ({s: self.codes[layer][s].cpu().numpy() for s in ORDER},
+                {s: self.scales[layer][s].cpu().numpy() for s in ORDER},
+                {s: self.signs[layer][s].cpu().numpy() for s in ORDER})
+

@@ -1,0 +1,121 @@
+"""CPU tests of libpingala's host side: the C ABI loads and exports every
+declared symbol, argument validation fails before any launch, the decode
+table equals the oracle's closed form, and the host reference encoder
+reproduces the oracle's codes."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import qgemv_amd as q
+from oracle import p8f
+from qgemv_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "pingala.h")).read()
+    return sorted(set(re.findall(r"\b(pg_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    import ctypes
+    lib = q.lib()
+    declared = _declared_symbols()
+    assert set(declared) == set(q.EXPORTS)
+    for name in declared:
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_version_and_footprint():
+    assert q.pg_version() == (1 << 16) | 1
+    assert q.pg_footprint_bytes(512, 2048) == 278528
+    assert q.pg_footprint_bytes(0, 2048) == 0
+    assert q.pg_footprint_bytes(4, 100) == 0
+
+
+def test_codebook_table_matches_oracle():
+    assert np.array_equal(q.pg_codebook_table(), p8f.codebook_table())
+
+
+@pytest.mark.parametrize("call", [
+    lambda: q.pg_qgemv(1 << 20, 1 << 20, 0, 2048, 1 << 20, 0, 1, 1 << 20, stream=0),        # n < 1
+    lambda: q.pg_qgemv(1 << 20, 1 << 20, 8, 100, 1 << 20, 0, 1, 1 << 20, stream=0),         # k % 128
+    lambda: q.pg_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 20, 0, 9, 1 << 20, stream=0),         # batch
+    lambda: q.pg_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 20, 2, 1, 1 << 20, stream=0),         # bf16 x
+    lambda: q.pg_qgemv(None, 1 << 20, 8, 256, 1 << 20, 0, 1, 1 << 20, stream=0),            # null
+    lambda: q.pg_qgemv((1 << 20) + 4, 1 << 20, 8, 256, 1 << 20, 0, 1, 1 << 20, stream=0),   # misaligned
+    lambda: q.pg_qgemm(1 << 20, 1 << 20, 8, 256, 1 << 20, 0, 1 << 20, stream=0),            # m < 1
+    lambda: q.pg_decode(1 << 20, (1 << 20) + 1, 8, 256, 1 << 20, stream=0),                 # scales odd
+    lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 20, 0, 1 << 20, 1, 256, 0, stream=0),         # overlap
+    lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 5, 1 << 20, 1, 256, 0, stream=0),         # dtype
+    lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 0, 1 << 20, 1, 256, 4, stream=0),         # flags
+])
+def test_invalid_arguments_fail_before_launch(call):
+    # the pointers are never dereferenced: validation rejects the call first
+    with pytest.raises(q.PgError) as ei:
+        call()
+    assert ei.value.code == q._lib.PG_ERR_INVALID_ARG
+    assert q.pg_last_error() != ""
+
+
+def test_encode_ref_equals_oracle_on_single_layer():
+    w = synth.single_layer_weights()
+    sb = synth.site_sign_bits(0, 0, 2048)
+    codes = np.zeros((512, 512), np.uint8)
+    scales = np.zeros((512, 16), np.uint16)
+    q.pg_encode_ref(w, 512, 2048, sb, codes, scales)
+    oc, os_ = p8f.encode_matrix(w, sb)
+    assert np.array_equal(scales, os_)
+    _assert_codes_equivalent(w, sb, codes, oc, scales)
+
+
+def test_encode_ref_equals_oracle_on_qwen_rows():
+    # 64 rows of each Qwen3-4B-shaped matrix (outliers included)
+    for name in ("q", "o", "down"):
+        w = synth.qwen_layer_weights(name)
+        n, k = w.shape
+        rows = np.random.default_rng(5).choice(n, 64, replace=False)
+        ws = np.ascontiguousarray(w[rows])
+        sb = synth.site_sign_bits(0, synth.SITE_OF[name], k)
+        codes = np.zeros((64, k // 4), np.uint8)
+        scales = np.zeros((64, k // 128), np.uint16)
+        q.pg_encode_ref(ws, 64, k, sb, codes, scales, 4)
+        oc, os_ = p8f.encode_matrix(ws, sb)
+        assert np.array_equal(scales, os_), name
+        _assert_codes_equivalent(ws, sb, codes, oc, scales)
+
+
+def _assert_codes_equivalent(w, sb, codes, oracle_codes, scales):
+    """Codes must be equal, except on blocks where the two searches are tied
+    (their rotated inputs differ by rounding order): there both paths must
+    reach the optimum distortion to 1e-12 relative."""
+    n, k = w.shape
+    diff = np.nonzero((codes != oracle_codes).reshape(n, k // 128, 32).any(axis=2))
+    wr = p8f.rotate(w, sb).reshape(n, k // 128, 128)
+    for r, b in zip(*diff):
+        d_lib = p8f.block_distortion(wr[r, b][None], codes[r, 32 * b:32 * b + 32][None], scales[r, b:b + 1])[0]
+        d_orc = p8f.block_distortion(wr[r, b][None], oracle_codes[r, 32 * b:32 * b + 32][None], scales[r, b:b + 1])[0]
+        assert abs(d_lib - d_orc) <= 1e-12 * d_orc
+    assert len(diff[0]) <= max(1, n * (k // 128) // 10000)
+
+
+def test_encode_ref_zero_and_constant_rows():
+    w = np.zeros((2, 256), np.float32)
+    w[1, :] = 0.5
+    sb = np.zeros(32, np.uint8)
+    codes = np.full((2, 64), 7, np.uint8)
+    scales = np.full((2, 2), 7, np.uint16)
+    q.pg_encode_ref(w, 2, 256, sb, codes, scales, 1)
+    oc, os_ = p8f.encode_matrix(w, sb)
+    assert np.array_equal(scales, os_) and np.array_equal(codes, oc)
+    assert not codes[0].any() and not scales[0].any()
+
+
+def test_encode_ref_rejects_bad_arguments():
+    w = np.zeros((2, 200), np.float32)
+    with pytest.raises(q.PgError):
+        q.pg_encode_ref(w, 2, 200, np.zeros(25, np.uint8), np.zeros((2, 50), np.uint8),
+                        np.zeros((2, 2), np.uint16))
