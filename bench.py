@@ -72,12 +72,16 @@ def run_stack(args):
     shapes = synth.qwen3_4b_shapes() if args.workload == "qwen36" else synth.llama31_8b_shapes()
     layers = 36 if args.workload == "qwen36" else 32
     log(f"building {args.workload}: {layers} layers")
-    st = Stack(shapes, layers, batch=1, x_dtype=q.PG_F32)
+    st = Stack(shapes, layers, batch=1, x_dtype=q.PG_Q16)
     stream = torch.cuda.current_stream()
+    use_graph = not args.no_graph
+    if use_graph:
+        st.capture()
+    step = st.replay if use_graph else st.token
     for _ in range(args.warmup):
-        st.token()
+        step()
     torch.cuda.synchronize()
-    log("warmup done")
+    log(f"warmup done (hip graph: {use_graph})")
     # timed region: exactly `steps` tokens
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -85,7 +89,7 @@ def run_stack(args):
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        st.token()
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -123,12 +127,12 @@ def run_stack(args):
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_tok, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8xi8->i32 (levels x 16-bit activation digits), f32 scales", "data": "synthetic",
         "config": {"workload": f"{'Qwen3-4B' if args.workload == 'qwen36' else 'Llama-3.1-8B'}-shaped "
                                f"{layers}-layer linear stack, batch 1, random trellis bitstreams",
                    "layers": layers, "batch": 1, "bytes_per_token": st.bytes_per_token,
                    "tok_per_s": round(tok_s, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "hip_graphs": False, "launches_per_token": 8 * layers},
+                   "hip_graphs": use_graph, "launches_per_token": 8 * layers},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "qgemv", "launches": launches, "avg_launch_us": round(1e3 * qg_ms / launches, 3)},
@@ -143,6 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen36", choices=["qwen36", "llama32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "

@@ -71,7 +71,8 @@ enum {
     PG_ERR_HIP = -3           /* a HIP runtime call or launch failed */
 };
 
-enum { PG_F32 = 0, PG_F16 = 1, PG_BF16 = 2 };   /* element types of x / y */
+enum { PG_F32 = 0, PG_F16 = 1, PG_BF16 = 2,     /* element types of x / y */
+       PG_Q16 = 3 };                               /* rotated activations, 16-bit fixed point */
 
 enum { PG_FLAG_RMSNORM = 1u };                   /* pg_fwht_rotate flags */
 
@@ -84,6 +85,21 @@ int pg_version(void);
 /* Bytes of codes + scales for an n x k matrix: n*k/4 + n*(k/128)*2.
  * Returns 0 if n < 1 or k is not a positive multiple of 128. */
 size_t pg_footprint_bytes(int64_t n, int64_t k);
+
+/* PG_Q16: the library's own format for rotated activations, written by
+ * pg_fwht_rotate and read by pg_qgemv.  Per row of k values (k % 128 == 0),
+ * pg_q16_row_bytes(k) bytes:
+ *   [0, 2k)          int8 digits; chunk c (values 16c..16c+15) holds 32 bytes:
+ *                    byte 4j+g = hi digit of value 16c+4g+j, byte 16+4j+g = lo
+ *                    digit, for group g = 0..3 and position j = 0..3;
+ *   [2k, 2k+k/32)    f32 sx per 128-block;
+ *   [2k+k/32, 2k+3k/32) int32 sum of the 16-bit values per 64-value half-block;
+ *   then zero padding to a multiple of 64 bytes.
+ * A value v of block b is q * sx[b], q = round(v / sx[b]) with |q| <= 32512,
+ * sx[b] = max|v| / 32512 over the block (0 for an all-zero block), and
+ * q = 256 * hi + lo with lo in [-128, 127].  Relative error <= 2^-16 of the
+ * block's largest value. */
+size_t pg_q16_row_bytes(int64_t k);
 
 /* Message of the calling thread's last failed call ("" if none). */
 const char* pg_last_error(void);
@@ -119,7 +135,8 @@ int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k
 /* Run-time activation rotation ("How it works": the random Hadamard
  * rotation; the activations take the same rotation as the weight rows):
  *   x        device [rows][k] of in_dtype (PG_F32 / PG_F16 / PG_BF16)
- *   y        device [rows][k] of out_dtype (PG_F32 / PG_F16 / PG_BF16)
+ *   y        device [rows][k] of out_dtype (PG_F32 / PG_F16 / PG_BF16), or
+ *            rows * pg_q16_row_bytes(k) bytes for PG_Q16
  *   sign_bits device u8 [k/8]
  *   flags    PG_FLAG_RMSNORM: first replace each row v by
  *            fp16_RNE(v / sqrt(mean(v^2) + 1e-6)) (fp32 math), as the
@@ -135,7 +152,10 @@ int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype,
  * weights per token):
  *   y[b][i] = sum_blk scale[i][blk] * sum_{k in blk} level[i][k] * x_rot[b][k]
  *   codes device u8 [n][k/4], scales device u16 [n][k/128]
- *   x_rot device [batch][k], PG_F32 or PG_F16, already rotated
+ *   x_rot device [batch][k] PG_F32 or PG_F16, or batch * pg_q16_row_bytes(k)
+ *         bytes of PG_Q16 (the fast path: exact integer dot products of the
+ *         levels with the 16-bit activations, one fp32 scale per half-block),
+ *         already rotated
  *   batch 1..8, y device f32 [batch][n] out.
  * fp32 accumulation; summation order is fixed, so repeated calls are
  * bitwise identical. */

@@ -17,10 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpingala.so")
 
 PG_OK, PG_ERR_INVALID_ARG, PG_ERR_UNSUPPORTED, PG_ERR_HIP = 0, -1, -2, -3
-PG_F32, PG_F16, PG_BF16 = 0, 1, 2
+PG_F32, PG_F16, PG_BF16, PG_Q16 = 0, 1, 2, 3
 PG_FLAG_RMSNORM = 1
 
-EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
+EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
            "pg_decode", "pg_fwht_rotate", "pg_qgemv", "pg_qgemm")
 
 
@@ -45,6 +45,8 @@ def lib():
         L.pg_version.argtypes = []
         L.pg_footprint_bytes.restype = ctypes.c_size_t
         L.pg_footprint_bytes.argtypes = [i64, i64]
+        L.pg_q16_row_bytes.restype = ctypes.c_size_t
+        L.pg_q16_row_bytes.argtypes = [i64]
         L.pg_last_error.restype = ctypes.c_char_p
         L.pg_last_error.argtypes = []
         L.pg_codebook_table.restype = i32
@@ -94,6 +96,10 @@ def pg_version() -> int:
 
 def pg_footprint_bytes(n: int, k: int) -> int:
     return lib().pg_footprint_bytes(n, k)
+
+
+def pg_q16_row_bytes(k: int) -> int:
+    return lib().pg_q16_row_bytes(k)
 
 
 def pg_last_error() -> str:

@@ -25,8 +25,8 @@ int check_ptr(const void* p, uintptr_t align, const char* name) {
     return PG_OK;
 }
 
-int check_dtype(int dt, const char* name, bool allow_bf16) {
-    if (dt == PG_F32 || dt == PG_F16 || (allow_bf16 && dt == PG_BF16)) return PG_OK;
+int check_dtype(int dt, const char* name, bool allow_bf16, bool allow_q16) {
+    if (dt == PG_F32 || dt == PG_F16 || (allow_bf16 && dt == PG_BF16) || (allow_q16 && dt == PG_Q16)) return PG_OK;
     return pg::fail(PG_ERR_INVALID_ARG, "%s: unsupported dtype %d", name, dt);
 }
 
@@ -41,6 +41,11 @@ int check_dtype(int dt, const char* name, bool allow_bf16) {
 extern "C" {
 
 int pg_version(void) { return (PG_FORMAT_VERSION << 16) | PG_LIB_VERSION; }
+
+size_t pg_q16_row_bytes(int64_t k) {
+    if (k < 128 || k % 128 != 0) return 0;
+    return pg::q16_row_bytes(k);
+}
 
 size_t pg_footprint_bytes(int64_t n, int64_t k) {
     if (n < 1 || k < 128 || k % 128 != 0) return 0;
@@ -82,14 +87,15 @@ int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype, const ui
     pg::clear_error();
     if (rows < 1) return pg::fail(PG_ERR_INVALID_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
     PG_TRY(check_nk(rows, k));
-    PG_TRY(check_dtype(in_dtype, "in_dtype", true));
-    PG_TRY(check_dtype(out_dtype, "out_dtype", true));
+    PG_TRY(check_dtype(in_dtype, "in_dtype", true, false));
+    PG_TRY(check_dtype(out_dtype, "out_dtype", true, true));
     PG_TRY(check_ptr(x, 16, "x"));
     PG_TRY(check_ptr(y, 16, "y"));
     PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
     if (flags & ~PG_FLAG_RMSNORM) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     const size_t in_b = (size_t)rows * k * (in_dtype == PG_F32 ? 4 : 2);
-    const size_t out_b = (size_t)rows * k * (out_dtype == PG_F32 ? 4 : 2);
+    const size_t out_b = out_dtype == PG_Q16 ? (size_t)rows * pg::q16_row_bytes(k)
+                                             : (size_t)rows * k * (out_dtype == PG_F32 ? 4 : 2);
     const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
     if (xa < ya + out_b && ya < xa + in_b) return pg::fail(PG_ERR_INVALID_ARG, "x and y overlap");
     return pg::launch_fwht(x, in_dtype, y, out_dtype, sign_bits, rows, k, flags, stream);
@@ -100,7 +106,7 @@ int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
     pg::clear_error();
     PG_TRY(check_nk(n, k));
     if (batch < 1 || batch > 8) return pg::fail(PG_ERR_INVALID_ARG, "batch must be 1..8 (got %d)", batch);
-    PG_TRY(check_dtype(x_dtype, "x_dtype", false));
+    PG_TRY(check_dtype(x_dtype, "x_dtype", false, true));
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 2, "scales"));
     PG_TRY(check_ptr(x_rot, 16, "x_rot"));

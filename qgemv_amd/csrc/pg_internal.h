@@ -13,6 +13,13 @@ int fail(int code, const char* fmt, ...);
 void clear_error();
 const char* last_error();
 
+// bytes of one PG_Q16 activation row (digits, block scales, half-block sums,
+// padded to 64 B)
+inline size_t q16_row_bytes(int64_t k) {
+    const size_t raw = (size_t)(2 * k + k / 32 + k / 16);
+    return (raw + 63) & ~(size_t)63;
+}
+
 // format helpers (pg_host.cpp)
 void group_levels(int s, int c, int out[4]);
 void build_codebook(int8_t* out /* [8][256][4] */);

@@ -8,6 +8,8 @@
 // rotation.  Bit layout: format P8F v1 as stated in include/pingala.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "pg_internal.h"
 
@@ -83,54 +85,176 @@ __global__ void k_decode(const uint8_t* __restrict__ codes, const uint16_t* __re
 }
 
 // ---------------------------------------------------------------- rotation
-// One workgroup (4 waves) per row.  Each wave transforms whole 128-blocks:
-// lane l holds elements l and l+64, the first butterfly stage (distance 64)
-// is inside the lane, the other six use lane exchanges.  Optional RMS
-// normalisation with fp16 rounding first (PG_FLAG_RMSNORM).
+// Grid (ceil(nblocks/4), rows): each of the 4 waves of a workgroup transforms
+// one 128-block; lane l holds elements l and l+64, the first butterfly stage
+// (distance 64) is inside the lane, the other six exchange across lanes.
+// With PG_FLAG_RMSNORM every workgroup first sums the squares of its whole
+// row (fixed order: strided per thread, then waves 0..3) and rounds the
+// normalised values to fp16.  PG_Q16 output writes the 16-bit fixed-point
+// activation format that pg_qgemv reads (layout in include/pingala.h).
+// Value of lane (lane ^ H) for H < 16, with DPP row shifts (no LDS trip).
+template <int H>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+    const int iv = __builtin_bit_cast(int, v);
+    if (H == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+    if (H == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+    const int up = __builtin_amdgcn_mov_dpp(iv, 0x100 + H, 0xf, 0xf, false);   // row_shl:H -> lane + H
+    const int dn = __builtin_amdgcn_mov_dpp(iv, 0x110 + H, 0xf, 0xf, false);   // row_shr:H -> lane - H
+    return __builtin_bit_cast(float, (lane & H) ? dn : up);
+}
+template <int H>
+__device__ __forceinline__ int xor_lane_i(int v, int lane) {
+    return __builtin_bit_cast(int, xor_lane<H>(__builtin_bit_cast(float, v), lane));
+}
+
+// Value of lane (lane ^ 16) / (lane ^ 32): gfx950's v_permlane16_swap /
+// v_permlane32_swap exchange rows of 16 / halves of 32 lanes in registers.
+__device__ __forceinline__ float xor_lane16(float v, int lane) {
+    const int iv = __builtin_bit_cast(int, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
+    return __builtin_bit_cast(float, (lane & 16) ? (int)r[0] : (int)r[1]);
+}
+__device__ __forceinline__ float xor_lane32(float v, int lane) {
+    const int iv = __builtin_bit_cast(int, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(iv, iv, false, false);
+    return __builtin_bit_cast(float, (lane & 32) ? (int)r[0] : (int)r[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    const int lane = threadIdx.x & 63;
+    v += xor_lane<1>(v, lane);
+    v += xor_lane<2>(v, lane);
+    v += xor_lane<4>(v, lane);
+    v += xor_lane<8>(v, lane);
+    v += xor_lane16(v, lane);
+    v += xor_lane32(v, lane);
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+    const int lane = threadIdx.x & 63;
+    v += xor_lane_i<1>(v, lane);
+    v += xor_lane_i<2>(v, lane);
+    v += xor_lane_i<4>(v, lane);
+    v += xor_lane_i<8>(v, lane);
+    v += __builtin_bit_cast(int, xor_lane16(__builtin_bit_cast(float, v), lane));
+    v += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, v), lane));
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+    const int lane = threadIdx.x & 63;
+    v = fmaxf(v, xor_lane<1>(v, lane));
+    v = fmaxf(v, xor_lane<2>(v, lane));
+    v = fmaxf(v, xor_lane<4>(v, lane));
+    v = fmaxf(v, xor_lane<8>(v, lane));
+    v = fmaxf(v, xor_lane16(v, lane));
+    v = fmaxf(v, xor_lane32(v, lane));
+    return v;
+}
+
+constexpr int Q16_MAXQ = 32512;
+
+__device__ __forceinline__ void q16_store(uint8_t* row, int k, int blk, int i, int q) {
+    // element i of block blk: chunk c' = i/16, group g = (i/4)%4, position j = i%4
+    const int hi = (q + 128) >> 8;
+    const int lo = q - (hi << 8);
+    const int off = (blk * 8 + (i >> 4)) * 32 + 4 * (i & 3) + ((i >> 2) & 3);
+    row[off] = (uint8_t)(int8_t)hi;
+    row[off + 16] = (uint8_t)(int8_t)lo;
+}
+
 __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, int in_dt, void* __restrict__ y,
                                               int out_dt, const uint8_t* __restrict__ sign_bits, int k,
-                                              uint32_t flags) {
-    const int64_t row = blockIdx.x;
+                                              uint32_t flags, int64_t q16_stride) {
+    const int64_t row = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int nblk = k >> 7;
+    const int blk = blockIdx.x * 4 + wave;
     const int64_t base = row * (int64_t)k;
     __shared__ float red[4];
+    // this wave's block first (its loads overlap the normalisation pass)
+    const bool active = blk < nblk;
+    const int i0 = (active ? blk : 0) * 128 + lane, i1 = i0 + 64;
+    float a = load_elem(x, in_dt, base + i0);
+    float c = load_elem(x, in_dt, base + i1);
+    const uint32_t sg0 = sign_bits[i0 >> 3], sg1 = sign_bits[i1 >> 3];
     float inv = 1.0f;
     if (flags & PG_FLAG_RMSNORM) {
+        // the whole row's squares: up to 64 loads per thread in flight at once
         float ss = 0.0f;
-        for (int i = threadIdx.x; i < k; i += 256) {
-            const float v = load_elem(x, in_dt, base + i);
-            ss += v * v;
+        for (int i0r = threadIdx.x; i0r < k; i0r += 256 * 64) {
+            float v[64];
+#pragma unroll
+            for (int u = 0; u < 64; ++u) {
+                const int i = i0r + 256 * u;
+                v[u] = i < k ? load_elem(x, in_dt, base + i) : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 64; ++u) ss += v[u] * v[u];
         }
-        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        ss = wave_sum(ss);
         if (lane == 0) red[wave] = ss;
         __syncthreads();
         const float tot = (red[0] + red[1]) + (red[2] + red[3]);
         inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
     }
+    if (!active) return;
     const float cnorm = 0.08838834764831845f;   // 2^-3.5
-    for (int b = wave; b < k / 128; b += 4) {
-        const int i0 = b * 128 + lane, i1 = i0 + 64;
-        float a = load_elem(x, in_dt, base + i0);
-        float c = load_elem(x, in_dt, base + i1);
-        if (flags & PG_FLAG_RMSNORM) {
-            a = h2f(f2h(a * inv));
-            c = h2f(f2h(c * inv));
-        }
-        if ((sign_bits[i0 >> 3] >> (i0 & 7)) & 1) a = -a;
-        if ((sign_bits[i1 >> 3] >> (i1 & 7)) & 1) c = -c;
-        float t0 = a + c, t1 = a - c;
+    if (flags & PG_FLAG_RMSNORM) {
+        a = h2f(f2h(a * inv));
+        c = h2f(f2h(c * inv));
+    }
+    if ((sg0 >> (i0 & 7)) & 1) a = -a;
+    if ((sg1 >> (i1 & 7)) & 1) c = -c;
+    {
+        const float t0 = a + c, t1 = a - c;
         a = t0;
         c = t1;
-#pragma unroll
-        for (int h = 32; h >= 1; h >>= 1) {
-            const float pa = __shfl_xor(a, h), pc = __shfl_xor(c, h);
-            const bool upper = (lane & h) != 0;
-            a = upper ? pa - a : a + pa;
-            c = upper ? pc - c : c + pc;
-        }
-        store_elem(y, out_dt, base + i0, a * cnorm);
-        store_elem(y, out_dt, base + i1, c * cnorm);
+    }
+    // butterflies at distance 32 and 16 cross DPP rows (lane exchange); 8..1
+    // stay inside a row of 16 lanes (DPP shifts)
+    {
+        float pa = xor_lane32(a, lane), pc = xor_lane32(c, lane);
+        bool upper = (lane & 32) != 0;
+        a = upper ? pa - a : a + pa;
+        c = upper ? pc - c : c + pc;
+        pa = xor_lane16(a, lane); pc = xor_lane16(c, lane); upper = (lane & 16) != 0;
+        a = upper ? pa - a : a + pa;
+        c = upper ? pc - c : c + pc;
+        pa = xor_lane<8>(a, lane); pc = xor_lane<8>(c, lane); upper = (lane & 8) != 0;
+        a = upper ? pa - a : a + pa;
+        c = upper ? pc - c : c + pc;
+        pa = xor_lane<4>(a, lane); pc = xor_lane<4>(c, lane); upper = (lane & 4) != 0;
+        a = upper ? pa - a : a + pa;
+        c = upper ? pc - c : c + pc;
+        pa = xor_lane<2>(a, lane); pc = xor_lane<2>(c, lane); upper = (lane & 2) != 0;
+        a = upper ? pa - a : a + pa;
+        c = upper ? pc - c : c + pc;
+        pa = xor_lane<1>(a, lane); pc = xor_lane<1>(c, lane); upper = (lane & 1) != 0;
+        a = upper ? pa - a : a + pa;
+        c = upper ? pc - c : c + pc;
+    }
+    a *= cnorm;
+    c *= cnorm;
+    if (out_dt != PG_Q16) {
+        store_elem(y, out_dt, base + i0, a);
+        store_elem(y, out_dt, base + i1, c);
+        return;
+    }
+    uint8_t* rowp = (uint8_t*)y + row * q16_stride;
+    const float mx = wave_max(fmaxf(fabsf(a), fabsf(c)));
+    const float inv_sx = mx > 0.0f ? (float)Q16_MAXQ / mx : 0.0f;
+    const int qa = (int)rintf(a * inv_sx);
+    const int qc = (int)rintf(c * inv_sx);
+    q16_store(rowp, k, blk, lane, qa);
+    q16_store(rowp, k, blk, lane + 64, qc);
+    const int sa = wave_sum_i(qa), sc = wave_sum_i(qc);
+    if (lane == 0) {
+        float* sxp = (float*)(rowp + 2 * (int64_t)k);
+        int* sump = (int*)(rowp + 2 * (int64_t)k + k / 32);
+        sxp[blk] = mx / (float)Q16_MAXQ;
+        sump[2 * blk] = sa;
+        sump[2 * blk + 1] = sc;
     }
 }
 
@@ -208,6 +332,224 @@ __global__ __launch_bounds__(256) void k_qgemv_v1(const uint8_t* __restrict__ co
             v += __shfl_xor(v, 2);
             v += __shfl_xor(v, 1);
             if (tl == 0 && row < n && q < bt) y[(int64_t)(b0 + q) * n + row] = v;
+        }
+    }
+}
+
+// ------------------------------------------------------- qgemv, fast path
+// Batch 1..8 product on PG_Q16 activations.  Same team layout as above
+// (8 lanes x 16-byte chunks per row step, each team reading whole 128-byte
+// lines), R rows per team, the workgroup's activations staged once in LDS
+// with direct global->LDS copies.  Decode never materialises a level: for a
+// code dword (4 groups) and position j, the bytes of plane P_j hold
+// (level + 7) / 2 = 4 e_j + 2 b_j + z0 of the four groups, built with a
+// handful of shifts and masks (z0 and the parity bit b3 come from bit 0 of
+// the three preceding bytes, obtained with byte-aligns against the previous
+// dword); v_dot4_i32_i8 then multiplies the plane by the four groups'
+// activation digits.  Per half-block:
+//   sum level * q = 2 * (256 * hi + lo) - 7 * sum q
+// exactly in int32, then one fp32 multiply by (weight scale * activation
+// block scale).
+__device__ __forceinline__ void planes_of(uint32_t d, uint32_t dp, uint32_t P[4]) {
+    const uint32_t a1 = __builtin_amdgcn_alignbyte(d, dp, 3);   // byte g = byte g-1
+    const uint32_t a2 = __builtin_amdgcn_alignbyte(d, dp, 2);   // byte g = byte g-2
+    const uint32_t a3 = __builtin_amdgcn_alignbyte(d, dp, 1);   // byte g = byte g-3
+    const uint32_t M1 = 0x01010101u, M2 = 0x02020202u, M4 = 0x04040404u;
+    const uint32_t zb = a2 & M1;                                  // z0 = u_{t-2}
+    const uint32_t d1 = d >> 1, d2 = d >> 2, d3 = d >> 3, d4 = d >> 4, d5 = d >> 5;
+    P[0] = (d2 & M4) | (d & M2) | zb;
+    P[1] = (d3 & M4) | (d1 & M2) | zb;
+    P[2] = (d4 & M4) | (d2 & M2) | zb;
+    const uint32_t par = d ^ d1 ^ d2 ^ d3 ^ a1 ^ a3;             // bit 0: b3 = z1^b0^b1^b2
+    P[3] = (d5 & M4) | ((par << 1) & M2) | zb;
+}
+
+// The workgroup's W waves share 8*R rows and split each row's chunks between
+// them (wave w, team lane tl takes chunks w*8 + tl + 8W*i), so a small matrix
+// still spreads over many waves.  Each wave copies only the activation digits
+// of its own chunks (1 KiB per round i, one direct global->LDS copy) plus the
+// block scales and half-block sums into its own LDS region, so no
+// workgroup-wide barrier precedes the dot products; the per-wave partial sums
+// meet in LDS at the end and are added in wave order.
+struct Q16Layout {
+    int rounds;      // chunk rounds per wave: ceil(nchunk / (8W))
+    int sxs_bytes;   // staged scale + sum bytes per batch row (multiple of 16)
+    int wave_bytes;  // LDS bytes per wave
+};
+
+__host__ __device__ inline Q16Layout q16_layout(int k, int W, int BS) {
+    Q16Layout L;
+    const int nchunk = k / 64;
+    L.rounds = (nchunk + 8 * W - 1) / (8 * W);
+    L.sxs_bytes = ((3 * k / 32) + 15) & ~15;
+    L.wave_bytes = BS * (L.rounds * 1024 + ((L.sxs_bytes + 1023) & ~1023));
+    return L;
+}
+
+template <int BS, int R>
+__global__ __launch_bounds__(512) void k_qgemv_q16(const uint8_t* __restrict__ codes,
+                                                   const uint16_t* __restrict__ scales, int n, int k,
+                                                   const uint8_t* __restrict__ xq, int xq_stride, int batch,
+                                                   float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int W = nthr >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int team = lane >> 3, tl = lane & 7;
+    const int rbase = blockIdx.x * 8 * R + team * R;
+    const int kg = k >> 2, nchunk = k >> 6, nbk = k >> 7;
+    const int cstep = 8 * W;
+    const Q16Layout L = q16_layout(k, W, BS);
+    const int bregion = L.wave_bytes / BS;                      // per batch row inside a wave's region
+    uint8_t* wlds = lds + wave * L.wave_bytes;
+    float* red = reinterpret_cast<float*>(lds + W * L.wave_bytes);   // [W][8][R][BS]
+    const uint8_t* rp[R];
+    const uint16_t* sp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rbase + r < n ? rbase + r : n - 1;
+        rp[r] = codes + (int64_t)row * kg;
+        sp[r] = scales + (int64_t)row * nbk;
+    }
+    const int cfirst = wave * 8 + tl;
+    for (int b0 = 0; b0 < batch; b0 += BS) {
+        const int bs = batch - b0 < BS ? batch - b0 : BS;
+        if (b0 > 0) __syncthreads();                            // previous round's reduction done
+        // first code chunk in flight before the activations are staged
+        uint4 q[R];
+        float ws[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            q[r] = cfirst < nchunk ? *reinterpret_cast<const uint4*>(rp[r] + 16 * cfirst) : make_uint4(0, 0, 0, 0);
+            ws[r] = cfirst < nchunk ? h2f(sp[r][cfirst >> 1]) : 0.0f;
+        }
+        // this wave's activation digits, block scales and half-block sums
+        for (int b = 0; b < bs; ++b) {
+            const uint8_t* xrow = xq + (int64_t)(b0 + b) * xq_stride;
+            uint8_t* dst = wlds + b * bregion;
+            for (int i = 0; i < L.rounds; ++i) {
+                const int c0 = wave * 8 + cstep * i;                 // first chunk of the round
+                if (c0 < nchunk && 128 * c0 + 16 * lane < 2 * k)
+                    __builtin_amdgcn_global_load_lds(xrow + 128 * c0 + 16 * lane, dst + 1024 * i, 16, 0, 0);
+            }
+            uint8_t* sdst = dst + 1024 * L.rounds;
+            for (int o = 0; o < L.sxs_bytes; o += 1024)
+                if (o + 16 * lane < L.sxs_bytes)
+                    __builtin_amdgcn_global_load_lds(xrow + 2 * k + o + 16 * lane, sdst + o, 16, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        float acc[R][BS];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < BS; ++b) acc[r][b] = 0.0f;
+        // Up to U chunks per lane are requested together before any is used,
+        // so a lane that owns only a few chunks (small matrices) waits for one
+        // memory latency, not one per chunk.  The loop bound is wave-uniform:
+        // every lane steps through the same iterations (lanes past the end
+        // compute on clamped data and discard it).
+        constexpr int U = 4;
+        for (int c0 = wave * 8; c0 < nchunk; c0 += U * cstep) {
+            uint4 qu[U][R];
+            float wsu[U][R];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + tl + u * cstep;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (u == 0 && c0 == wave * 8) {
+                        qu[u][r] = q[r];
+                        wsu[u][r] = ws[r];
+                    } else {
+                        qu[u][r] = c < nchunk ? *reinterpret_cast<const uint4*>(rp[r] + 16 * c) : make_uint4(0, 0, 0, 0);
+                        wsu[u][r] = c < nchunk ? h2f(sp[r][c >> 1]) : 0.0f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (c0 + u * cstep >= nchunk) break;                 // wave-uniform
+                const int c = c0 + tl + u * cstep;
+                const bool valid = c < nchunk;
+                const int round = (c0 - wave * 8) / cstep + u;
+                uint32_t dp0[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    // last dword of the left neighbour's chunk (same team when c is odd)
+                    const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)qu[u][r].w, 0x111, 0xf, 0xf, true);
+                    dp0[r] = (c & 1) ? left : 0u;
+                }
+                int hi[R][BS], lo[R][BS];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int b = 0; b < BS; ++b) { hi[r][b] = 0; lo[r][b] = 0; }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    uint32_t P[R][4];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t w4[4] = {qu[u][r].x, qu[u][r].y, qu[u][r].z, qu[u][r].w};
+                        planes_of(w4[m], m == 0 ? dp0[r] : w4[m - 1], P[r]);
+                    }
+#pragma unroll
+                    for (int b = 0; b < BS; ++b) {
+                        if (b < bs) {
+                            const uint4* xp = reinterpret_cast<const uint4*>(wlds + b * bregion + 1024 * round +
+                                                                             128 * tl + 32 * m);
+                            const uint4 xh = xp[0], xl = xp[1];
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                int h = hi[r][b], l = lo[r][b];
+                                h = __builtin_amdgcn_sdot4((int)P[r][0], (int)xh.x, h, false);
+                                l = __builtin_amdgcn_sdot4((int)P[r][0], (int)xl.x, l, false);
+                                h = __builtin_amdgcn_sdot4((int)P[r][1], (int)xh.y, h, false);
+                                l = __builtin_amdgcn_sdot4((int)P[r][1], (int)xl.y, l, false);
+                                h = __builtin_amdgcn_sdot4((int)P[r][2], (int)xh.z, h, false);
+                                l = __builtin_amdgcn_sdot4((int)P[r][2], (int)xl.z, l, false);
+                                h = __builtin_amdgcn_sdot4((int)P[r][3], (int)xh.w, h, false);
+                                l = __builtin_amdgcn_sdot4((int)P[r][3], (int)xl.w, l, false);
+                                hi[r][b] = h;
+                                lo[r][b] = l;
+                            }
+                        }
+                    }
+                }
+                if (valid) {
+#pragma unroll
+                    for (int b = 0; b < BS; ++b) {
+                        if (b < bs) {
+                            const uint8_t* sx_base = wlds + b * bregion + 1024 * L.rounds;
+                            const float sxv = reinterpret_cast<const float*>(sx_base)[c >> 1];
+                            const int qs = reinterpret_cast<const int*>(sx_base + k / 32)[c];
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                const int t = 2 * (hi[r][b] * 256 + lo[r][b]) - 7 * qs;
+                                acc[r][b] += (wsu[u][r] * sxv) * (float)t;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        // team sums (lanes tl = 0..7), then wave partials through LDS
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < BS; ++b) {
+                float v = acc[r][b];
+                v += xor_lane<4>(v, lane);
+                v += xor_lane<2>(v, lane);
+                v += xor_lane<1>(v, lane);
+                if (tl == 0) red[((wave * 8 + team) * R + r) * BS + b] = v;
+            }
+        __syncthreads();
+        for (int o = tid; o < 8 * R * BS; o += nthr) {
+            const int b = o % BS, r = (o / BS) % R, t = o / (BS * R);
+            float v = 0.0f;
+            for (int w = 0; w < W; ++w) v += red[((w * 8 + t) * R + r) * BS + b];
+            const int row = blockIdx.x * 8 * R + t * R + r;
+            if (row < n && b < bs) y[(int64_t)(b0 + b) * n + row] = v;
         }
     }
 }
@@ -350,14 +692,59 @@ int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64
 
 int launch_fwht(const void* x, int in_dt, void* y, int out_dt, const uint8_t* sign_bits, int64_t rows,
                 int64_t k, uint32_t flags, pg_stream_t s) {
-    if (rows > 0x7fffffff) return fail(PG_ERR_UNSUPPORTED, "rows too large");
-    hipLaunchKernelGGL(k_fwht, dim3((unsigned)rows), dim3(256), 0, (hipStream_t)s, x, in_dt, y, out_dt,
-                       sign_bits, (int)k, flags);
+    if (rows > 65535) return fail(PG_ERR_UNSUPPORTED, "rows > 65535");
+    const dim3 grid((unsigned)((k / 128 + 3) / 4), (unsigned)rows);
+    hipLaunchKernelGGL(k_fwht, grid, dim3(256), 0, (hipStream_t)s, x, in_dt, y, out_dt, sign_bits, (int)k, flags,
+                       (int64_t)q16_row_bytes(k));
     return hip_check(hipGetLastError(), "pg_fwht_rotate launch");
 }
 
+namespace {
+
+template <int BS>
+int launch_q16_bs(int R, int W, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                  const uint8_t* xq, int stride, int batch, float* y, hipStream_t st) {
+    const int rows_per_wg = 8 * R;
+    const dim3 grid((unsigned)((n + rows_per_wg - 1) / rows_per_wg));
+    const Q16Layout L = q16_layout((int)k, W, BS);
+    const size_t lds = (size_t)W * L.wave_bytes + (size_t)W * 8 * R * BS * 4;
+    if (R == 2)
+        hipLaunchKernelGGL((k_qgemv_q16<BS, 2>), grid, dim3(64 * W), lds, st, codes, scales, (int)n, (int)k, xq,
+                           stride, batch, y);
+    else
+        hipLaunchKernelGGL((k_qgemv_q16<BS, 1>), grid, dim3(64 * W), lds, st, codes, scales, (int)n, (int)k, xq,
+                           stride, batch, y);
+    return hip_check(hipGetLastError(), "pg_qgemv launch");
+}
+
+}  // namespace
+
 int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
                  int x_dt, int batch, float* y, pg_stream_t s) {
+    if (x_dt == PG_Q16) {
+        const int stride = (int)q16_row_bytes(k);
+        // rows per workgroup 8*R; waves per workgroup W split each row's
+        // 64-weight chunks, chosen so that the launch has about 2048+ waves
+        // while every lane still gets at least one chunk
+        int R = 1;
+        const int64_t wgs = (n + 7) / 8;
+        int W = 1;
+        while (W < 8 && wgs * W < 2048 && (k / 64) >= 16 * W) W *= 2;
+        const char* env = getenv("PG_QGEMV_SHAPE");          // development override "R,W"
+        if (env) { int a = 0, b = 0; if (sscanf(env, "%d,%d", &a, &b) == 2 && (a == 1 || a == 2) && (b == 1 || b == 2 || b == 4 || b == 8)) { R = a; W = b; } }
+        // batch rows per pass: the staged activations fit the LDS budget
+        const size_t budget = 96 * 1024;
+        int bs = 1;
+        while (bs < 8 && bs < batch && (size_t)W * q16_layout((int)k, W, 2 * bs).wave_bytes + (size_t)W * 8 * R * 2 * bs * 4 <= budget) bs *= 2;
+        if ((size_t)W * q16_layout((int)k, W, 1).wave_bytes + (size_t)W * 8 * R * 4 > budget)
+            return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for the PG_Q16 path", (long long)k);
+        hipStream_t st = (hipStream_t)s;
+        const uint8_t* xq = (const uint8_t*)x;
+        if (bs >= 8) return launch_q16_bs<8>(R, W, codes, scales, n, k, xq, stride, batch, y, st);
+        if (bs >= 4) return launch_q16_bs<4>(R, W, codes, scales, n, k, xq, stride, batch, y, st);
+        if (bs >= 2) return launch_q16_bs<2>(R, W, codes, scales, n, k, xq, stride, batch, y, st);
+        return launch_q16_bs<1>(R, W, codes, scales, n, k, xq, stride, batch, y, st);
+    }
     // activations of a tile of batch rows live in LDS as fp32 (<= 64 KiB)
     const int64_t per_row = k * 4;
     int bt = (int)(65536 / per_row);

@@ -21,7 +21,7 @@ ORDER = ("qkv", "o", "gu", "down")
 
 
 class Stack:
-    def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_F32):
+    def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_Q16):
         import torch
         self.shapes = synth.merged_shapes(shapes)
         self.raw_shapes = shapes
@@ -44,8 +44,12 @@ class Stack:
             self.signs.append(g)
         b = batch
         kmax = max(k for _, k in self.shapes.values())
-        xt = torch.float32 if x_dtype == L.PG_F32 else torch.float16
-        self.xrot = torch.empty((b, kmax), dtype=xt, device=device)
+        if x_dtype == L.PG_Q16:
+            self.xrot = torch.zeros((b, L.pg_q16_row_bytes(kmax)), dtype=torch.uint8, device=device)
+        else:
+            xt = torch.float32 if x_dtype == L.PG_F32 else torch.float16
+            self.xrot = torch.empty((b, kmax), dtype=xt, device=device)
+        self.graph = None
         self.out = {site: torch.empty((b, n), dtype=torch.float32, device=device)
                     for site, (n, _) in self.shapes.items()}
         h = shapes["q"][1]
@@ -71,6 +75,26 @@ class Stack:
                                  stream)
                 L.pg_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.xrot, self.x_dtype,
                            1, self.out[site], stream)
+        return self.out["down"]
+
+    def capture(self):
+        """Record one token's launches into a HIP graph (torch.cuda.CUDAGraph
+        drives hipStreamBeginCapture on its own stream; the library launches
+        on the current stream, which is that capture stream)."""
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.token()                      # warm the launch path outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.token()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
         return self.out["down"]
 
     def host_arrays(self, layer):

@@ -25,3 +25,30 @@ def test_chain_matches_oracle(shapes_fn, layers):
     # a second token from the same input is bitwise identical
     d2 = host(st.token())
     assert np.array_equal(d2.view(np.uint32), got.view(np.uint32))
+
+
+def test_graph_replays_match_eager():
+    """A captured token replays bitwise-identically to the eager token, on
+    every replay, with eager work and synchronisations in between."""
+    import torch
+    st = Stack(synth.qwen3_4b_shapes(), 3)
+    eager = host(st.token()).copy()
+    st.capture()
+    for i in range(4):
+        st.out["down"].zero_()
+        torch.cuda.synchronize()
+        got = host(st.replay())
+        torch.cuda.synchronize()
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), i
+        e2 = host(st.token())                 # eager work between replays
+        assert np.array_equal(e2.view(np.uint32), eager.view(np.uint32))
+
+
+def test_chain_f32_path_matches_q16_path():
+    """The fp32-activation path and the PG_Q16 path agree to well within the
+    bar on the same stack (they differ only in the 16-bit activation rounding)."""
+    import qgemv_amd as q
+    shapes = synth.qwen3_4b_shapes()
+    a = host(Stack(shapes, 2, x_dtype=q.PG_Q16).token())
+    b = host(Stack(shapes, 2, x_dtype=q.PG_F32).token())
+    assert rel_err(a, b) <= 1e-3
