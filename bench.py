@@ -3,13 +3,13 @@
 Default workload: the 36-layer Qwen3-4B-shaped linear stack at batch 1
 (uniform random trellis bitstreams, fp16 U(0.005, 0.05) scales, fp16 N(0,1)
 input fed layer to layer; 965,099,520 coded bytes per token).  One step is
-one token through the whole stack: per layer four activation rotations
-(three with the fused RMS normalisation) and four qgemv launches (qkv and
-gate/up merged).  Inputs are resident in HBM before timing starts.
+one token through the whole stack: per layer four launches of the fused
+stage kernel (RMS normalisation + activation rotation + qgemv; qkv and
+gate/up merged), replayed from a HIP graph.  Inputs are resident in HBM before timing starts.
 
 Printed: one JSON line with the whole-job compressed-weight GB/s
 (bytes per token x tokens per second), tokens per second, the qgemv
-kernel-sum roofline (HIP events around every qgemv launch of a separate
+kernel-sum roofline (HIP events around every stage launch of a separate
 pass over the same tokens) and the oracle's CPU throughput on a bounded
 sample of the same workload.
 """
@@ -72,7 +72,7 @@ def run_stack(args):
     shapes = synth.qwen3_4b_shapes() if args.workload == "qwen36" else synth.llama31_8b_shapes()
     layers = 36 if args.workload == "qwen36" else 32
     log(f"building {args.workload}: {layers} layers")
-    st = Stack(shapes, layers, batch=1, x_dtype=q.PG_Q16)
+    st = Stack(shapes, layers, batch=1, x_dtype=q.PG_Q16, fused=args.fused)
     stream = torch.cuda.current_stream()
     use_graph = not args.no_graph
     if use_graph:
@@ -97,24 +97,44 @@ def run_stack(args):
     ms_per_tok = max(gpu_ms, wall * 1e3) / args.steps
     log(f"timed {args.steps} tokens: {gpu_ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
 
-    # qgemv kernel durations: events around every qgemv launch of a second pass
+    # Per-launch kernel durations: events around every product launch of a
+    # second pass over the same tokens.  A spin kernel queued first holds the
+    # GPU while the host enqueues, so the events time back-to-back GPU work,
+    # not the host's launch rate.
     qg_ms, qg_bytes, launches = 0.0, 0, 0
     evs = []
-    for _ in range(args.steps):
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.25))             # ~0.25 s of GPU clock cycles
+    prof_tokens = 2
+    for _ in range(prof_tokens):
         for layer in range(layers):
             for site in ORDER:
                 n, k = st.shapes[site]
-                src = st.h0 if (site == "qkv" and layer == 0) else st.out["down" if site == "qkv" else
-                                                                          {"o": "qkv", "gu": "o", "down": "gu"}[site]]
-                dt_in = q.PG_F16 if (site == "qkv" and layer == 0) else q.PG_F32
-                flags = 0 if (site == "qkv" and layer == 0) else q.PG_FLAG_RMSNORM
-                q.pg_fwht_rotate(src, dt_in, st.xrot, st.x_dtype, st.signs[layer][site], 1, k, flags)
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                q.pg_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.xrot, st.x_dtype, 1,
-                           st.out[site])
-                b.record(stream)
+                if not st.fused:
+                    # split path: the rotation launch is not timed, the product is
+                    first = site == "qkv" and layer == 0
+                    prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
+                    q.pg_fwht_rotate(st.h0 if first else st.out[prev], q.PG_F16 if first else q.PG_F32, st.xrot,
+                                     q.PG_Q16, st.signs[layer][site], 1, k, 0 if first else q.PG_FLAG_RMSNORM)
+                    a.record(stream)
+                    q.pg_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.xrot, q.PG_Q16, 1,
+                               st.out[site])
+                    b.record(stream)
+                elif site == "qkv" and layer == 0:
+                    a.record(stream)
+                    q.pg_rot_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.h0, q.PG_F16, k,
+                                   st.signs[layer][site], 0, None, 0, 1, st.out[site], st.ss[site])
+                    b.record(stream)
+                else:
+                    prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
+                    n_prev = st.shapes[prev][0]
+                    a.record(stream)
+                    q.pg_rot_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.out[prev], q.PG_F32,
+                                   n_prev, st.signs[layer][site], q.PG_FLAG_RMSNORM, st.ss[prev],
+                                   (n_prev + 7) // 8, 1, st.out[site], st.ss[site])
+                    b.record(stream)
                 evs.append((a, b))
                 qg_bytes += st.codes[layer][site].numel() + 2 * st.scales[layer][site].numel()
                 launches += 1
@@ -132,10 +152,13 @@ def run_stack(args):
                                f"{layers}-layer linear stack, batch 1, random trellis bitstreams",
                    "layers": layers, "batch": 1, "bytes_per_token": st.bytes_per_token,
                    "tok_per_s": round(tok_s, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "hip_graphs": use_graph, "launches_per_token": 8 * layers},
+                   "hip_graphs": use_graph, "launches_per_token": (4 if st.fused else 8) * layers,
+                   "path": "fused" if st.fused else "split"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "qgemv", "launches": launches, "avg_launch_us": round(1e3 * qg_ms / launches, 3)},
+                     "kernel": ("k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
+                                if st.fused else "k_qgemv_q16 (pg_qgemv on PG_Q16 activations)"),
+                     "launches": launches, "avg_launch_us": round(1e3 * qg_ms / launches, 3)},
     }
     return res
 
@@ -148,6 +171,7 @@ def main():
     ap.add_argument("--workload", default="qwen36", choices=["qwen36", "llama32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--fused", action="store_true", help="one pg_rot_qgemv launch per stage instead of rotation + qgemv")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "

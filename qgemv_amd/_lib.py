@@ -21,7 +21,7 @@ PG_F32, PG_F16, PG_BF16, PG_Q16 = 0, 1, 2, 3
 PG_FLAG_RMSNORM = 1
 
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
-           "pg_decode", "pg_fwht_rotate", "pg_qgemv", "pg_qgemm")
+           "pg_decode", "pg_fwht_rotate", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm")
 
 
 class PgError(RuntimeError):
@@ -39,6 +39,11 @@ def lib():
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        # torch ships its own HIP runtime under the same soname
+        # (libamdhip64.so.7); loading torch first makes libpingala bind to that
+        # one, so the process holds a single HIP runtime and torch's device
+        # buffers and streams are valid in the library
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
         L.pg_version.restype = i32
@@ -59,6 +64,8 @@ def lib():
         L.pg_fwht_rotate.argtypes = [vp, i32, vp, i32, vp, i64, i64, u32, vp]
         L.pg_qgemv.restype = i32
         L.pg_qgemv.argtypes = [vp, vp, i64, i64, vp, i32, i32, vp, vp]
+        L.pg_rot_qgemv.restype = i32
+        L.pg_rot_qgemv.argtypes = [vp, vp, i64, i64, vp, i32, i64, vp, u32, vp, i64, i32, vp, vp, vp]
         L.pg_qgemm.restype = i32
         L.pg_qgemm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
         _LIB = L
@@ -135,6 +142,12 @@ def pg_fwht_rotate(x, in_dtype: int, y, out_dtype: int, sign_bits, rows: int, k:
 def pg_qgemv(codes, scales, n: int, k: int, x_rot, x_dtype: int, batch: int, y, stream=None) -> None:
     _check(lib().pg_qgemv(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot), x_dtype, batch, _ptr(y),
                           _stream(stream)))
+
+
+def pg_rot_qgemv(codes, scales, n: int, k: int, x, x_dtype: int, ldx: int, sign_bits, flags: int, ss_in,
+                 ss_ld: int, batch: int, y, ss_out=None, stream=None) -> None:
+    _check(lib().pg_rot_qgemv(_ptr(codes), _ptr(scales), n, k, _ptr(x), x_dtype, ldx, _ptr(sign_bits), flags,
+                              _ptr(ss_in), ss_ld, batch, _ptr(y), _ptr(ss_out), _stream(stream)))
 
 
 def pg_qgemm(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, stream=None) -> None:

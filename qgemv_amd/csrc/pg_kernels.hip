@@ -554,6 +554,258 @@ __global__ __launch_bounds__(512) void k_qgemv_q16(const uint8_t* __restrict__ c
     }
 }
 
+// ------------------------------------------------ fused stage of a stack
+// y = W~ . R . n(x) in one launch: the activation rotation (with the RMS
+// normalisation and fp16 rounding of PG_FLAG_RMSNORM) moves into the
+// product's prologue.  Each wave rotates exactly the 128-blocks whose chunks
+// it consumes (block w*4 + jb + 4W*i for team lanes 2jb, 2jb+1 of round i),
+// quantises them to 16-bit digits in its own LDS region and then runs the
+// same decode / dot-product loop as k_qgemv_q16.  Every workgroup redoes the
+// rotation of the whole row (spread over its waves).  The RMS of x comes
+// from the per-8-row sums of squares the previous stage wrote (ss_in), or
+// from x itself.  The epilogue writes y and the sums of squares of this
+// launch's 8-row groups (ss_out).
+struct RotLayout {
+    int rounds;      // ceil(nchunk / (8W))
+    int bregion;     // LDS bytes per batch row in a wave's region
+    int wave_bytes;
+};
+
+__host__ __device__ inline RotLayout rot_layout(int k, int W, int BS) {
+    RotLayout L;
+    const int nchunk = k / 64;
+    L.rounds = (nchunk + 8 * W - 1) / (8 * W);
+    L.bregion = L.rounds * (1024 + 16 + 32);
+    L.wave_bytes = BS * L.bregion;
+    return L;
+}
+
+template <int BS>
+__global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ codes,
+                                                   const uint16_t* __restrict__ scales, int n, int k,
+                                                   const void* __restrict__ x, int x_dt, int64_t ldx,
+                                                   const uint8_t* __restrict__ sign_bits, uint32_t flags,
+                                                   const float* __restrict__ ss_in, int64_t ss_ld, int batch,
+                                                   float* __restrict__ y, float* __restrict__ ss_out) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int W = nthr >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int team = lane >> 3, tl = lane & 7;
+    const int row = blockIdx.x * 8 + team;
+    const int kg = k >> 2, nchunk = k >> 6, nbk = k >> 7;
+    const int cstep = 8 * W;
+    const RotLayout L = rot_layout(k, W, BS);
+    uint8_t* wlds = lds + wave * L.wave_bytes;
+    float* red = reinterpret_cast<float*>(lds + W * L.wave_bytes);     // [W][8][BS]
+    float* invs = red + W * 8 * BS;                                    // [BS]
+    float* wsum = invs + BS;                                           // [W][BS]
+    const uint8_t* rp = codes + (int64_t)(row < n ? row : n - 1) * kg;
+    const uint16_t* sp = scales + (int64_t)(row < n ? row : n - 1) * nbk;
+    const int cfirst = wave * 8 + tl;
+    const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
+    const float cnorm = 0.08838834764831845f;   // 2^-3.5
+    for (int b0 = 0; b0 < batch; b0 += BS) {
+        const int bs = batch - b0 < BS ? batch - b0 : BS;
+        if (b0 > 0) __syncthreads();
+        // codes of the first chunk in flight first
+        uint4 q0 = cfirst < nchunk ? *reinterpret_cast<const uint4*>(rp + 16 * cfirst) : make_uint4(0, 0, 0, 0);
+        float ws0 = cfirst < nchunk ? h2f(sp[cfirst >> 1]) : 0.0f;
+        // RMS of each batch row's input
+        if (norm) {
+            for (int b = 0; b < bs; ++b) {
+                float ssum = 0.0f;
+                if (ss_in) {
+                    const float* sr = ss_in + (int64_t)(b0 + b) * ss_ld;
+                    for (int i = tid; i < k / 8; i += nthr) ssum += sr[i];
+                } else {
+                    for (int i = tid; i < k; i += nthr) {
+                        const float v = load_elem(x, x_dt, (int64_t)(b0 + b) * ldx + i);
+                        ssum += v * v;
+                    }
+                }
+                ssum = wave_sum(ssum);
+                if (lane == 0) wsum[wave * BS + b] = ssum;
+            }
+            __syncthreads();
+            if (tid < bs) {
+                float t = 0.0f;
+                for (int w = 0; w < W; ++w) t += wsum[w * BS + tid];
+                invs[tid] = 1.0f / sqrtf(t / (float)k + 1e-6f);
+            }
+            __syncthreads();
+        }
+        // rotate this wave's blocks into 16-bit digits in its LDS region
+        for (int b = 0; b < bs; ++b) {
+            const float inv = norm ? invs[b] : 1.0f;
+            uint8_t* breg = wlds + b * L.bregion;
+            float* sxw = reinterpret_cast<float*>(breg + L.rounds * 1024);
+            int* sumw = reinterpret_cast<int*>(breg + L.rounds * 1024 + L.rounds * 16);
+            const int64_t xb = (int64_t)(b0 + b) * ldx;
+            for (int i = 0; i < L.rounds; ++i) {
+                float va[4], vc[4];
+                uint32_t sg[4][2];
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    const int bl = wave * 4 + jb + 4 * W * i;
+                    const int blc = bl < nbk ? bl : nbk - 1;
+                    const int i0 = blc * 128 + lane, i1 = i0 + 64;
+                    va[jb] = load_elem(x, x_dt, xb + i0);
+                    vc[jb] = load_elem(x, x_dt, xb + i1);
+                    sg[jb][0] = sign_bits[i0 >> 3];
+                    sg[jb][1] = sign_bits[i1 >> 3];
+                }
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    const int bl = wave * 4 + jb + 4 * W * i;
+                    if (bl >= nbk) break;                                   // wave-uniform
+                    float a = va[jb], c = vc[jb];
+                    if (norm) {
+                        a = h2f(f2h(a * inv));
+                        c = h2f(f2h(c * inv));
+                    }
+                    if ((sg[jb][0] >> (lane & 7)) & 1) a = -a;
+                    if ((sg[jb][1] >> (lane & 7)) & 1) c = -c;
+                    {
+                        const float t0 = a + c, t1 = a - c;
+                        a = t0;
+                        c = t1;
+                    }
+                    float pa = xor_lane32(a, lane), pc = xor_lane32(c, lane);
+                    bool up = (lane & 32) != 0;
+                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
+                    pa = xor_lane16(a, lane); pc = xor_lane16(c, lane); up = (lane & 16) != 0;
+                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
+                    pa = xor_lane<8>(a, lane); pc = xor_lane<8>(c, lane); up = (lane & 8) != 0;
+                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
+                    pa = xor_lane<4>(a, lane); pc = xor_lane<4>(c, lane); up = (lane & 4) != 0;
+                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
+                    pa = xor_lane<2>(a, lane); pc = xor_lane<2>(c, lane); up = (lane & 2) != 0;
+                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
+                    pa = xor_lane<1>(a, lane); pc = xor_lane<1>(c, lane); up = (lane & 1) != 0;
+                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
+                    a *= cnorm;
+                    c *= cnorm;
+                    const float mx = wave_max(fmaxf(fabsf(a), fabsf(c)));
+                    const float inv_sx = mx > 0.0f ? (float)Q16_MAXQ / mx : 0.0f;
+                    const int qa = (int)rintf(a * inv_sx);
+                    const int qc = (int)rintf(c * inv_sx);
+                    // element e = lane (first half-block) and lane + 64 (second)
+                    const int off = 1024 * i + 128 * (2 * jb) + 32 * (lane >> 4) + 4 * (lane & 3) + ((lane >> 2) & 3);
+                    const int ha = (qa + 128) >> 8, hc = (qc + 128) >> 8;
+                    breg[off] = (uint8_t)(int8_t)ha;
+                    breg[off + 16] = (uint8_t)(int8_t)(qa - (ha << 8));
+                    breg[off + 128] = (uint8_t)(int8_t)hc;
+                    breg[off + 128 + 16] = (uint8_t)(int8_t)(qc - (hc << 8));
+                    const int sa = wave_sum_i(qa), sc = wave_sum_i(qc);
+                    if (lane == 0) {
+                        sxw[4 * i + jb] = mx / (float)Q16_MAXQ;
+                        sumw[8 * i + 2 * jb] = sa;
+                        sumw[8 * i + 2 * jb + 1] = sc;
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        float acc[BS];
+#pragma unroll
+        for (int b = 0; b < BS; ++b) acc[b] = 0.0f;
+        constexpr int U = 4;
+        for (int c0 = wave * 8; c0 < nchunk; c0 += U * cstep) {
+            uint4 qu[U];
+            float wsu[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + tl + u * cstep;
+                if (u == 0 && c0 == wave * 8) {
+                    qu[u] = q0;
+                    wsu[u] = ws0;
+                } else {
+                    qu[u] = c < nchunk ? *reinterpret_cast<const uint4*>(rp + 16 * c) : make_uint4(0, 0, 0, 0);
+                    wsu[u] = c < nchunk ? h2f(sp[c >> 1]) : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (c0 + u * cstep >= nchunk) break;                 // wave-uniform
+                const int c = c0 + tl + u * cstep;
+                const bool valid = c < nchunk;
+                const int round = (c0 - wave * 8) / cstep + u;
+                const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)qu[u].w, 0x111, 0xf, 0xf, true);
+                const uint32_t dp0 = (c & 1) ? left : 0u;
+                int hi[BS], lo[BS];
+#pragma unroll
+                for (int b = 0; b < BS; ++b) { hi[b] = 0; lo[b] = 0; }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    uint32_t P[4];
+                    const uint32_t w4[4] = {qu[u].x, qu[u].y, qu[u].z, qu[u].w};
+                    planes_of(w4[m], m == 0 ? dp0 : w4[m - 1], P);
+#pragma unroll
+                    for (int b = 0; b < BS; ++b) {
+                        if (b < bs) {
+                            const uint4* xp = reinterpret_cast<const uint4*>(wlds + b * L.bregion + 1024 * round +
+                                                                             128 * tl + 32 * m);
+                            const uint4 xh = xp[0], xl = xp[1];
+                            int h = hi[b], l = lo[b];
+                            h = __builtin_amdgcn_sdot4((int)P[0], (int)xh.x, h, false);
+                            l = __builtin_amdgcn_sdot4((int)P[0], (int)xl.x, l, false);
+                            h = __builtin_amdgcn_sdot4((int)P[1], (int)xh.y, h, false);
+                            l = __builtin_amdgcn_sdot4((int)P[1], (int)xl.y, l, false);
+                            h = __builtin_amdgcn_sdot4((int)P[2], (int)xh.z, h, false);
+                            l = __builtin_amdgcn_sdot4((int)P[2], (int)xl.z, l, false);
+                            h = __builtin_amdgcn_sdot4((int)P[3], (int)xh.w, h, false);
+                            l = __builtin_amdgcn_sdot4((int)P[3], (int)xl.w, l, false);
+                            hi[b] = h;
+                            lo[b] = l;
+                        }
+                    }
+                }
+                if (valid) {
+#pragma unroll
+                    for (int b = 0; b < BS; ++b) {
+                        if (b < bs) {
+                            const uint8_t* breg = wlds + b * L.bregion;
+                            const float sxv = reinterpret_cast<const float*>(breg + L.rounds * 1024)[4 * round + (tl >> 1)];
+                            const int qs = reinterpret_cast<const int*>(breg + L.rounds * 1024 + L.rounds * 16)[8 * round + tl];
+                            const int t = 2 * (hi[b] * 256 + lo[b]) - 7 * qs;
+                            acc[b] += (wsu[u] * sxv) * (float)t;
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < BS; ++b) {
+            float v = acc[b];
+            v += xor_lane<4>(v, lane);
+            v += xor_lane<2>(v, lane);
+            v += xor_lane<1>(v, lane);
+            if (tl == 0) red[(wave * 8 + team) * BS + b] = v;
+        }
+        __syncthreads();
+        float v = 0.0f;
+        const int t = tid / BS, b = tid % BS;
+        if (tid < 8 * BS) {
+            for (int w = 0; w < W; ++w) v += red[(w * 8 + t) * BS + b];
+            const int r = blockIdx.x * 8 + t;
+            if (r < n && b < bs) y[(int64_t)(b0 + b) * n + r] = v;
+        }
+        if (ss_out) {
+            // sum of squares of this workgroup's 8 rows, per batch row
+            __syncthreads();
+            if (tid < 8 * BS) red[tid] = (blockIdx.x * 8 + t < n) ? v * v : 0.0f;
+            __syncthreads();
+            if (tid < bs) {
+                float ssq = 0.0f;
+                for (int tt = 0; tt < 8; ++tt) ssq += red[tt * BS + tid];
+                ss_out[(int64_t)(b0 + tid) * ((n + 7) / 8) + blockIdx.x] = ssq;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------- qgemm
 // Prompt product Y[m][n] on the matrix cores.  Workgroup tile: 128 rows of X
 // by 128 weight rows, K advanced 64 at a time (half a scale block).  Each
@@ -761,6 +1013,40 @@ int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
         hipLaunchKernelGGL(k_qgemv_v1<1>, grid, dim3(256), per_row, st, codes, scales, (int)n, (int)k, x, x_dt, batch, y);
     }
     return hip_check(hipGetLastError(), "pg_qgemv launch");
+}
+
+namespace {
+
+template <int BS>
+int launch_rot_bs(int W, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
+                  int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, const float* ss_in,
+                  int64_t ss_ld, int batch, float* y, float* ss_out, hipStream_t st) {
+    const dim3 grid((unsigned)((n + 7) / 8));
+    const RotLayout L = rot_layout((int)k, W, BS);
+    const size_t lds = (size_t)W * L.wave_bytes + (size_t)W * 8 * BS * 4 + BS * 4 + (size_t)W * BS * 4;
+    hipLaunchKernelGGL((k_rot_qgemv<BS>), grid, dim3(64 * W), lds, st, codes, scales, (int)n, (int)k, x, x_dt, ldx,
+                       sign_bits, flags, ss_in, ss_ld, batch, y, ss_out);
+    return hip_check(hipGetLastError(), "pg_rot_qgemv launch");
+}
+
+}  // namespace
+
+int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
+                     int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, const float* ss_in,
+                     int64_t ss_ld, int batch, float* y, float* ss_out, pg_stream_t s) {
+    const int64_t wgs = (n + 7) / 8;
+    int W = 1;
+    while (W < 8 && wgs * W < 2048 && (k / 64) >= 16 * W) W *= 2;
+    const size_t budget = 96 * 1024;
+    int bs = 1;
+    while (bs < 8 && bs < batch && (size_t)W * rot_layout((int)k, W, 2 * bs).wave_bytes + (size_t)W * 8 * 2 * bs * 8 <= budget) bs *= 2;
+    if ((size_t)W * rot_layout((int)k, W, 1).wave_bytes > budget)
+        return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    hipStream_t st = (hipStream_t)s;
+    if (bs >= 8) return launch_rot_bs<8>(W, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, ss_in, ss_ld, batch, y, ss_out, st);
+    if (bs >= 4) return launch_rot_bs<4>(W, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, ss_in, ss_ld, batch, y, ss_out, st);
+    if (bs >= 2) return launch_rot_bs<2>(W, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, ss_in, ss_ld, batch, y, ss_out, st);
+    return launch_rot_bs<1>(W, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, ss_in, ss_ld, batch, y, ss_out, st);
 }
 
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x,

@@ -21,7 +21,8 @@ ORDER = ("qkv", "o", "gu", "down")
 
 
 class Stack:
-    def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_Q16):
+    def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_Q16,
+                 fused: bool = False):
         import torch
         self.shapes = synth.merged_shapes(shapes)
         self.raw_shapes = shapes
@@ -50,6 +51,11 @@ class Stack:
             xt = torch.float32 if x_dtype == L.PG_F32 else torch.float16
             self.xrot = torch.empty((b, kmax), dtype=xt, device=device)
         self.graph = None
+        # fused path: one pg_rot_qgemv per launch group; each stage also writes
+        # per-8-row sums of squares that the next stage's normalisation reads
+        self.fused = fused
+        self.ss = {site: torch.empty((b, (n + 7) // 8), dtype=torch.float32, device=device)
+                   for site, (n, _) in self.shapes.items()}
         self.out = {site: torch.empty((b, n), dtype=torch.float32, device=device)
                     for site, (n, _) in self.shapes.items()}
         h = shapes["q"][1]
@@ -57,6 +63,28 @@ class Stack:
 
     def token(self, stream=None, h_in=None):
         """Run one token through all layers; returns the last layer's d."""
+        if self.fused:
+            return self._token_fused(stream, h_in)
+        return self._token_split(stream, h_in)
+
+    def _token_fused(self, stream=None, h_in=None):
+        b = self.batch
+        for layer in range(self.layers):
+            for site in ORDER:
+                n, k = self.shapes[site]
+                if site == "qkv" and layer == 0:
+                    src = h_in if h_in is not None else self.h0
+                    L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, src, L.PG_F16, k,
+                                   self.signs[layer][site], 0, None, 0, b, self.out[site], self.ss[site], stream)
+                    continue
+                prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
+                n_prev = self.shapes[prev][0]
+                L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.out[prev], L.PG_F32,
+                               n_prev, self.signs[layer][site], L.PG_FLAG_RMSNORM, self.ss[prev], (n_prev + 7) // 8,
+                               b, self.out[site], self.ss[site], stream)
+        return self.out["down"]
+
+    def _token_split(self, stream=None, h_in=None):
         if self.batch != 1:
             raise NotImplementedError("the chained driver runs batch 1 (per-matrix batch products are separate)")
         for layer in range(self.layers):

@@ -1,0 +1,91 @@
+"""GPU parity of the fused stage pg_rot_qgemv (RMS normalisation + rotation +
+product in one launch) against the oracle's fp64 chain of the same steps."""
+import numpy as np
+import pytest
+
+import qgemv_amd as q
+from oracle import p8f
+from qgemv_amd import synth
+from qgemv_amd.stack import Stack
+from tests.helpers import TOL, dev, encoded_qwen, host, oracle_chain, rel_err, rel_err_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(codes, scales, x, x_dt, ldx, k, sb, flags, ss_in=None, ss_ld=0, want_ss=False):
+    import torch
+    n = codes.shape[0]
+    b = x.shape[0]
+    y = torch.empty((b, n), dtype=torch.float32, device="cuda")
+    ss = torch.empty((b, (n + 7) // 8), dtype=torch.float32, device="cuda") if want_ss else None
+    q.pg_rot_qgemv(dev(codes), dev(scales), n, k, dev(x), x_dt, ldx, dev(sb), flags,
+                   None if ss_in is None else dev(ss_in), ss_ld, b, y, ss)
+    torch.cuda.synchronize()
+    return host(y), (host(ss) if want_ss else None)
+
+
+@pytest.mark.parametrize("name", ["q", "o", "gate", "down"])
+def test_fp16_input_no_norm(name):
+    codes, scales = encoded_qwen(name)
+    k = codes.shape[1] * 4
+    x = synth.activations_fp16(1, k)
+    sb = synth.site_sign_bits(0, synth.SITE_OF[name], k)
+    y, _ = _run(codes, scales, x, q.PG_F16, k, k, sb, 0)
+    ref = p8f.gemv_ref(codes, scales, p8f.rotate(x.astype(np.float64), sb))
+    assert rel_err(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+@pytest.mark.parametrize("n,k,ldx", [(33, 128, 128), (100, 640, 700), (512, 2560, 6144), (64, 9728, 19456)])
+def test_rmsnorm_strided_input_sums_from_x_and_from_partials(n, k, ldx, batch):
+    rng = np.random.default_rng(n + k + batch)
+    codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
+    scales = synth.random_scale_bits(n, k, n)
+    x = (rng.standard_normal((batch, ldx)) * 7.0).astype(np.float32)
+    sb = rng.integers(0, 256, k // 8, dtype=np.uint8)
+    ref = p8f.gemv_ref(codes, scales, p8f.rotate(p8f.rmsnorm16(x[:, :k].astype(np.float64)), sb))
+    y1, ss1 = _run(codes, scales, x, q.PG_F32, ldx, k, sb, q.PG_FLAG_RMSNORM, want_ss=True)
+    assert np.max(rel_err_rows(y1, ref)) <= TOL
+    # partial sums of squares per 8 input values, as a previous stage writes them
+    ss_in = (x[:, :(ldx // 8) * 8].astype(np.float64) ** 2).reshape(batch, ldx // 8, 8).sum(axis=2).astype(np.float32)
+    y2, _ = _run(codes, scales, x, q.PG_F32, ldx, k, sb, q.PG_FLAG_RMSNORM, ss_in=ss_in, ss_ld=ldx // 8)
+    assert np.max(rel_err_rows(y2, ref)) <= TOL
+    # the output sums of squares match the oracle's output
+    ref_ss = np.zeros((batch, (n + 7) // 8))
+    for i in range((n + 7) // 8):
+        ref_ss[:, i] = np.sum(ref[:, 8 * i:8 * i + 8] ** 2, axis=1)
+    assert np.allclose(ss1, ref_ss, rtol=3e-3, atol=1e-30)
+
+
+@pytest.mark.parametrize("shapes_fn,layers", [(synth.qwen3_4b_shapes, 2), (synth.llama31_8b_shapes, 2)])
+def test_fused_chain_matches_oracle(shapes_fn, layers):
+    import torch
+    shapes = shapes_fn()
+    st = Stack(shapes, layers, fused=True)
+    got = host(st.token()).copy()
+    torch.cuda.synchronize()
+    codes, scales, signs = zip(*[st.host_arrays(l) for l in range(layers)])
+    ref = oracle_chain(list(codes), list(scales), list(signs), shapes, host(st.h0).astype(np.float64), layers)
+    assert rel_err(got, ref) <= TOL
+    d2 = host(st.token())
+    assert np.array_equal(d2.view(np.uint32), got.view(np.uint32))
+
+
+def test_fused_graph_replays_match_eager():
+    import torch
+    st = Stack(synth.qwen3_4b_shapes(), 3, fused=True)
+    eager = host(st.token()).copy()
+    st.capture()
+    for i in range(4):
+        st.out["down"].zero_()
+        torch.cuda.synchronize()
+        got = host(st.replay())
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), i
+        assert np.array_equal(host(st.token()).view(np.uint32), eager.view(np.uint32))
+
+
+def test_fused_and_split_paths_agree():
+    shapes = synth.llama31_8b_shapes()
+    a = host(Stack(shapes, 3, fused=True).token())
+    b = host(Stack(shapes, 3, fused=False).token())
+    assert rel_err(a, b) <= 1e-3

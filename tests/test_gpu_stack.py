@@ -11,11 +11,12 @@ from tests.helpers import TOL, host, oracle_chain, rel_err
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("shapes_fn,layers", [(synth.qwen3_4b_shapes, 2), (synth.llama31_8b_shapes, 2)])
-def test_chain_matches_oracle(shapes_fn, layers):
+def test_chain_matches_oracle(shapes_fn, layers, fused):
     import torch
     shapes = shapes_fn()
-    st = Stack(shapes, layers)
+    st = Stack(shapes, layers, fused=fused)
     d = st.token()
     torch.cuda.synchronize()
     got = host(d)
@@ -31,7 +32,7 @@ def test_graph_replays_match_eager():
     """A captured token replays bitwise-identically to the eager token, on
     every replay, with eager work and synchronisations in between."""
     import torch
-    st = Stack(synth.qwen3_4b_shapes(), 3)
+    st = Stack(synth.qwen3_4b_shapes(), 3, fused=False)
     eager = host(st.token()).copy()
     st.capture()
     for i in range(4):
@@ -49,6 +50,6 @@ def test_chain_f32_path_matches_q16_path():
     bar on the same stack (they differ only in the 16-bit activation rounding)."""
     import qgemv_amd as q
     shapes = synth.qwen3_4b_shapes()
-    a = host(Stack(shapes, 2, x_dtype=q.PG_Q16).token())
-    b = host(Stack(shapes, 2, x_dtype=q.PG_F32).token())
+    a = host(Stack(shapes, 2, x_dtype=q.PG_Q16, fused=False).token())
+    b = host(Stack(shapes, 2, x_dtype=q.PG_F32, fused=False).token())
     assert rel_err(a, b) <= 1e-3
