@@ -33,6 +33,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading),
+    or None when there is none or the kernel's source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if line.startswith(("traffic_bytes_per_launch:", "kernel_source:", "kernel_source_sha256:")))
+    src = os.path.join(ROOT, fields.get("kernel_source", "").strip())
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get(
+            "kernel_source_sha256", "").strip():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(seconds: float = 12.0):
     """The oracle (numpy fp64 decode + product), as it stands, on a bounded
     sample of the stack: layer-0 launch groups of the Qwen3-4B-shaped stack,
@@ -142,6 +159,9 @@ def run_stack(args):
     for a, b in evs:
         qg_ms += a.elapsed_time(b)
     achieved = qg_bytes / (qg_ms * 1e-3) / 1e9
+    kname = "k_rot_qgemv" if st.fused else "k_qgemv_q16"
+    wl = "qwen3-4b-36L-b1" if args.workload == "qwen36" else "llama3.1-8b-32L-b1"
+    traffic = committed_traffic(kname, wl)
     tok_s = 1e3 / ms_per_tok
     value = st.bytes_per_token * tok_s / 1e9
     res = {
@@ -155,7 +175,9 @@ def run_stack(args):
                    "hip_graphs": use_graph, "launches_per_token": (4 if st.fused else 8) * layers,
                    "path": "fused" if st.fused else "split"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes_per_launch": qg_bytes // launches,
                      "kernel": ("k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
                                 if st.fused else "k_qgemv_q16 (pg_qgemv on PG_Q16 activations)"),
                      "launches": launches, "avg_launch_us": round(1e3 * qg_ms / launches, 3)},
@@ -171,6 +193,8 @@ def main():
     ap.add_argument("--workload", default="qwen36", choices=["qwen36", "llama32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy 4 times (HBM-counter calibration) and exit")
     ap.add_argument("--fused", action="store_true", help="one pg_rot_qgemv launch per stage instead of rotation + qgemv")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -181,6 +205,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": 256 << 20, "bytes_written": 256 << 20,
+                          "launches": 4}), flush=True)
+        return
     res = run_stack(args)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
