@@ -142,15 +142,14 @@ def run_stack(args):
                 elif site == "qkv" and layer == 0:
                     a.record(stream)
                     q.pg_rot_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.h0, q.PG_F16, k,
-                                   st.signs[layer][site], 0, None, 0, 1, st.out[site], st.ss[site])
+                                   st.signs[layer][site], 0, 1, st.out[site])
                     b.record(stream)
                 else:
                     prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
                     n_prev = st.shapes[prev][0]
                     a.record(stream)
                     q.pg_rot_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.out[prev], q.PG_F32,
-                                   n_prev, st.signs[layer][site], q.PG_FLAG_RMSNORM, st.ss[prev],
-                                   (n_prev + 7) // 8, 1, st.out[site], st.ss[site])
+                                   n_prev, st.signs[layer][site], q.PG_FLAG_RMSNORM, 1, st.out[site])
                     b.record(stream)
                 evs.append((a, b))
                 qg_bytes += st.codes[layer][site].numel() + 2 * st.scales[layer][site].numel()

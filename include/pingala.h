@@ -162,28 +162,28 @@ int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype,
 int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
              const void* x_rot, int x_dtype, int batch, float* y, pg_stream_t stream);
 
-/* One stage of a linear stack in a single launch (the survey's next step:
- * RMS normalisation and rotation moved into the product's prologue):
+/* One stage of a linear stack in a single launch: the RMS normalisation and
+ * the run-time rotation of the activations (landing page, section "How it
+ * works": a random Hadamard rotation is applied before coding, so the
+ * activations take the same rotation) are the product's prologue:
  *   y[b] = W~ . R . n(x[b][0:k])
  * with n(v) = fp16_RNE(v / sqrt(mean(v^2) + 1e-6)) under PG_FLAG_RMSNORM
- * (fp32 math), n(v) = v otherwise, R the input site's rotation, and the
- * rotated activations carried at 16-bit precision as in PG_Q16.
+ * (fp32 math, mean over the k values), n(v) = v otherwise, R the input
+ * site's rotation (as pg_fwht_rotate), and the rotated activations carried
+ * at 16-bit precision as in PG_Q16 (relative error <= 2^-16 of each
+ * 128-block's largest value).
  *   codes, scales  as for pg_qgemv
  *   x        device [batch][ldx] of x_dtype (PG_F32 / PG_F16); the first k
  *            values of each row are the input (e.g. the q part of a merged
  *            q/k/v output); ldx >= k
  *   sign_bits device u8 [k/8]
- *   ss_in    NULL, or (PG_FLAG_RMSNORM only) device f32 [batch][ss_ld] with
- *            ss_in[b][i] = sum of x[b][8i..8i+7]^2, as written by the previous
- *            stage's ss_out; ss_ld >= k/8.  NULL: the sum is taken over x.
  *   y        device f32 [batch][n] out
- *   ss_out   NULL, or device f32 [batch][ceil(n/8)] out: sum of y[b][8i..8i+7]^2
  *   batch    1..8
- * x and y may not overlap. */
+ * k <= 16384 (PG_ERR_UNSUPPORTED beyond).  x and y may not overlap.  The
+ * summation order is fixed: repeated calls are bitwise identical. */
 int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const void* x, int x_dtype, int64_t ldx, const uint8_t* sign_bits,
-                 uint32_t flags, const float* ss_in, int64_t ss_ld, int batch, float* y,
-                 float* ss_out, pg_stream_t stream);
+                 uint32_t flags, int batch, float* y, pg_stream_t stream);
 
 /* Prompt-processing product for m activation rows (landing page, section
  * "Results": prompt reading is the mat-mat path):

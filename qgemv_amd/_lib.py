@@ -65,7 +65,7 @@ def lib():
         L.pg_qgemv.restype = i32
         L.pg_qgemv.argtypes = [vp, vp, i64, i64, vp, i32, i32, vp, vp]
         L.pg_rot_qgemv.restype = i32
-        L.pg_rot_qgemv.argtypes = [vp, vp, i64, i64, vp, i32, i64, vp, u32, vp, i64, i32, vp, vp, vp]
+        L.pg_rot_qgemv.argtypes = [vp, vp, i64, i64, vp, i32, i64, vp, u32, i32, vp, vp]
         L.pg_qgemm.restype = i32
         L.pg_qgemm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
         _LIB = L
@@ -144,10 +144,10 @@ def pg_qgemv(codes, scales, n: int, k: int, x_rot, x_dtype: int, batch: int, y, 
                           _stream(stream)))
 
 
-def pg_rot_qgemv(codes, scales, n: int, k: int, x, x_dtype: int, ldx: int, sign_bits, flags: int, ss_in,
-                 ss_ld: int, batch: int, y, ss_out=None, stream=None) -> None:
+def pg_rot_qgemv(codes, scales, n: int, k: int, x, x_dtype: int, ldx: int, sign_bits, flags: int, batch: int, y,
+                 stream=None) -> None:
     _check(lib().pg_rot_qgemv(_ptr(codes), _ptr(scales), n, k, _ptr(x), x_dtype, ldx, _ptr(sign_bits), flags,
-                              _ptr(ss_in), ss_ld, batch, _ptr(y), _ptr(ss_out), _stream(stream)))
+                              batch, _ptr(y), _stream(stream)))
 
 
 def pg_qgemm(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, stream=None) -> None:

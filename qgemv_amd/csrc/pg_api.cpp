@@ -115,8 +115,7 @@ int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
 }
 
 int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x, int x_dtype,
-                 int64_t ldx, const uint8_t* sign_bits, uint32_t flags, const float* ss_in, int64_t ss_ld,
-                 int batch, float* y, float* ss_out, pg_stream_t stream) {
+                 int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y, pg_stream_t stream) {
     pg::clear_error();
     PG_TRY(check_nk(n, k));
     if (batch < 1 || batch > 8) return pg::fail(PG_ERR_INVALID_ARG, "batch must be 1..8 (got %d)", batch);
@@ -127,18 +126,11 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
     PG_TRY(check_ptr(scales, 2, "scales"));
     PG_TRY(check_ptr(x, x_dtype == PG_F32 ? 4 : 2, "x"));
     PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
-    PG_TRY(check_ptr(y, 16, "y"));
-    if (ss_in) {
-        PG_TRY(check_ptr(ss_in, 4, "ss_in"));
-        if (!(flags & PG_FLAG_RMSNORM)) return pg::fail(PG_ERR_INVALID_ARG, "ss_in given without PG_FLAG_RMSNORM");
-        if (ss_ld < k / 8) return pg::fail(PG_ERR_INVALID_ARG, "ss_ld (%lld) < k/8", (long long)ss_ld);
-    }
-    if (ss_out) PG_TRY(check_ptr(ss_out, 4, "ss_out"));
+    PG_TRY(check_ptr(y, 4, "y"));
     const uintptr_t ya = (uintptr_t)y, xa = (uintptr_t)x;
     const size_t yb = (size_t)batch * n * 4, xb = (size_t)batch * ldx * (x_dtype == PG_F32 ? 4 : 2);
     if (xa < ya + yb && ya < xa + xb) return pg::fail(PG_ERR_INVALID_ARG, "x and y overlap");
-    return pg::launch_rot_qgemv(codes, scales, n, k, x, x_dtype, ldx, sign_bits, flags, ss_in, ss_ld, batch, y,
-                                ss_out, stream);
+    return pg::launch_rot_qgemv(codes, scales, n, k, x, x_dtype, ldx, sign_bits, flags, batch, y, stream);
 }
 
 int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,

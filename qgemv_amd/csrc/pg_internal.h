@@ -37,8 +37,8 @@ int launch_fwht(const void* x, int in_dt, void* y, int out_dt, const uint8_t* si
 int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const void* x, int x_dt, int batch, float* y, pg_stream_t s);
 int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
-                     int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, const float* ss_in,
-                     int64_t ss_ld, int batch, float* y, float* ss_out, pg_stream_t s);
+                     int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
+                     pg_stream_t s);
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const uint16_t* x, int64_t m, float* y, pg_stream_t s);
 

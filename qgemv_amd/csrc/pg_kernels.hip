@@ -556,252 +556,248 @@ __global__ __launch_bounds__(512) void k_qgemv_q16(const uint8_t* __restrict__ c
 
 // ------------------------------------------------ fused stage of a stack
 // y = W~ . R . n(x) in one launch: the activation rotation (with the RMS
-// normalisation and fp16 rounding of PG_FLAG_RMSNORM) moves into the
-// product's prologue.  Each wave rotates exactly the 128-blocks whose chunks
-// it consumes (block w*4 + jb + 4W*i for team lanes 2jb, 2jb+1 of round i),
-// quantises them to 16-bit digits in its own LDS region and then runs the
-// same decode / dot-product loop as k_qgemv_q16.  Every workgroup redoes the
-// rotation of the whole row (spread over its waves).  The RMS of x comes
-// from the per-8-row sums of squares the previous stage wrote (ss_in), or
-// from x itself.  The epilogue writes y and the sums of squares of this
-// launch's 8-row groups (ss_out).
-struct RotLayout {
-    int rounds;      // ceil(nchunk / (8W))
-    int bregion;     // LDS bytes per batch row in a wave's region
-    int wave_bytes;
+// normalisation and fp16 rounding of PG_FLAG_RMSNORM) is the product's
+// prologue.  One workgroup per CU owns R consecutive weight rows with all of
+// their k columns, so the whole launch is one pass over the codes with a
+// single memory round trip per lane:
+//   1. every lane requests its x values first and then all of its code
+//      chunks at once (they do not depend on x), so the rotation below runs
+//      while the codes are still in flight;
+//   2. the sum of squares of x gives the RMS; each wave rotates the 128-blocks
+//      w, w + W, ... (lane l holds elements l and l + 64: the distance-64
+//      butterfly is inside the lane, the others exchange lanes), quantises
+//      them to 16-bit digits (PG_Q16 arithmetic) and stores them in LDS,
+//      where each 64-value chunk takes 144 bytes (128 + 16 of padding, so the
+//      8 lanes of a team reading consecutive chunks hit distinct banks);
+//   3. team T of 8 lanes takes column group cg = T % CG (chunks 8 cg .. 8 cg
+//      + 7, one 128-byte line of a row per team) and rows rp, rp + RP, ...
+//      with rp = T / CG, so a lane reads its chunk's digits once per batch
+//      row and uses them for all of its rows; levels come from bit planes
+//      (planes_of) and meet the digits in v_dot4_i32_i8;
+//   4. team sums go to LDS per (row, column group) and are added in column
+//      group order.
+// Launch shape (host): W waves, R rows per workgroup, CG = ceil(k/512),
+// RP = 8W / CG, at most RS rows per lane and XS 128-blocks per wave.
+struct FusedShape {
+    int W, R, CG, RP, RS, XS, BT;
 };
 
-__host__ __device__ inline RotLayout rot_layout(int k, int W, int BS) {
-    RotLayout L;
-    const int nchunk = k / 64;
-    L.rounds = (nchunk + 8 * W - 1) / (8 * W);
-    L.bregion = L.rounds * (1024 + 16 + 32);
-    L.wave_bytes = BS * L.bregion;
-    return L;
+__host__ __device__ inline int fused_chunk_pitch() { return 144; }
+
+// LDS bytes per batch row: digits, block scales, chunk sums
+__host__ __device__ inline int fused_row_bytes(int k) {
+    return ((k / 64) * fused_chunk_pitch() + (k / 128) * 4 + (k / 64) * 4 + 15) & ~15;
 }
 
-template <int BS>
+__host__ inline size_t fused_lds_bytes(int k, const FusedShape& S) {
+    return (size_t)S.BT * fused_row_bytes(k) + (size_t)S.BT * S.R * S.CG * 4 + (size_t)S.W * 4;
+}
+
+template <int XDT, int XS, int RS>
 __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ codes,
-                                                   const uint16_t* __restrict__ scales, int n, int k,
-                                                   const void* __restrict__ x, int x_dt, int64_t ldx,
-                                                   const uint8_t* __restrict__ sign_bits, uint32_t flags,
-                                                   const float* __restrict__ ss_in, int64_t ss_ld, int batch,
-                                                   float* __restrict__ y, float* __restrict__ ss_out) {
+                                                    const uint16_t* __restrict__ scales, int n, int k,
+                                                    const void* __restrict__ x, int64_t ldx,
+                                                    const uint8_t* __restrict__ sign_bits, uint32_t flags,
+                                                    int batch, float* __restrict__ y, int R, int CG, int RP,
+                                                    int BT) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int W = nthr >> 6;
     const int lane = tid & 63, wave = tid >> 6;
-    const int team = lane >> 3, tl = lane & 7;
-    const int row = blockIdx.x * 8 + team;
+    const int T = wave * 8 + (lane >> 3), tl = lane & 7;
     const int kg = k >> 2, nchunk = k >> 6, nbk = k >> 7;
-    const int cstep = 8 * W;
-    const RotLayout L = rot_layout(k, W, BS);
-    uint8_t* wlds = lds + wave * L.wave_bytes;
-    float* red = reinterpret_cast<float*>(lds + W * L.wave_bytes);     // [W][8][BS]
-    float* invs = red + W * 8 * BS;                                    // [BS]
-    float* wsum = invs + BS;                                           // [W][BS]
-    const uint8_t* rp = codes + (int64_t)(row < n ? row : n - 1) * kg;
-    const uint16_t* sp = scales + (int64_t)(row < n ? row : n - 1) * nbk;
-    const int cfirst = wave * 8 + tl;
+    const int row0 = blockIdx.x * R;
+    const int rb = fused_row_bytes(k);
+    const int PITCH = fused_chunk_pitch();
+    float* part = reinterpret_cast<float*>(lds + (size_t)BT * rb);      // [BT][R][CG]
+    float* wsum = part + (size_t)BT * R * CG;                           // [W]
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
-    const float cnorm = 0.08838834764831845f;   // 2^-3.5
-    for (int b0 = 0; b0 < batch; b0 += BS) {
-        const int bs = batch - b0 < BS ? batch - b0 : BS;
-        if (b0 > 0) __syncthreads();
-        // codes of the first chunk in flight first
-        uint4 q0 = cfirst < nchunk ? *reinterpret_cast<const uint4*>(rp + 16 * cfirst) : make_uint4(0, 0, 0, 0);
-        float ws0 = cfirst < nchunk ? h2f(sp[cfirst >> 1]) : 0.0f;
-        // RMS of each batch row's input
-        if (norm) {
-            for (int b = 0; b < bs; ++b) {
-                float ssum = 0.0f;
-                if (ss_in) {
-                    const float* sr = ss_in + (int64_t)(b0 + b) * ss_ld;
-                    for (int i = tid; i < k / 8; i += nthr) ssum += sr[i];
-                } else {
-                    for (int i = tid; i < k; i += nthr) {
-                        const float v = load_elem(x, x_dt, (int64_t)(b0 + b) * ldx + i);
-                        ssum += v * v;
-                    }
-                }
-                ssum = wave_sum(ssum);
-                if (lane == 0) wsum[wave * BS + b] = ssum;
-            }
-            __syncthreads();
-            if (tid < bs) {
-                float t = 0.0f;
-                for (int w = 0; w < W; ++w) t += wsum[w * BS + tid];
-                invs[tid] = 1.0f / sqrtf(t / (float)k + 1e-6f);
-            }
-            __syncthreads();
-        }
-        // rotate this wave's blocks into 16-bit digits in its LDS region
-        for (int b = 0; b < bs; ++b) {
-            const float inv = norm ? invs[b] : 1.0f;
-            uint8_t* breg = wlds + b * L.bregion;
-            float* sxw = reinterpret_cast<float*>(breg + L.rounds * 1024);
-            int* sumw = reinterpret_cast<int*>(breg + L.rounds * 1024 + L.rounds * 16);
-            const int64_t xb = (int64_t)(b0 + b) * ldx;
-            for (int i = 0; i < L.rounds; ++i) {
-                float va[4], vc[4];
-                uint32_t sg[4][2];
+    const float cnorm = 0.08838834764831845f;                          // 2^-3.5
+
+    // this lane's column of chunks and its rows
+    const int cg = T % CG, rp = T / CG;
+    const int c = 8 * cg + tl;
+    const bool col_ok = rp < RP && c < nchunk;
+    const int cc = c < nchunk ? c : nchunk - 1;
+
+    // x of one batch row: block bb = wave + W i, elements bb*128 + lane and + 64
+    float xv[XS][2];
+    auto load_x = [&](int b) {
+        const int64_t base = (int64_t)b * ldx;
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    const int bl = wave * 4 + jb + 4 * W * i;
-                    const int blc = bl < nbk ? bl : nbk - 1;
-                    const int i0 = blc * 128 + lane, i1 = i0 + 64;
-                    va[jb] = load_elem(x, x_dt, xb + i0);
-                    vc[jb] = load_elem(x, x_dt, xb + i1);
-                    sg[jb][0] = sign_bits[i0 >> 3];
-                    sg[jb][1] = sign_bits[i1 >> 3];
-                }
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    const int bl = wave * 4 + jb + 4 * W * i;
-                    if (bl >= nbk) break;                                   // wave-uniform
-                    float a = va[jb], c = vc[jb];
-                    if (norm) {
-                        a = h2f(f2h(a * inv));
-                        c = h2f(f2h(c * inv));
-                    }
-                    if ((sg[jb][0] >> (lane & 7)) & 1) a = -a;
-                    if ((sg[jb][1] >> (lane & 7)) & 1) c = -c;
-                    {
-                        const float t0 = a + c, t1 = a - c;
-                        a = t0;
-                        c = t1;
-                    }
-                    float pa = xor_lane32(a, lane), pc = xor_lane32(c, lane);
-                    bool up = (lane & 32) != 0;
-                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
-                    pa = xor_lane16(a, lane); pc = xor_lane16(c, lane); up = (lane & 16) != 0;
-                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
-                    pa = xor_lane<8>(a, lane); pc = xor_lane<8>(c, lane); up = (lane & 8) != 0;
-                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
-                    pa = xor_lane<4>(a, lane); pc = xor_lane<4>(c, lane); up = (lane & 4) != 0;
-                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
-                    pa = xor_lane<2>(a, lane); pc = xor_lane<2>(c, lane); up = (lane & 2) != 0;
-                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
-                    pa = xor_lane<1>(a, lane); pc = xor_lane<1>(c, lane); up = (lane & 1) != 0;
-                    a = up ? pa - a : a + pa; c = up ? pc - c : c + pc;
-                    a *= cnorm;
-                    c *= cnorm;
-                    const float mx = wave_max(fmaxf(fabsf(a), fabsf(c)));
-                    const float inv_sx = mx > 0.0f ? (float)Q16_MAXQ / mx : 0.0f;
-                    const int qa = (int)rintf(a * inv_sx);
-                    const int qc = (int)rintf(c * inv_sx);
-                    // element e = lane (first half-block) and lane + 64 (second)
-                    const int off = 1024 * i + 128 * (2 * jb) + 32 * (lane >> 4) + 4 * (lane & 3) + ((lane >> 2) & 3);
-                    const int ha = (qa + 128) >> 8, hc = (qc + 128) >> 8;
-                    breg[off] = (uint8_t)(int8_t)ha;
-                    breg[off + 16] = (uint8_t)(int8_t)(qa - (ha << 8));
-                    breg[off + 128] = (uint8_t)(int8_t)hc;
-                    breg[off + 128 + 16] = (uint8_t)(int8_t)(qc - (hc << 8));
-                    const int sa = wave_sum_i(qa), sc = wave_sum_i(qc);
-                    if (lane == 0) {
-                        sxw[4 * i + jb] = mx / (float)Q16_MAXQ;
-                        sumw[8 * i + 2 * jb] = sa;
-                        sumw[8 * i + 2 * jb + 1] = sc;
-                    }
-                }
+        for (int i = 0; i < XS; ++i) {
+            const int bb = wave + W * i;
+            const int e = (bb < nbk ? bb : 0) * 128 + lane;
+            if (XDT == PG_F32) {
+                xv[i][0] = ((const float*)x)[base + e];
+                xv[i][1] = ((const float*)x)[base + e + 64];
+            } else {
+                xv[i][0] = h2f(((const uint16_t*)x)[base + e]);
+                xv[i][1] = h2f(((const uint16_t*)x)[base + e + 64]);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_wave_barrier();
-        float acc[BS];
+    };
+    load_x(0);
+    // sign bits of elements lane and lane + 64 of each block (bits 2i, 2i + 1)
+    uint32_t sgn = 0;
 #pragma unroll
-        for (int b = 0; b < BS; ++b) acc[b] = 0.0f;
-        constexpr int U = 4;
-        for (int c0 = wave * 8; c0 < nchunk; c0 += U * cstep) {
-            uint4 qu[U];
-            float wsu[U];
+    for (int i = 0; i < XS; ++i) {
+        const int bb = wave + W * i;
+        const int e = (bb < nbk ? bb : 0) * 128 + lane;
+        sgn |= (uint32_t)((sign_bits[e >> 3] >> (e & 7)) & 1u) << (2 * i);
+        sgn |= (uint32_t)((sign_bits[(e + 64) >> 3] >> (e & 7)) & 1u) << (2 * i + 1);
+    }
+    // all code chunks of this lane (rows past n or R, and chunks past k, are
+    // clamped to valid addresses and masked out of the sums)
+    uint4 q[RS];
+    float ws[RS];
+    bool rok[RS];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + tl + u * cstep;
-                if (u == 0 && c0 == wave * 8) {
-                    qu[u] = q0;
-                    wsu[u] = ws0;
-                } else {
-                    qu[u] = c < nchunk ? *reinterpret_cast<const uint4*>(rp + 16 * c) : make_uint4(0, 0, 0, 0);
-                    wsu[u] = c < nchunk ? h2f(sp[c >> 1]) : 0.0f;
+    for (int j = 0; j < RS; ++j) {
+        const int r = rp + j * RP;
+        rok[j] = col_ok && r < R && row0 + r < n;
+        const int row = rok[j] ? row0 + r : (row0 < n ? row0 : n - 1);
+        q[j] = *reinterpret_cast<const uint4*>(codes + (int64_t)row * kg + 16 * cc);
+        ws[j] = h2f(scales[(int64_t)row * nbk + (cc >> 1)]);
+    }
+    for (int b0 = 0; b0 < batch; b0 += BT) {
+        const int bt = batch - b0 < BT ? batch - b0 : BT;
+        if (b0 > 0) __syncthreads();                      // previous tile's LDS reads are done
+        // ---- rotation of each batch row of the tile into LDS
+        for (int b = 0; b < bt; ++b) {
+            if (b0 + b > 0) load_x(b0 + b);
+            float inv = 1.0f;
+            if (norm) {
+                float ss = 0.0f;
+#pragma unroll
+                for (int i = 0; i < XS; ++i)
+                    if (wave + W * i < nbk) ss += xv[i][0] * xv[i][0] + xv[i][1] * xv[i][1];
+                ss = wave_sum(ss);
+                if (b > 0) __syncthreads();                    // wsum of the previous row consumed
+                if (lane == 0) wsum[wave] = ss;
+                __syncthreads();
+                float tot = 0.0f;
+                for (int w = 0; w < W; ++w) tot += wsum[w];
+                inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+            }
+            uint8_t* dig = lds + (size_t)b * rb;
+            float* sxr = reinterpret_cast<float*>(dig + nchunk * PITCH);
+            int* qsr = reinterpret_cast<int*>(dig + nchunk * PITCH + nbk * 4);
+#pragma unroll
+            for (int i = 0; i < XS; ++i) {
+                const int bb = wave + W * i;
+                if (bb >= nbk) break;                              // wave-uniform
+                float a = xv[i][0], cv = xv[i][1];
+                if (norm) {
+                    a = h2f(f2h(a * inv));
+                    cv = h2f(f2h(cv * inv));
+                }
+                if ((sgn >> (2 * i)) & 1u) a = -a;
+                if ((sgn >> (2 * i + 1)) & 1u) cv = -cv;
+                {
+                    const float t0 = a + cv, t1 = a - cv;
+                    a = t0;
+                    cv = t1;
+                }
+                float pa, pc;
+                bool up;
+                pa = xor_lane32(a, lane); pc = xor_lane32(cv, lane); up = (lane & 32) != 0;
+                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
+                pa = xor_lane16(a, lane); pc = xor_lane16(cv, lane); up = (lane & 16) != 0;
+                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
+                pa = xor_lane<8>(a, lane); pc = xor_lane<8>(cv, lane); up = (lane & 8) != 0;
+                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
+                pa = xor_lane<4>(a, lane); pc = xor_lane<4>(cv, lane); up = (lane & 4) != 0;
+                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
+                pa = xor_lane<2>(a, lane); pc = xor_lane<2>(cv, lane); up = (lane & 2) != 0;
+                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
+                pa = xor_lane<1>(a, lane); pc = xor_lane<1>(cv, lane); up = (lane & 1) != 0;
+                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
+                a *= cnorm;
+                cv *= cnorm;
+                const float mx = wave_max(fmaxf(fabsf(a), fabsf(cv)));
+                const float inv_sx = mx > 0.0f ? (float)Q16_MAXQ / mx : 0.0f;
+                const int qa = (int)rintf(a * inv_sx);
+                const int qc = (int)rintf(cv * inv_sx);
+                // element e of chunk 2bb (+1 for qc): group e/4 -> part m = e/16,
+                // byte 4 (e%4) + (e/4)%4 of the part's hi (and, +16, lo) digits
+                const int off = (lane >> 4) * 32 + 4 * (lane & 3) + ((lane >> 2) & 3);
+                uint8_t* d0 = dig + (2 * bb) * PITCH + off;
+                uint8_t* d1 = d0 + PITCH;
+                const int ha = (qa + 128) >> 8, hc = (qc + 128) >> 8;
+                d0[0] = (uint8_t)ha;
+                d0[16] = (uint8_t)(qa - 256 * ha);
+                d1[0] = (uint8_t)hc;
+                d1[16] = (uint8_t)(qc - 256 * hc);
+                const int sa = wave_sum_i(qa), sc = wave_sum_i(qc);
+                if (lane == 0) {
+                    sxr[bb] = mx / (float)Q16_MAXQ;
+                    qsr[2 * bb] = sa;
+                    qsr[2 * bb + 1] = sc;
                 }
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (c0 + u * cstep >= nchunk) break;                 // wave-uniform
-                const int c = c0 + tl + u * cstep;
-                const bool valid = c < nchunk;
-                const int round = (c0 - wave * 8) / cstep + u;
-                const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)qu[u].w, 0x111, 0xf, 0xf, true);
-                const uint32_t dp0 = (c & 1) ? left : 0u;
-                int hi[BS], lo[BS];
-#pragma unroll
-                for (int b = 0; b < BS; ++b) { hi[b] = 0; lo[b] = 0; }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    uint32_t P[4];
-                    const uint32_t w4[4] = {qu[u].x, qu[u].y, qu[u].z, qu[u].w};
-                    planes_of(w4[m], m == 0 ? dp0 : w4[m - 1], P);
-#pragma unroll
-                    for (int b = 0; b < BS; ++b) {
-                        if (b < bs) {
-                            const uint4* xp = reinterpret_cast<const uint4*>(wlds + b * L.bregion + 1024 * round +
-                                                                             128 * tl + 32 * m);
-                            const uint4 xh = xp[0], xl = xp[1];
-                            int h = hi[b], l = lo[b];
-                            h = __builtin_amdgcn_sdot4((int)P[0], (int)xh.x, h, false);
-                            l = __builtin_amdgcn_sdot4((int)P[0], (int)xl.x, l, false);
-                            h = __builtin_amdgcn_sdot4((int)P[1], (int)xh.y, h, false);
-                            l = __builtin_amdgcn_sdot4((int)P[1], (int)xl.y, l, false);
-                            h = __builtin_amdgcn_sdot4((int)P[2], (int)xh.z, h, false);
-                            l = __builtin_amdgcn_sdot4((int)P[2], (int)xl.z, l, false);
-                            h = __builtin_amdgcn_sdot4((int)P[3], (int)xh.w, h, false);
-                            l = __builtin_amdgcn_sdot4((int)P[3], (int)xl.w, l, false);
-                            hi[b] = h;
-                            lo[b] = l;
-                        }
-                    }
-                }
-                if (valid) {
-#pragma unroll
-                    for (int b = 0; b < BS; ++b) {
-                        if (b < bs) {
-                            const uint8_t* breg = wlds + b * L.bregion;
-                            const float sxv = reinterpret_cast<const float*>(breg + L.rounds * 1024)[4 * round + (tl >> 1)];
-                            const int qs = reinterpret_cast<const int*>(breg + L.rounds * 1024 + L.rounds * 16)[8 * round + tl];
-                            const int t = 2 * (hi[b] * 256 + lo[b]) - 7 * qs;
-                            acc[b] += (wsu[u] * sxv) * (float)t;
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < BS; ++b) {
-            float v = acc[b];
-            v += xor_lane<4>(v, lane);
-            v += xor_lane<2>(v, lane);
-            v += xor_lane<1>(v, lane);
-            if (tl == 0) red[(wave * 8 + team) * BS + b] = v;
         }
         __syncthreads();
-        float v = 0.0f;
-        const int t = tid / BS, b = tid % BS;
-        if (tid < 8 * BS) {
-            for (int w = 0; w < W; ++w) v += red[(w * 8 + t) * BS + b];
-            const int r = blockIdx.x * 8 + t;
-            if (r < n && b < bs) y[(int64_t)(b0 + b) * n + r] = v;
-        }
-        if (ss_out) {
-            // sum of squares of this workgroup's 8 rows, per batch row
-            __syncthreads();
-            if (tid < 8 * BS) red[tid] = (blockIdx.x * 8 + t < n) ? v * v : 0.0f;
-            __syncthreads();
-            if (tid < bs) {
-                float ssq = 0.0f;
-                for (int tt = 0; tt < 8; ++tt) ssq += red[tt * BS + tid];
-                ss_out[(int64_t)(b0 + tid) * ((n + 7) / 8) + blockIdx.x] = ssq;
+        // ---- decode and dot products, one batch row at a time
+        for (int b = 0; b < bt; ++b) {
+            // the planes are rebuilt per batch row rather than kept for all
+            // rows and positions at once (that would take 16 RS registers)
+#pragma unroll
+            for (int j = 0; j < RS; ++j) asm volatile("" : "+v"(q[j].x), "+v"(q[j].y), "+v"(q[j].z), "+v"(q[j].w));
+            const uint8_t* dig = lds + (size_t)b * rb;
+            const float sxv = reinterpret_cast<const float*>(dig + nchunk * PITCH)[cc >> 1];
+            const int qsv = reinterpret_cast<const int*>(dig + nchunk * PITCH + nbk * 4)[cc];
+            int hi[RS], lo[RS];
+#pragma unroll
+            for (int j = 0; j < RS; ++j) { hi[j] = 0; lo[j] = 0; }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint4 xh = *reinterpret_cast<const uint4*>(dig + cc * PITCH + 32 * m);
+                const uint4 xl = *reinterpret_cast<const uint4*>(dig + cc * PITCH + 32 * m + 16);
+#pragma unroll
+                for (int j = 0; j < RS; ++j) {
+                    const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+                    uint32_t prev;
+                    if (m == 0) {
+                        // last dword of the left neighbour's chunk (same row, chunk c - 1)
+                        const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)q[j].w, 0x111, 0xf, 0xf, true);
+                        prev = (c & 1) ? left : 0u;
+                    } else {
+                        prev = w4[m - 1];
+                    }
+                    uint32_t P[4];
+                    planes_of(w4[m], prev, P);
+                    int h = hi[j], l = lo[j];
+                    h = __builtin_amdgcn_sdot4((int)P[0], (int)xh.x, h, false);
+                    l = __builtin_amdgcn_sdot4((int)P[0], (int)xl.x, l, false);
+                    h = __builtin_amdgcn_sdot4((int)P[1], (int)xh.y, h, false);
+                    l = __builtin_amdgcn_sdot4((int)P[1], (int)xl.y, l, false);
+                    h = __builtin_amdgcn_sdot4((int)P[2], (int)xh.z, h, false);
+                    l = __builtin_amdgcn_sdot4((int)P[2], (int)xl.z, l, false);
+                    h = __builtin_amdgcn_sdot4((int)P[3], (int)xh.w, h, false);
+                    l = __builtin_amdgcn_sdot4((int)P[3], (int)xl.w, l, false);
+                    hi[j] = h;
+                    lo[j] = l;
+                }
             }
+#pragma unroll
+            for (int j = 0; j < RS; ++j) {
+                const int t = 2 * (hi[j] * 256 + lo[j]) - 7 * qsv;
+                float v = rok[j] ? (ws[j] * sxv) * (float)t : 0.0f;
+                v += xor_lane<4>(v, lane);
+                v += xor_lane<2>(v, lane);
+                v += xor_lane<1>(v, lane);
+                if (tl == 0 && rp < RP && rp + j * RP < R) part[((size_t)b * R + rp + j * RP) * CG + cg] = v;
+            }
+        }
+        __syncthreads();
+        for (int o = tid; o < bt * R; o += nthr) {
+            const int b = o / R, r = o - b * R;
+            if (row0 + r >= n) continue;
+            const float* pr = part + ((size_t)b * R + r) * CG;
+            float v = 0.0f;
+            for (int g = 0; g < CG; ++g) v += pr[g];
+            y[(int64_t)(b0 + b) * n + row0 + r] = v;
         }
     }
 }
@@ -1017,36 +1013,94 @@ int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
 
 namespace {
 
-template <int BS>
-int launch_rot_bs(int W, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
-                  int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, const float* ss_in,
-                  int64_t ss_ld, int batch, float* y, float* ss_out, hipStream_t st) {
-    const dim3 grid((unsigned)((n + 7) / 8));
-    const RotLayout L = rot_layout((int)k, W, BS);
-    const size_t lds = (size_t)W * L.wave_bytes + (size_t)W * 8 * BS * 4 + BS * 4 + (size_t)W * BS * 4;
-    hipLaunchKernelGGL((k_rot_qgemv<BS>), grid, dim3(64 * W), lds, st, codes, scales, (int)n, (int)k, x, x_dt, ldx,
-                       sign_bits, flags, ss_in, ss_ld, batch, y, ss_out);
+template <int XDT, int XS, int RS>
+int launch_fused_t(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                   const void* x, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
+                   hipStream_t st) {
+    const dim3 grid((unsigned)((n + S.R - 1) / S.R));
+    hipLaunchKernelGGL((k_rot_qgemv<XDT, XS, RS>), grid, dim3(64 * S.W), fused_lds_bytes((int)k, S), st, codes,
+                       scales, (int)n, (int)k, x, ldx, sign_bits, flags, batch, y, S.R, S.CG, S.RP, S.BT);
     return hip_check(hipGetLastError(), "pg_rot_qgemv launch");
+}
+
+template <int XDT, int XS>
+int launch_fused_rs(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                    const void* x, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
+                    hipStream_t st) {
+    if (S.RS <= 1) return launch_fused_t<XDT, XS, 1>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.RS <= 2) return launch_fused_t<XDT, XS, 2>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.RS <= 4) return launch_fused_t<XDT, XS, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.RS <= 8) return launch_fused_t<XDT, XS, 8>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    return launch_fused_t<XDT, XS, 16>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+}
+
+int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
 }
 
 }  // namespace
 
+// Launch shape of the fused stage: about one workgroup per CU, each with
+// all of its rows' codes in registers (at most 16 rows per lane).
+int fused_shape(int64_t n, int64_t k, int batch, FusedShape* out) {
+    FusedShape S;
+    S.W = 8;
+    int R_req = 0;
+    if (const char* e = getenv("PG_FUSED_SHAPE")) {   // "W,R" for tuning sweeps
+        int w2 = 0, r2 = 0;
+        if (sscanf(e, "%d,%d", &w2, &r2) == 2 && (w2 == 4 || w2 == 8) && r2 >= 0) {
+            S.W = w2;
+            R_req = r2;
+        }
+    }
+    const int nchunk = (int)(k / 64), nbk = (int)(k / 128);
+    S.CG = (nchunk + 7) / 8;
+    while (S.CG > 8 * S.W && S.W < 8) S.W *= 2;
+    if (S.CG > 8 * S.W) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    S.RP = 8 * S.W / S.CG;
+    S.XS = (nbk + S.W - 1) / S.W;
+    if (S.XS > 16) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    const int64_t cus = compute_units();
+    int64_t R = R_req > 0 ? R_req : (n + cus - 1) / cus;
+    const int rs_max = S.XS > 4 ? 8 : 16;                 // register budget of the unrolled rows
+    if (R > rs_max * S.RP) R = rs_max * S.RP;
+    if (R > n) R = n;
+    S.R = (int)R;
+    S.RS = (S.R + S.RP - 1) / S.RP;
+    const size_t budget = 128 * 1024;
+    S.BT = 1;
+    while (S.BT < 8 && S.BT < batch) {
+        FusedShape T = S;
+        T.BT = S.BT + 1;
+        if (fused_lds_bytes((int)k, T) > budget) break;
+        S.BT = T.BT;
+    }
+    if (fused_lds_bytes((int)k, S) > budget) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    *out = S;
+    return PG_OK;
+}
+
 int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
-                     int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, const float* ss_in,
-                     int64_t ss_ld, int batch, float* y, float* ss_out, pg_stream_t s) {
-    const int64_t wgs = (n + 7) / 8;
-    int W = 1;
-    while (W < 8 && wgs * W < 2048 && (k / 64) >= 16 * W) W *= 2;
-    const size_t budget = 96 * 1024;
-    int bs = 1;
-    while (bs < 8 && bs < batch && (size_t)W * rot_layout((int)k, W, 2 * bs).wave_bytes + (size_t)W * 8 * 2 * bs * 8 <= budget) bs *= 2;
-    if ((size_t)W * rot_layout((int)k, W, 1).wave_bytes > budget)
-        return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+                     int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
+                     pg_stream_t s) {
+    FusedShape S;
+    const int rc = fused_shape(n, k, batch, &S);
+    if (rc != PG_OK) return rc;
     hipStream_t st = (hipStream_t)s;
-    if (bs >= 8) return launch_rot_bs<8>(W, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, ss_in, ss_ld, batch, y, ss_out, st);
-    if (bs >= 4) return launch_rot_bs<4>(W, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, ss_in, ss_ld, batch, y, ss_out, st);
-    if (bs >= 2) return launch_rot_bs<2>(W, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, ss_in, ss_ld, batch, y, ss_out, st);
-    return launch_rot_bs<1>(W, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, ss_in, ss_ld, batch, y, ss_out, st);
+    if (x_dt == PG_F32) {
+        if (S.XS <= 4) return launch_fused_rs<PG_F32, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+        return launch_fused_rs<PG_F32, 16>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    }
+    if (S.XS <= 4) return launch_fused_rs<PG_F16, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    return launch_fused_rs<PG_F16, 16>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
 }
 
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x,

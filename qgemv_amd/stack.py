@@ -51,11 +51,9 @@ class Stack:
             xt = torch.float32 if x_dtype == L.PG_F32 else torch.float16
             self.xrot = torch.empty((b, kmax), dtype=xt, device=device)
         self.graph = None
-        # fused path: one pg_rot_qgemv per launch group; each stage also writes
-        # per-8-row sums of squares that the next stage's normalisation reads
+        # fused path: one pg_rot_qgemv (normalisation + rotation + product)
+        # per launch group
         self.fused = fused
-        self.ss = {site: torch.empty((b, (n + 7) // 8), dtype=torch.float32, device=device)
-                   for site, (n, _) in self.shapes.items()}
         self.out = {site: torch.empty((b, n), dtype=torch.float32, device=device)
                     for site, (n, _) in self.shapes.items()}
         h = shapes["q"][1]
@@ -75,13 +73,12 @@ class Stack:
                 if site == "qkv" and layer == 0:
                     src = h_in if h_in is not None else self.h0
                     L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, src, L.PG_F16, k,
-                                   self.signs[layer][site], 0, None, 0, b, self.out[site], self.ss[site], stream)
+                                   self.signs[layer][site], 0, b, self.out[site], stream)
                     continue
                 prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
                 n_prev = self.shapes[prev][0]
                 L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.out[prev], L.PG_F32,
-                               n_prev, self.signs[layer][site], L.PG_FLAG_RMSNORM, self.ss[prev], (n_prev + 7) // 8,
-                               b, self.out[site], self.ss[site], stream)
+                               n_prev, self.signs[layer][site], L.PG_FLAG_RMSNORM, b, self.out[site], stream)
         return self.out["down"]
 
     def _token_split(self, stream=None, h_in=None):

@@ -52,6 +52,11 @@ def test_codebook_table_matches_oracle():
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 20, 0, 1 << 20, 1, 256, 0, stream=0),         # overlap
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 5, 1 << 20, 1, 256, 0, stream=0),         # dtype
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 0, 1 << 20, 1, 256, 4, stream=0),         # flags
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 255, 1 << 20, 1, 1, 1 << 24, stream=0),  # ldx < k
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 2, 1, 1 << 24, stream=0),  # flags
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 1, 0, 1 << 24, stream=0),  # batch
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 3, 256, 1 << 20, 1, 1, 1 << 24, stream=0),  # dtype
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 1, 2, 1 << 22, stream=0),  # overlap
 ])
 def test_invalid_arguments_fail_before_launch(call):
     # the pointers are never dereferenced: validation rejects the call first
@@ -119,3 +124,9 @@ def test_encode_ref_rejects_bad_arguments():
     with pytest.raises(q.PgError):
         q.pg_encode_ref(w, 2, 200, np.zeros(25, np.uint8), np.zeros((2, 50), np.uint8),
                         np.zeros((2, 2), np.uint16))
+
+
+def test_rot_qgemv_rejects_k_beyond_its_register_staging():
+    with pytest.raises(q.PgError) as ei:
+        q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 32768, 1 << 22, 0, 32768, 1 << 20, 1, 1, 1 << 28, stream=0)
+    assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
