@@ -170,16 +170,21 @@ int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
  * with n(v) = fp16_RNE(v / sqrt(mean(v^2) + 1e-6)) under PG_FLAG_RMSNORM
  * (fp32 math, mean over the k values), n(v) = v otherwise, R the input
  * site's rotation (as pg_fwht_rotate), and the rotated activations carried
- * at 16-bit precision as in PG_Q16 (relative error <= 2^-16 of each
- * 128-block's largest value).
- *   codes, scales  as for pg_qgemv
+ * at 16-bit precision (error <= 2^-16 of the largest value of each 32
+ * consecutive rotated values).
+ *   codes, scales  as for pg_qgemv (scales 4-byte aligned)
  *   x        device [batch][ldx] of x_dtype (PG_F32 / PG_F16); the first k
  *            values of each row are the input (e.g. the q part of a merged
- *            q/k/v output); ldx >= k
- *   sign_bits device u8 [k/8]
+ *            q/k/v output); ldx >= k; x and every row start 16-byte
+ *            aligned (ldx a multiple of 4 for PG_F32, of 8 for PG_F16)
+ *   sign_bits device u8 [k/8], 4-byte aligned
  *   y        device f32 [batch][n] out
  *   batch    1..8
- * k <= 16384 (PG_ERR_UNSUPPORTED beyond).  x and y may not overlap.  The
+ * k <= 16384 (PG_ERR_UNSUPPORTED beyond).  PG_F32 input needs
+ * PG_FLAG_RMSNORM (the rotation runs on fp16 values, exact after the
+ * normalisation's fp16 rounding or for fp16 input; PG_ERR_UNSUPPORTED
+ * otherwise).  The rotated values are quantised with one scale per 32
+ * values.  x and y may not overlap.  The
  * summation order is fixed: repeated calls are bitwise identical. */
 int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const void* x, int x_dtype, int64_t ldx, const uint8_t* sign_bits,

@@ -123,9 +123,11 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
     if (ldx < k) return pg::fail(PG_ERR_INVALID_ARG, "ldx (%lld) < k (%lld)", (long long)ldx, (long long)k);
     if (flags & ~PG_FLAG_RMSNORM) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     PG_TRY(check_ptr(codes, 16, "codes"));
-    PG_TRY(check_ptr(scales, 2, "scales"));
-    PG_TRY(check_ptr(x, x_dtype == PG_F32 ? 4 : 2, "x"));
-    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    PG_TRY(check_ptr(scales, 4, "scales"));
+    PG_TRY(check_ptr(x, 16, "x"));
+    if ((ldx * (x_dtype == PG_F32 ? 4 : 2)) % 16 != 0)
+        return pg::fail(PG_ERR_INVALID_ARG, "rows of x (ldx = %lld) are not 16-byte multiples", (long long)ldx);
+    PG_TRY(check_ptr(sign_bits, 4, "sign_bits"));
     PG_TRY(check_ptr(y, 4, "y"));
     const uintptr_t ya = (uintptr_t)y, xa = (uintptr_t)x;
     const size_t yb = (size_t)batch * n * 4, xb = (size_t)batch * ldx * (x_dtype == PG_F32 ? 4 : 2);

@@ -558,42 +558,78 @@ __global__ __launch_bounds__(512) void k_qgemv_q16(const uint8_t* __restrict__ c
 // y = W~ . R . n(x) in one launch: the activation rotation (with the RMS
 // normalisation and fp16 rounding of PG_FLAG_RMSNORM) is the product's
 // prologue.  One workgroup per CU owns R consecutive weight rows with all of
-// their k columns, so the whole launch is one pass over the codes with a
-// single memory round trip per lane:
-//   1. every lane requests its x values first and then all of its code
-//      chunks at once (they do not depend on x), so the rotation below runs
-//      while the codes are still in flight;
-//   2. the sum of squares of x gives the RMS; each wave rotates the 128-blocks
-//      w, w + W, ... (lane l holds elements l and l + 64: the distance-64
-//      butterfly is inside the lane, the others exchange lanes), quantises
-//      them to 16-bit digits (PG_Q16 arithmetic) and stores them in LDS,
-//      where each 64-value chunk takes 144 bytes (128 + 16 of padding, so the
-//      8 lanes of a team reading consecutive chunks hit distinct banks);
-//   3. team T of 8 lanes takes column group cg = T % CG (chunks 8 cg .. 8 cg
+// their k columns, so the launch is one pass over the codes and each lane
+// waits for memory once:
+//   1. the input row is copied to LDS (direct global -> LDS copies) and then
+//      every code chunk of the lane is requested; waiting until only the code
+//      requests are outstanding means x has arrived (memory operations of a
+//      wave complete in order);
+//   2. the RMS of x is summed, and the normalised, sign-flipped values are
+//      staged in LDS as fp16 (exact: n() rounds to fp16, and fp16 inputs are
+//      exact), one 128-block per 272-byte row;
+//   3. the Hadamard products run on the matrix cores: v_mfma_f32_32x32x16_f16
+//      with the +-1 entries of H as the A operand (built from bit patterns in
+//      registers, no memory), 32 blocks per tile.  The rows of H are ordered
+//      so that each lane's four accumulators r = 4i .. 4i + 3 are the four
+//      groups of one position in a PG_Q16-style digit dword;
+//   4. each wave quantises its 32 x 32 tile (one scale per 32 elements, from
+//      the tile's own maximum, so no other wave is waited for): q =
+//      rint(v * 32512 / max) by one fma with 1.5 * 2^23, which leaves q as a
+//      16-bit two's complement integer in the low half of the float's bits;
+//      byte permutes split it into a signed high digit floor(q / 256) and an
+//      unsigned low digit q mod 256, four groups per dword;
+//   5. team T of 8 lanes takes column group cg = T % CG (chunks 8 cg .. 8 cg
 //      + 7, one 128-byte line of a row per team) and rows rp, rp + RP, ...
-//      with rp = T / CG, so a lane reads its chunk's digits once per batch
-//      row and uses them for all of its rows; levels come from bit planes
-//      (planes_of) and meet the digits in v_dot4_i32_i8;
-//   4. team sums go to LDS per (row, column group) and are added in column
+//      (rp = T / CG); a lane reads its chunk's digits once per batch row and
+//      uses them for all of its rows: levels come from bit planes (planes_of)
+//      and meet the digits in v_dot4 (signed for the high digit, unsigned for
+//      the low one);
+//   6. team sums go to LDS per (row, column group) and are added in column
 //      group order.
 // Launch shape (host): W waves, R rows per workgroup, CG = ceil(k/512),
-// RP = 8W / CG, at most RS rows per lane and XS 128-blocks per wave.
+// RP = 8W / CG, at most RS rows per lane and XG 8-value groups of x per
+// thread.
 struct FusedShape {
-    int W, R, CG, RP, RS, XS, BT;
+    int W, R, CG, RP, RS, XG, BT;
 };
 
-__host__ __device__ inline int fused_chunk_pitch() { return 144; }
+constexpr int FS_PITCH = 144;      // LDS bytes per 64-value chunk of digits (128 + 16 against bank conflicts)
+constexpr int FS_XPITCH = 272;     // LDS bytes per staged fp16 128-block (256 + 16)
 
-// LDS bytes per batch row: digits, block scales, chunk sums
-__host__ __device__ inline int fused_row_bytes(int k) {
-    return ((k / 64) * fused_chunk_pitch() + (k / 128) * 4 + (k / 64) * 4 + 15) & ~15;
+// LDS bytes per batch row: digits, then per 32-value quarter its scale and
+// its sum of q
+__host__ __device__ inline int fused_row_bytes(int k) { return ((k / 64) * FS_PITCH + (k / 32) * 8 + 15) & ~15; }
+
+// LDS staging of one input row (x as given, fp32 or fp16; later the fp16
+// blocks), then the sign bits
+__host__ __device__ inline int fused_xreg_bytes(int k, int esz) {
+    const int a = k * esz, b = (k / 128) * FS_XPITCH;
+    return ((a > b ? a : b) + 15) & ~15;
+}
+__host__ __device__ inline int fused_xbuf_bytes(int k, int esz) {
+    return fused_xreg_bytes(k, esz) + ((k / 8 + 15) & ~15);
 }
 
-__host__ inline size_t fused_lds_bytes(int k, const FusedShape& S) {
-    return (size_t)S.BT * fused_row_bytes(k) + (size_t)S.BT * S.R * S.CG * 4 + (size_t)S.W * 4;
+__host__ inline size_t fused_lds_bytes(int k, int esz, const FusedShape& S) {
+    return (size_t)fused_xbuf_bytes(k, esz) + (size_t)S.BT * fused_row_bytes(k) + (size_t)S.BT * S.R * S.CG * 4 +
+           (size_t)S.W * 4;
 }
 
-template <int XDT, int XS, int RS>
+// s_waitcnt operand: at most n vector-memory operations of this wave still
+// outstanding, the other counters unrestricted (gfx9 encoding)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Element of a 128-block held by accumulator row M = 8 i + 4 h + r of row
+// tile mt: quarter mt, part i / 2 of the quarter, group r, position
+// 2 (i % 2) + h.
+__device__ __forceinline__ int fs_elem(int mt, int M) {
+    const int i = M >> 3, h = (M >> 2) & 1, r = M & 3;
+    return 32 * mt + 16 * (i >> 1) + 4 * r + 2 * (i & 1) + h;
+}
+
+typedef _Float16 fs_f16x8 __attribute__((ext_vector_type(8)));
+
+template <int XDT, int XG, int RS>
 __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ codes,
                                                     const uint16_t* __restrict__ scales, int n, int k,
                                                     const void* __restrict__ x, int64_t ldx,
@@ -605,14 +641,16 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     const int W = nthr >> 6;
     const int lane = tid & 63, wave = tid >> 6;
     const int T = wave * 8 + (lane >> 3), tl = lane & 7;
-    const int kg = k >> 2, nchunk = k >> 6, nbk = k >> 7;
+    const int kg = k >> 2, nchunk = k >> 6, nbk = k >> 7, ngr = k >> 3;
     const int row0 = blockIdx.x * R;
     const int rb = fused_row_bytes(k);
-    const int PITCH = fused_chunk_pitch();
-    float* part = reinterpret_cast<float*>(lds + (size_t)BT * rb);      // [BT][R][CG]
-    float* wsum = part + (size_t)BT * R * CG;                           // [W]
+    const int esz = XDT == PG_F32 ? 4 : 2;
+    uint8_t* xbuf = lds;                                     // x as given, later the fp16 blocks
+    uint8_t* sbuf = lds + fused_xreg_bytes(k, esz);          // sign bits
+    uint8_t* rows_lds = lds + fused_xbuf_bytes(k, esz);      // [BT][rb] digits, scales, sums
+    float* part = reinterpret_cast<float*>(rows_lds + (size_t)BT * rb);   // [BT][R][CG]
+    float* wsum = part + (size_t)BT * R * CG;                             // [W]
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
-    const float cnorm = 0.08838834764831845f;                          // 2^-3.5
 
     // this lane's column of chunks and its rows
     const int cg = T % CG, rp = T / CG;
@@ -620,185 +658,264 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     const bool col_ok = rp < RP && c < nchunk;
     const int cc = c < nchunk ? c : nchunk - 1;
 
-    // x of one batch row: block bb = wave + W i, elements bb*128 + lane and + 64
-    float xv[XS][2];
-    auto load_x = [&](int b) {
-        const int64_t base = (int64_t)b * ldx;
-#pragma unroll
-        for (int i = 0; i < XS; ++i) {
-            const int bb = wave + W * i;
-            const int e = (bb < nbk ? bb : 0) * 128 + lane;
-            if (XDT == PG_F32) {
-                xv[i][0] = ((const float*)x)[base + e];
-                xv[i][1] = ((const float*)x)[base + e + 64];
-            } else {
-                xv[i][0] = h2f(((const uint16_t*)x)[base + e]);
-                xv[i][1] = h2f(((const uint16_t*)x)[base + e + 64]);
-            }
-        }
+    // ---- 1. x to LDS (16 bytes per lane), sign bits, then all code chunks
+    auto stage_x = [&](int b) {
+        const uint8_t* src = (const uint8_t*)x + (int64_t)b * ldx * esz;
+        const int bytes = k * esz;
+        for (int o = wave * 1024; o < bytes; o += W * 1024)
+            if (o + 16 * lane < bytes) __builtin_amdgcn_global_load_lds(src + o + 16 * lane, xbuf + o, 16, 0, 0);
     };
-    load_x(0);
-    // sign bits of elements lane and lane + 64 of each block (bits 2i, 2i + 1)
-    uint32_t sgn = 0;
-#pragma unroll
-    for (int i = 0; i < XS; ++i) {
-        const int bb = wave + W * i;
-        const int e = (bb < nbk ? bb : 0) * 128 + lane;
-        sgn |= (uint32_t)((sign_bits[e >> 3] >> (e & 7)) & 1u) << (2 * i);
-        sgn |= (uint32_t)((sign_bits[(e + 64) >> 3] >> (e & 7)) & 1u) << (2 * i + 1);
-    }
-    // all code chunks of this lane (rows past n or R, and chunks past k, are
-    // clamped to valid addresses and masked out of the sums)
+    stage_x(0);
+    uint32_t sg = 0;
+    const bool sg_on = tid < k / 32;
+    if (sg_on) sg = reinterpret_cast<const uint32_t*>(sign_bits)[tid];
+    asm volatile("" ::: "memory");
+    // The scale of a chunk comes with its neighbour in one aligned dword (the
+    // half is picked where it is used, so nothing converts it early).
     uint4 q[RS];
-    float ws[RS];
-    bool rok[RS];
+    uint32_t wsr[RS];
+    bool rok[RS], whi[RS];
 #pragma unroll
     for (int j = 0; j < RS; ++j) {
         const int r = rp + j * RP;
         rok[j] = col_ok && r < R && row0 + r < n;
         const int row = rok[j] ? row0 + r : (row0 < n ? row0 : n - 1);
         q[j] = *reinterpret_cast<const uint4*>(codes + (int64_t)row * kg + 16 * cc);
-        ws[j] = h2f(scales[(int64_t)row * nbk + (cc >> 1)]);
+        const int64_t si = (int64_t)row * nbk + (cc >> 1);
+        whi[j] = (si & 1) != 0;
+        wsr[j] = reinterpret_cast<const uint32_t*>(scales)[si >> 1];
     }
-    for (int b0 = 0; b0 < batch; b0 += BT) {
-        const int bt = batch - b0 < BT ? batch - b0 : BT;
-        if (b0 > 0) __syncthreads();                      // previous tile's LDS reads are done
-        // ---- rotation of each batch row of the tile into LDS
-        for (int b = 0; b < bt; ++b) {
-            if (b0 + b > 0) load_x(b0 + b);
-            float inv = 1.0f;
-            if (norm) {
-                float ss = 0.0f;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * RS));      // x copies and sign loads done
+    if (sg_on) reinterpret_cast<uint32_t*>(sbuf)[tid] = sg;
+    __syncthreads();
+
+    // A operand patterns of the Hadamard product (see fs_elem): lane l holds
+    // row M = l % 32 and inputs 8 (l / 32) + t of a 16-wide step; the entry is
+    //   (-1)^popcount(e & 7 & t) (-1)^(bit 3 of e & l / 32)   (fixed per lane)
+    //   (-1)^(bit 4 of e & step % 2)                            (odd steps)
+    //   (-1)^popcount(mt & step / 2)                            (uniform)
+    uint32_t apat[2][4];
+    {
+        const int e0 = fs_elem(0, lane & 31);
+        const int ha = lane >> 5;
+        const bool f_lane = ((e0 >> 3) & 1) & ha;
+        const bool f_odd = (e0 >> 4) & 1;
 #pragma unroll
-                for (int i = 0; i < XS; ++i)
-                    if (wave + W * i < nbk) ss += xv[i][0] * xv[i][0] + xv[i][1] * xv[i][1];
-                ss = wave_sum(ss);
-                if (b > 0) __syncthreads();                    // wsum of the previous row consumed
-                if (lane == 0) wsum[wave] = ss;
-                __syncthreads();
-                float tot = 0.0f;
-                for (int w = 0; w < W; ++w) tot += wsum[w];
-                inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+        for (int t = 0; t < 8; t += 2) {
+            const bool n0 = (__builtin_popcount(e0 & 7 & t) & 1) ^ f_lane;
+            const bool n1 = (__builtin_popcount(e0 & 7 & (t + 1)) & 1) ^ f_lane;
+            const uint32_t wv = (n0 ? 0xBC00u : 0x3C00u) | ((n1 ? 0xBC00u : 0x3C00u) << 16);
+            apat[0][t >> 1] = wv;
+            apat[1][t >> 1] = f_odd ? (wv ^ 0x80008000u) : wv;
+        }
+    }
+    const int ntile = (nbk + 31) >> 5;
+
+    const int bt = batch;                      // one launch covers bt <= BT batch rows
+    for (int b = 0; b < bt; ++b) {
+        if (b > 0) {
+            __syncthreads();                   // the previous row's fp16 blocks are consumed
+            stage_x(b);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        // ---- 2. norm and fp16 staging: thread t takes 8-value groups t + nthr u
+        float xv[XG][8];
+        uint32_t xs8[XG];
+        float ss = 0.0f;
+#pragma unroll
+        for (int u = 0; u < XG; ++u) {
+            const int gi = tid + nthr * u;
+            const int gc = gi < ngr ? gi : 0;
+            if (XDT == PG_F32) {
+                const float4 v0 = *reinterpret_cast<const float4*>(xbuf + 32 * gc);
+                const float4 v1 = *reinterpret_cast<const float4*>(xbuf + 32 * gc + 16);
+                xv[u][0] = v0.x; xv[u][1] = v0.y; xv[u][2] = v0.z; xv[u][3] = v0.w;
+                xv[u][4] = v1.x; xv[u][5] = v1.y; xv[u][6] = v1.z; xv[u][7] = v1.w;
+            } else {
+                const uint4 v = *reinterpret_cast<const uint4*>(xbuf + 16 * gc);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    xv[u][2 * t] = h2f((uint16_t)(w4[t] & 0xffffu));
+                    xv[u][2 * t + 1] = h2f((uint16_t)(w4[t] >> 16));
+                }
             }
-            uint8_t* dig = lds + (size_t)b * rb;
-            float* sxr = reinterpret_cast<float*>(dig + nchunk * PITCH);
-            int* qsr = reinterpret_cast<int*>(dig + nchunk * PITCH + nbk * 4);
+            xs8[u] = sbuf[gc];
+            if (gi < ngr)
 #pragma unroll
-            for (int i = 0; i < XS; ++i) {
-                const int bb = wave + W * i;
-                if (bb >= nbk) break;                              // wave-uniform
-                float a = xv[i][0], cv = xv[i][1];
-                if (norm) {
-                    a = h2f(f2h(a * inv));
-                    cv = h2f(f2h(cv * inv));
+                for (int t = 0; t < 8; ++t) ss += xv[u][t] * xv[u][t];
+        }
+        float inv = 1.0f;
+        if (norm) {
+            ss = wave_sum(ss);
+            if (b > 0) __syncthreads();        // wsum of the previous row consumed
+            if (lane == 0) wsum[wave] = ss;
+        }
+        __syncthreads();                       // every x read is done: the blocks may overwrite x
+        if (norm) {
+            float tot = 0.0f;
+            for (int w = 0; w < W; ++w) tot += wsum[w];
+            inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+        }
+#pragma unroll
+        for (int u = 0; u < XG; ++u) {
+            const int gi = tid + nthr * u;
+            if (gi < ngr) {
+                uint32_t hw[4];
+#pragma unroll
+                for (int t = 0; t < 8; t += 2) {
+                    uint32_t h0 = f2h(norm ? xv[u][t] * inv : xv[u][t]);
+                    uint32_t h1 = f2h(norm ? xv[u][t + 1] * inv : xv[u][t + 1]);
+                    h0 ^= ((xs8[u] >> t) & 1u) << 15;
+                    h1 ^= ((xs8[u] >> (t + 1)) & 1u) << 15;
+                    hw[t >> 1] = h0 | (h1 << 16);
                 }
-                if ((sgn >> (2 * i)) & 1u) a = -a;
-                if ((sgn >> (2 * i + 1)) & 1u) cv = -cv;
-                {
-                    const float t0 = a + cv, t1 = a - cv;
-                    a = t0;
-                    cv = t1;
-                }
-                float pa, pc;
-                bool up;
-                pa = xor_lane32(a, lane); pc = xor_lane32(cv, lane); up = (lane & 32) != 0;
-                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
-                pa = xor_lane16(a, lane); pc = xor_lane16(cv, lane); up = (lane & 16) != 0;
-                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
-                pa = xor_lane<8>(a, lane); pc = xor_lane<8>(cv, lane); up = (lane & 8) != 0;
-                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
-                pa = xor_lane<4>(a, lane); pc = xor_lane<4>(cv, lane); up = (lane & 4) != 0;
-                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
-                pa = xor_lane<2>(a, lane); pc = xor_lane<2>(cv, lane); up = (lane & 2) != 0;
-                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
-                pa = xor_lane<1>(a, lane); pc = xor_lane<1>(cv, lane); up = (lane & 1) != 0;
-                a = up ? pa - a : a + pa; cv = up ? pc - cv : cv + pc;
-                a *= cnorm;
-                cv *= cnorm;
-                const float mx = wave_max(fmaxf(fabsf(a), fabsf(cv)));
-                const float inv_sx = mx > 0.0f ? (float)Q16_MAXQ / mx : 0.0f;
-                const int qa = (int)rintf(a * inv_sx);
-                const int qc = (int)rintf(cv * inv_sx);
-                // element e of chunk 2bb (+1 for qc): group e/4 -> part m = e/16,
-                // byte 4 (e%4) + (e/4)%4 of the part's hi (and, +16, lo) digits
-                const int off = (lane >> 4) * 32 + 4 * (lane & 3) + ((lane >> 2) & 3);
-                uint8_t* d0 = dig + (2 * bb) * PITCH + off;
-                uint8_t* d1 = d0 + PITCH;
-                const int ha = (qa + 128) >> 8, hc = (qc + 128) >> 8;
-                d0[0] = (uint8_t)ha;
-                d0[16] = (uint8_t)(qa - 256 * ha);
-                d1[0] = (uint8_t)hc;
-                d1[16] = (uint8_t)(qc - 256 * hc);
-                const int sa = wave_sum_i(qa), sc = wave_sum_i(qc);
-                if (lane == 0) {
-                    sxr[bb] = mx / (float)Q16_MAXQ;
-                    qsr[2 * bb] = sa;
-                    qsr[2 * bb + 1] = sc;
-                }
+                *reinterpret_cast<uint4*>(xbuf + (gi >> 4) * FS_XPITCH + (gi & 15) * 16) =
+                    make_uint4(hw[0], hw[1], hw[2], hw[3]);
             }
         }
         __syncthreads();
-        // ---- decode and dot products, one batch row at a time
-        for (int b = 0; b < bt; ++b) {
-            // the planes are rebuilt per batch row rather than kept for all
-            // rows and positions at once (that would take 16 RS registers)
+        // ---- 3./4. Hadamard tiles on the matrix cores, quantised per 32 values
+        uint8_t* dig = rows_lds + (size_t)b * rb;
+        float* sxq = reinterpret_cast<float*>(dig + nchunk * FS_PITCH);
+        int* sqq = reinterpret_cast<int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
+        for (int job = wave; job < 4 * ntile; job += W) {
+            const int nt = job >> 2, mt = job & 3;
+            const int blk = nt * 32 + (lane & 31);
+            const bool bok = blk < nbk;
+            const uint8_t* xrow = xbuf + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
+            f32x16 acc;
 #pragma unroll
-            for (int j = 0; j < RS; ++j) asm volatile("" : "+v"(q[j].x), "+v"(q[j].y), "+v"(q[j].z), "+v"(q[j].w));
-            const uint8_t* dig = lds + (size_t)b * rb;
-            const float sxv = reinterpret_cast<const float*>(dig + nchunk * PITCH)[cc >> 1];
-            const int qsv = reinterpret_cast<const int*>(dig + nchunk * PITCH + nbk * 4)[cc];
-            int hi[RS], lo[RS];
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < RS; ++j) { hi[j] = 0; lo[j] = 0; }
+            for (int st = 0; st < 8; ++st) {
+                uint4 bw = *reinterpret_cast<const uint4*>(xrow + 32 * st);
+                if (!bok) bw = make_uint4(0, 0, 0, 0);
+                const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
+                const uint32_t* av = apat[st & 1];
+                const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
+                                                             __builtin_bit_cast(fs_f16x8, bw), acc, 0, 0, 0);
+            }
+            // quarter maximum: 16 values per lane, then the lane pair (l, l + 32)
+            float mx = 0.0f;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint4 xh = *reinterpret_cast<const uint4*>(dig + cc * PITCH + 32 * m);
-                const uint4 xl = *reinterpret_cast<const uint4*>(dig + cc * PITCH + 32 * m + 16);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc[r]));
+            mx = fmaxf(mx, xor_lane32(mx, lane));
+            const float s = mx > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(mx) : 0.0f;
+            const int ch = 2 * blk + (mt >> 1);              // chunk of this quarter
+            uint8_t* dq = dig + (bok ? ch : 0) * FS_PITCH + 32 * 2 * (mt & 1) + 4 * (lane >> 5);
+            int shi = 0, slo = 0;
 #pragma unroll
-                for (int j = 0; j < RS; ++j) {
-                    const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
-                    uint32_t prev;
-                    if (m == 0) {
-                        // last dword of the left neighbour's chunk (same row, chunk c - 1)
-                        const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)q[j].w, 0x111, 0xf, 0xf, true);
-                        prev = (c & 1) ? left : 0u;
-                    } else {
-                        prev = w4[m - 1];
-                    }
-                    uint32_t P[4];
-                    planes_of(w4[m], prev, P);
-                    int h = hi[j], l = lo[j];
-                    h = __builtin_amdgcn_sdot4((int)P[0], (int)xh.x, h, false);
-                    l = __builtin_amdgcn_sdot4((int)P[0], (int)xl.x, l, false);
-                    h = __builtin_amdgcn_sdot4((int)P[1], (int)xh.y, h, false);
-                    l = __builtin_amdgcn_sdot4((int)P[1], (int)xl.y, l, false);
-                    h = __builtin_amdgcn_sdot4((int)P[2], (int)xh.z, h, false);
-                    l = __builtin_amdgcn_sdot4((int)P[2], (int)xl.z, l, false);
-                    h = __builtin_amdgcn_sdot4((int)P[3], (int)xh.w, h, false);
-                    l = __builtin_amdgcn_sdot4((int)P[3], (int)xl.w, l, false);
-                    hi[j] = h;
-                    lo[j] = l;
+            for (int i = 0; i < 4; ++i) {
+                uint32_t bits[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bits[r] = __builtin_bit_cast(uint32_t, fmaf(acc[4 * i + r], s, 12582912.0f));
+                const uint32_t t01 = __builtin_amdgcn_perm(bits[1], bits[0], 0x05040100u);
+                const uint32_t t23 = __builtin_amdgcn_perm(bits[3], bits[2], 0x05040100u);
+                const uint32_t dl = __builtin_amdgcn_perm(t23, t01, 0x06040200u);   // q mod 256 of groups 0..3
+                const uint32_t dh = __builtin_amdgcn_perm(t23, t01, 0x07050301u);   // floor(q / 256)
+                shi = __builtin_amdgcn_sdot4((int)dh, 0x01010101, shi, false);
+                slo = (int)__builtin_amdgcn_udot4(dl, 0x01010101u, (uint32_t)slo, false);
+                // part 2 (mt % 2) + i / 2 of the chunk, position 2 (i % 2) + l / 32
+                if (bok) {
+                    uint8_t* dd = dq + 32 * (i >> 1) + 8 * (i & 1);
+                    *reinterpret_cast<uint32_t*>(dd) = dh;
+                    *reinterpret_cast<uint32_t*>(dd + 16) = dl;
                 }
             }
+            int qs = 256 * shi + slo;
+            qs += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, qs), lane));
+            if (bok && lane < 32) {
+                sxq[4 * blk + mt] = mx * (0.08838834764831845f / (float)Q16_MAXQ);   // 2^-3.5 max / 32512
+                sqq[4 * blk + mt] = qs;
+            }
+        }
+    }
+    __syncthreads();
+    // ---- 5. decode and dot products, one batch row at a time
+    for (int b = 0; b < bt; ++b) {
+        // codes and scales are used only here, through copies passed
+        // through an opaque move: that keeps the compiler from hoisting
+        // their decode above the rotation (which would wait for every code
+        // request first) and rebuilds the planes per batch row rather than
+        // keeping 16 RS of them
+        uint4 qb[RS];
+        uint32_t wb[RS];
+#pragma unroll
+        for (int j = 0; j < RS; ++j) {
+            qb[j] = q[j];
+            wb[j] = wsr[j];
+            asm volatile("" : "+v"(qb[j].x), "+v"(qb[j].y), "+v"(qb[j].z), "+v"(qb[j].w), "+v"(wb[j]));
+        }
+        const uint8_t* dig = rows_lds + (size_t)b * rb;
+        const float* sxq = reinterpret_cast<const float*>(dig + nchunk * FS_PITCH);
+        const int* sqq = reinterpret_cast<const int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
+        const float sx0 = sxq[2 * cc], sx1 = sxq[2 * cc + 1];
+        const int sq0 = sqq[2 * cc], sq1 = sqq[2 * cc + 1];
+        float tq[RS];
+        int hi[RS], lo[RS];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            if (m == 0 || m == 2)
+#pragma unroll
+                for (int j = 0; j < RS; ++j) { hi[j] = 0; lo[j] = 0; }
+            const uint4 xh = *reinterpret_cast<const uint4*>(dig + cc * FS_PITCH + 32 * m);
+            const uint4 xl = *reinterpret_cast<const uint4*>(dig + cc * FS_PITCH + 32 * m + 16);
 #pragma unroll
             for (int j = 0; j < RS; ++j) {
-                const int t = 2 * (hi[j] * 256 + lo[j]) - 7 * qsv;
-                float v = rok[j] ? (ws[j] * sxv) * (float)t : 0.0f;
-                v += xor_lane<4>(v, lane);
-                v += xor_lane<2>(v, lane);
-                v += xor_lane<1>(v, lane);
-                if (tl == 0 && rp < RP && rp + j * RP < R) part[((size_t)b * R + rp + j * RP) * CG + cg] = v;
+                const uint32_t w4[4] = {qb[j].x, qb[j].y, qb[j].z, qb[j].w};
+                uint32_t prev;
+                if (m == 0) {
+                    // last dword of the left neighbour's chunk (same row, chunk c - 1)
+                    const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb[j].w, 0x111, 0xf, 0xf, true);
+                    prev = (c & 1) ? left : 0u;
+                } else {
+                    prev = w4[m - 1];
+                }
+                uint32_t P[4];
+                planes_of(w4[m], prev, P);
+                int h = hi[j];
+                uint32_t l = (uint32_t)lo[j];
+                h = __builtin_amdgcn_sdot4((int)P[0], (int)xh.x, h, false);
+                l = __builtin_amdgcn_udot4(P[0], xl.x, l, false);
+                h = __builtin_amdgcn_sdot4((int)P[1], (int)xh.y, h, false);
+                l = __builtin_amdgcn_udot4(P[1], xl.y, l, false);
+                h = __builtin_amdgcn_sdot4((int)P[2], (int)xh.z, h, false);
+                l = __builtin_amdgcn_udot4(P[2], xl.z, l, false);
+                h = __builtin_amdgcn_sdot4((int)P[3], (int)xh.w, h, false);
+                l = __builtin_amdgcn_udot4(P[3], xl.w, l, false);
+                hi[j] = h;
+                lo[j] = (int)l;
             }
+            // quarter done: sum level * q = 2 (256 hi + lo) - 7 sum q
+            if (m == 1)
+#pragma unroll
+                for (int j = 0; j < RS; ++j) tq[j] = sx0 * (float)(2 * (hi[j] * 256 + lo[j]) - 7 * sq0);
+            if (m == 3)
+#pragma unroll
+                for (int j = 0; j < RS; ++j) tq[j] += sx1 * (float)(2 * (hi[j] * 256 + lo[j]) - 7 * sq1);
         }
-        __syncthreads();
-        for (int o = tid; o < bt * R; o += nthr) {
-            const int b = o / R, r = o - b * R;
-            if (row0 + r >= n) continue;
-            const float* pr = part + ((size_t)b * R + r) * CG;
-            float v = 0.0f;
-            for (int g = 0; g < CG; ++g) v += pr[g];
-            y[(int64_t)(b0 + b) * n + row0 + r] = v;
+#pragma unroll
+        for (int j = 0; j < RS; ++j) {
+            const float wsc = h2f((uint16_t)(whi[j] ? wb[j] >> 16 : wb[j]));
+            float v = rok[j] ? wsc * tq[j] : 0.0f;
+            v += xor_lane<4>(v, lane);
+            v += xor_lane<2>(v, lane);
+            v += xor_lane<1>(v, lane);
+            if (tl == 0 && rp < RP && rp + j * RP < R) part[((size_t)b * R + rp + j * RP) * CG + cg] = v;
         }
+    }
+    __syncthreads();
+    for (int o = tid; o < bt * R; o += nthr) {
+        const int b = o / R, r = o - b * R;
+        if (row0 + r >= n) continue;
+        const float* pr = part + ((size_t)b * R + r) * CG;
+        float v = 0.0f;
+        for (int g = 0; g < CG; ++g) v += pr[g];
+        y[(int64_t)b * n + row0 + r] = v;
     }
 }
 
@@ -1013,25 +1130,33 @@ int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
 
 namespace {
 
-template <int XDT, int XS, int RS>
+template <int XDT, int XG, int RS>
 int launch_fused_t(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                    const void* x, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
                    hipStream_t st) {
     const dim3 grid((unsigned)((n + S.R - 1) / S.R));
-    hipLaunchKernelGGL((k_rot_qgemv<XDT, XS, RS>), grid, dim3(64 * S.W), fused_lds_bytes((int)k, S), st, codes,
-                       scales, (int)n, (int)k, x, ldx, sign_bits, flags, batch, y, S.R, S.CG, S.RP, S.BT);
-    return hip_check(hipGetLastError(), "pg_rot_qgemv launch");
+    const int esz = XDT == PG_F32 ? 4 : 2;
+    for (int b0 = 0; b0 < batch; b0 += S.BT) {
+        const int bt = batch - b0 < S.BT ? batch - b0 : S.BT;
+        const void* xb = (const uint8_t*)x + (int64_t)b0 * ldx * esz;
+        hipLaunchKernelGGL((k_rot_qgemv<XDT, XG, RS>), grid, dim3(64 * S.W), fused_lds_bytes((int)k, esz, S), st,
+                           codes, scales, (int)n, (int)k, xb, ldx, sign_bits, flags, bt, y + (int64_t)b0 * n, S.R,
+                           S.CG, S.RP, S.BT);
+        const int rc = hip_check(hipGetLastError(), "pg_rot_qgemv launch");
+        if (rc != PG_OK) return rc;
+    }
+    return PG_OK;
 }
 
-template <int XDT, int XS>
+template <int XDT, int XG>
 int launch_fused_rs(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                     const void* x, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
                     hipStream_t st) {
-    if (S.RS <= 1) return launch_fused_t<XDT, XS, 1>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    if (S.RS <= 2) return launch_fused_t<XDT, XS, 2>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    if (S.RS <= 4) return launch_fused_t<XDT, XS, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    if (S.RS <= 8) return launch_fused_t<XDT, XS, 8>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    return launch_fused_t<XDT, XS, 16>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.RS <= 1) return launch_fused_t<XDT, XG, 1>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.RS <= 2) return launch_fused_t<XDT, XG, 2>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.RS <= 4) return launch_fused_t<XDT, XG, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.RS <= 8) return launch_fused_t<XDT, XG, 8>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    return launch_fused_t<XDT, XG, 16>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
 }
 
 int compute_units() {
@@ -1066,24 +1191,25 @@ int fused_shape(int64_t n, int64_t k, int batch, FusedShape* out) {
     while (S.CG > 8 * S.W && S.W < 8) S.W *= 2;
     if (S.CG > 8 * S.W) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
     S.RP = 8 * S.W / S.CG;
-    S.XS = (nbk + S.W - 1) / S.W;
-    if (S.XS > 16) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    S.XG = (int)((k / 8 + 64 * S.W - 1) / (64 * S.W));   // 8-value groups of x per thread
+    if (k / 32 > 64 * S.W || S.XG > 4)
+        return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    (void)nbk;
     const int64_t cus = compute_units();
     int64_t R = R_req > 0 ? R_req : (n + cus - 1) / cus;
-    const int rs_max = S.XS > 4 ? 8 : 16;                 // register budget of the unrolled rows
-    if (R > rs_max * S.RP) R = rs_max * S.RP;
+    if (R > 16 * S.RP) R = 16 * S.RP;                      // at most 16 rows per lane
     if (R > n) R = n;
     S.R = (int)R;
     S.RS = (S.R + S.RP - 1) / S.RP;
-    const size_t budget = 128 * 1024;
+    const size_t budget = 150 * 1024;
     S.BT = 1;
     while (S.BT < 8 && S.BT < batch) {
         FusedShape T = S;
         T.BT = S.BT + 1;
-        if (fused_lds_bytes((int)k, T) > budget) break;
+        if (fused_lds_bytes((int)k, 4, T) > budget) break;
         S.BT = T.BT;
     }
-    if (fused_lds_bytes((int)k, S) > budget) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    if (fused_lds_bytes((int)k, 4, S) > budget) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
     *out = S;
     return PG_OK;
 }
@@ -1096,11 +1222,15 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
     if (rc != PG_OK) return rc;
     hipStream_t st = (hipStream_t)s;
     if (x_dt == PG_F32) {
-        if (S.XS <= 4) return launch_fused_rs<PG_F32, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-        return launch_fused_rs<PG_F32, 16>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+        if (!(flags & PG_FLAG_RMSNORM))
+            return fail(PG_ERR_UNSUPPORTED, "pg_rot_qgemv: fp32 input needs PG_FLAG_RMSNORM (its rotation runs in fp16)");
+        if (S.XG <= 1) return launch_fused_rs<PG_F32, 1>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+        if (S.XG <= 2) return launch_fused_rs<PG_F32, 2>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+        return launch_fused_rs<PG_F32, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
     }
-    if (S.XS <= 4) return launch_fused_rs<PG_F16, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    return launch_fused_rs<PG_F16, 16>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.XG <= 1) return launch_fused_rs<PG_F16, 1>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    if (S.XG <= 2) return launch_fused_rs<PG_F16, 2>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+    return launch_fused_rs<PG_F16, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
 }
 
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x,

@@ -68,11 +68,11 @@ def test_zero_input_gives_zero_output():
     rng = np.random.default_rng(5)
     codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
     scales = synth.random_scale_bits(n, k, 5)
-    x = np.zeros((2, k), np.float32)
     sb = rng.integers(0, 256, k // 8, dtype=np.uint8)
-    for flags in (0, q.PG_FLAG_RMSNORM):
-        y = _run(codes, scales, x, q.PG_F32, k, k, sb, flags)
-        assert np.all(y == 0.0)
+    y = _run(codes, scales, np.zeros((2, k), np.float16), q.PG_F16, k, k, sb, 0)
+    assert np.all(y == 0.0)
+    y = _run(codes, scales, np.zeros((2, k), np.float32), q.PG_F32, k, k, sb, q.PG_FLAG_RMSNORM)
+    assert np.all(y == 0.0)
 
 
 @pytest.mark.parametrize("shapes_fn,layers", [(synth.qwen3_4b_shapes, 2), (synth.llama31_8b_shapes, 2)])

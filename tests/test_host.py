@@ -57,6 +57,10 @@ def test_codebook_table_matches_oracle():
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 1, 0, 1 << 24, stream=0),  # batch
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 3, 256, 1 << 20, 1, 1, 1 << 24, stream=0),  # dtype
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 1, 2, 1 << 22, stream=0),  # overlap
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 258, 1 << 20, 1, 1, 1 << 24, stream=0),  # row align
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 1, 260, 1 << 20, 1, 1, 1 << 24, stream=0),  # row align
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, (1 << 22) + 8, 0, 256, 1 << 20, 1, 1, 1 << 24, stream=0),
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, (1 << 20) + 2, 1, 1, 1 << 24, stream=0),
 ])
 def test_invalid_arguments_fail_before_launch(call):
     # the pointers are never dereferenced: validation rejects the call first
@@ -129,4 +133,10 @@ def test_encode_ref_rejects_bad_arguments():
 def test_rot_qgemv_rejects_k_beyond_its_register_staging():
     with pytest.raises(q.PgError) as ei:
         q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 32768, 1 << 22, 0, 32768, 1 << 20, 1, 1, 1 << 28, stream=0)
+    assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
+
+
+def test_rot_qgemv_rejects_fp32_input_without_normalisation():
+    with pytest.raises(q.PgError) as ei:
+        q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, q.PG_F32, 256, 1 << 20, 0, 1, 1 << 24, stream=0)
     assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
