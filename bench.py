@@ -8,10 +8,10 @@ stage kernel (RMS normalisation + activation rotation + qgemv; qkv and
 gate/up merged), replayed from a HIP graph.  Inputs are resident in HBM before timing starts.
 
 Printed: one JSON line with the whole-job compressed-weight GB/s
-(bytes per token x tokens per second), tokens per second, the qgemv
-kernel-sum roofline (HIP events around every stage launch of a separate
-pass over the same tokens) and the oracle's CPU throughput on a bounded
-sample of the same workload.
+(bytes per token x tokens per second), tokens per second, the roofline of
+the stage kernel (coded bytes per launch over its average duration, from
+the HIP events around the timed region) and the oracle's CPU throughput on
+a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -88,8 +88,11 @@ def run_stack(args):
 
     shapes = synth.qwen3_4b_shapes() if args.workload == "qwen36" else synth.llama31_8b_shapes()
     layers = 36 if args.workload == "qwen36" else 32
-    log(f"building {args.workload}: {layers} layers")
-    st = Stack(shapes, layers, batch=1, x_dtype=q.PG_Q16, fused=args.fused)
+    fused = args.path == "fused"
+    if not fused and args.batch != 1:
+        raise SystemExit("the split path runs batch 1 only")
+    log(f"building {args.workload}: {layers} layers, batch {args.batch}, {args.path} path")
+    st = Stack(shapes, layers, batch=args.batch, x_dtype=q.PG_Q16, fused=fused)
     stream = torch.cuda.current_stream()
     use_graph = not args.no_graph
     if use_graph:
@@ -99,7 +102,8 @@ def run_stack(args):
         step()
     torch.cuda.synchronize()
     log(f"warmup done (hip graph: {use_graph})")
-    # timed region: exactly `steps` tokens
+    # timed region: exactly `steps` tokens (one step = one pass of the batch
+    # through every layer), HIP events on the launch stream
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -111,75 +115,66 @@ def run_stack(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_tok = max(gpu_ms, wall * 1e3) / args.steps
-    log(f"timed {args.steps} tokens: {gpu_ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    log(f"timed {args.steps} steps: {gpu_ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
 
-    # Per-launch kernel durations: events around every product launch of a
-    # second pass over the same tokens.  A spin kernel queued first holds the
-    # GPU while the host enqueues, so the events time back-to-back GPU work,
-    # not the host's launch rate.
-    qg_ms, qg_bytes, launches = 0.0, 0, 0
-    evs = []
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.4e9 * 0.25))             # ~0.25 s of GPU clock cycles
-    prof_tokens = 2
-    for _ in range(prof_tokens):
-        for layer in range(layers):
-            for site in ORDER:
-                n, k = st.shapes[site]
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                if not st.fused:
-                    # split path: the rotation launch is not timed, the product is
+    launches_per_step = (4 if fused else 8) * layers
+    bytes_per_launch = st.bytes_per_token // (4 * layers)
+    if fused:
+        # every launch of the step is the fused stage kernel: its average
+        # duration is the timed region over the launches (gaps included)
+        avg_us = 1e3 * gpu_ms / (args.steps * launches_per_step)
+        kname = "k_rot_qgemv"
+        kdesc = "k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
+        nlaunch = args.steps * launches_per_step
+    else:
+        # split path: events around every product launch of a separate pass;
+        # a spin kernel queued first holds the GPU while the host enqueues, so
+        # the events time back-to-back GPU work, not the host's launch rate
+        evs = []
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.25))
+        for _ in range(2):
+            for layer in range(layers):
+                for site in ORDER:
+                    n, k = st.shapes[site]
                     first = site == "qkv" and layer == 0
                     prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
                     q.pg_fwht_rotate(st.h0 if first else st.out[prev], q.PG_F16 if first else q.PG_F32, st.xrot,
                                      q.PG_Q16, st.signs[layer][site], 1, k, 0 if first else q.PG_FLAG_RMSNORM)
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
                     q.pg_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.xrot, q.PG_Q16, 1,
                                st.out[site])
                     b.record(stream)
-                elif site == "qkv" and layer == 0:
-                    a.record(stream)
-                    q.pg_rot_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.h0, q.PG_F16, k,
-                                   st.signs[layer][site], 0, 1, st.out[site])
-                    b.record(stream)
-                else:
-                    prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
-                    n_prev = st.shapes[prev][0]
-                    a.record(stream)
-                    q.pg_rot_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.out[prev], q.PG_F32,
-                                   n_prev, st.signs[layer][site], q.PG_FLAG_RMSNORM, 1, st.out[site])
-                    b.record(stream)
-                evs.append((a, b))
-                qg_bytes += st.codes[layer][site].numel() + 2 * st.scales[layer][site].numel()
-                launches += 1
-    torch.cuda.synchronize()
-    for a, b in evs:
-        qg_ms += a.elapsed_time(b)
-    achieved = qg_bytes / (qg_ms * 1e-3) / 1e9
-    kname = "k_rot_qgemv" if st.fused else "k_qgemv_q16"
-    wl = "qwen3-4b-36L-b1" if args.workload == "qwen36" else "llama3.1-8b-32L-b1"
+                    evs.append((a, b))
+        torch.cuda.synchronize()
+        avg_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        kname = "k_qgemv_q16"
+        kdesc = "k_qgemv_q16 (pg_qgemv on PG_Q16 activations)"
+        nlaunch = len(evs)
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    wl = ("qwen3-4b-36L" if args.workload == "qwen36" else "llama3.1-8b-32L") + f"-b{args.batch}"
     traffic = committed_traffic(kname, wl)
-    tok_s = 1e3 / ms_per_tok
-    value = st.bytes_per_token * tok_s / 1e9
+    tok_s = args.batch * 1e3 / ms_per_step
+    value = st.bytes_per_token * (1e3 / ms_per_step) / 1e9
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_tok, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "i8xi8->i32 (levels x 16-bit activation digits), f32 scales", "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8xi8->i32 (levels x 16-bit activation digits), f16 MFMA rotation, f32 scales",
+        "data": "synthetic",
         "config": {"workload": f"{'Qwen3-4B' if args.workload == 'qwen36' else 'Llama-3.1-8B'}-shaped "
-                               f"{layers}-layer linear stack, batch 1, random trellis bitstreams",
-                   "layers": layers, "batch": 1, "bytes_per_token": st.bytes_per_token,
+                               f"{layers}-layer linear stack, batch {args.batch}, random trellis bitstreams",
+                   "layers": layers, "batch": args.batch, "bytes_per_token": st.bytes_per_token,
                    "tok_per_s": round(tok_s, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "hip_graphs": use_graph, "launches_per_token": (4 if st.fused else 8) * layers,
-                   "path": "fused" if st.fused else "split"},
+                   "hip_graphs": use_graph, "launches_per_token": launches_per_step, "path": args.path},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_bytes_per_launch": qg_bytes // launches,
-                     "kernel": ("k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
-                                if st.fused else "k_qgemv_q16 (pg_qgemv on PG_Q16 activations)"),
-                     "launches": launches, "avg_launch_us": round(1e3 * qg_ms / launches, 3)},
+                     "algorithmic_bytes_per_launch": bytes_per_launch, "kernel": kdesc,
+                     "launches": nlaunch, "avg_launch_us": round(avg_us, 3)},
     }
     return res
 
@@ -194,7 +189,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 4 times (HBM-counter calibration) and exit")
-    ap.add_argument("--fused", action="store_true", help="one pg_rot_qgemv launch per stage instead of rotation + qgemv")
+    ap.add_argument("--path", default="fused", choices=["fused", "split"],
+                    help="fused: one pg_rot_qgemv per stage; split: pg_fwht_rotate + pg_qgemv per stage")
+    ap.add_argument("--batch", type=int, default=1, help="activation rows per step (fused path: 1..8)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "

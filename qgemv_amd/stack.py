@@ -2,15 +2,17 @@
 Llama-3.1-8B-shaped layers) on one GPU.
 
 Orchestration only: device buffers come from torch, every step is a
-libpingala call (pg_fwht_rotate, pg_qgemv) on one stream.  Per layer, the
-four launch groups that share an input are chained as
+libpingala call on one stream.  Per layer, the four launch groups that
+share an input are chained as
     x~ = R_qkv h        -> [q k v] = W~qkv x~
     x~ = R_o n16(q)     -> o        = W~o x~
     x~ = R_gu n16(o)    -> [g u]    = W~gu x~
     x~ = R_down n16(g)  -> d        = W~down x~ ,   h' = d
-where n16 is the RMS normalisation with fp16 rounding fused into the
-rotation (PG_FLAG_RMSNORM); the first layer's input is fp16 and is not
-normalised.  k, v and u are computed and stored but not consumed.
+where n16 is the RMS normalisation with fp16 rounding; the first layer's
+input is fp16 and is not normalised.  k, v and u are computed and stored but
+not consumed.  The fused path (default) runs each group as one
+pg_rot_qgemv launch (normalisation + rotation + product, batch 1..8); the
+split path runs pg_fwht_rotate then pg_qgemv (batch 1).
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ ORDER = ("qkv", "o", "gu", "down")
 
 class Stack:
     def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_Q16,
-                 fused: bool = False):
+                 fused: bool = True):
         import torch
         self.shapes = synth.merged_shapes(shapes)
         self.raw_shapes = shapes

@@ -28,6 +28,22 @@ def test_chain_matches_oracle(shapes_fn, layers, fused):
     assert np.array_equal(d2.view(np.uint32), got.view(np.uint32))
 
 
+@pytest.mark.parametrize("batch", [3, 4])
+def test_fused_chain_batched_matches_oracle(batch):
+    """Batched decode through the fused stage (several activation rows per
+    launch) against the oracle's chain, row by row."""
+    import torch
+    from tests.helpers import rel_err_rows
+    shapes = synth.llama31_8b_shapes()
+    st = Stack(shapes, 2, batch=batch, fused=True)
+    got = host(st.token())
+    torch.cuda.synchronize()
+    codes, scales, signs = zip(*[st.host_arrays(l) for l in range(2)])
+    ref = oracle_chain(list(codes), list(scales), list(signs), shapes, host(st.h0).astype(np.float64), 2)
+    assert got.shape == ref.shape == (batch, shapes["down"][0])
+    assert np.max(rel_err_rows(got, ref)) <= TOL
+
+
 def test_graph_replays_match_eager():
     """A captured token replays bitwise-identically to the eager token, on
     every replay, with eager work and synchronisations in between."""
