@@ -590,7 +590,8 @@ __global__ __launch_bounds__(512) void k_qgemv_q16(const uint8_t* __restrict__ c
 // RP = 8W / CG, at most RS rows per lane and XG 8-value groups of x per
 // thread.
 struct FusedShape {
-    int W, R, CG, RP, RS, XG, BT;
+    int W, R, CG, RP, RS, XG;
+    int BT, BTM;         // batch rows per launch, and the kernel's compile-time bound on them
 };
 
 constexpr int FS_PITCH = 144;      // LDS bytes per 64-value chunk of digits (128 + 16 against bank conflicts)
@@ -599,20 +600,15 @@ constexpr int FS_XPITCH = 272;     // LDS bytes per staged fp16 128-block (256 +
 // LDS bytes per batch row: digits, then per 32-value quarter its scale and
 // its sum of q
 __host__ __device__ inline int fused_row_bytes(int k) { return ((k / 64) * FS_PITCH + (k / 32) * 8 + 15) & ~15; }
+// one input row as given (fp32 or fp16), and its fp16 blocks
+__host__ __device__ inline int fused_xrow_bytes(int k, int esz) { return (k * esz + 15) & ~15; }
+__host__ __device__ inline int fused_xhrow_bytes(int k) { return (k / 128) * FS_XPITCH; }
 
-// LDS staging of one input row (x as given, fp32 or fp16; later the fp16
-// blocks), then the sign bits
-__host__ __device__ inline int fused_xreg_bytes(int k, int esz) {
-    const int a = k * esz, b = (k / 128) * FS_XPITCH;
-    return ((a > b ? a : b) + 15) & ~15;
-}
-__host__ __device__ inline int fused_xbuf_bytes(int k, int esz) {
-    return fused_xreg_bytes(k, esz) + ((k / 8 + 15) & ~15);
-}
-
+// LDS of one launch: BT rows of x, of fp16 blocks and of digits, the sign
+// bits, the team sums and the per-wave sums of squares
 __host__ inline size_t fused_lds_bytes(int k, int esz, const FusedShape& S) {
-    return (size_t)fused_xbuf_bytes(k, esz) + (size_t)S.BT * fused_row_bytes(k) + (size_t)S.BT * S.R * S.CG * 4 +
-           (size_t)S.W * 4;
+    return (size_t)S.BT * (fused_xrow_bytes(k, esz) + fused_xhrow_bytes(k) + fused_row_bytes(k)) +
+           (size_t)((k / 8 + 15) & ~15) + (size_t)S.BT * S.R * S.CG * 4 + (size_t)S.BT * S.W * 4;
 }
 
 // s_waitcnt operand: at most n vector-memory operations of this wave still
@@ -629,7 +625,7 @@ __device__ __forceinline__ int fs_elem(int mt, int M) {
 
 typedef _Float16 fs_f16x8 __attribute__((ext_vector_type(8)));
 
-template <int XDT, int XG, int RS>
+template <int XDT, int XG, int RS, int BTM>
 __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ codes,
                                                     const uint16_t* __restrict__ scales, int n, int k,
                                                     const void* __restrict__ x, int64_t ldx,
@@ -643,13 +639,15 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     const int T = wave * 8 + (lane >> 3), tl = lane & 7;
     const int kg = k >> 2, nchunk = k >> 6, nbk = k >> 7, ngr = k >> 3;
     const int row0 = blockIdx.x * R;
-    const int rb = fused_row_bytes(k);
+    const int bt = batch;                                    // batch rows of this launch (<= BT <= BTM)
     const int esz = XDT == PG_F32 ? 4 : 2;
-    uint8_t* xbuf = lds;                                     // x as given, later the fp16 blocks
-    uint8_t* sbuf = lds + fused_xreg_bytes(k, esz);          // sign bits
-    uint8_t* rows_lds = lds + fused_xbuf_bytes(k, esz);      // [BT][rb] digits, scales, sums
+    const int xrow = fused_xrow_bytes(k, esz), xhrow = fused_xhrow_bytes(k), rb = fused_row_bytes(k);
+    uint8_t* xbuf = lds;                                     // [BT][xrow] x as given
+    uint8_t* xh = xbuf + (size_t)BT * xrow;                  // [BT][nbk][FS_XPITCH] fp16 blocks
+    uint8_t* sbuf = xh + (size_t)BT * xhrow;                 // sign bits
+    uint8_t* rows_lds = sbuf + ((k / 8 + 15) & ~15);         // [BT][rb] digits, scales, sums
     float* part = reinterpret_cast<float*>(rows_lds + (size_t)BT * rb);   // [BT][R][CG]
-    float* wsum = part + (size_t)BT * R * CG;                             // [W]
+    float* wsum = part + (size_t)BT * R * CG;                             // [BT][W]
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
 
     // this lane's column of chunks and its rows
@@ -658,14 +656,14 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     const bool col_ok = rp < RP && c < nchunk;
     const int cc = c < nchunk ? c : nchunk - 1;
 
-    // ---- 1. x to LDS (16 bytes per lane), sign bits, then all code chunks
-    auto stage_x = [&](int b) {
+    // ---- 1. x rows to LDS (16 bytes per lane), sign bits, then all code chunks
+    for (int b = 0; b < bt; ++b) {
         const uint8_t* src = (const uint8_t*)x + (int64_t)b * ldx * esz;
         const int bytes = k * esz;
         for (int o = wave * 1024; o < bytes; o += W * 1024)
-            if (o + 16 * lane < bytes) __builtin_amdgcn_global_load_lds(src + o + 16 * lane, xbuf + o, 16, 0, 0);
-    };
-    stage_x(0);
+            if (o + 16 * lane < bytes)
+                __builtin_amdgcn_global_load_lds(src + o + 16 * lane, xbuf + (size_t)b * xrow + o, 16, 0, 0);
+    }
     uint32_t sg = 0;
     const bool sg_on = tid < k / 32;
     if (sg_on) sg = reinterpret_cast<const uint32_t*>(sign_bits)[tid];
@@ -712,136 +710,137 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     }
     const int ntile = (nbk + 31) >> 5;
 
-    const int bt = batch;                      // one launch covers bt <= BT batch rows
-    for (int b = 0; b < bt; ++b) {
-        if (b > 0) {
-            __syncthreads();                   // the previous row's fp16 blocks are consumed
-            stage_x(b);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+    // ---- 2. sums of squares of every batch row: thread t takes 8-value
+    // groups t + nthr u, then wave sums
+    auto read8 = [&](int b, int gi, float v[8]) {
+        const uint8_t* xr = xbuf + (size_t)b * xrow;
+        if (XDT == PG_F32) {
+            const float4 v0 = *reinterpret_cast<const float4*>(xr + 32 * gi);
+            const float4 v1 = *reinterpret_cast<const float4*>(xr + 32 * gi + 16);
+            v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+            v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+        } else {
+            const uint4 w = *reinterpret_cast<const uint4*>(xr + 16 * gi);
+            const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v[2 * t] = h2f((uint16_t)(w4[t] & 0xffffu));
+                v[2 * t + 1] = h2f((uint16_t)(w4[t] >> 16));
+            }
         }
-        // ---- 2. norm and fp16 staging: thread t takes 8-value groups t + nthr u
-        float xv[XG][8];
-        uint32_t xs8[XG];
-        float ss = 0.0f;
+    };
+    if (norm) {
+        for (int b = 0; b < bt; ++b) {
+            float ss = 0.0f;
 #pragma unroll
-        for (int u = 0; u < XG; ++u) {
-            const int gi = tid + nthr * u;
-            const int gc = gi < ngr ? gi : 0;
-            if (XDT == PG_F32) {
-                const float4 v0 = *reinterpret_cast<const float4*>(xbuf + 32 * gc);
-                const float4 v1 = *reinterpret_cast<const float4*>(xbuf + 32 * gc + 16);
-                xv[u][0] = v0.x; xv[u][1] = v0.y; xv[u][2] = v0.z; xv[u][3] = v0.w;
-                xv[u][4] = v1.x; xv[u][5] = v1.y; xv[u][6] = v1.z; xv[u][7] = v1.w;
-            } else {
-                const uint4 v = *reinterpret_cast<const uint4*>(xbuf + 16 * gc);
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            for (int u = 0; u < XG; ++u) {
+                const int gi = tid + nthr * u;
+                if (gi < ngr) {
+                    float v[8];
+                    read8(b, gi, v);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    xv[u][2 * t] = h2f((uint16_t)(w4[t] & 0xffffu));
-                    xv[u][2 * t + 1] = h2f((uint16_t)(w4[t] >> 16));
+                    for (int t = 0; t < 8; ++t) ss += v[t] * v[t];
                 }
             }
-            xs8[u] = sbuf[gc];
-            if (gi < ngr)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) ss += xv[u][t] * xv[u][t];
+            ss = wave_sum(ss);
+            if (lane == 0) wsum[b * W + wave] = ss;
         }
+        __syncthreads();
+    }
+    // ---- 3. normalised, sign-flipped fp16 blocks of every batch row
+    for (int b = 0; b < bt; ++b) {
         float inv = 1.0f;
         if (norm) {
-            ss = wave_sum(ss);
-            if (b > 0) __syncthreads();        // wsum of the previous row consumed
-            if (lane == 0) wsum[wave] = ss;
-        }
-        __syncthreads();                       // every x read is done: the blocks may overwrite x
-        if (norm) {
             float tot = 0.0f;
-            for (int w = 0; w < W; ++w) tot += wsum[w];
+            for (int w = 0; w < W; ++w) tot += wsum[b * W + w];
             inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
         }
 #pragma unroll
         for (int u = 0; u < XG; ++u) {
             const int gi = tid + nthr * u;
             if (gi < ngr) {
+                float v[8];
+                read8(b, gi, v);
+                const uint32_t s8 = sbuf[gi];
                 uint32_t hw[4];
 #pragma unroll
                 for (int t = 0; t < 8; t += 2) {
-                    uint32_t h0 = f2h(norm ? xv[u][t] * inv : xv[u][t]);
-                    uint32_t h1 = f2h(norm ? xv[u][t + 1] * inv : xv[u][t + 1]);
-                    h0 ^= ((xs8[u] >> t) & 1u) << 15;
-                    h1 ^= ((xs8[u] >> (t + 1)) & 1u) << 15;
+                    uint32_t h0 = f2h(norm ? v[t] * inv : v[t]);
+                    uint32_t h1 = f2h(norm ? v[t + 1] * inv : v[t + 1]);
+                    h0 ^= ((s8 >> t) & 1u) << 15;
+                    h1 ^= ((s8 >> (t + 1)) & 1u) << 15;
                     hw[t >> 1] = h0 | (h1 << 16);
                 }
-                *reinterpret_cast<uint4*>(xbuf + (gi >> 4) * FS_XPITCH + (gi & 15) * 16) =
+                *reinterpret_cast<uint4*>(xh + (size_t)b * xhrow + (gi >> 4) * FS_XPITCH + (gi & 15) * 16) =
                     make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            }
-        }
-        __syncthreads();
-        // ---- 3./4. Hadamard tiles on the matrix cores, quantised per 32 values
-        uint8_t* dig = rows_lds + (size_t)b * rb;
-        float* sxq = reinterpret_cast<float*>(dig + nchunk * FS_PITCH);
-        int* sqq = reinterpret_cast<int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
-        for (int job = wave; job < 4 * ntile; job += W) {
-            const int nt = job >> 2, mt = job & 3;
-            const int blk = nt * 32 + (lane & 31);
-            const bool bok = blk < nbk;
-            const uint8_t* xrow = xbuf + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
-            f32x16 acc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                uint4 bw = *reinterpret_cast<const uint4*>(xrow + 32 * st);
-                if (!bok) bw = make_uint4(0, 0, 0, 0);
-                const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
-                const uint32_t* av = apat[st & 1];
-                const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
-                                                             __builtin_bit_cast(fs_f16x8, bw), acc, 0, 0, 0);
-            }
-            // quarter maximum: 16 values per lane, then the lane pair (l, l + 32)
-            float mx = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc[r]));
-            mx = fmaxf(mx, xor_lane32(mx, lane));
-            const float s = mx > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(mx) : 0.0f;
-            const int ch = 2 * blk + (mt >> 1);              // chunk of this quarter
-            uint8_t* dq = dig + (bok ? ch : 0) * FS_PITCH + 32 * 2 * (mt & 1) + 4 * (lane >> 5);
-            int shi = 0, slo = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t bits[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) bits[r] = __builtin_bit_cast(uint32_t, fmaf(acc[4 * i + r], s, 12582912.0f));
-                const uint32_t t01 = __builtin_amdgcn_perm(bits[1], bits[0], 0x05040100u);
-                const uint32_t t23 = __builtin_amdgcn_perm(bits[3], bits[2], 0x05040100u);
-                const uint32_t dl = __builtin_amdgcn_perm(t23, t01, 0x06040200u);   // q mod 256 of groups 0..3
-                const uint32_t dh = __builtin_amdgcn_perm(t23, t01, 0x07050301u);   // floor(q / 256)
-                shi = __builtin_amdgcn_sdot4((int)dh, 0x01010101, shi, false);
-                slo = (int)__builtin_amdgcn_udot4(dl, 0x01010101u, (uint32_t)slo, false);
-                // part 2 (mt % 2) + i / 2 of the chunk, position 2 (i % 2) + l / 32
-                if (bok) {
-                    uint8_t* dd = dq + 32 * (i >> 1) + 8 * (i & 1);
-                    *reinterpret_cast<uint32_t*>(dd) = dh;
-                    *reinterpret_cast<uint32_t*>(dd + 16) = dl;
-                }
-            }
-            int qs = 256 * shi + slo;
-            qs += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, qs), lane));
-            if (bok && lane < 32) {
-                sxq[4 * blk + mt] = mx * (0.08838834764831845f / (float)Q16_MAXQ);   // 2^-3.5 max / 32512
-                sqq[4 * blk + mt] = qs;
             }
         }
     }
     __syncthreads();
-    // ---- 5. decode and dot products, one batch row at a time
-    for (int b = 0; b < bt; ++b) {
-        // codes and scales are used only here, through copies passed
-        // through an opaque move: that keeps the compiler from hoisting
-        // their decode above the rotation (which would wait for every code
-        // request first) and rebuilds the planes per batch row rather than
-        // keeping 16 RS of them
+    // ---- 4. Hadamard tiles on the matrix cores, quantised per 32 values
+    for (int job = wave; job < bt * 4 * ntile; job += W) {
+        const int b = job / (4 * ntile), jj = job - b * 4 * ntile;
+        const int nt = jj >> 2, mt = jj & 3;
+        const int blk = nt * 32 + (lane & 31);
+        const bool bok = blk < nbk;
+        uint8_t* dig = rows_lds + (size_t)b * rb;
+        float* sxq = reinterpret_cast<float*>(dig + nchunk * FS_PITCH);
+        int* sqq = reinterpret_cast<int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
+        const uint8_t* xr = xh + (size_t)b * xhrow + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            uint4 bw = *reinterpret_cast<const uint4*>(xr + 32 * st);
+            if (!bok) bw = make_uint4(0, 0, 0, 0);
+            const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
+            const uint32_t* av = apat[st & 1];
+            const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
+                                                         __builtin_bit_cast(fs_f16x8, bw), acc, 0, 0, 0);
+        }
+        // quarter maximum: 16 values per lane, then the lane pair (l, l + 32)
+        float mx = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc[r]));
+        mx = fmaxf(mx, xor_lane32(mx, lane));
+        const float s = mx > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(mx) : 0.0f;
+        const int ch = 2 * blk + (mt >> 1);                  // chunk of this quarter
+        uint8_t* dq = dig + (bok ? ch : 0) * FS_PITCH + 32 * 2 * (mt & 1) + 4 * (lane >> 5);
+        int shi = 0, slo = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t bits[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bits[r] = __builtin_bit_cast(uint32_t, fmaf(acc[4 * i + r], s, 12582912.0f));
+            const uint32_t t01 = __builtin_amdgcn_perm(bits[1], bits[0], 0x05040100u);
+            const uint32_t t23 = __builtin_amdgcn_perm(bits[3], bits[2], 0x05040100u);
+            const uint32_t dl = __builtin_amdgcn_perm(t23, t01, 0x06040200u);   // q mod 256 of groups 0..3
+            const uint32_t dh = __builtin_amdgcn_perm(t23, t01, 0x07050301u);   // floor(q / 256)
+            shi = __builtin_amdgcn_sdot4((int)dh, 0x01010101, shi, false);
+            slo = (int)__builtin_amdgcn_udot4(dl, 0x01010101u, (uint32_t)slo, false);
+            // part 2 (mt % 2) + i / 2 of the chunk, position 2 (i % 2) + l / 32
+            if (bok) {
+                uint8_t* dd = dq + 32 * (i >> 1) + 8 * (i & 1);
+                *reinterpret_cast<uint32_t*>(dd) = dh;
+                *reinterpret_cast<uint32_t*>(dd + 16) = dl;
+            }
+        }
+        int qs = 256 * shi + slo;
+        qs += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, qs), lane));
+        if (bok && lane < 32) {
+            sxq[4 * blk + mt] = mx * (0.08838834764831845f / (float)Q16_MAXQ);   // 2^-3.5 max / 32512
+            sqq[4 * blk + mt] = qs;
+        }
+    }
+    __syncthreads();
+    // ---- 5. decode and dot products: the planes of a code dword are built
+    // once and used for every batch row
+    {
+        // codes and scales are used only here, through copies passed through
+        // an opaque move: that keeps the compiler from hoisting their decode
+        // above the rotation (which would wait for every code request first)
         uint4 qb[RS];
         uint32_t wb[RS];
 #pragma unroll
@@ -850,20 +849,34 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
             wb[j] = wsr[j];
             asm volatile("" : "+v"(qb[j].x), "+v"(qb[j].y), "+v"(qb[j].z), "+v"(qb[j].w), "+v"(wb[j]));
         }
-        const uint8_t* dig = rows_lds + (size_t)b * rb;
-        const float* sxq = reinterpret_cast<const float*>(dig + nchunk * FS_PITCH);
-        const int* sqq = reinterpret_cast<const int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
-        const float sx0 = sxq[2 * cc], sx1 = sxq[2 * cc + 1];
-        const int sq0 = sqq[2 * cc], sq1 = sqq[2 * cc + 1];
-        float tq[RS];
-        int hi[RS], lo[RS];
+        float sx0[BTM], sx1[BTM];
+        int sq0[BTM], sq1[BTM];
+#pragma unroll
+        for (int b = 0; b < BTM; ++b) {
+            const uint8_t* dig = rows_lds + (size_t)(b < bt ? b : 0) * rb;
+            const float* sxq = reinterpret_cast<const float*>(dig + nchunk * FS_PITCH);
+            const int* sqq = reinterpret_cast<const int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
+            sx0[b] = sxq[2 * cc];
+            sx1[b] = sxq[2 * cc + 1];
+            sq0[b] = sqq[2 * cc];
+            sq1[b] = sqq[2 * cc + 1];
+        }
+        float tq[RS][BTM];
+        int hi[RS][BTM], lo[RS][BTM];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             if (m == 0 || m == 2)
 #pragma unroll
-                for (int j = 0; j < RS; ++j) { hi[j] = 0; lo[j] = 0; }
-            const uint4 xh = *reinterpret_cast<const uint4*>(dig + cc * FS_PITCH + 32 * m);
-            const uint4 xl = *reinterpret_cast<const uint4*>(dig + cc * FS_PITCH + 32 * m + 16);
+                for (int j = 0; j < RS; ++j)
+#pragma unroll
+                    for (int b = 0; b < BTM; ++b) { hi[j][b] = 0; lo[j][b] = 0; }
+            uint4 xh4[BTM], xl4[BTM];
+#pragma unroll
+            for (int b = 0; b < BTM; ++b) {
+                const uint8_t* dig = rows_lds + (size_t)(b < bt ? b : 0) * rb + cc * FS_PITCH + 32 * m;
+                xh4[b] = *reinterpret_cast<const uint4*>(dig);
+                xl4[b] = *reinterpret_cast<const uint4*>(dig + 16);
+            }
 #pragma unroll
             for (int j = 0; j < RS; ++j) {
                 const uint32_t w4[4] = {qb[j].x, qb[j].y, qb[j].z, qb[j].w};
@@ -877,35 +890,47 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
                 }
                 uint32_t P[4];
                 planes_of(w4[m], prev, P);
-                int h = hi[j];
-                uint32_t l = (uint32_t)lo[j];
-                h = __builtin_amdgcn_sdot4((int)P[0], (int)xh.x, h, false);
-                l = __builtin_amdgcn_udot4(P[0], xl.x, l, false);
-                h = __builtin_amdgcn_sdot4((int)P[1], (int)xh.y, h, false);
-                l = __builtin_amdgcn_udot4(P[1], xl.y, l, false);
-                h = __builtin_amdgcn_sdot4((int)P[2], (int)xh.z, h, false);
-                l = __builtin_amdgcn_udot4(P[2], xl.z, l, false);
-                h = __builtin_amdgcn_sdot4((int)P[3], (int)xh.w, h, false);
-                l = __builtin_amdgcn_udot4(P[3], xl.w, l, false);
-                hi[j] = h;
-                lo[j] = (int)l;
+#pragma unroll
+                for (int b = 0; b < BTM; ++b) {
+                    if (BTM > 1 && b >= bt) break;                 // uniform
+                    int h = hi[j][b];
+                    uint32_t l = (uint32_t)lo[j][b];
+                    h = __builtin_amdgcn_sdot4((int)P[0], (int)xh4[b].x, h, false);
+                    l = __builtin_amdgcn_udot4(P[0], xl4[b].x, l, false);
+                    h = __builtin_amdgcn_sdot4((int)P[1], (int)xh4[b].y, h, false);
+                    l = __builtin_amdgcn_udot4(P[1], xl4[b].y, l, false);
+                    h = __builtin_amdgcn_sdot4((int)P[2], (int)xh4[b].z, h, false);
+                    l = __builtin_amdgcn_udot4(P[2], xl4[b].z, l, false);
+                    h = __builtin_amdgcn_sdot4((int)P[3], (int)xh4[b].w, h, false);
+                    l = __builtin_amdgcn_udot4(P[3], xl4[b].w, l, false);
+                    hi[j][b] = h;
+                    lo[j][b] = (int)l;
+                }
             }
             // quarter done: sum level * q = 2 (256 hi + lo) - 7 sum q
             if (m == 1)
 #pragma unroll
-                for (int j = 0; j < RS; ++j) tq[j] = sx0 * (float)(2 * (hi[j] * 256 + lo[j]) - 7 * sq0);
+                for (int j = 0; j < RS; ++j)
+#pragma unroll
+                    for (int b = 0; b < BTM; ++b) tq[j][b] = sx0[b] * (float)(2 * (hi[j][b] * 256 + lo[j][b]) - 7 * sq0[b]);
             if (m == 3)
 #pragma unroll
-                for (int j = 0; j < RS; ++j) tq[j] += sx1 * (float)(2 * (hi[j] * 256 + lo[j]) - 7 * sq1);
+                for (int j = 0; j < RS; ++j)
+#pragma unroll
+                    for (int b = 0; b < BTM; ++b) tq[j][b] += sx1[b] * (float)(2 * (hi[j][b] * 256 + lo[j][b]) - 7 * sq1[b]);
         }
 #pragma unroll
         for (int j = 0; j < RS; ++j) {
             const float wsc = h2f((uint16_t)(whi[j] ? wb[j] >> 16 : wb[j]));
-            float v = rok[j] ? wsc * tq[j] : 0.0f;
-            v += xor_lane<4>(v, lane);
-            v += xor_lane<2>(v, lane);
-            v += xor_lane<1>(v, lane);
-            if (tl == 0 && rp < RP && rp + j * RP < R) part[((size_t)b * R + rp + j * RP) * CG + cg] = v;
+#pragma unroll
+            for (int b = 0; b < BTM; ++b) {
+                if (BTM > 1 && b >= bt) break;                     // uniform
+                float v = rok[j] ? wsc * tq[j][b] : 0.0f;
+                v += xor_lane<4>(v, lane);
+                v += xor_lane<2>(v, lane);
+                v += xor_lane<1>(v, lane);
+                if (tl == 0 && rp < RP && rp + j * RP < R) part[((size_t)b * R + rp + j * RP) * CG + cg] = v;
+            }
         }
     }
     __syncthreads();
@@ -1130,7 +1155,7 @@ int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
 
 namespace {
 
-template <int XDT, int XG, int RS>
+template <int XDT, int XG, int RS, int BTM>
 int launch_fused_t(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                    const void* x, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
                    hipStream_t st) {
@@ -1139,24 +1164,38 @@ int launch_fused_t(const FusedShape& S, const uint8_t* codes, const uint16_t* sc
     for (int b0 = 0; b0 < batch; b0 += S.BT) {
         const int bt = batch - b0 < S.BT ? batch - b0 : S.BT;
         const void* xb = (const uint8_t*)x + (int64_t)b0 * ldx * esz;
-        hipLaunchKernelGGL((k_rot_qgemv<XDT, XG, RS>), grid, dim3(64 * S.W), fused_lds_bytes((int)k, esz, S), st,
-                           codes, scales, (int)n, (int)k, xb, ldx, sign_bits, flags, bt, y + (int64_t)b0 * n, S.R,
-                           S.CG, S.RP, S.BT);
+        hipLaunchKernelGGL((k_rot_qgemv<XDT, XG, RS, BTM>), grid, dim3(64 * S.W), fused_lds_bytes((int)k, esz, S),
+                           st, codes, scales, (int)n, (int)k, xb, ldx, sign_bits, flags, bt, y + (int64_t)b0 * n,
+                           S.R, S.CG, S.RP, S.BT);
         const int rc = hip_check(hipGetLastError(), "pg_rot_qgemv launch");
         if (rc != PG_OK) return rc;
     }
     return PG_OK;
 }
 
+// (rows per lane, batch rows per launch) combinations that fit the register
+// budget (RS * BTM <= 32, and RS <= 2 for 8 rows)
 template <int XDT, int XG>
 int launch_fused_rs(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                     const void* x, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
                     hipStream_t st) {
-    if (S.RS <= 1) return launch_fused_t<XDT, XG, 1>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    if (S.RS <= 2) return launch_fused_t<XDT, XG, 2>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    if (S.RS <= 4) return launch_fused_t<XDT, XG, 4>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    if (S.RS <= 8) return launch_fused_t<XDT, XG, 8>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
-    return launch_fused_t<XDT, XG, 16>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st);
+#define PG_FUSED(RS_, BTM_) return launch_fused_t<XDT, XG, RS_, BTM_>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st)
+    if (S.BTM == 1) {
+        if (S.RS <= 1) PG_FUSED(1, 1);
+        if (S.RS <= 2) PG_FUSED(2, 1);
+        if (S.RS <= 4) PG_FUSED(4, 1);
+        if (S.RS <= 8) PG_FUSED(8, 1);
+        PG_FUSED(16, 1);
+    }
+    if (S.BTM == 2) PG_FUSED(16, 2);
+    if (S.BTM == 4) {
+        if (S.RS <= 2) PG_FUSED(2, 4);
+        if (S.RS <= 4) PG_FUSED(4, 4);
+        PG_FUSED(8, 4);
+    }
+    if (S.RS <= 1) PG_FUSED(1, 8);
+    PG_FUSED(2, 8);
+#undef PG_FUSED
 }
 
 int compute_units() {
@@ -1201,9 +1240,13 @@ int fused_shape(int64_t n, int64_t k, int batch, FusedShape* out) {
     if (R > n) R = n;
     S.R = (int)R;
     S.RS = (S.R + S.RP - 1) / S.RP;
+    // batch rows per launch: the template's bound BTM (registers: RS * BTM <= 32,
+    // RS <= 2 for 8 rows)
+    // and as many rows as the LDS budget holds
+    S.BTM = batch <= 1 ? 1 : (S.RS <= 2 && batch > 4) ? 8 : S.RS <= 8 ? 4 : 2;
     const size_t budget = 150 * 1024;
     S.BT = 1;
-    while (S.BT < 8 && S.BT < batch) {
+    while (S.BT < S.BTM && S.BT < batch) {
         FusedShape T = S;
         T.BT = S.BT + 1;
         if (fused_lds_bytes((int)k, 4, T) > budget) break;
