@@ -350,18 +350,26 @@ __global__ __launch_bounds__(256) void k_qgemv_v1(const uint8_t* __restrict__ co
 //   sum level * q = 2 * (256 * hi + lo) - 7 * sum q
 // exactly in int32, then one fp32 multiply by (weight scale * activation
 // block scale).
+// (a & m) | c and a ^ b ^ c, one gfx950 three-input bit operation each
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
+}
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 __device__ __forceinline__ void planes_of(uint32_t d, uint32_t dp, uint32_t P[4]) {
-    const uint32_t a1 = __builtin_amdgcn_alignbyte(d, dp, 3);   // byte g = byte g-1
-    const uint32_t a2 = __builtin_amdgcn_alignbyte(d, dp, 2);   // byte g = byte g-2
-    const uint32_t a3 = __builtin_amdgcn_alignbyte(d, dp, 1);   // byte g = byte g-3
     const uint32_t M1 = 0x01010101u, M2 = 0x02020202u, M4 = 0x04040404u;
-    const uint32_t zb = a2 & M1;                                  // z0 = u_{t-2}
+    const uint32_t z = __builtin_amdgcn_alignbyte(d, dp, 2) & M1;    // z0 = u_{t-2}: bit 0 of byte g-2
     const uint32_t d1 = d >> 1, d2 = d >> 2, d3 = d >> 3, d4 = d >> 4, d5 = d >> 5;
-    P[0] = (d2 & M4) | (d & M2) | zb;
-    P[1] = (d3 & M4) | (d1 & M2) | zb;
-    P[2] = (d4 & M4) | (d2 & M2) | zb;
-    const uint32_t par = d ^ d1 ^ d2 ^ d3 ^ a1 ^ a3;             // bit 0: b3 = z1^b0^b1^b2
-    P[3] = (d5 & M4) | ((par << 1) & M2) | zb;
+    P[0] = and_or(d2, M4, and_or(d, M2, z));
+    P[1] = and_or(d3, M4, and_or(d1, M2, z));
+    P[2] = and_or(d4, M4, and_or(d2, M2, z));
+    // b3 = z1 ^ b0 ^ b1 ^ b2 with z1 = u_t ^ u_{t-1} ^ u_{t-3} (bit 0 of bytes
+    // g, g-1, g-3), formed directly at bit 1 of each byte: the funnel shifts
+    // move those bit-0s there
+    const uint32_t x1 = xor3(__builtin_amdgcn_alignbit(d, dp, 31), d, d1);
+    const uint32_t x2 = xor3(d2, __builtin_amdgcn_alignbit(d, dp, 23), __builtin_amdgcn_alignbit(d, dp, 7));
+    P[3] = and_or(d5, M4, and_or(x1 ^ x2, M2, z));
 }
 
 // The workgroup's W waves share 8*R rows and split each row's chunks between
@@ -753,7 +761,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
         if (norm) {
             float tot = 0.0f;
             for (int w = 0; w < W; ++w) tot += wsum[b * W + w];
-            inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+            inv = __builtin_amdgcn_rsqf(tot * __builtin_amdgcn_rcpf((float)k) + 1e-6f);
         }
 #pragma unroll
         for (int u = 0; u < XG; ++u) {
@@ -790,10 +798,12 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        uint4 bv[8];                                         // all B operands first: one LDS wait
+#pragma unroll
+        for (int st = 0; st < 8; ++st) bv[st] = *reinterpret_cast<const uint4*>(xr + 32 * st);
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            uint4 bw = *reinterpret_cast<const uint4*>(xr + 32 * st);
-            if (!bok) bw = make_uint4(0, 0, 0, 0);
+            const uint4 bw = bok ? bv[st] : make_uint4(0, 0, 0, 0);
             const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
             const uint32_t* av = apat[st & 1];
             const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
@@ -1180,11 +1190,18 @@ int launch_fused_rs(const FusedShape& S, const uint8_t* codes, const uint16_t* s
                     const void* x, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
                     hipStream_t st) {
 #define PG_FUSED(RS_, BTM_) return launch_fused_t<XDT, XG, RS_, BTM_>(S, codes, scales, n, k, x, ldx, sign_bits, flags, batch, y, st)
-    if (S.BTM == 1) {
+    if (S.BTM == 1) {                  // rows per lane as exact as possible: each one costs a full decode
         if (S.RS <= 1) PG_FUSED(1, 1);
         if (S.RS <= 2) PG_FUSED(2, 1);
+        if (S.RS <= 3) PG_FUSED(3, 1);
         if (S.RS <= 4) PG_FUSED(4, 1);
+        if (S.RS <= 5) PG_FUSED(5, 1);
+        if (S.RS <= 6) PG_FUSED(6, 1);
+        if (S.RS <= 7) PG_FUSED(7, 1);
         if (S.RS <= 8) PG_FUSED(8, 1);
+        if (S.RS <= 10) PG_FUSED(10, 1);
+        if (S.RS <= 12) PG_FUSED(12, 1);
+        if (S.RS <= 14) PG_FUSED(14, 1);
         PG_FUSED(16, 1);
     }
     if (S.BTM == 2) PG_FUSED(16, 2);
