@@ -641,8 +641,13 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
                                                     int batch, float* __restrict__ y, int R, int CG, int RP,
                                                     int BT) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int W = nthr >> 6;
+    // every argument is fetched by one scalar load burst here: loads left to
+    // the point of first use each cost a full round trip, and a scalar load
+    // in flight also holds back every later wait for LDS
+    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(ldx), "s"(sign_bits), "s"(flags),
+                 "s"(batch), "s"(y), "s"(R), "s"(CG), "s"(RP), "s"(BT));
+    constexpr int nthr = 512, W = 8;                           // the launch shape is fixed
+    const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int T = wave * 8 + (lane >> 3), tl = lane & 7;
     const int kg = k >> 2, nchunk = k >> 6, nbk = k >> 7, ngr = k >> 3;
@@ -1233,18 +1238,14 @@ int compute_units() {
 // all of its rows' codes in registers (at most 16 rows per lane).
 int fused_shape(int64_t n, int64_t k, int batch, FusedShape* out) {
     FusedShape S;
-    S.W = 8;
+    S.W = 8;                                           // the kernel assumes 512 threads
     int R_req = 0;
-    if (const char* e = getenv("PG_FUSED_SHAPE")) {   // "W,R" for tuning sweeps
-        int w2 = 0, r2 = 0;
-        if (sscanf(e, "%d,%d", &w2, &r2) == 2 && (w2 == 4 || w2 == 8) && r2 >= 0) {
-            S.W = w2;
-            R_req = r2;
-        }
+    if (const char* e = getenv("PG_FUSED_ROWS")) {     // rows per workgroup, for tuning sweeps
+        const int r2 = atoi(e);
+        if (r2 > 0) R_req = r2;
     }
     const int nchunk = (int)(k / 64), nbk = (int)(k / 128);
     S.CG = (nchunk + 7) / 8;
-    while (S.CG > 8 * S.W && S.W < 8) S.W *= 2;
     if (S.CG > 8 * S.W) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
     S.RP = 8 * S.W / S.CG;
     S.XG = (int)((k / 8 + 64 * S.W - 1) / (64 * S.W));   // 8-value groups of x per thread
