@@ -23,8 +23,21 @@ def _qgemm(codes, scales, xb):
     return host(y)
 
 
-@pytest.mark.parametrize("m,n,k", [(128, 128, 128), (256, 384, 512), (77, 130, 640), (1, 5, 256), (300, 1024, 2560)])
-def test_small_and_ragged(m, n, k):
+@pytest.fixture(params=["auto", "1", "2"])
+def kernel(request, monkeypatch):
+    """Which product kernel pg_qgemm runs: its own choice by grid size, or
+    one forced through PG_QGEMM_KERNEL (the 128x128 tile or the pipelined
+    256x128 tile)."""
+    if request.param == "auto":
+        monkeypatch.delenv("PG_QGEMM_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("PG_QGEMM_KERNEL", request.param)
+    return request.param
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 128, 128), (256, 384, 512), (77, 130, 640), (1, 5, 256), (300, 1024, 2560),
+                                   (513, 257, 1152)])
+def test_small_and_ragged(m, n, k, kernel):
     rng = np.random.default_rng(m * n + k)
     codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
     scales = synth.random_scale_bits(n, k, m + n)
@@ -34,7 +47,7 @@ def test_small_and_ragged(m, n, k):
     assert np.max(rel_err_rows(y, ref)) <= TOL
 
 
-def test_encoded_matrix_m512():
+def test_encoded_matrix_m512(kernel):
     codes, scales = encoded_qwen("k")
     xb = synth.bf16_activations_bits(512, codes.shape[1] * 4)
     y = _qgemm(codes, scales, xb)
@@ -57,7 +70,7 @@ def test_prompt_shapes_sampled_rows(m):
         assert np.max(rel_err_rows(y[rows], ref)) <= TOL, site
 
 
-def test_one_hot_column():
+def test_one_hot_column(kernel):
     codes, scales = encoded_qwen("v")
     n, kg = codes.shape
     k = 4 * kg
