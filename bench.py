@@ -10,8 +10,9 @@ gate/up merged), replayed from a HIP graph.  Inputs are resident in HBM before t
 Printed: one JSON line with the whole-job compressed-weight GB/s
 (bytes per token x tokens per second), tokens per second, the roofline of
 the stage kernel (coded bytes per launch over its average duration, from
-the HIP events around the timed region) and the oracle's CPU throughput on
-a bounded sample of the same workload.
+the HIP events around the timed region), the prompt path's matrix-core
+fraction (pg_qgemm on the Qwen3-4B layer shapes at m = 512 and 4096) and the
+oracle's CPU throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "qgemv compressed-weight GB/s (% HBM peak) + linear-stack tok/s at batch 1"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0          # dense bf16
 
 
 def log(*a):
@@ -179,6 +181,62 @@ def run_stack(args):
     return res
 
 
+def run_qgemm(stream_iters: int = 10):
+    """Prompt path on the matrix cores: pg_qgemm on the Qwen3-4B layer-0
+    launch groups (random codes and scales as in the stack), X = bf16 N(0,1)
+    rows rotated once by pg_fwht_rotate (bf16 -> bf16), at m = 512 and 4096.
+    Each product is timed alone with HIP events on the launch stream over
+    `stream_iters` back-to-back calls; the fraction is 2 m n k per second over
+    the 2.5 PFLOP/s dense bf16 peak."""
+    import numpy as np
+    import torch
+
+    import qgemv_amd as q
+    from qgemv_amd import synth
+
+    shapes = synth.qwen3_4b_shapes()
+    merged = synth.random_layer_merged(0, shapes)
+    site_no = {"qkv": 0, "o": 1, "gu": 2, "down": 3}
+    stream = torch.cuda.current_stream()
+    out = {"bound": "mfma", "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16 x bf16 -> f32",
+           "kernel": "k_qgemm_v2 (pg_qgemm)", "workload": "Qwen3-4B layer-0 launch groups qkv/o/gu/down, "
+           "random trellis bitstreams, bf16 N(0,1) rows", "per_m": {}}
+    for m in (512, 4096):
+        tot_flop = tot_us = 0.0
+        per = {}
+        for site, (codes, scales) in merged.items():
+            n, k = codes.shape[0], codes.shape[1] * 4
+            cd = torch.from_numpy(codes).cuda()
+            sc = torch.from_numpy(scales.view(np.int16)).cuda()
+            xb = torch.from_numpy(synth.bf16_activations_bits(m, k, seed=m + k).view(np.int16)).cuda()
+            xr = torch.empty_like(xb)
+            sb = torch.from_numpy(synth.site_sign_bits(0, site_no[site], k)).cuda()
+            q.pg_fwht_rotate(xb, q.PG_BF16, xr, q.PG_BF16, sb, m, k, 0)
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            for _ in range(2):
+                q.pg_qgemm(cd, sc, n, k, xr, m, y)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(stream_iters):
+                q.pg_qgemm(cd, sc, n, k, xr, m, y)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / stream_iters
+            flop = 2.0 * m * n * k
+            tf = flop / (us * 1e-6) / 1e12
+            per[site] = {"n": n, "k": k, "us": round(us, 2), "tflops": round(tf, 1),
+                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4)}
+            tot_flop += flop
+            tot_us += us
+        tf = tot_flop / (tot_us * 1e-6) / 1e12
+        out["per_m"][str(m)] = {"achieved": round(tf, 1), "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+                                "gflop": round(tot_flop / 1e9, 1), "us": round(tot_us, 1), "sites": per}
+        log(f"qgemm m={m}: {tf:.1f} TFLOP/s ({100 * tf / MFMA_PEAK_TFLOPS:.1f}% of peak)")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +250,7 @@ def main():
     ap.add_argument("--path", default="fused", choices=["fused", "split"],
                     help="fused: one pg_rot_qgemv per stage; split: pg_fwht_rotate + pg_qgemv per stage")
     ap.add_argument("--batch", type=int, default=1, help="activation rows per step (fused path: 1..8)")
+    ap.add_argument("--no-qgemm", action="store_true", help="skip the prompt-path (pg_qgemm) measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "
@@ -211,6 +270,9 @@ def main():
                           "launches": 4}), flush=True)
         return
     res = run_stack(args)
+    if not args.no_qgemm:
+        log("timing the prompt path (pg_qgemm)")
+        res["qgemm"] = run_qgemm()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline()
