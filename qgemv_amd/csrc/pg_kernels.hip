@@ -634,6 +634,13 @@ __device__ __forceinline__ int fs_elem(int mt, int M) {
 
 typedef _Float16 fs_f16x8 __attribute__((ext_vector_type(8)));
 
+// Instances that loop over batch tiles themselves (the codes stay in
+// registers); the others get one launch per tile.  The loop keeps more
+// values live, so only instances with registers to spare have it.
+__host__ __device__ constexpr bool fused_loops(int RS, int BTM) {
+    return BTM > 1 && RS * BTM <= 16 && !(RS == 2 && BTM == 8);
+}
+
 template <int XDT, int XG, int RS, int BTM>
 __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ codes,
                                                     const uint16_t* __restrict__ scales, int n, int k,
@@ -653,7 +660,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     const int T = wave * 8 + (lane >> 3), tl = lane & 7;
     const int kg = k >> 2, nchunk = k >> 6, nbk = k >> 7, ngr = k >> 3;
     const int row0 = blockIdx.x * R;
-    const int bt = batch;                                    // batch rows of this launch (<= BT <= BTM)
+    const int bt0 = batch < BT ? batch : BT;                 // batch rows of the first tile (<= BT <= BTM)
     const int esz = XDT == PG_F32 ? 4 : 2;
     const int xrow = fused_xrow_bytes(k, esz), xhrow = fused_xhrow_bytes(k), rb = fused_row_bytes(k);
     uint8_t* xbuf = lds;                                     // [BT][xrow] x as given
@@ -671,13 +678,16 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     const int cc = c < nchunk ? c : nchunk - 1;
 
     // ---- 1. x rows to LDS (16 bytes per lane), sign bits, then all code chunks
-    for (int b = 0; b < bt; ++b) {
-        const uint8_t* src = (const uint8_t*)x + (int64_t)b * ldx * esz;
-        const int bytes = k * esz;
-        for (int o = wave * 1024; o < bytes; o += W * 1024)
-            if (o + 16 * lane < bytes)
-                __builtin_amdgcn_global_load_lds(src + o + 16 * lane, xbuf + (size_t)b * xrow + o, 16, 0, 0);
-    }
+    auto copy_x = [&](int b0, int bt) {
+        for (int b = 0; b < bt; ++b) {
+            const uint8_t* src = (const uint8_t*)x + (int64_t)(b0 + b) * ldx * esz;
+            const int bytes = k * esz;
+            for (int o = wave * 1024; o < bytes; o += W * 1024)
+                if (o + 16 * lane < bytes)
+                    __builtin_amdgcn_global_load_lds(src + o + 16 * lane, xbuf + (size_t)b * xrow + o, 16, 0, 0);
+        }
+    };
+    copy_x(0, bt0);
     uint32_t sg = 0;
     const bool sg_on = tid < k / 32;
     if (sg_on) sg = reinterpret_cast<const uint32_t*>(sign_bits)[tid];
@@ -724,239 +734,255 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     }
     const int ntile = (nbk + 31) >> 5;
 
-    // ---- 2. sums of squares of every batch row: thread t takes 8-value
-    // groups t + nthr u, then wave sums
-    auto read8 = [&](int b, int gi, float v[8]) {
-        const uint8_t* xr = xbuf + (size_t)b * xrow;
-        if (XDT == PG_F32) {
-            const float4 v0 = *reinterpret_cast<const float4*>(xr + 32 * gi);
-            const float4 v1 = *reinterpret_cast<const float4*>(xr + 32 * gi + 16);
-            v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-            v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        } else {
-            const uint4 w = *reinterpret_cast<const uint4*>(xr + 16 * gi);
-            const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                v[2 * t] = h2f((uint16_t)(w4[t] & 0xffffu));
-                v[2 * t + 1] = h2f((uint16_t)(w4[t] >> 16));
+    // ---- 2.-6. one tile of at most BT batch rows, x already in LDS; the
+    // codes stay in registers from one tile to the next
+    auto tile = [&](int b0, int bt) {
+        // ---- 2. sums of squares of every batch row: thread t takes 8-value
+        // groups t + nthr u, then wave sums
+        auto read8 = [&](int b, int gi, float v[8]) {
+            const uint8_t* xr = xbuf + (size_t)b * xrow;
+            if (XDT == PG_F32) {
+                const float4 v0 = *reinterpret_cast<const float4*>(xr + 32 * gi);
+                const float4 v1 = *reinterpret_cast<const float4*>(xr + 32 * gi + 16);
+                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+                v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+            } else {
+                const uint4 w = *reinterpret_cast<const uint4*>(xr + 16 * gi);
+                const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+    #pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v[2 * t] = h2f((uint16_t)(w4[t] & 0xffffu));
+                    v[2 * t + 1] = h2f((uint16_t)(w4[t] >> 16));
+                }
             }
+        };
+        if (norm) {
+            for (int b = 0; b < bt; ++b) {
+                float ss = 0.0f;
+    #pragma unroll
+                for (int u = 0; u < XG; ++u) {
+                    const int gi = tid + nthr * u;
+                    if (gi < ngr) {
+                        float v[8];
+                        read8(b, gi, v);
+    #pragma unroll
+                        for (int t = 0; t < 8; ++t) ss += v[t] * v[t];
+                    }
+                }
+                ss = wave_sum(ss);
+                if (lane == 0) wsum[b * W + wave] = ss;
+            }
+            __syncthreads();
         }
-    };
-    if (norm) {
+        // ---- 3. normalised, sign-flipped fp16 blocks of every batch row
         for (int b = 0; b < bt; ++b) {
-            float ss = 0.0f;
-#pragma unroll
+            float inv = 1.0f;
+            if (norm) {
+                float tot = 0.0f;
+                for (int w = 0; w < W; ++w) tot += wsum[b * W + w];
+                inv = __builtin_amdgcn_rsqf(tot * __builtin_amdgcn_rcpf((float)k) + 1e-6f);
+            }
+    #pragma unroll
             for (int u = 0; u < XG; ++u) {
                 const int gi = tid + nthr * u;
                 if (gi < ngr) {
                     float v[8];
                     read8(b, gi, v);
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) ss += v[t] * v[t];
+                    const uint32_t s8 = sbuf[gi];
+                    uint32_t hw[4];
+    #pragma unroll
+                    for (int t = 0; t < 8; t += 2) {
+                        uint32_t h0 = f2h(norm ? v[t] * inv : v[t]);
+                        uint32_t h1 = f2h(norm ? v[t + 1] * inv : v[t + 1]);
+                        h0 ^= ((s8 >> t) & 1u) << 15;
+                        h1 ^= ((s8 >> (t + 1)) & 1u) << 15;
+                        hw[t >> 1] = h0 | (h1 << 16);
+                    }
+                    *reinterpret_cast<uint4*>(xh + (size_t)b * xhrow + (gi >> 4) * FS_XPITCH + (gi & 15) * 16) =
+                        make_uint4(hw[0], hw[1], hw[2], hw[3]);
                 }
             }
-            ss = wave_sum(ss);
-            if (lane == 0) wsum[b * W + wave] = ss;
         }
         __syncthreads();
-    }
-    // ---- 3. normalised, sign-flipped fp16 blocks of every batch row
-    for (int b = 0; b < bt; ++b) {
-        float inv = 1.0f;
-        if (norm) {
-            float tot = 0.0f;
-            for (int w = 0; w < W; ++w) tot += wsum[b * W + w];
-            inv = __builtin_amdgcn_rsqf(tot * __builtin_amdgcn_rcpf((float)k) + 1e-6f);
-        }
-#pragma unroll
-        for (int u = 0; u < XG; ++u) {
-            const int gi = tid + nthr * u;
-            if (gi < ngr) {
-                float v[8];
-                read8(b, gi, v);
-                const uint32_t s8 = sbuf[gi];
-                uint32_t hw[4];
-#pragma unroll
-                for (int t = 0; t < 8; t += 2) {
-                    uint32_t h0 = f2h(norm ? v[t] * inv : v[t]);
-                    uint32_t h1 = f2h(norm ? v[t + 1] * inv : v[t + 1]);
-                    h0 ^= ((s8 >> t) & 1u) << 15;
-                    h1 ^= ((s8 >> (t + 1)) & 1u) << 15;
-                    hw[t >> 1] = h0 | (h1 << 16);
+        // ---- 4. Hadamard tiles on the matrix cores, quantised per 32 values
+        for (int job = wave; job < bt * 4 * ntile; job += W) {
+            const int b = job / (4 * ntile), jj = job - b * 4 * ntile;
+            const int nt = jj >> 2, mt = jj & 3;
+            const int blk = nt * 32 + (lane & 31);
+            const bool bok = blk < nbk;
+            uint8_t* dig = rows_lds + (size_t)b * rb;
+            float* sxq = reinterpret_cast<float*>(dig + nchunk * FS_PITCH);
+            int* sqq = reinterpret_cast<int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
+            const uint8_t* xr = xh + (size_t)b * xhrow + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
+            f32x16 acc;
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            uint4 bv[8];                                         // all B operands first: one LDS wait
+    #pragma unroll
+            for (int st = 0; st < 8; ++st) bv[st] = *reinterpret_cast<const uint4*>(xr + 32 * st);
+    #pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const uint4 bw = bok ? bv[st] : make_uint4(0, 0, 0, 0);
+                const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
+                const uint32_t* av = apat[st & 1];
+                const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
+                                                             __builtin_bit_cast(fs_f16x8, bw), acc, 0, 0, 0);
+            }
+            // quarter maximum: 16 values per lane, then the lane pair (l, l + 32)
+            float mx = 0.0f;
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc[r]));
+            mx = fmaxf(mx, xor_lane32(mx, lane));
+            const float s = mx > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(mx) : 0.0f;
+            const int ch = 2 * blk + (mt >> 1);                  // chunk of this quarter
+            uint8_t* dq = dig + (bok ? ch : 0) * FS_PITCH + 32 * 2 * (mt & 1) + 4 * (lane >> 5);
+            int shi = 0, slo = 0;
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t bits[4];
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) bits[r] = __builtin_bit_cast(uint32_t, fmaf(acc[4 * i + r], s, 12582912.0f));
+                const uint32_t t01 = __builtin_amdgcn_perm(bits[1], bits[0], 0x05040100u);
+                const uint32_t t23 = __builtin_amdgcn_perm(bits[3], bits[2], 0x05040100u);
+                const uint32_t dl = __builtin_amdgcn_perm(t23, t01, 0x06040200u);   // q mod 256 of groups 0..3
+                const uint32_t dh = __builtin_amdgcn_perm(t23, t01, 0x07050301u);   // floor(q / 256)
+                shi = __builtin_amdgcn_sdot4((int)dh, 0x01010101, shi, false);
+                slo = (int)__builtin_amdgcn_udot4(dl, 0x01010101u, (uint32_t)slo, false);
+                // part 2 (mt % 2) + i / 2 of the chunk, position 2 (i % 2) + l / 32
+                if (bok) {
+                    uint8_t* dd = dq + 32 * (i >> 1) + 8 * (i & 1);
+                    *reinterpret_cast<uint32_t*>(dd) = dh;
+                    *reinterpret_cast<uint32_t*>(dd + 16) = dl;
                 }
-                *reinterpret_cast<uint4*>(xh + (size_t)b * xhrow + (gi >> 4) * FS_XPITCH + (gi & 15) * 16) =
-                    make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            }
+            int qs = 256 * shi + slo;
+            qs += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, qs), lane));
+            if (bok && lane < 32) {
+                sxq[4 * blk + mt] = mx * (0.08838834764831845f / (float)Q16_MAXQ);   // 2^-3.5 max / 32512
+                sqq[4 * blk + mt] = qs;
             }
         }
-    }
-    __syncthreads();
-    // ---- 4. Hadamard tiles on the matrix cores, quantised per 32 values
-    for (int job = wave; job < bt * 4 * ntile; job += W) {
-        const int b = job / (4 * ntile), jj = job - b * 4 * ntile;
-        const int nt = jj >> 2, mt = jj & 3;
-        const int blk = nt * 32 + (lane & 31);
-        const bool bok = blk < nbk;
-        uint8_t* dig = rows_lds + (size_t)b * rb;
-        float* sxq = reinterpret_cast<float*>(dig + nchunk * FS_PITCH);
-        int* sqq = reinterpret_cast<int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
-        const uint8_t* xr = xh + (size_t)b * xhrow + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-        uint4 bv[8];                                         // all B operands first: one LDS wait
-#pragma unroll
-        for (int st = 0; st < 8; ++st) bv[st] = *reinterpret_cast<const uint4*>(xr + 32 * st);
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const uint4 bw = bok ? bv[st] : make_uint4(0, 0, 0, 0);
-            const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
-            const uint32_t* av = apat[st & 1];
-            const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
-                                                         __builtin_bit_cast(fs_f16x8, bw), acc, 0, 0, 0);
-        }
-        // quarter maximum: 16 values per lane, then the lane pair (l, l + 32)
-        float mx = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc[r]));
-        mx = fmaxf(mx, xor_lane32(mx, lane));
-        const float s = mx > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(mx) : 0.0f;
-        const int ch = 2 * blk + (mt >> 1);                  // chunk of this quarter
-        uint8_t* dq = dig + (bok ? ch : 0) * FS_PITCH + 32 * 2 * (mt & 1) + 4 * (lane >> 5);
-        int shi = 0, slo = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t bits[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bits[r] = __builtin_bit_cast(uint32_t, fmaf(acc[4 * i + r], s, 12582912.0f));
-            const uint32_t t01 = __builtin_amdgcn_perm(bits[1], bits[0], 0x05040100u);
-            const uint32_t t23 = __builtin_amdgcn_perm(bits[3], bits[2], 0x05040100u);
-            const uint32_t dl = __builtin_amdgcn_perm(t23, t01, 0x06040200u);   // q mod 256 of groups 0..3
-            const uint32_t dh = __builtin_amdgcn_perm(t23, t01, 0x07050301u);   // floor(q / 256)
-            shi = __builtin_amdgcn_sdot4((int)dh, 0x01010101, shi, false);
-            slo = (int)__builtin_amdgcn_udot4(dl, 0x01010101u, (uint32_t)slo, false);
-            // part 2 (mt % 2) + i / 2 of the chunk, position 2 (i % 2) + l / 32
-            if (bok) {
-                uint8_t* dd = dq + 32 * (i >> 1) + 8 * (i & 1);
-                *reinterpret_cast<uint32_t*>(dd) = dh;
-                *reinterpret_cast<uint32_t*>(dd + 16) = dl;
-            }
-        }
-        int qs = 256 * shi + slo;
-        qs += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, qs), lane));
-        if (bok && lane < 32) {
-            sxq[4 * blk + mt] = mx * (0.08838834764831845f / (float)Q16_MAXQ);   // 2^-3.5 max / 32512
-            sqq[4 * blk + mt] = qs;
-        }
-    }
-    __syncthreads();
-    // ---- 5. decode and dot products: the planes of a code dword are built
-    // once and used for every batch row
-    {
-        // codes and scales are used only here, through copies passed through
-        // an opaque move: that keeps the compiler from hoisting their decode
-        // above the rotation (which would wait for every code request first)
-        uint4 qb[RS];
-        uint32_t wb[RS];
-#pragma unroll
-        for (int j = 0; j < RS; ++j) {
-            qb[j] = q[j];
-            wb[j] = wsr[j];
-            asm volatile("" : "+v"(qb[j].x), "+v"(qb[j].y), "+v"(qb[j].z), "+v"(qb[j].w), "+v"(wb[j]));
-        }
-        float sx0[BTM], sx1[BTM];
-        int sq0[BTM], sq1[BTM];
-#pragma unroll
-        for (int b = 0; b < BTM; ++b) {
-            const uint8_t* dig = rows_lds + (size_t)(b < bt ? b : 0) * rb;
-            const float* sxq = reinterpret_cast<const float*>(dig + nchunk * FS_PITCH);
-            const int* sqq = reinterpret_cast<const int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
-            sx0[b] = sxq[2 * cc];
-            sx1[b] = sxq[2 * cc + 1];
-            sq0[b] = sqq[2 * cc];
-            sq1[b] = sqq[2 * cc + 1];
-        }
-        float tq[RS][BTM];
-        int hi[RS][BTM], lo[RS][BTM];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (m == 0 || m == 2)
-#pragma unroll
-                for (int j = 0; j < RS; ++j)
-#pragma unroll
-                    for (int b = 0; b < BTM; ++b) { hi[j][b] = 0; lo[j][b] = 0; }
-            uint4 xh4[BTM], xl4[BTM];
-#pragma unroll
-            for (int b = 0; b < BTM; ++b) {
-                const uint8_t* dig = rows_lds + (size_t)(b < bt ? b : 0) * rb + cc * FS_PITCH + 32 * m;
-                xh4[b] = *reinterpret_cast<const uint4*>(dig);
-                xl4[b] = *reinterpret_cast<const uint4*>(dig + 16);
-            }
-#pragma unroll
+        __syncthreads();
+        // ---- 5. decode and dot products: the planes of a code dword are built
+        // once and used for every batch row
+        {
+            // codes and scales are used only here, through copies passed through
+            // an opaque move: that keeps the compiler from hoisting their decode
+            // above the rotation (which would wait for every code request first)
+            uint4 qb[RS];
+            uint32_t wb[RS];
+    #pragma unroll
             for (int j = 0; j < RS; ++j) {
-                const uint32_t w4[4] = {qb[j].x, qb[j].y, qb[j].z, qb[j].w};
-                uint32_t prev;
-                if (m == 0) {
-                    // last dword of the left neighbour's chunk (same row, chunk c - 1)
-                    const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb[j].w, 0x111, 0xf, 0xf, true);
-                    prev = (c & 1) ? left : 0u;
-                } else {
-                    prev = w4[m - 1];
-                }
-                uint32_t P[4];
-                planes_of(w4[m], prev, P);
-#pragma unroll
-                for (int b = 0; b < BTM; ++b) {
-                    if (BTM > 1 && b >= bt) break;                 // uniform
-                    int h = hi[j][b];
-                    uint32_t l = (uint32_t)lo[j][b];
-                    h = __builtin_amdgcn_sdot4((int)P[0], (int)xh4[b].x, h, false);
-                    l = __builtin_amdgcn_udot4(P[0], xl4[b].x, l, false);
-                    h = __builtin_amdgcn_sdot4((int)P[1], (int)xh4[b].y, h, false);
-                    l = __builtin_amdgcn_udot4(P[1], xl4[b].y, l, false);
-                    h = __builtin_amdgcn_sdot4((int)P[2], (int)xh4[b].z, h, false);
-                    l = __builtin_amdgcn_udot4(P[2], xl4[b].z, l, false);
-                    h = __builtin_amdgcn_sdot4((int)P[3], (int)xh4[b].w, h, false);
-                    l = __builtin_amdgcn_udot4(P[3], xl4[b].w, l, false);
-                    hi[j][b] = h;
-                    lo[j][b] = (int)l;
-                }
+                qb[j] = q[j];
+                wb[j] = wsr[j];
+                asm volatile("" : "+v"(qb[j].x), "+v"(qb[j].y), "+v"(qb[j].z), "+v"(qb[j].w), "+v"(wb[j]));
             }
-            // quarter done: sum level * q = 2 (256 hi + lo) - 7 sum q
-            if (m == 1)
-#pragma unroll
-                for (int j = 0; j < RS; ++j)
-#pragma unroll
-                    for (int b = 0; b < BTM; ++b) tq[j][b] = sx0[b] * (float)(2 * (hi[j][b] * 256 + lo[j][b]) - 7 * sq0[b]);
-            if (m == 3)
-#pragma unroll
-                for (int j = 0; j < RS; ++j)
-#pragma unroll
-                    for (int b = 0; b < BTM; ++b) tq[j][b] += sx1[b] * (float)(2 * (hi[j][b] * 256 + lo[j][b]) - 7 * sq1[b]);
-        }
-#pragma unroll
-        for (int j = 0; j < RS; ++j) {
-            const float wsc = h2f((uint16_t)(whi[j] ? wb[j] >> 16 : wb[j]));
-#pragma unroll
+            float sx0[BTM], sx1[BTM];
+            int sq0[BTM], sq1[BTM];
+    #pragma unroll
             for (int b = 0; b < BTM; ++b) {
-                if (BTM > 1 && b >= bt) break;                     // uniform
-                float v = rok[j] ? wsc * tq[j][b] : 0.0f;
-                v += xor_lane<4>(v, lane);
-                v += xor_lane<2>(v, lane);
-                v += xor_lane<1>(v, lane);
-                if (tl == 0 && rp < RP && rp + j * RP < R) part[((size_t)b * R + rp + j * RP) * CG + cg] = v;
+                const uint8_t* dig = rows_lds + (size_t)(b < bt ? b : 0) * rb;
+                const float* sxq = reinterpret_cast<const float*>(dig + nchunk * FS_PITCH);
+                const int* sqq = reinterpret_cast<const int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
+                sx0[b] = sxq[2 * cc];
+                sx1[b] = sxq[2 * cc + 1];
+                sq0[b] = sqq[2 * cc];
+                sq1[b] = sqq[2 * cc + 1];
+            }
+            float tq[RS][BTM];
+            int hi[RS][BTM], lo[RS][BTM];
+    #pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (m == 0 || m == 2)
+    #pragma unroll
+                    for (int j = 0; j < RS; ++j)
+    #pragma unroll
+                        for (int b = 0; b < BTM; ++b) { hi[j][b] = 0; lo[j][b] = 0; }
+                uint4 xh4[BTM], xl4[BTM];
+    #pragma unroll
+                for (int b = 0; b < BTM; ++b) {
+                    const uint8_t* dig = rows_lds + (size_t)(b < bt ? b : 0) * rb + cc * FS_PITCH + 32 * m;
+                    xh4[b] = *reinterpret_cast<const uint4*>(dig);
+                    xl4[b] = *reinterpret_cast<const uint4*>(dig + 16);
+                }
+    #pragma unroll
+                for (int j = 0; j < RS; ++j) {
+                    const uint32_t w4[4] = {qb[j].x, qb[j].y, qb[j].z, qb[j].w};
+                    uint32_t prev;
+                    if (m == 0) {
+                        // last dword of the left neighbour's chunk (same row, chunk c - 1)
+                        const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb[j].w, 0x111, 0xf, 0xf, true);
+                        prev = (c & 1) ? left : 0u;
+                    } else {
+                        prev = w4[m - 1];
+                    }
+                    uint32_t P[4];
+                    planes_of(w4[m], prev, P);
+    #pragma unroll
+                    for (int b = 0; b < BTM; ++b) {
+                        if (BTM > 1 && b >= bt) break;                 // uniform
+                        int h = hi[j][b];
+                        uint32_t l = (uint32_t)lo[j][b];
+                        h = __builtin_amdgcn_sdot4((int)P[0], (int)xh4[b].x, h, false);
+                        l = __builtin_amdgcn_udot4(P[0], xl4[b].x, l, false);
+                        h = __builtin_amdgcn_sdot4((int)P[1], (int)xh4[b].y, h, false);
+                        l = __builtin_amdgcn_udot4(P[1], xl4[b].y, l, false);
+                        h = __builtin_amdgcn_sdot4((int)P[2], (int)xh4[b].z, h, false);
+                        l = __builtin_amdgcn_udot4(P[2], xl4[b].z, l, false);
+                        h = __builtin_amdgcn_sdot4((int)P[3], (int)xh4[b].w, h, false);
+                        l = __builtin_amdgcn_udot4(P[3], xl4[b].w, l, false);
+                        hi[j][b] = h;
+                        lo[j][b] = (int)l;
+                    }
+                }
+                // quarter done: sum level * q = 2 (256 hi + lo) - 7 sum q
+                if (m == 1)
+    #pragma unroll
+                    for (int j = 0; j < RS; ++j)
+    #pragma unroll
+                        for (int b = 0; b < BTM; ++b) tq[j][b] = sx0[b] * (float)(2 * (hi[j][b] * 256 + lo[j][b]) - 7 * sq0[b]);
+                if (m == 3)
+    #pragma unroll
+                    for (int j = 0; j < RS; ++j)
+    #pragma unroll
+                        for (int b = 0; b < BTM; ++b) tq[j][b] += sx1[b] * (float)(2 * (hi[j][b] * 256 + lo[j][b]) - 7 * sq1[b]);
+            }
+    #pragma unroll
+            for (int j = 0; j < RS; ++j) {
+                const float wsc = h2f((uint16_t)(whi[j] ? wb[j] >> 16 : wb[j]));
+    #pragma unroll
+                for (int b = 0; b < BTM; ++b) {
+                    if (BTM > 1 && b >= bt) break;                     // uniform
+                    float v = rok[j] ? wsc * tq[j][b] : 0.0f;
+                    v += xor_lane<4>(v, lane);
+                    v += xor_lane<2>(v, lane);
+                    v += xor_lane<1>(v, lane);
+                    if (tl == 0 && rp < RP && rp + j * RP < R) part[((size_t)b * R + rp + j * RP) * CG + cg] = v;
+                }
             }
         }
-    }
-    __syncthreads();
-    for (int o = tid; o < bt * R; o += nthr) {
-        const int b = o / R, r = o - b * R;
-        if (row0 + r >= n) continue;
-        const float* pr = part + ((size_t)b * R + r) * CG;
-        float v = 0.0f;
-        for (int g = 0; g < CG; ++g) v += pr[g];
-        y[(int64_t)b * n + row0 + r] = v;
+        __syncthreads();
+        for (int o = tid; o < bt * R; o += nthr) {
+            const int b = o / R, r = o - b * R;
+            if (row0 + r >= n) continue;
+            const float* pr = part + ((size_t)b * R + r) * CG;
+            float v = 0.0f;
+            for (int g = 0; g < CG; ++g) v += pr[g];
+            y[(int64_t)(b0 + b) * n + row0 + r] = v;
+        }
+    };
+    tile(0, bt0);
+    if constexpr (fused_loops(RS, BTM))
+    for (int b0 = BT; b0 < batch; b0 += BT) {
+        // further tiles (when the LDS holds fewer rows than the batch): the
+        // same codes against the next rows of x, no second pass over memory
+        const int bt = batch - b0 < BT ? batch - b0 : BT;
+        __syncthreads();                                     // last tile's sums read
+        copy_x(b0, bt);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        tile(b0, bt);
     }
 }
 
@@ -1379,8 +1405,9 @@ int launch_fused_t(const FusedShape& S, const uint8_t* codes, const uint16_t* sc
                    hipStream_t st) {
     const dim3 grid((unsigned)((n + S.R - 1) / S.R));
     const int esz = XDT == PG_F32 ? 4 : 2;
-    for (int b0 = 0; b0 < batch; b0 += S.BT) {
-        const int bt = batch - b0 < S.BT ? batch - b0 : S.BT;
+    const int tile = fused_loops(RS, BTM) ? batch : S.BT;  // rows handed to one launch
+    for (int b0 = 0; b0 < batch; b0 += tile) {
+        const int bt = batch - b0 < tile ? batch - b0 : tile;
         const void* xb = (const uint8_t*)x + (int64_t)b0 * ldx * esz;
         hipLaunchKernelGGL((k_rot_qgemv<XDT, XG, RS, BTM>), grid, dim3(64 * S.W), fused_lds_bytes((int)k, esz, S),
                            st, codes, scales, (int)n, (int)k, xb, ldx, sign_bits, flags, bt, y + (int64_t)b0 * n,
@@ -1412,7 +1439,10 @@ int launch_fused_rs(const FusedShape& S, const uint8_t* codes, const uint16_t* s
         if (S.RS <= 14) PG_FUSED(14, 1);
         PG_FUSED(16, 1);
     }
-    if (S.BTM == 2) PG_FUSED(16, 2);
+    if (S.BTM == 2) {
+        if (S.RS <= 8) PG_FUSED(8, 2);
+        PG_FUSED(16, 2);
+    }
     if (S.BTM == 4) {
         if (S.RS <= 2) PG_FUSED(2, 4);
         if (S.RS <= 4) PG_FUSED(4, 4);
@@ -1461,18 +1491,21 @@ int fused_shape(int64_t n, int64_t k, int batch, FusedShape* out) {
     if (R > n) R = n;
     S.R = (int)R;
     S.RS = (S.R + S.RP - 1) / S.RP;
-    // batch rows per launch: the template's bound BTM (registers: RS * BTM <= 32,
-    // RS <= 2 for 8 rows)
-    // and as many rows as the LDS budget holds
-    S.BTM = batch <= 1 ? 1 : (S.RS <= 2 && batch > 4) ? 8 : S.RS <= 8 ? 4 : 2;
+    // batch rows per tile: as many as the LDS holds, up to the template's bound
+    // BTM (registers: RS * BTM <= 32, RS <= 2 for 8 rows); with fewer rows
+    // per tile than the batch, the kernel loops over tiles itself where its
+    // registers allow (fused_loops), else one launch per tile
     const size_t budget = 150 * 1024;
-    S.BT = 1;
-    while (S.BT < S.BTM && S.BT < batch) {
+    int bt_lds = 1;                                    // rows of x the LDS holds at once
+    for (;;) {
         FusedShape T = S;
-        T.BT = S.BT + 1;
-        if (fused_lds_bytes((int)k, 4, T) > budget) break;
-        S.BT = T.BT;
+        T.BTM = T.BT = bt_lds + 1;
+        if (bt_lds >= 8 || fused_lds_bytes((int)k, 4, T) > budget) break;
+        ++bt_lds;
     }
+    const int t = batch < bt_lds ? batch : bt_lds;
+    S.BTM = batch <= 1 ? 1 : S.RS <= 2 ? (t > 4 ? 8 : 4) : S.RS <= 4 ? 4 : S.RS <= 8 ? (t <= 2 ? 2 : 4) : 2;
+    S.BT = t < S.BTM ? t : S.BTM;
     if (fused_lds_bytes((int)k, 4, S) > budget) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
     *out = S;
     return PG_OK;
