@@ -126,6 +126,19 @@ int pg_codebook_table(int8_t* out);
 int pg_encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits,
                   uint8_t* codes, uint16_t* scales, int n_threads);
 
+/* The same encoder on the GPU, asynchronous on `stream`: codes and scales
+ * are bit-identical to pg_encode_ref's for the same input (every step runs in
+ * fp64 in the same operation order, without fused multiply-add).  One
+ * workgroup per 128-block: rotation, scale rule, the nearest point of each
+ * coset per group, then the 8-state add-compare-select and traceback.
+ *   w          device fp32 [n][k], original (unrotated) weights
+ *   sign_bits  device u8 [k/8]
+ *   codes      device u8 [n][k/4] out (16-byte aligned)
+ *   scales     device u16 [n][k/128] out (fp16 bits)
+ * Buffers are the caller's; nothing is allocated.  n * k / 128 < 2^31. */
+int pg_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
+              uint16_t* scales, pg_stream_t stream);
+
 /* Decode to rotated-domain fp32 weights (bit-exact: scale * level in fp32).
  *   codes device u8 [n][k/4], scales device u16 [n][k/128],
  *   w_rot device f32 [n][k] out. */

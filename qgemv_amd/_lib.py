@@ -21,6 +21,7 @@ PG_F32, PG_F16, PG_BF16, PG_Q16 = 0, 1, 2, 3
 PG_FLAG_RMSNORM = 1
 
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
+           "pg_encode",
            "pg_decode", "pg_fwht_rotate", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm")
 
 
@@ -58,6 +59,8 @@ def lib():
         L.pg_codebook_table.argtypes = [vp]
         L.pg_encode_ref.restype = i32
         L.pg_encode_ref.argtypes = [vp, i64, i64, vp, vp, vp, i32]
+        L.pg_encode.restype = i32
+        L.pg_encode.argtypes = [vp, i64, i64, vp, vp, vp, vp]
         L.pg_decode.restype = i32
         L.pg_decode.argtypes = [vp, vp, i64, i64, vp, vp]
         L.pg_fwht_rotate.restype = i32
@@ -127,6 +130,12 @@ def pg_encode_ref(w: np.ndarray, n: int, k: int, sign_bits: np.ndarray, codes: n
         if not a.flags["C_CONTIGUOUS"]:
             raise ValueError("host buffers must be C-contiguous")
     _check(lib().pg_encode_ref(_ptr(w), n, k, _ptr(sign_bits), _ptr(codes), _ptr(scales), n_threads))
+
+
+def pg_encode(w, n: int, k: int, sign_bits, codes, scales, stream=None) -> None:
+    """Device buffers: w f32 [n][k], sign_bits u8 [k/8], codes u8 [n][k/4]
+    out, scales 16-bit [n][k/128] out (fp16 bits)."""
+    _check(lib().pg_encode(_ptr(w), n, k, _ptr(sign_bits), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def pg_decode(codes, scales, n: int, k: int, w_rot, stream=None) -> None:

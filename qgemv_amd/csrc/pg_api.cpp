@@ -72,6 +72,17 @@ int pg_encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits
     return pg::encode_ref(w, n, k, sign_bits, codes, scales, n_threads);
 }
 
+int pg_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes, uint16_t* scales,
+              pg_stream_t stream) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    PG_TRY(check_ptr(w, 4, "w"));
+    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    return pg::launch_encode(w, n, k, sign_bits, codes, scales, stream);
+}
+
 int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w_rot,
               pg_stream_t stream) {
     pg::clear_error();

@@ -41,5 +41,8 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
                      pg_stream_t s);
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const uint16_t* x, int64_t m, float* y, pg_stream_t s);
+// (pg_encode.hip)
+int launch_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
+                  uint16_t* scales, pg_stream_t s);
 
 }  // namespace pg

@@ -83,3 +83,17 @@ def oracle_chain(codes, scales, signs, shapes, h0, layers):
             xr = p8f.rotate(src[:, :k], signs[layer][site])
             out[site] = p8f.gemv_ref(codes[layer][site], scales[layer][site], xr)
     return out["down"]
+
+
+def assert_codes_equivalent(w, sb, codes, oracle_codes, scales):
+    """Codes must be equal, except on blocks where the two searches are tied
+    (their rotated inputs differ by rounding order): there both paths must
+    reach the optimum distortion to 1e-12 relative."""
+    n, k = w.shape
+    diff = np.nonzero((codes != oracle_codes).reshape(n, k // 128, 32).any(axis=2))
+    wr = p8f.rotate(w, sb).reshape(n, k // 128, 128)
+    for r, b in zip(*diff):
+        d_lib = p8f.block_distortion(wr[r, b][None], codes[r, 32 * b:32 * b + 32][None], scales[r, b:b + 1])[0]
+        d_orc = p8f.block_distortion(wr[r, b][None], oracle_codes[r, 32 * b:32 * b + 32][None], scales[r, b:b + 1])[0]
+        assert abs(d_lib - d_orc) <= 1e-12 * d_orc
+    assert len(diff[0]) <= max(1, n * (k // 128) // 10000)

@@ -11,6 +11,7 @@ import pytest
 import qgemv_amd as q
 from oracle import p8f
 from qgemv_amd import synth
+from tests.helpers import assert_codes_equivalent
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -41,6 +42,11 @@ def test_codebook_table_matches_oracle():
 
 
 @pytest.mark.parametrize("call", [
+    lambda: q.pg_encode(1 << 20, 8, 200, 1 << 20, 1 << 20, 1 << 20, stream=0),                # k % 128
+    lambda: q.pg_encode(1 << 20, 0, 256, 1 << 20, 1 << 20, 1 << 20, stream=0),                # n < 1
+    lambda: q.pg_encode(None, 8, 256, 1 << 20, 1 << 20, 1 << 20, stream=0),                   # null w
+    lambda: q.pg_encode(1 << 20, 8, 256, 1 << 20, (1 << 20) + 4, 1 << 20, stream=0),          # codes align
+    lambda: q.pg_encode((1 << 20) + 2, 8, 256, 1 << 20, 1 << 20, 1 << 20, stream=0),          # w align
     lambda: q.pg_qgemv(1 << 20, 1 << 20, 0, 2048, 1 << 20, 0, 1, 1 << 20, stream=0),        # n < 1
     lambda: q.pg_qgemv(1 << 20, 1 << 20, 8, 100, 1 << 20, 0, 1, 1 << 20, stream=0),         # k % 128
     lambda: q.pg_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 20, 0, 9, 1 << 20, stream=0),         # batch
@@ -78,7 +84,7 @@ def test_encode_ref_equals_oracle_on_single_layer():
     q.pg_encode_ref(w, 512, 2048, sb, codes, scales)
     oc, os_ = p8f.encode_matrix(w, sb)
     assert np.array_equal(scales, os_)
-    _assert_codes_equivalent(w, sb, codes, oc, scales)
+    assert_codes_equivalent(w, sb, codes, oc, scales)
 
 
 def test_encode_ref_equals_oracle_on_qwen_rows():
@@ -94,21 +100,7 @@ def test_encode_ref_equals_oracle_on_qwen_rows():
         q.pg_encode_ref(ws, 64, k, sb, codes, scales, 4)
         oc, os_ = p8f.encode_matrix(ws, sb)
         assert np.array_equal(scales, os_), name
-        _assert_codes_equivalent(ws, sb, codes, oc, scales)
-
-
-def _assert_codes_equivalent(w, sb, codes, oracle_codes, scales):
-    """Codes must be equal, except on blocks where the two searches are tied
-    (their rotated inputs differ by rounding order): there both paths must
-    reach the optimum distortion to 1e-12 relative."""
-    n, k = w.shape
-    diff = np.nonzero((codes != oracle_codes).reshape(n, k // 128, 32).any(axis=2))
-    wr = p8f.rotate(w, sb).reshape(n, k // 128, 128)
-    for r, b in zip(*diff):
-        d_lib = p8f.block_distortion(wr[r, b][None], codes[r, 32 * b:32 * b + 32][None], scales[r, b:b + 1])[0]
-        d_orc = p8f.block_distortion(wr[r, b][None], oracle_codes[r, 32 * b:32 * b + 32][None], scales[r, b:b + 1])[0]
-        assert abs(d_lib - d_orc) <= 1e-12 * d_orc
-    assert len(diff[0]) <= max(1, n * (k // 128) // 10000)
+        assert_codes_equivalent(ws, sb, codes, oc, scales)
 
 
 def test_encode_ref_zero_and_constant_rows():
