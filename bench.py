@@ -11,8 +11,9 @@ Printed: one JSON line with the whole-job compressed-weight GB/s
 (bytes per token x tokens per second), tokens per second, the roofline of
 the stage kernel (coded bytes per launch over its average duration, from
 the HIP events around the timed region), the prompt path's matrix-core
-fraction (pg_qgemm on the Qwen3-4B layer shapes at m = 512 and 4096) and the
-oracle's CPU throughput on a bounded sample of the same workload.
+fraction (pg_qgemm on the Qwen3-4B layer shapes at m = 512 and 4096), the
+GPU encoder's throughput on one Qwen3-4B-shaped layer, and the oracle's CPU
+throughput on a bounded sample of the stack workload.
 """
 from __future__ import annotations
 
@@ -237,6 +238,65 @@ def run_qgemm(stream_iters: int = 10):
     return out
 
 
+def run_encode():
+    """Offline side: the GPU trellis encoder (pg_encode) on the seven
+    Qwen3-4B-shaped matrices of one layer (0.02 N(0,1) weights with 0.1%
+    outliers x20), each timed alone with HIP events on the launch stream, and
+    the host reference encoder (pg_encode_ref, all host cores) on 64 rows of
+    each as the CPU figure.  The search scores 128 points of 4 values in each
+    of 4 cosets per group of 4 weights: 4 x 128 x 11 / 4 = 1408 fp64
+    operations per weight, the encoder's algorithmic work."""
+    import numpy as np
+    import torch
+
+    import qgemv_amd as q
+    from qgemv_amd import synth
+
+    stream = torch.cuda.current_stream()
+    tot_w = tot_ms = cpu_w = cpu_s = 0.0
+    per = {}
+    for name in synth.MATS:
+        w = synth.qwen_layer_weights(name)
+        n, k = w.shape
+        sb = synth.site_sign_bits(0, synth.SITE_OF[name], k)
+        wd = torch.from_numpy(w).cuda()
+        sbd = torch.from_numpy(sb).cuda()
+        c = torch.empty((n, k // 4), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((n, k // 128), dtype=torch.int16, device="cuda")
+        q.pg_encode(wd, n, k, sbd, c, sc)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        q.pg_encode(wd, n, k, sbd, c, sc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        rows = 64
+        hc = np.zeros((rows, k // 4), np.uint8)
+        hs = np.zeros((rows, k // 128), np.uint16)
+        t0 = time.perf_counter()
+        q.pg_encode_ref(np.ascontiguousarray(w[:rows]), rows, k, sb, hc, hs, 0)
+        cpu_s += time.perf_counter() - t0
+        cpu_w += rows * k
+        if not np.array_equal(c[:rows].cpu().numpy(), hc):
+            raise SystemExit(f"pg_encode differs from pg_encode_ref on {name}")
+        per[name] = {"n": n, "k": k, "ms": round(ms, 3), "gweights_per_s": round(n * k / ms / 1e6, 2)}
+        tot_w += n * k
+        tot_ms += ms
+    gws = tot_w / tot_ms / 1e6
+    tflops = 1408.0 * gws * 1e9 / 1e12
+    log(f"encode: {gws:.2f} Gweights/s on the GPU")
+    return {"kernel": "k_encode (pg_encode)", "workload": "Qwen3-4B-shaped layer, 7 matrices, "
+            f"{int(tot_w)} weights", "ms": round(tot_ms, 3), "gweights_per_s": round(gws, 2),
+            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": 78.6, "unit": "TFLOP/s (fp64)",
+                         "frac": round(tflops / 78.6, 4), "flop_per_weight": 1408},
+            "cpu_reference": {"mweights_per_s": round(cpu_w / cpu_s / 1e6, 2), "threads": os.cpu_count(),
+                              "kind": "pg_encode_ref (host C++, bit-identical output)",
+                              "sample": "64 rows of each matrix"},
+            "matrices": per}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +311,7 @@ def main():
                     help="fused: one pg_rot_qgemv per stage; split: pg_fwht_rotate + pg_qgemv per stage")
     ap.add_argument("--batch", type=int, default=1, help="activation rows per step (fused path: 1..8)")
     ap.add_argument("--no-qgemm", action="store_true", help="skip the prompt-path (pg_qgemm) measurement")
+    ap.add_argument("--no-encode", action="store_true", help="skip the GPU encoder (pg_encode) measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "
@@ -273,6 +334,9 @@ def main():
     if not args.no_qgemm:
         log("timing the prompt path (pg_qgemm)")
         res["qgemm"] = run_qgemm()
+    if not args.no_encode:
+        log("timing the GPU encoder (pg_encode)")
+        res["encode"] = run_encode()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline()
