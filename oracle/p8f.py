@@ -182,16 +182,22 @@ def codebook_table() -> np.ndarray:
     return t
 
 
-def decode_levels(codes: np.ndarray) -> np.ndarray:
+def decode_levels(codes: np.ndarray, carry: bool = False) -> np.ndarray:
     """Vectorised form of decode_block_levels for codes [..., K/4] (uint8).
 
-    Pinned against the scalar walk in the tests.  Returns int8 [..., K]."""
+    carry=False: the state restarts at 0 in every block (format P8F v1).
+    carry=True: the variant whose state runs on from block to block along
+    the row (decode_row_levels_carry is its definition).  Pinned against the
+    scalar walks in the tests.  Returns int8 [..., K]."""
     c = np.asarray(codes, dtype=np.uint8)
     lead = c.shape[:-1]
     g = c.shape[-1]
     if g % GROUPS_PER_BLOCK:
         raise ValueError("K/4 must be a multiple of 32")
-    c = c.reshape(lead + (g // GROUPS_PER_BLOCK, GROUPS_PER_BLOCK)).astype(np.int32)
+    if carry:
+        c = c.reshape(lead + (1, g)).astype(np.int32)            # one trellis path per row
+    else:
+        c = c.reshape(lead + (g // GROUPS_PER_BLOCK, GROUPS_PER_BLOCK)).astype(np.int32)
     u = c & 1
 
     def prev(a, d):
@@ -212,10 +218,10 @@ def decode_levels(codes: np.ndarray) -> np.ndarray:
     return lv.reshape(lead + (g * 4,))
 
 
-def decode_weights(codes: np.ndarray, scales_u16: np.ndarray) -> np.ndarray:
+def decode_weights(codes: np.ndarray, scales_u16: np.ndarray, carry: bool = False) -> np.ndarray:
     """Rotated-domain weights s * level as fp64 [..., K] (each value is exact
     in fp32 as well: an 11-bit scale times |level| <= 7)."""
-    lv = decode_levels(codes).astype(np.float64)
+    lv = decode_levels(codes, carry).astype(np.float64)
     s = fp16_bits_to_float(scales_u16)
     k = lv.shape[-1]
     return (lv.reshape(lv.shape[:-1] + (k // BLOCK, BLOCK)) * s[..., None]).reshape(lv.shape)
@@ -490,11 +496,12 @@ def encode_matrix(w: np.ndarray, sign_bits: np.ndarray, c: float = SCALE_C,
 
 
 # -------------------------------------------------------------- products
-def gemv_ref(codes: np.ndarray, scales_u16: np.ndarray, x_rot: np.ndarray) -> np.ndarray:
+def gemv_ref(codes: np.ndarray, scales_u16: np.ndarray, x_rot: np.ndarray, carry: bool = False) -> np.ndarray:
     """y[b][n] = sum_blk s[n][blk] * sum_{k in blk} level[n][k] * x~[b][k], fp64.
 
-    x_rot [B][K] (any float dtype; taken exactly).  Returns fp64 [B][N]."""
-    lv = decode_levels(codes).astype(np.float64)              # [N, K]
+    x_rot [B][K] (any float dtype; taken exactly).  Returns fp64 [B][N].
+    carry selects the carried-state variant's levels."""
+    lv = decode_levels(codes, carry).astype(np.float64)       # [N, K]
     n, k = lv.shape
     x = np.asarray(x_rot, dtype=np.float64).reshape(-1, k)
     s = fp16_bits_to_float(scales_u16)                          # [N, nb]
@@ -523,3 +530,115 @@ def rmsnorm16(v: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64)
     r = np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
     return fp16_rne(v / r)
+
+
+# ------------------------------------------- variant: state carried on
+# The landing page's "Paper" section places the format in the small-state
+# coset-trellis design space; one point of that space keeps the trellis
+# state running from block to block along a row instead of restarting it at
+# 0 in every 128-block.  Scales stay per block; a zero-scale block is still
+# coded as 32 zero bytes (which leaves the state at 0 for the next block).
+def decode_row_levels_carry(codes_row) -> list[int]:
+    """Definition of the variant's decode: one scalar trellis walk over all
+    code bytes of a row from state 0, never reset."""
+    s = 0
+    out: list[int] = []
+    for byte in codes_row:
+        byte = int(byte)
+        out.extend(decode_group(byte, s))
+        s = next_state(s, byte & 1)
+    return out
+
+
+def viterbi_encode_row_carry(w_rot_blocks: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Minimum-squared-error path through all blocks of one row with the
+    state carried on: w_rot_blocks [nb, 4G] fp64 (G = 32 for real blocks),
+    scale_bits [nb] u16.  One Viterbi over nb * G steps from state 0 with a
+    free end state; block b's branch metrics use its own scale.  In a
+    zero-scale block the only branch is byte 0 (u = 0, point 0) at no cost.
+    Tie-breaks as in viterbi_encode.  Returns codes [nb, G]."""
+    w = np.asarray(w_rot_blocks, dtype=np.float64)
+    nb, g = w.shape[0], w.shape[1] // 4
+    s_val = fp16_bits_to_float(np.asarray(scale_bits, dtype=np.uint16))
+    bm = branch_metrics(w.reshape(nb, g, 4), s_val)
+    inf = np.inf
+    metric = np.full(8, inf)
+    metric[0] = 0.0
+    steps = nb * g
+    back_prev = np.zeros((steps, 8), dtype=np.int64)
+    back_byte = np.zeros((steps, 8), dtype=np.int64)
+    for b in range(nb):
+        for t in range(g):
+            new = np.full(8, inf)
+            i = b * g + t
+            for sn in range(8):
+                u = sn & 1
+                for cand in (sn >> 1, (sn >> 1) | 4):
+                    if s_val[b] == 0:
+                        if u != 0:
+                            continue
+                        m_t, byte = 0.0, 0
+                    else:
+                        m_b, byte_b = bm[(z0_of_state(cand), z1_of_branch(cand, u))]
+                        m_t, byte = m_b[b, t], (int(byte_b[b, t]) & 0xFE) | u
+                    tot = metric[cand] + m_t
+                    if tot < new[sn]:
+                        new[sn] = tot
+                        back_prev[i, sn] = cand
+                        back_byte[i, sn] = byte
+            metric = new
+    st = int(np.argmin(metric))
+    out = np.zeros(steps, dtype=np.uint8)
+    for i in range(steps - 1, -1, -1):
+        out[i] = back_byte[i, st]
+        st = int(back_prev[i, st])
+    return out.reshape(nb, g)
+
+
+def row_distortion_carry(w_rot_blocks: np.ndarray, codes_row_blocks: np.ndarray, scale_bits: np.ndarray) -> float:
+    """Squared error of a row's decoded path in the carried-state variant."""
+    w = np.asarray(w_rot_blocks, dtype=np.float64)
+    lv = np.array(decode_row_levels_carry(np.asarray(codes_row_blocks).reshape(-1)), dtype=np.float64)
+    s = np.repeat(fp16_bits_to_float(np.asarray(scale_bits, dtype=np.uint16)), w.shape[1])
+    d = w.reshape(-1) - s * lv
+    return float(np.sum(d * d))
+
+
+def exhaustive_encode_paths_carry(w_rot_blocks: np.ndarray, scale_bits) -> float:
+    """Minimum distortion over all 2^(nb G) branch paths of a short row in
+    the carried-state variant, each group taking the nearest point of its
+    coset by brute force (nb G <= 12; no zero-scale blocks)."""
+    w = np.asarray(w_rot_blocks, dtype=np.float64)
+    nb, g = w.shape[0], w.shape[1] // 4
+    near = []
+    for b in range(nb):
+        sv = float(fp16_bits_to_float(np.array([scale_bits[b]], dtype=np.uint16))[0])
+        nb_near = {}
+        for key, (_, pts) in _tabs().items():
+            d = w[b].reshape(g, 1, 4) - sv * pts[None, :, :]
+            nb_near[key] = np.min(np.sum(d * d, axis=2), axis=1)
+        near.append(nb_near)
+    best = np.inf
+    for path in range(1 << (nb * g)):
+        st, acc = 0, 0.0
+        for i in range(nb * g):
+            u = (path >> i) & 1
+            acc += near[i // g][(z0_of_state(st), z1_of_branch(st, u))][i % g]
+            st = next_state(st, u)
+        best = min(best, acc)
+    return best
+
+
+def encode_matrix_carry(w: np.ndarray, sign_bits: np.ndarray, c: float = SCALE_C):
+    """Offline compression in the carried-state variant: rotate, per-block
+    scales (the same rule), one Viterbi per row.  Returns codes u8 [N][K/4]
+    and scale bits u16 [N][K/128]."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    n, k = w.shape
+    nbk = k // BLOCK
+    wr = rotate(w, sign_bits).reshape(n, nbk, BLOCK)
+    scales = block_scale_bits(wr.reshape(-1, BLOCK), c).reshape(n, nbk)
+    codes = np.empty((n, k // 4), dtype=np.uint8)
+    for r in range(n):
+        codes[r] = viterbi_encode_row_carry(wr[r], scales[r]).reshape(-1)
+    return codes, scales
