@@ -46,9 +46,14 @@ def committed_traffic(kernel: str, workload: str):
         return None
     fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                   if line.startswith(("traffic_bytes_per_launch:", "kernel_source:", "kernel_source_sha256:")))
-    src = os.path.join(ROOT, fields.get("kernel_source", "").strip())
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get(
-            "kernel_source_sha256", "").strip():
+    # the kernel's source files, hashed in the order listed
+    srcs = [os.path.join(ROOT, f) for f in fields.get("kernel_source", "").split()]
+    if not srcs or not all(os.path.exists(f) for f in srcs):
+        return None
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != fields.get("kernel_source_sha256", "").strip():
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -95,7 +100,7 @@ def run_stack(args):
     if not fused and args.batch != 1:
         raise SystemExit("the split path runs batch 1 only")
     log(f"building {args.workload}: {layers} layers, batch {args.batch}, {args.path} path")
-    st = Stack(shapes, layers, batch=args.batch, x_dtype=q.PG_Q16, fused=fused)
+    st = Stack(shapes, layers, batch=args.batch, x_dtype=q.PG_Q16, fused=fused, carry=args.carry)
     stream = torch.cuda.current_stream()
     use_graph = not args.no_graph
     if use_graph:
@@ -172,7 +177,8 @@ def run_stack(args):
                                f"{layers}-layer linear stack, batch {args.batch}, random trellis bitstreams",
                    "layers": layers, "batch": args.batch, "bytes_per_token": st.bytes_per_token,
                    "tok_per_s": round(tok_s, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "hip_graphs": use_graph, "launches_per_token": launches_per_step, "path": args.path},
+                   "hip_graphs": use_graph, "launches_per_token": launches_per_step, "path": args.path,
+                   "format": "carried-state variant" if args.carry else "P8F v1"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
@@ -310,6 +316,8 @@ def main():
     ap.add_argument("--path", default="fused", choices=["fused", "split"],
                     help="fused: one pg_rot_qgemv per stage; split: pg_fwht_rotate + pg_qgemv per stage")
     ap.add_argument("--batch", type=int, default=1, help="activation rows per step (fused path: 1..8)")
+    ap.add_argument("--carry", action="store_true",
+                    help="read the codes as the carried-state variant (state runs on across blocks; fused path)")
     ap.add_argument("--no-qgemm", action="store_true", help="skip the prompt-path (pg_qgemm) measurement")
     ap.add_argument("--no-encode", action="store_true", help="skip the GPU encoder (pg_encode) measurement")
     args = ap.parse_args()

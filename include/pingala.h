@@ -74,7 +74,15 @@ enum {
 enum { PG_F32 = 0, PG_F16 = 1, PG_BF16 = 2,     /* element types of x / y */
        PG_Q16 = 3 };                               /* rotated activations, 16-bit fixed point */
 
-enum { PG_FLAG_RMSNORM = 1u };                   /* pg_fwht_rotate flags */
+enum { PG_FLAG_RMSNORM = 1u,                    /* pg_fwht_rotate / pg_rot_qgemv flags */
+       PG_FLAG_CARRY_STATE = 2u };               /* codes of the carried-state variant (below) */
+
+/* Carried-state variant of the format (the small-state coset-trellis design
+ * space of the landing page, section "Paper"): the same bytes, scales and
+ * per-group rule, but the trellis state runs on from one 128-block to the
+ * next along a row instead of restarting at 0; a zero-scale block is 32
+ * zero bytes.  Calls that take PG_FLAG_CARRY_STATE read (or write) codes of
+ * this variant: pg_decode_ex, pg_encode_ex and pg_rot_qgemv. */
 
 #define PG_FORMAT_VERSION 1
 #define PG_LIB_VERSION 1
@@ -139,11 +147,25 @@ int pg_encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits
 int pg_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
               uint16_t* scales, pg_stream_t stream);
 
+/* pg_encode with format flags: 0 is pg_encode (format P8F v1);
+ * PG_FLAG_CARRY_STATE codes the carried-state variant with one Viterbi
+ * search per row over all of its blocks (state carried on, per-block scales
+ * and branch metrics, free end state, the same tie-breaks; in a zero-scale
+ * block the only branch is byte 0).  One workgroup per row; k <= 16384 for
+ * the variant (PG_ERR_UNSUPPORTED beyond).  Other arguments as pg_encode. */
+int pg_encode_ex(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint32_t flags,
+                 uint8_t* codes, uint16_t* scales, pg_stream_t stream);
+
 /* Decode to rotated-domain fp32 weights (bit-exact: scale * level in fp32).
  *   codes device u8 [n][k/4], scales device u16 [n][k/128],
  *   w_rot device f32 [n][k] out. */
 int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
               float* w_rot, pg_stream_t stream);
+
+/* pg_decode with format flags: 0 is pg_decode; PG_FLAG_CARRY_STATE decodes
+ * codes of the carried-state variant.  Bit-exact. */
+int pg_decode_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, uint32_t flags,
+                 float* w_rot, pg_stream_t stream);
 
 /* Run-time activation rotation ("How it works": the random Hadamard
  * rotation; the activations take the same rotation as the weight rows):
@@ -197,7 +219,8 @@ int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
  * PG_FLAG_RMSNORM (the rotation runs on fp16 values, exact after the
  * normalisation's fp16 rounding or for fp16 input; PG_ERR_UNSUPPORTED
  * otherwise).  The rotated values are quantised with one scale per 32
- * values.  x and y may not overlap.  The
+ * values.  PG_FLAG_CARRY_STATE: the codes are of the carried-state
+ * variant.  x and y may not overlap.  The
  * summation order is fixed: repeated calls are bitwise identical. */
 int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const void* x, int x_dtype, int64_t ldx, const uint8_t* sign_bits,

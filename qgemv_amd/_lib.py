@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(HERE, "libpingala.so")
 PG_OK, PG_ERR_INVALID_ARG, PG_ERR_UNSUPPORTED, PG_ERR_HIP = 0, -1, -2, -3
 PG_F32, PG_F16, PG_BF16, PG_Q16 = 0, 1, 2, 3
 PG_FLAG_RMSNORM = 1
+PG_FLAG_CARRY_STATE = 2
 
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
-           "pg_encode",
+           "pg_encode", "pg_encode_ex", "pg_decode_ex",
            "pg_decode", "pg_fwht_rotate", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm")
 
 
@@ -61,6 +62,10 @@ def lib():
         L.pg_encode_ref.argtypes = [vp, i64, i64, vp, vp, vp, i32]
         L.pg_encode.restype = i32
         L.pg_encode.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+        L.pg_encode_ex.restype = i32
+        L.pg_encode_ex.argtypes = [vp, i64, i64, vp, u32, vp, vp, vp]
+        L.pg_decode_ex.restype = i32
+        L.pg_decode_ex.argtypes = [vp, vp, i64, i64, u32, vp, vp]
         L.pg_decode.restype = i32
         L.pg_decode.argtypes = [vp, vp, i64, i64, vp, vp]
         L.pg_fwht_rotate.restype = i32
@@ -136,6 +141,16 @@ def pg_encode(w, n: int, k: int, sign_bits, codes, scales, stream=None) -> None:
     """Device buffers: w f32 [n][k], sign_bits u8 [k/8], codes u8 [n][k/4]
     out, scales 16-bit [n][k/128] out (fp16 bits)."""
     _check(lib().pg_encode(_ptr(w), n, k, _ptr(sign_bits), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def pg_encode_ex(w, n: int, k: int, sign_bits, flags: int, codes, scales, stream=None) -> None:
+    """pg_encode with format flags (PG_FLAG_CARRY_STATE: the carried-state variant)."""
+    _check(lib().pg_encode_ex(_ptr(w), n, k, _ptr(sign_bits), flags, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def pg_decode_ex(codes, scales, n: int, k: int, flags: int, w_rot, stream=None) -> None:
+    """pg_decode with format flags (PG_FLAG_CARRY_STATE: the carried-state variant)."""
+    _check(lib().pg_decode_ex(_ptr(codes), _ptr(scales), n, k, flags, _ptr(w_rot), _stream(stream)))
 
 
 def pg_decode(codes, scales, n: int, k: int, w_rot, stream=None) -> None:

@@ -83,6 +83,31 @@ int pg_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, ui
     return pg::launch_encode(w, n, k, sign_bits, codes, scales, stream);
 }
 
+int pg_encode_ex(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint32_t flags, uint8_t* codes,
+                 uint16_t* scales, pg_stream_t stream) {
+    pg::clear_error();
+    if (flags & ~PG_FLAG_CARRY_STATE) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if (!(flags & PG_FLAG_CARRY_STATE)) return pg_encode(w, n, k, sign_bits, codes, scales, stream);
+    PG_TRY(check_nk(n, k));
+    if (k > 16384) return pg::fail(PG_ERR_UNSUPPORTED, "pg_encode_ex: carried state needs k <= 16384");
+    PG_TRY(check_ptr(w, 4, "w"));
+    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    return pg::launch_encode_carry(w, n, k, sign_bits, codes, scales, stream);
+}
+
+int pg_decode_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, uint32_t flags, float* w_rot,
+                 pg_stream_t stream) {
+    pg::clear_error();
+    if (flags & ~PG_FLAG_CARRY_STATE) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    PG_TRY(check_nk(n, k));
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    PG_TRY(check_ptr(w_rot, 16, "w_rot"));
+    return pg::launch_decode(codes, scales, n, k, w_rot, (flags & PG_FLAG_CARRY_STATE) != 0, stream);
+}
+
 int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w_rot,
               pg_stream_t stream) {
     pg::clear_error();
@@ -90,7 +115,7 @@ int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 2, "scales"));
     PG_TRY(check_ptr(w_rot, 16, "w_rot"));
-    return pg::launch_decode(codes, scales, n, k, w_rot, stream);
+    return pg::launch_decode(codes, scales, n, k, w_rot, false, stream);
 }
 
 int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype, const uint8_t* sign_bits,
@@ -132,7 +157,8 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
     if (batch < 1 || batch > 8) return pg::fail(PG_ERR_INVALID_ARG, "batch must be 1..8 (got %d)", batch);
     PG_TRY(check_dtype(x_dtype, "x_dtype", false, false));
     if (ldx < k) return pg::fail(PG_ERR_INVALID_ARG, "ldx (%lld) < k (%lld)", (long long)ldx, (long long)k);
-    if (flags & ~PG_FLAG_RMSNORM) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if (flags & ~(PG_FLAG_RMSNORM | PG_FLAG_CARRY_STATE))
+        return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 4, "scales"));
     PG_TRY(check_ptr(x, 16, "x"));

@@ -163,7 +163,123 @@ __global__ __launch_bounds__(128) void k_encode(const float* __restrict__ w, int
     }
 }
 
+// Carried-state variant: one workgroup per row walks its blocks in order,
+// each block rotated, scaled and scored as above, the path metrics carried
+// from block to block; the survivors of all 32 nb steps stay in LDS (2 bytes
+// per step and state) for one traceback at the end of the row.  In a
+// zero-scale block the only branch is byte 0 (u = 0) at no cost.
+__global__ __launch_bounds__(128) void k_encode_carry(const float* __restrict__ w, int n, int k,
+                                                      const uint8_t* __restrict__ sign_bits,
+                                                      uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+#pragma clang fp contract(off)
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    __shared__ double v[128];
+    __shared__ double bm[32][4];
+    __shared__ int barg[32][4];
+    __shared__ double metric[8];
+    __shared__ uint32_t sbits;
+    const int tid = threadIdx.x;
+    const int nb = k >> 7, row = blockIdx.x;
+    int8_t* prv = reinterpret_cast<int8_t*>(lds_dyn);              // [32 nb][8]
+    uint8_t* byt = lds_dyn + (size_t)32 * nb * 8;                   // [32 nb][8]
+    if (tid < 8) metric[tid] = tid == 0 ? 0.0 : __builtin_inf();
+    for (int b = 0; b < nb; ++b) {
+        const int64_t kk = (int64_t)b * 128 + tid;
+        double x = (double)w[(int64_t)row * k + kk];
+        if ((sign_bits[kk >> 3] >> (kk & 7)) & 1) x = -x;
+        v[tid] = x;
+        __syncthreads();
+        for (int h = 1; h < 128; h <<= 1) {
+            const int j = (tid / h) * 2 * h + (tid % h);
+            double a = 0.0, c = 0.0;
+            if (tid < 64) { a = v[j]; c = v[j + h]; }
+            __syncthreads();
+            if (tid < 64) { v[j] = a + c; v[j + h] = a - c; }
+            __syncthreads();
+        }
+        v[tid] = v[tid] * 0x1.6a09e667f3bcdp-4;
+        __syncthreads();
+        if (tid == 0) {
+            double acc = 0.0;
+            for (int i = 0; i < 128; ++i) acc = acc + v[i] * v[i];
+            const double rms = sqrt(acc / 128.0);
+            const double sc = 0.29 * rms;
+            const double val = 65504.0 < sc ? 65504.0 : sc;
+            sbits = enc_half_rne(val);
+            scales[(int64_t)row * nb + b] = (uint16_t)sbits;
+        }
+        __syncthreads();
+        const double s = enc_half_to_double((uint16_t)sbits);
+        {
+            const int t = tid >> 2, cs = tid & 3, z0 = cs >> 1, z1 = cs & 1;
+            const double w0 = v[4 * t], w1 = v[4 * t + 1], w2 = v[4 * t + 2], w3 = v[4 * t + 3];
+            double best = __builtin_inf();
+            int arg = 0;
+            for (int i = 0; i < 128; ++i) {
+                const int b0 = i & 1, b1 = (i >> 1) & 1, b2 = (i >> 2) & 1, b3 = z1 ^ b0 ^ b1 ^ b2;
+                const double p0 = (double)(4 * (2 * ((i >> 3) & 1) + b0) + 2 * z0 - 7);
+                const double p1 = (double)(4 * (2 * ((i >> 4) & 1) + b1) + 2 * z0 - 7);
+                const double p2 = (double)(4 * (2 * ((i >> 5) & 1) + b2) + 2 * z0 - 7);
+                const double p3 = (double)(4 * (2 * ((i >> 6) & 1) + b3) + 2 * z0 - 7);
+                const double d0 = w0 - s * p0, d1 = w1 - s * p1, d2 = w2 - s * p2, d3 = w3 - s * p3;
+                const double m = ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
+                if (m < best) { best = m; arg = i; }
+            }
+            bm[t][cs] = best;
+            barg[t][cs] = arg;
+        }
+        __syncthreads();
+        for (int t = 0; t < 32; ++t) {
+            double nxt = __builtin_inf();
+            if (tid < 8) {
+                const int sn = tid, u = sn & 1;
+                int pv = 0, by = 0;
+                for (int c = 0; c < 2; ++c) {
+                    const int ps = c == 0 ? sn >> 1 : (sn >> 1) | 4;
+                    double tot;
+                    int byte;
+                    if (s == 0.0) {
+                        if (u != 0) continue;
+                        tot = metric[ps] + 0.0;
+                        byte = 0;
+                    } else {
+                        const int z0 = (ps >> 1) & 1, z1 = u ^ (ps & 1) ^ ((ps >> 2) & 1);
+                        tot = metric[ps] + bm[t][2 * z0 + z1];
+                        byte = (barg[t][2 * z0 + z1] << 1) | u;
+                    }
+                    if (tot < nxt) { nxt = tot; pv = ps; by = byte; }
+                }
+                prv[(32 * b + t) * 8 + sn] = (int8_t)pv;
+                byt[(32 * b + t) * 8 + sn] = (uint8_t)by;
+            }
+            __syncthreads();
+            if (tid < 8) metric[tid] = nxt;
+            __syncthreads();
+        }
+    }
+    if (tid == 0) {
+        int st = 0;
+        for (int q = 1; q < 8; ++q)
+            if (metric[q] < metric[st]) st = q;
+        uint8_t* dst = codes + (int64_t)row * (k >> 2);
+        for (int i = 32 * nb - 1; i >= 0; --i) {
+            dst[i] = byt[i * 8 + st];
+            st = prv[i * 8 + st];
+        }
+    }
+}
+
 }  // namespace
+
+int launch_encode_carry(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
+                        uint16_t* scales, pg_stream_t s) {
+    const size_t lds = (size_t)(k / 128) * 32 * 16;        // survivors: 2 bytes per step and state
+    hipLaunchKernelGGL(k_encode_carry, dim3((unsigned)n), dim3(128), lds, (hipStream_t)s, w, (int)n, (int)k, sign_bits,
+                       codes, scales);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PG_ERR_HIP, "pg_encode_ex launch: %s", hipGetErrorString(e));
+    return PG_OK;
+}
 
 int launch_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
                   uint16_t* scales, pg_stream_t s) {

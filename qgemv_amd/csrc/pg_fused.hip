@@ -1,0 +1,80 @@
+// Launch side of the fused stage (pg_fused.h): the launch shape and the
+// P8F v1 instances; the carried-state ones are in pg_fused_carry.hip.
+#include "pg_fused.h"
+
+namespace pg {
+namespace {
+
+int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
+}
+
+}  // namespace
+
+// Launch shape of the fused stage: about one workgroup per CU, each with
+// all of its rows' codes in registers (at most 16 rows per lane).
+int fused_shape(int64_t n, int64_t k, int batch, FusedShape* out) {
+    FusedShape S;
+    S.W = 8;                                           // the kernel assumes 512 threads
+    int R_req = 0;
+    if (const char* e = getenv("PG_FUSED_ROWS")) {     // rows per workgroup, for tuning sweeps
+        const int r2 = atoi(e);
+        if (r2 > 0) R_req = r2;
+    }
+    const int nchunk = (int)(k / 64), nbk = (int)(k / 128);
+    S.CG = (nchunk + 7) / 8;
+    if (S.CG > 8 * S.W) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    S.RP = 8 * S.W / S.CG;
+    S.XG = (int)((k / 8 + 64 * S.W - 1) / (64 * S.W));   // 8-value groups of x per thread
+    if (k / 32 > 64 * S.W || S.XG > 4)
+        return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    (void)nbk;
+    const int64_t cus = compute_units();
+    int64_t R = R_req > 0 ? R_req : (n + cus - 1) / cus;
+    if (R > 16 * S.RP) R = 16 * S.RP;                      // at most 16 rows per lane
+    if (R > n) R = n;
+    S.R = (int)R;
+    S.RS = (S.R + S.RP - 1) / S.RP;
+    // batch rows per tile: as many as the LDS holds, up to the template's bound
+    // BTM (registers: RS * BTM <= 32, RS <= 2 for 8 rows); with fewer rows
+    // per tile than the batch, the kernel loops over tiles itself where its
+    // registers allow (fused_loops), else one launch per tile
+    const size_t budget = 150 * 1024;
+    int bt_lds = 1;                                    // rows of x the LDS holds at once
+    for (;;) {
+        FusedShape T = S;
+        T.BTM = T.BT = bt_lds + 1;
+        if (bt_lds >= 8 || fused_lds_bytes((int)k, 4, T) > budget) break;
+        ++bt_lds;
+    }
+    const int t = batch < bt_lds ? batch : bt_lds;
+    S.BTM = batch <= 1 ? 1 : S.RS <= 2 ? (t > 4 ? 8 : 4) : S.RS <= 4 ? 4 : S.RS <= 8 ? (t <= 2 ? 2 : 4) : 2;
+    S.BT = t < S.BTM ? t : S.BTM;
+    if (fused_lds_bytes((int)k, 4, S) > budget) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
+    *out = S;
+    return PG_OK;
+}
+
+int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
+                     int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
+                     pg_stream_t s) {
+    FusedShape S;
+    const int rc = fused_shape(n, k, batch, &S);
+    if (rc != PG_OK) return rc;
+    if (x_dt == PG_F32 && !(flags & PG_FLAG_RMSNORM))
+        return fail(PG_ERR_UNSUPPORTED, "pg_rot_qgemv: fp32 input needs PG_FLAG_RMSNORM (its rotation runs in fp16)");
+    hipStream_t st = (hipStream_t)s;
+    if (flags & PG_FLAG_CARRY_STATE)
+        return launch_fused_carry(S, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
+    return launch_fused_all<false>(S, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
+}
+
+}  // namespace pg

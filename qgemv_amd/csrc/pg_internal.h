@@ -28,10 +28,11 @@ double half_to_double(uint16_t h);
 int encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
                uint16_t* scales, int n_threads);
 
-// HIP launchers (pg_kernels.hip); arguments are already validated.
+// HIP launchers (pg_kernels.hip, pg_fused.hip, pg_qgemm.hip); arguments are
+// already validated.
 // Each returns PG_OK or PG_ERR_HIP (message set).
 int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w,
-                  pg_stream_t s);
+                  bool carry, pg_stream_t s);
 int launch_fwht(const void* x, int in_dt, void* y, int out_dt, const uint8_t* sign_bits,
                 int64_t rows, int64_t k, uint32_t flags, pg_stream_t s);
 int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
@@ -44,5 +45,7 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
 // (pg_encode.hip)
 int launch_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
                   uint16_t* scales, pg_stream_t s);
+int launch_encode_carry(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
+                        uint16_t* scales, pg_stream_t s);
 
 }  // namespace pg

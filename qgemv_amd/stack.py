@@ -24,8 +24,13 @@ ORDER = ("qkv", "o", "gu", "down")
 
 class Stack:
     def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_Q16,
-                 fused: bool = True):
+                 fused: bool = True, carry: bool = False):
         import torch
+        if carry and not fused:
+            raise ValueError("carried-state codes run on the fused path only")
+        # random bytes are valid paths of both the per-block and the
+        # carried-state trellis; carry selects how the stages read them
+        self.cflag = L.PG_FLAG_CARRY_STATE if carry else 0
         self.shapes = synth.merged_shapes(shapes)
         self.raw_shapes = shapes
         self.layers = layers
@@ -75,12 +80,13 @@ class Stack:
                 if site == "qkv" and layer == 0:
                     src = h_in if h_in is not None else self.h0
                     L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, src, L.PG_F16, k,
-                                   self.signs[layer][site], 0, b, self.out[site], stream)
+                                   self.signs[layer][site], self.cflag, b, self.out[site], stream)
                     continue
                 prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
                 n_prev = self.shapes[prev][0]
                 L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.out[prev], L.PG_F32,
-                               n_prev, self.signs[layer][site], L.PG_FLAG_RMSNORM, b, self.out[site], stream)
+                               n_prev, self.signs[layer][site], L.PG_FLAG_RMSNORM | self.cflag, b, self.out[site],
+                               stream)
         return self.out["down"]
 
     def _token_split(self, stream=None, h_in=None):

@@ -65,9 +65,10 @@ def encoded_qwen(name: str):
     return _cached(f"qwen_{name}", run)
 
 
-def oracle_chain(codes, scales, signs, shapes, h0, layers):
+def oracle_chain(codes, scales, signs, shapes, h0, layers, carry=False):
     """The stack driver's chain (qgemv_amd.stack) written with the oracle's
-    fp64 functions: rotate, RMS-normalise with fp16 rounding, product."""
+    fp64 functions: rotate, RMS-normalise with fp16 rounding, product
+    (carry: codes of the carried-state variant)."""
     from qgemv_amd.stack import ORDER
     merged = synth.merged_shapes(shapes)
     h = np.asarray(h0, dtype=np.float64)
@@ -81,7 +82,7 @@ def oracle_chain(codes, scales, signs, shapes, h0, layers):
                 prev = {"o": "qkv", "gu": "o", "down": "gu"}[site]
                 src = p8f.rmsnorm16(out[prev][:, :k])
             xr = p8f.rotate(src[:, :k], signs[layer][site])
-            out[site] = p8f.gemv_ref(codes[layer][site], scales[layer][site], xr)
+            out[site] = p8f.gemv_ref(codes[layer][site], scales[layer][site], xr, carry)
     return out["down"]
 
 

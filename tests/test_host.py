@@ -59,7 +59,13 @@ def test_codebook_table_matches_oracle():
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 5, 1 << 20, 1, 256, 0, stream=0),         # dtype
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 0, 1 << 20, 1, 256, 4, stream=0),         # flags
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 255, 1 << 20, 1, 1, 1 << 24, stream=0),  # ldx < k
-    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 2, 1, 1 << 24, stream=0),  # flags
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 4, 1, 1 << 24, stream=0),  # flags
+    lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 256, 4, 1 << 24, stream=0),                  # flags
+    lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 200, 2, 1 << 24, stream=0),                  # k % 128
+    lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 256, 2, (1 << 24) + 4, stream=0),            # w align
+    lambda: q.pg_encode_ex(1 << 20, 8, 256, 1 << 20, 4, 1 << 20, 1 << 20, stream=0),          # flags
+    lambda: q.pg_encode_ex(1 << 20, 8, 200, 1 << 20, 2, 1 << 20, 1 << 20, stream=0),          # k % 128
+    lambda: q.pg_encode_ex(None, 8, 256, 1 << 20, 2, 1 << 20, 1 << 20, stream=0),             # null w
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 1, 0, 1 << 24, stream=0),  # batch
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 3, 256, 1 << 20, 1, 1, 1 << 24, stream=0),  # dtype
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 1, 2, 1 << 22, stream=0),  # overlap
@@ -131,4 +137,10 @@ def test_rot_qgemv_rejects_k_beyond_its_register_staging():
 def test_rot_qgemv_rejects_fp32_input_without_normalisation():
     with pytest.raises(q.PgError) as ei:
         q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, q.PG_F32, 256, 1 << 20, 0, 1, 1 << 24, stream=0)
+    assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
+
+
+def test_carried_state_encoder_rejects_k_beyond_its_lds_survivors():
+    with pytest.raises(q.PgError) as ei:
+        q.pg_encode_ex(1 << 20, 8, 32768, 1 << 20, q.PG_FLAG_CARRY_STATE, 1 << 20, 1 << 20, stream=0)
     assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
