@@ -96,10 +96,11 @@ def run_stack(args):
 
     shapes = synth.qwen3_4b_shapes() if args.workload == "qwen36" else synth.llama31_8b_shapes()
     layers = 36 if args.workload == "qwen36" else 32
-    fused = args.path == "fused"
-    if not fused and args.batch != 1:
-        raise SystemExit("the split path runs batch 1 only")
-    log(f"building {args.workload}: {layers} layers, batch {args.batch}, {args.path} path")
+    # auto: the fused stage up to batch 3; from batch 4 on the rotation + the
+    # matrix-core product, whose cost hardly grows with the batch
+    path = args.path if args.path != "auto" else ("fused" if args.batch <= 3 or args.carry else "split")
+    fused = path == "fused"
+    log(f"building {args.workload}: {layers} layers, batch {args.batch}, {path} path")
     st = Stack(shapes, layers, batch=args.batch, x_dtype=q.PG_Q16, fused=fused, carry=args.carry)
     stream = torch.cuda.current_stream()
     use_graph = not args.no_graph
@@ -148,19 +149,24 @@ def run_stack(args):
                     n, k = st.shapes[site]
                     first = site == "qkv" and layer == 0
                     prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
-                    q.pg_fwht_rotate(st.h0 if first else st.out[prev], q.PG_F16 if first else q.PG_F32, st.xrot,
-                                     q.PG_Q16, st.signs[layer][site], 1, k, 0 if first else q.PG_FLAG_RMSNORM)
+                    q.pg_fwht_rotate_ex(st.h0 if first else st.out[prev], q.PG_F16 if first else q.PG_F32,
+                                        k if first else st.shapes[prev][0], st.xrot, q.PG_Q16, st.signs[layer][site],
+                                        args.batch, k, 0 if first else q.PG_FLAG_RMSNORM)
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
-                    q.pg_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.xrot, q.PG_Q16, 1,
+                    q.pg_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.xrot, q.PG_Q16, args.batch,
                                st.out[site])
                     b.record(stream)
                     evs.append((a, b))
         torch.cuda.synchronize()
         avg_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-        kname = "k_qgemv_q16"
-        kdesc = "k_qgemv_q16 (pg_qgemv on PG_Q16 activations)"
+        if args.batch == 1:
+            kname = "k_qgemv_q16"
+            kdesc = "k_qgemv_q16 (pg_qgemv on PG_Q16 activations)"
+        else:
+            kname = "k_qgemv_mma"
+            kdesc = "k_qgemv_mma (pg_qgemv on PG_Q16 activations, int8 matrix cores, batch 2..8)"
         nlaunch = len(evs)
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
     wl = ("qwen3-4b-36L" if args.workload == "qwen36" else "llama3.1-8b-32L") + f"-b{args.batch}"
@@ -171,13 +177,14 @@ def run_stack(args):
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8xi8->i32 (levels x 16-bit activation digits), f16 MFMA rotation, f32 scales",
+        "dtype": ("i8xi8->i32 (levels x 16-bit activation digits), f16 MFMA rotation, f32 scales" if fused or
+                  args.batch == 1 else "i8xi8->i32 MFMA (level planes x 16-bit activation digits), f32 scales"),
         "data": "synthetic",
         "config": {"workload": f"{'Qwen3-4B' if args.workload == 'qwen36' else 'Llama-3.1-8B'}-shaped "
                                f"{layers}-layer linear stack, batch {args.batch}, random trellis bitstreams",
                    "layers": layers, "batch": args.batch, "bytes_per_token": st.bytes_per_token,
                    "tok_per_s": round(tok_s, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "hip_graphs": use_graph, "launches_per_token": launches_per_step, "path": args.path,
+                   "hip_graphs": use_graph, "launches_per_token": launches_per_step, "path": path,
                    "format": "carried-state variant" if args.carry else "P8F v1"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -313,9 +320,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 4 times (HBM-counter calibration) and exit")
-    ap.add_argument("--path", default="fused", choices=["fused", "split"],
-                    help="fused: one pg_rot_qgemv per stage; split: pg_fwht_rotate + pg_qgemv per stage")
-    ap.add_argument("--batch", type=int, default=1, help="activation rows per step (fused path: 1..8)")
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
+                    help="fused: one pg_rot_qgemv per stage; split: pg_fwht_rotate_ex + pg_qgemv per stage; "
+                         "auto: fused up to batch 3, split from batch 4")
+    ap.add_argument("--batch", type=int, default=1, help="activation rows per step (1..8)")
     ap.add_argument("--carry", action="store_true",
                     help="read the codes as the carried-state variant (state runs on across blocks; fused path)")
     ap.add_argument("--no-qgemm", action="store_true", help="skip the prompt-path (pg_qgemm) measurement")

@@ -182,6 +182,14 @@ int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype,
                    const uint8_t* sign_bits, int64_t rows, int64_t k, uint32_t flags,
                    pg_stream_t stream);
 
+/* pg_fwht_rotate over rows of x that are ldx >= k elements apart (the first
+ * k columns of each row are rotated, as when a stage reads part of the
+ * previous stage's output); y as in pg_fwht_rotate.  pg_fwht_rotate is this
+ * call with ldx = k. */
+int pg_fwht_rotate_ex(const void* x, int in_dtype, int64_t ldx, void* y, int out_dtype,
+                      const uint8_t* sign_bits, int64_t rows, int64_t k, uint32_t flags,
+                      pg_stream_t stream);
+
 /* Batch-1..8 product over the compressed weights (the generation path,
  * article "8 open models...", section "What 2-bit keeps": one pass over all
  * weights per token):
@@ -193,7 +201,10 @@ int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype,
  *         already rotated
  *   batch 1..8, y device f32 [batch][n] out.
  * fp32 accumulation; summation order is fixed, so repeated calls are
- * bitwise identical. */
+ * bitwise identical.  With PG_Q16 and batch >= 2 the products run on the
+ * int8 matrix cores (the level planes of a code dword serve up to 16 batch
+ * rows at once); the results agree with the batch-1 kernel's within fp32
+ * rounding, not bit for bit. */
 int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
              const void* x_rot, int x_dtype, int batch, float* y, pg_stream_t stream);
 

@@ -23,7 +23,7 @@ PG_FLAG_CARRY_STATE = 2
 
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
            "pg_encode", "pg_encode_ex", "pg_decode_ex",
-           "pg_decode", "pg_fwht_rotate", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm")
+           "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm")
 
 
 class PgError(RuntimeError):
@@ -70,6 +70,8 @@ def lib():
         L.pg_decode.argtypes = [vp, vp, i64, i64, vp, vp]
         L.pg_fwht_rotate.restype = i32
         L.pg_fwht_rotate.argtypes = [vp, i32, vp, i32, vp, i64, i64, u32, vp]
+        L.pg_fwht_rotate_ex.restype = i32
+        L.pg_fwht_rotate_ex.argtypes = [vp, i32, i64, vp, i32, vp, i64, i64, u32, vp]
         L.pg_qgemv.restype = i32
         L.pg_qgemv.argtypes = [vp, vp, i64, i64, vp, i32, i32, vp, vp]
         L.pg_rot_qgemv.restype = i32
@@ -161,6 +163,12 @@ def pg_fwht_rotate(x, in_dtype: int, y, out_dtype: int, sign_bits, rows: int, k:
                    stream=None) -> None:
     _check(lib().pg_fwht_rotate(_ptr(x), in_dtype, _ptr(y), out_dtype, _ptr(sign_bits), rows, k, flags,
                                 _stream(stream)))
+
+
+def pg_fwht_rotate_ex(x, in_dtype: int, ldx: int, y, out_dtype: int, sign_bits, rows: int, k: int, flags: int = 0,
+                      stream=None) -> None:
+    _check(lib().pg_fwht_rotate_ex(_ptr(x), in_dtype, ldx, _ptr(y), out_dtype, _ptr(sign_bits), rows, k, flags,
+                                   _stream(stream)))
 
 
 def pg_qgemv(codes, scales, n: int, k: int, x_rot, x_dtype: int, batch: int, y, stream=None) -> None:

@@ -118,23 +118,29 @@ int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k
     return pg::launch_decode(codes, scales, n, k, w_rot, false, stream);
 }
 
-int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype, const uint8_t* sign_bits,
-                   int64_t rows, int64_t k, uint32_t flags, pg_stream_t stream) {
+int pg_fwht_rotate_ex(const void* x, int in_dtype, int64_t ldx, void* y, int out_dtype, const uint8_t* sign_bits,
+                      int64_t rows, int64_t k, uint32_t flags, pg_stream_t stream) {
     pg::clear_error();
     if (rows < 1) return pg::fail(PG_ERR_INVALID_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
     PG_TRY(check_nk(rows, k));
+    if (ldx < k) return pg::fail(PG_ERR_INVALID_ARG, "ldx (%lld) < k (%lld)", (long long)ldx, (long long)k);
     PG_TRY(check_dtype(in_dtype, "in_dtype", true, false));
     PG_TRY(check_dtype(out_dtype, "out_dtype", true, true));
     PG_TRY(check_ptr(x, 16, "x"));
     PG_TRY(check_ptr(y, 16, "y"));
     PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
     if (flags & ~PG_FLAG_RMSNORM) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-    const size_t in_b = (size_t)rows * k * (in_dtype == PG_F32 ? 4 : 2);
+    const size_t in_b = ((size_t)(rows - 1) * ldx + k) * (in_dtype == PG_F32 ? 4 : 2);
     const size_t out_b = out_dtype == PG_Q16 ? (size_t)rows * pg::q16_row_bytes(k)
                                              : (size_t)rows * k * (out_dtype == PG_F32 ? 4 : 2);
     const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
     if (xa < ya + out_b && ya < xa + in_b) return pg::fail(PG_ERR_INVALID_ARG, "x and y overlap");
-    return pg::launch_fwht(x, in_dtype, y, out_dtype, sign_bits, rows, k, flags, stream);
+    return pg::launch_fwht(x, in_dtype, ldx, y, out_dtype, sign_bits, rows, k, flags, stream);
+}
+
+int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype, const uint8_t* sign_bits,
+                   int64_t rows, int64_t k, uint32_t flags, pg_stream_t stream) {
+    return pg_fwht_rotate_ex(x, in_dtype, k, y, out_dtype, sign_bits, rows, k, flags, stream);
 }
 
 int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x_rot,

@@ -150,5 +150,30 @@ int hip_check(hipError_t e, const char* what) {
 }
 
 
+// Workgroup barrier that waits only for this wave's LDS accesses (not for
+// its global loads or direct-to-LDS copies in flight, which __syncthreads'
+// fences would wait for).  The builtin barrier alone is no compiler fence:
+// the empty asm statements with a memory clobber keep every memory access
+// on its side.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// compute units of the current device (cached per device)
+int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
+}
+
 }  // namespace
 }  // namespace pg

@@ -3,21 +3,6 @@
 #include "pg_fused.h"
 
 namespace pg {
-namespace {
-
-int compute_units() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cu = 0;
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
-        cached[dev] = cu;
-    }
-    return cached[dev];
-}
-
-}  // namespace
 
 // Launch shape of the fused stage: about one workgroup per CU, each with
 // all of its rows' codes in registers (at most 16 rows per lane).

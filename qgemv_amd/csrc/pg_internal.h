@@ -33,13 +33,16 @@ int encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, u
 // Each returns PG_OK or PG_ERR_HIP (message set).
 int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w,
                   bool carry, pg_stream_t s);
-int launch_fwht(const void* x, int in_dt, void* y, int out_dt, const uint8_t* sign_bits,
+int launch_fwht(const void* x, int in_dt, int64_t ldx, void* y, int out_dt, const uint8_t* sign_bits,
                 int64_t rows, int64_t k, uint32_t flags, pg_stream_t s);
 int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const void* x, int x_dt, int batch, float* y, pg_stream_t s);
 int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
                      int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
                      pg_stream_t s);
+// (pg_qgemv_mma.hip) batched product on PG_Q16 activations, matrix cores
+int launch_qgemv_mma(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint8_t* xq,
+                     int batch, float* y, pg_stream_t s);
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const uint16_t* x, int64_t m, float* y, pg_stream_t s);
 // (pg_encode.hip)

@@ -6,6 +6,8 @@
 // Ungerboeck trellis over groups of 4 weights, the state carried from group
 // to group choosing the value set of the next group, plus a random Hadamard
 // rotation.  Bit layout: format P8F v1 as stated in include/pingala.h.
+#include <string.h>
+
 #include "pg_device.h"
 
 namespace pg {
@@ -59,19 +61,20 @@ __device__ __forceinline__ void q16_store(uint8_t* row, int k, int blk, int i, i
 
 __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, int in_dt, void* __restrict__ y,
                                               int out_dt, const uint8_t* __restrict__ sign_bits, int k,
-                                              uint32_t flags, int64_t q16_stride) {
+                                              int64_t ldx, uint32_t flags, int64_t q16_stride) {
     const int64_t row = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nblk = k >> 7;
     const int blk = blockIdx.x * 4 + wave;
-    const int64_t base = row * (int64_t)k;
+    const int64_t xbase = row * ldx;                          // row of x (ldx elements apart)
+    const int64_t base = row * (int64_t)k;                    // row of an fp output
     __shared__ float red[4];
     // this wave's block first (its loads overlap the normalisation pass)
     const bool active = blk < nblk;
     const int i0 = (active ? blk : 0) * 128 + lane, i1 = i0 + 64;
-    float a = load_elem(x, in_dt, base + i0);
-    float c = load_elem(x, in_dt, base + i1);
+    float a = load_elem(x, in_dt, xbase + i0);
+    float c = load_elem(x, in_dt, xbase + i1);
     const uint32_t sg0 = sign_bits[i0 >> 3], sg1 = sign_bits[i1 >> 3];
     float inv = 1.0f;
     if (flags & PG_FLAG_RMSNORM) {
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, int in
 #pragma unroll
             for (int u = 0; u < 64; ++u) {
                 const int i = i0r + 256 * u;
-                v[u] = i < k ? load_elem(x, in_dt, base + i) : 0.0f;
+                v[u] = i < k ? load_elem(x, in_dt, xbase + i) : 0.0f;
             }
 #pragma unroll
             for (int u = 0; u < 64; ++u) ss += v[u] * v[u];
@@ -446,11 +449,11 @@ int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64
     return hip_check(hipGetLastError(), "pg_decode launch");
 }
 
-int launch_fwht(const void* x, int in_dt, void* y, int out_dt, const uint8_t* sign_bits, int64_t rows,
-                int64_t k, uint32_t flags, pg_stream_t s) {
+int launch_fwht(const void* x, int in_dt, int64_t ldx, void* y, int out_dt, const uint8_t* sign_bits,
+                int64_t rows, int64_t k, uint32_t flags, pg_stream_t s) {
     if (rows > 65535) return fail(PG_ERR_UNSUPPORTED, "rows > 65535");
     const dim3 grid((unsigned)((k / 128 + 3) / 4), (unsigned)rows);
-    hipLaunchKernelGGL(k_fwht, grid, dim3(256), 0, (hipStream_t)s, x, in_dt, y, out_dt, sign_bits, (int)k, flags,
+    hipLaunchKernelGGL(k_fwht, grid, dim3(256), 0, (hipStream_t)s, x, in_dt, y, out_dt, sign_bits, (int)k, ldx, flags,
                        (int64_t)q16_row_bytes(k));
     return hip_check(hipGetLastError(), "pg_fwht_rotate launch");
 }
@@ -478,6 +481,13 @@ int launch_q16_bs(int R, int W, const uint8_t* codes, const uint16_t* scales, in
 int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
                  int x_dt, int batch, float* y, pg_stream_t s) {
     if (x_dt == PG_Q16) {
+        // batch 2..8: the matrix-core kernel, whose vector work per weight
+        // does not grow with the batch (PG_QGEMV_KERNEL=q16 keeps the
+        // v_dot4 kernel, =mma takes the matrix cores at any batch; for tests)
+        const char* kern = getenv("PG_QGEMV_KERNEL");
+        const bool force_q16 = kern && strcmp(kern, "q16") == 0, force_mma = kern && strcmp(kern, "mma") == 0;
+        if (force_mma || (!force_q16 && batch >= 2))
+            return launch_qgemv_mma(codes, scales, n, k, (const uint8_t*)x, batch, y, s);
         const int stride = (int)q16_row_bytes(k);
         // rows per workgroup 8*R; waves per workgroup W split each row's
         // 64-weight chunks, chosen so that the launch has about 2048+ waves

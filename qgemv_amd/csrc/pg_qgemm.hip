@@ -303,8 +303,7 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
                     }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);                     // lgkmcnt(0): level writes, operand reads
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();                                          // level writes and operand reads done
     };
     for (int st = 0; st < steps; st += 6) {                     // steps is even (k % 128 == 0)
         body(std::integral_constant<int, 0>(), st);

@@ -12,7 +12,8 @@ where n16 is the RMS normalisation with fp16 rounding; the first layer's
 input is fp16 and is not normalised.  k, v and u are computed and stored but
 not consumed.  The fused path (default) runs each group as one
 pg_rot_qgemv launch (normalisation + rotation + product, batch 1..8); the
-split path runs pg_fwht_rotate then pg_qgemv (batch 1).
+split path runs pg_fwht_rotate_ex then pg_qgemv (batch 1..8; from batch 2 on
+pg_qgemv's products run on the matrix cores).
 """
 from __future__ import annotations
 
@@ -90,24 +91,23 @@ class Stack:
         return self.out["down"]
 
     def _token_split(self, stream=None, h_in=None):
-        if self.batch != 1:
-            raise NotImplementedError("the chained driver runs batch 1 (per-matrix batch products are separate)")
+        b = self.batch
         for layer in range(self.layers):
             for site in ORDER:
                 n, k = self.shapes[site]
                 if site == "qkv":
                     if layer == 0:
-                        src, src_dt, flags = (h_in if h_in is not None else self.h0), L.PG_F16, 0
+                        src, src_dt, flags, ldx = (h_in if h_in is not None else self.h0), L.PG_F16, 0, k
                     else:
-                        src, src_dt, flags = self.out["down"], L.PG_F32, L.PG_FLAG_RMSNORM
+                        src, src_dt, flags, ldx = self.out["down"], L.PG_F32, L.PG_FLAG_RMSNORM, self.shapes["down"][0]
                 else:
                     prev = {"o": "qkv", "gu": "o", "down": "gu"}[site]
-                    src, src_dt, flags = self.out[prev], L.PG_F32, L.PG_FLAG_RMSNORM
-                # batch 1: the first k columns of the previous output are the input
-                L.pg_fwht_rotate(src, src_dt, self.xrot, self.x_dtype, self.signs[layer][site], 1, k, flags,
-                                 stream)
+                    src, src_dt, flags, ldx = self.out[prev], L.PG_F32, L.PG_FLAG_RMSNORM, self.shapes[prev][0]
+                # the first k columns of each row of the previous output are the input
+                L.pg_fwht_rotate_ex(src, src_dt, ldx, self.xrot, self.x_dtype, self.signs[layer][site], b, k, flags,
+                                    stream)
                 L.pg_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.xrot, self.x_dtype,
-                           1, self.out[site], stream)
+                           b, self.out[site], stream)
         return self.out["down"]
 
     def capture(self):

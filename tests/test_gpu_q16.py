@@ -1,4 +1,6 @@
-"""The PG_Q16 fast path: rotation to 16-bit fixed point, and qgemv on it.
+"""The PG_Q16 fast path: rotation to 16-bit fixed point, and qgemv on it
+(both product kernels: v_dot4 per batch row, and the int8 matrix cores that
+take batch 2..8 by default).
 
 qgemv is checked against the oracle on host-packed activations (exact fp64
 reference of the very values the kernel reads: the bar is fp32 accumulation,
@@ -13,6 +15,17 @@ from tests import q16pack
 from tests.helpers import TOL, dev, encoded_qwen, encoded_single, host, rel_err_rows
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["auto", "q16", "mma"])
+def kernel(request, monkeypatch):
+    """Which PG_Q16 product kernel pg_qgemv runs: its own choice by batch,
+    or one forced through PG_QGEMV_KERNEL."""
+    if request.param == "auto":
+        monkeypatch.delenv("PG_QGEMV_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("PG_QGEMV_KERNEL", request.param)
+    return request.param
 
 
 def _rotate_q16(x_np, in_dt, sb, rows, k, flags=0):
@@ -54,9 +67,30 @@ def test_rotation_to_q16_matches_oracle(k):
     assert np.array_equal(sums, qv.reshape(rows, k // 64, 64).sum(axis=2))
 
 
+@pytest.mark.parametrize("out_dt", ["q16", "f32"])
+def test_rotate_ex_strided_rows_equal_contiguous(out_dt):
+    """pg_fwht_rotate_ex over the first k columns of rows ldx apart gives
+    exactly what pg_fwht_rotate gives on a contiguous copy of them."""
+    import torch
+    rows, k, ldx = 5, 2560, 6144
+    rng = np.random.default_rng(8)
+    xfull = torch.from_numpy(rng.standard_normal((rows, ldx)).astype(np.float32)).cuda()
+    xc = xfull[:, :k].contiguous()
+    sb = torch.from_numpy(rng.integers(0, 256, k // 8, dtype=np.uint8)).cuda()
+    if out_dt == "q16":
+        dt, ya, yb = q.PG_Q16, *(torch.zeros((rows, q16pack.row_bytes(k)), dtype=torch.uint8, device="cuda")
+                                  for _ in range(2))
+    else:
+        dt, ya, yb = q.PG_F32, *(torch.zeros((rows, k), dtype=torch.float32, device="cuda") for _ in range(2))
+    q.pg_fwht_rotate_ex(xfull, q.PG_F32, ldx, ya, dt, sb, rows, k, q.PG_FLAG_RMSNORM)
+    q.pg_fwht_rotate(xc, q.PG_F32, yb, dt, sb, rows, k, q.PG_FLAG_RMSNORM)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ya).view(np.uint8), host(yb).view(np.uint8))
+
+
 @pytest.mark.parametrize("batch", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("n,k", [(512, 2048), (45, 384), (33, 128), (1000, 2560), (300, 9728), (64, 14336)])
-def test_qgemv_q16_exact_inputs(n, k, batch):
+def test_qgemv_q16_exact_inputs(n, k, batch, kernel):
     rng = np.random.default_rng(n * 31 + k + batch)
     codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
     scales = synth.random_scale_bits(n, k, n + k)
@@ -67,7 +101,7 @@ def test_qgemv_q16_exact_inputs(n, k, batch):
     assert np.max(rel_err_rows(y, ref)) <= 1e-5
 
 
-def test_qgemv_q16_one_hot_per_block():
+def test_qgemv_q16_one_hot_per_block(kernel):
     codes, scales = encoded_single()
     k = 2048
     w = p8f.decode_weights(codes, scales)
@@ -93,13 +127,13 @@ def test_rotate_then_qgemv_end_to_end(name):
 
 
 @pytest.mark.parametrize("shapes_fn", [synth.qwen3_4b_shapes, synth.llama31_8b_shapes])
-def test_stack_shapes_q16_sampled_rows(shapes_fn):
+def test_stack_shapes_q16_sampled_rows(shapes_fn, kernel):
     merged = synth.random_layer_merged(1, shapes_fn())
     rng = np.random.default_rng(3)
     for site, (codes, scales) in merged.items():
         n, kg = codes.shape
         k = 4 * kg
-        for b in (1, 4):
+        for b in (1, 4, 8):
             qv, sx = q16pack.random_q16(b, k, seed=b)
             y = _qgemv_q16(codes, scales, q16pack.pack(qv, sx), b)
             rows = np.sort(rng.choice(n, 256, replace=False))
@@ -107,11 +141,12 @@ def test_stack_shapes_q16_sampled_rows(shapes_fn):
             assert np.max(rel_err_rows(y[:, rows], ref)) <= 1e-5, site
 
 
-def test_qgemv_q16_deterministic():
+@pytest.mark.parametrize("batch", [1, 8])
+def test_qgemv_q16_deterministic(batch, kernel):
     codes, scales = encoded_qwen("gate")
     k = codes.shape[1] * 4
-    qv, sx = q16pack.random_q16(1, k, seed=5)
+    qv, sx = q16pack.random_q16(batch, k, seed=5)
     buf = q16pack.pack(qv, sx)
-    a = _qgemv_q16(codes, scales, buf, 1)
-    b = _qgemv_q16(codes, scales, buf, 1)
+    a = _qgemv_q16(codes, scales, buf, batch)
+    b = _qgemv_q16(codes, scales, buf, batch)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -28,14 +28,16 @@ def test_chain_matches_oracle(shapes_fn, layers, fused):
     assert np.array_equal(d2.view(np.uint32), got.view(np.uint32))
 
 
-@pytest.mark.parametrize("batch", [3, 4])
-def test_fused_chain_batched_matches_oracle(batch):
-    """Batched decode through the fused stage (several activation rows per
-    launch) against the oracle's chain, row by row."""
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("batch", [3, 4, 8])
+def test_chain_batched_matches_oracle(batch, fused):
+    """Batched decode, through the fused stage (several activation rows per
+    launch) or the rotation + matrix-core product, against the oracle's
+    chain, row by row."""
     import torch
     from tests.helpers import rel_err_rows
     shapes = synth.llama31_8b_shapes()
-    st = Stack(shapes, 2, batch=batch, fused=True)
+    st = Stack(shapes, 2, batch=batch, fused=fused)
     got = host(st.token())
     torch.cuda.synchronize()
     codes, scales, signs = zip(*[st.host_arrays(l) for l in range(2)])
@@ -44,11 +46,13 @@ def test_fused_chain_batched_matches_oracle(batch):
     assert np.max(rel_err_rows(got, ref)) <= TOL
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("batch", [1, 8])
+def test_graph_replays_match_eager(batch):
     """A captured token replays bitwise-identically to the eager token, on
-    every replay, with eager work and synchronisations in between."""
+    every replay, with eager work and synchronisations in between (batch 8:
+    the matrix-core product)."""
     import torch
-    st = Stack(synth.qwen3_4b_shapes(), 3, fused=False)
+    st = Stack(synth.qwen3_4b_shapes(), 3, batch=batch, fused=False)
     eager = host(st.token()).copy()
     st.capture()
     for i in range(4):

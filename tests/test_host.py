@@ -58,6 +58,9 @@ def test_codebook_table_matches_oracle():
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 20, 0, 1 << 20, 1, 256, 0, stream=0),         # overlap
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 5, 1 << 20, 1, 256, 0, stream=0),         # dtype
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 0, 1 << 20, 1, 256, 4, stream=0),         # flags
+    lambda: q.pg_fwht_rotate_ex(1 << 20, 0, 128, 1 << 22, 0, 1 << 20, 1, 256, 0, stream=0),  # ldx < k
+    lambda: q.pg_fwht_rotate_ex(1 << 20, 0, 4096, (1 << 20) + 4 * 4096 + 16, 0, 1 << 20, 2, 256, 0,
+                                stream=0),                                                   # overlap, 2nd row
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 255, 1 << 20, 1, 1, 1 << 24, stream=0),  # ldx < k
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 4, 1, 1 << 24, stream=0),  # flags
     lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 256, 4, 1 << 24, stream=0),                  # flags
