@@ -154,18 +154,15 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
         rowj[j] = rok[j] ? row0 + r : (row0 < n ? row0 : n - 1);
     }
     asm volatile("" ::: "memory");
-    // The scale of a chunk comes with its neighbour in one aligned dword (the
-    // half is picked where it is used, so nothing converts it early).
+    // The scale of a chunk: a 16-bit load into a whole register (converted
+    // only where it is used).
     uint4 q[RS];
     uint32_t wsr[RS];
-    bool whi[RS];
 #pragma unroll
     for (int j = 0; j < RS; ++j) {
         const int row = rowj[j];
         q[j] = *reinterpret_cast<const uint4*>(codes + (int64_t)row * kg + 16 * cc);
-        const int64_t si = (int64_t)row * nbk + (cc >> 1);
-        whi[j] = (si & 1) != 0;
-        wsr[j] = reinterpret_cast<const uint32_t*>(scales)[si >> 1];
+        wsr[j] = scales[(int64_t)row * nbk + (cc >> 1)];
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * RS));      // x copies and sign loads done
@@ -433,7 +430,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
             }
     #pragma unroll
             for (int j = 0; j < RS; ++j) {
-                const float wsc = h2f((uint16_t)(whi[j] ? wb[j] >> 16 : wb[j]));
+                const float wsc = h2f((uint16_t)wb[j]);
     #pragma unroll
                 for (int b = 0; b < BTM; ++b) {
                     if (BTM > 1 && b >= bt) break;                     // uniform
