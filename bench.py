@@ -96,12 +96,16 @@ def run_stack(args):
 
     shapes = synth.qwen3_4b_shapes() if args.workload == "qwen36" else synth.llama31_8b_shapes()
     layers = 36 if args.workload == "qwen36" else 32
-    # auto: the fused stage up to batch 3; from batch 4 on the rotation + the
-    # matrix-core product, whose cost hardly grows with the batch
-    path = args.path if args.path != "auto" else ("fused" if args.batch <= 3 or args.carry else "split")
-    fused = path == "fused"
+    # auto: the v_dot4 fused stage up to batch 3; from batch 4 on the matrix
+    # cores, whose cost hardly grows with the batch: the fused stage where
+    # the batch's rotated activations fit in LDS (k <= 4096), the rotation +
+    # product elsewhere (hybrid)
+    path = args.path if args.path != "auto" else ("fused" if args.batch <= 3 or args.carry else "hybrid")
+    fused = path in ("fused", "hybrid")
+    split_above = 4096 if path == "hybrid" else None
     log(f"building {args.workload}: {layers} layers, batch {args.batch}, {path} path")
-    st = Stack(shapes, layers, batch=args.batch, x_dtype=q.PG_Q16, fused=fused, carry=args.carry)
+    st = Stack(shapes, layers, batch=args.batch, x_dtype=q.PG_Q16, fused=fused, carry=args.carry,
+               split_above=split_above)
     stream = torch.cuda.current_stream()
     use_graph = not args.no_graph
     if use_graph:
@@ -127,14 +131,20 @@ def run_stack(args):
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     log(f"timed {args.steps} steps: {gpu_ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
 
-    launches_per_step = (4 if fused else 8) * layers
+    n_split = sum(1 for _, k in st.shapes.values() if split_above is not None and k > split_above)
+    launches_per_step = (4 + n_split if fused else 8) * layers
     bytes_per_launch = st.bytes_per_token // (4 * layers)
     if fused:
         # every launch of the step is the fused stage kernel: its average
         # duration is the timed region over the launches (gaps included)
         avg_us = 1e3 * gpu_ms / (args.steps * launches_per_step)
-        kname = "k_rot_qgemv"
-        kdesc = "k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
+        if path == "fused" and args.batch <= 3:
+            kname = "k_rot_qgemv"
+            kdesc = "k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
+        else:
+            kname = "k_rot_qmma"
+            kdesc = ("k_rot_qmma (pg_rot_qgemv at batch 4..8: RMS norm + rotation + int8 matrix-core product) "
+                     "where k <= 4096" + ("; k_fwht + k_qgemv_mma above" if n_split else ""))
         nlaunch = args.steps * launches_per_step
     else:
         # split path: events around every product launch of a separate pass;
@@ -320,9 +330,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 4 times (HBM-counter calibration) and exit")
-    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split", "hybrid"],
                     help="fused: one pg_rot_qgemv per stage; split: pg_fwht_rotate_ex + pg_qgemv per stage; "
-                         "auto: fused up to batch 3, split from batch 4")
+                         "hybrid: fused where k <= 4096, split above; auto: fused up to batch 3, hybrid from batch 4")
     ap.add_argument("--batch", type=int, default=1, help="activation rows per step (1..8)")
     ap.add_argument("--carry", action="store_true",
                     help="read the codes as the carried-state variant (state runs on across blocks; fused path)")

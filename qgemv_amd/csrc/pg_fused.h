@@ -85,6 +85,49 @@ __device__ __forceinline__ int fs_elem(int mt, int M) {
 
 typedef _Float16 fs_f16x8 __attribute__((ext_vector_type(8)));
 
+// A operand patterns of the Hadamard product (see fs_elem): lane l holds
+// row M = l % 32 and inputs 8 (l / 32) + t of a 16-wide step; the entry is
+//   (-1)^popcount(e & 7 & t) (-1)^(bit 3 of e & l / 32)   (fixed per lane)
+//   (-1)^(bit 4 of e & step % 2)                            (odd steps)
+//   (-1)^popcount(mt & step / 2)                            (uniform)
+__device__ __forceinline__ void fs_apat(int lane, uint32_t (&apat)[2][4]) {
+    const int e0 = fs_elem(0, lane & 31);
+    const int ha = lane >> 5;
+    const bool f_lane = ((e0 >> 3) & 1) & ha;
+    const bool f_odd = (e0 >> 4) & 1;
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        const bool n0 = (__builtin_popcount(e0 & 7 & t) & 1) ^ f_lane;
+        const bool n1 = (__builtin_popcount(e0 & 7 & (t + 1)) & 1) ^ f_lane;
+        const uint32_t wv = (n0 ? 0xBC00u : 0x3C00u) | ((n1 ? 0xBC00u : 0x3C00u) << 16);
+        apat[0][t >> 1] = wv;
+        apat[1][t >> 1] = f_odd ? (wv ^ 0x80008000u) : wv;
+    }
+}
+
+// One 32 x 32 rotation tile: the rows of quarter mt of H_128 (ordered as
+// fs_elem) times 32 staged fp16 blocks, one per lane column (lane % 32);
+// xr is this lane's block plus 16 (lane / 32) bytes, bok whether the block
+// exists (else zeros).  The B operands are read first, for one LDS wait.
+__device__ __forceinline__ f32x16 fs_rot_tile(const uint8_t* xr, bool bok, int mt, const uint32_t (&apat)[2][4]) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    uint4 bv[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) bv[st] = *reinterpret_cast<const uint4*>(xr + 32 * st);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        const uint4 bw = bok ? bv[st] : make_uint4(0, 0, 0, 0);
+        const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
+        const uint32_t* av = apat[st & 1];
+        const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw), __builtin_bit_cast(fs_f16x8, bw),
+                                                     acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 // Instances that loop over batch tiles themselves (the codes stay in
 // registers); the others get one launch per tile.  The loop keeps more
 // values live, so only instances with registers to spare have it.
@@ -169,26 +212,8 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     if (sg_on) reinterpret_cast<uint32_t*>(sbuf)[tid] = sg;
     __syncthreads();
 
-    // A operand patterns of the Hadamard product (see fs_elem): lane l holds
-    // row M = l % 32 and inputs 8 (l / 32) + t of a 16-wide step; the entry is
-    //   (-1)^popcount(e & 7 & t) (-1)^(bit 3 of e & l / 32)   (fixed per lane)
-    //   (-1)^(bit 4 of e & step % 2)                            (odd steps)
-    //   (-1)^popcount(mt & step / 2)                            (uniform)
-    uint32_t apat[2][4];
-    {
-        const int e0 = fs_elem(0, lane & 31);
-        const int ha = lane >> 5;
-        const bool f_lane = ((e0 >> 3) & 1) & ha;
-        const bool f_odd = (e0 >> 4) & 1;
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-            const bool n0 = (__builtin_popcount(e0 & 7 & t) & 1) ^ f_lane;
-            const bool n1 = (__builtin_popcount(e0 & 7 & (t + 1)) & 1) ^ f_lane;
-            const uint32_t wv = (n0 ? 0xBC00u : 0x3C00u) | ((n1 ? 0xBC00u : 0x3C00u) << 16);
-            apat[0][t >> 1] = wv;
-            apat[1][t >> 1] = f_odd ? (wv ^ 0x80008000u) : wv;
-        }
-    }
+    uint32_t apat[2][4];                                     // A operand patterns of the Hadamard product
+    fs_apat(lane, apat);
     const int ntile = (nbk + 31) >> 5;
 
     // ---- 2.-6. one tile of at most BT batch rows, x already in LDS; the
@@ -271,21 +296,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
             float* sxq = reinterpret_cast<float*>(dig + nchunk * FS_PITCH);
             int* sqq = reinterpret_cast<int*>(dig + nchunk * FS_PITCH + (k / 32) * 4);
             const uint8_t* xr = xh + (size_t)b * xhrow + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
-            f32x16 acc;
-    #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-            uint4 bv[8];                                         // all B operands first: one LDS wait
-    #pragma unroll
-            for (int st = 0; st < 8; ++st) bv[st] = *reinterpret_cast<const uint4*>(xr + 32 * st);
-    #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const uint4 bw = bok ? bv[st] : make_uint4(0, 0, 0, 0);
-                const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
-                const uint32_t* av = apat[st & 1];
-                const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
-                                                             __builtin_bit_cast(fs_f16x8, bw), acc, 0, 0, 0);
-            }
+            const f32x16 acc = fs_rot_tile(xr, bok, mt, apat);
             // quarter maximum: 16 values per lane, then the lane pair (l, l + 32)
             float mx = 0.0f;
     #pragma unroll
@@ -537,6 +548,12 @@ int launch_fused_all(const FusedShape& S, const uint8_t* codes, const uint16_t* 
 }
 
 }  // namespace
+
+// batch 4..8 on the int8 matrix cores (pg_fused_mma.hip): the same stage
+// with activations quantised per 128-block; PG_ERR_UNSUPPORTED (message not
+// set) when the shape does not fit it
+int launch_rot_qmma(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x, int x_dt,
+                    int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y, hipStream_t st);
 
 // the carried-state instances (pg_fused_carry.hip, compiled on their own)
 int launch_fused_carry(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,

@@ -1,5 +1,7 @@
 // Launch side of the fused stage (pg_fused.h): the launch shape and the
 // P8F v1 instances; the carried-state ones are in pg_fused_carry.hip.
+#include <string.h>
+
 #include "pg_fused.h"
 
 namespace pg {
@@ -57,6 +59,14 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
     if (x_dt == PG_F32 && !(flags & PG_FLAG_RMSNORM))
         return fail(PG_ERR_UNSUPPORTED, "pg_rot_qgemv: fp32 input needs PG_FLAG_RMSNORM (its rotation runs in fp16)");
     hipStream_t st = (hipStream_t)s;
+    // batch 4..8 on the matrix cores where the shape fits (PG_FUSED_KERNEL=vdot
+    // keeps the v_dot4 stage, =mma takes the matrix cores at any batch; for tests)
+    const char* kern = getenv("PG_FUSED_KERNEL");
+    const bool force_v = kern && strcmp(kern, "vdot") == 0, force_m = kern && strcmp(kern, "mma") == 0;
+    if (!(flags & PG_FLAG_CARRY_STATE) && !force_v && (force_m || batch >= 4)) {
+        const int r = launch_rot_qmma(codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
+        if (r != PG_ERR_UNSUPPORTED) return r;
+    }
     if (flags & PG_FLAG_CARRY_STATE)
         return launch_fused_carry(S, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
     return launch_fused_all<false>(S, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);

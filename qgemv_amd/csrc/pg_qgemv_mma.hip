@@ -7,36 +7,17 @@
 // Method: "Pingala-8" landing page, section "How it works" (trellis decode,
 // rotation before coding); batched generation is the case the same page's
 // section on limits calls weakest.  Bit layout and PG_Q16: include/pingala.h.
-#include "pg_device.h"
+#include "pg_mma.h"
 
 namespace pg {
 namespace {
 
-typedef int mma_v4i __attribute__((ext_vector_type(4)));
-typedef unsigned int mma_v4u __attribute__((ext_vector_type(4)));
-
-// One item = (16 weight rows, one 128-block).  For every item the
-// 16 x 16 x 64 int8 product
-//   D[b][r] += sum_k A[b][k] B[k][r]
-// takes A = activation digits (row b = batch row, 16 rows of which the first
-// `batch` are real) and B = bit planes P = (level + 7) / 2 of the weight rows.
-// Lane l supplies A row / B column l % 16 and the k slice l / 16 (16 bytes);
-// it receives D[4 (l / 16) + i][l % 16], i = 0..3.  Lane group kq = l / 16
-// takes code dwords 2 kq and 2 kq + 1 of the block: the product mm = 0, 1
-// pairs dword 2 kq + mm of every lane group, so two products cover the
-// block's 8 dwords.  PG_Q16 chunk 8 blk + d holds dword d's 16 values in
-// plane order (byte 4 j + g is group g, position j; hi digits, then lo), the
-// order of the planes, so both operands are 16 bytes as stored.  Per block,
-// exactly in int32,
-//   sum level q = 2 (256 H + L) - 7 sum q,  H = sum P hi,  L = sum P lo,
-// then y[b][r] += sw[r][blk] * sx[b][blk] * that, in fp32.
+// One item = (16 weight rows, one 128-block): the matrix-core block step of
+// pg_mma.h, with the PG_Q16 digits of the batch rows as the A operand
+// (PG_Q16 chunk 8 blk + d holds code dword d's 16 values in plane order).
 //
-// Workgroup: 8 waves over R = 16 NRT rows and all k columns.  The codes come
-// in tiles of 16 rows x 4 blocks (128 bytes of each row, one cache line):
-// eight lanes read a row's line, 16 bytes each, and the tile passes through a
-// small LDS area of the wave to reach the operand layout above (a lane's
-// share of a block is 8 bytes of one row, so reading it in that layout would
-// touch 16 lines for every 512 bytes).  Each wave takes a consecutive run of
+// Workgroup: 8 waves over R = 16 NRT rows and all k columns, the codes in
+// tiles of 16 rows x 4 blocks (pg_mma.h).  Each wave takes a consecutive run of
 // tiles (row tile t / (nbk / 4), blocks 4 (t % (nbk / 4)) ..), all requested
 // at entry; the weight scales of the workgroup's rows are copied to LDS once.
 // The activation digits, which every workgroup reads, are copied to LDS at
@@ -47,8 +28,6 @@ typedef unsigned int mma_v4u __attribute__((ext_vector_type(4)));
 constexpr int MMA_PITCH_PAD = 16;            // staged digit row: 2k + 16 bytes, so that the 16-byte reads of
                                              // 8 consecutive batch rows fall in distinct banks
 constexpr int MMA_STAGE_BYTES = 80 * 1024;   // staged digits, at most (10 chunks of 16 bytes per thread)
-constexpr int MMA_CPITCH = 144;              // LDS bytes per row of a code tile (128 + 16)
-constexpr int MMA_TILE_BYTES = 16 * MMA_CPITCH;
 constexpr int MMA_MAX_ITEMS = 256;           // items per workgroup: at most 8 tiles of 4 per wave
 constexpr size_t MMA_LDS_LIMIT = 160 * 1024;
 
@@ -203,40 +182,15 @@ __global__ __launch_bounds__(512) void k_qgemv_mma(const uint8_t* __restrict__ c
         if (i < mine) {                                      // uniform
             const int t = tile_of(i);
             const int rt = t / tpr, tb = t - rt * tpr;
-            // the tile to this wave's LDS area: rows lane / 8 and 8 + lane / 8,
-            // bytes 16 (lane % 8) .. of the 128 (LDS accesses of a wave run in order)
-            *reinterpret_cast<mma_v4u*>(ctile + (lane >> 3) * MMA_CPITCH + 16 * (lane & 7)) = ct[i][0];
-            *reinterpret_cast<mma_v4u*>(ctile + (8 + (lane >> 3)) * MMA_CPITCH + 16 * (lane & 7)) = ct[i][1];
+            mma_put_tile(ctile, lane, ct[i][0], ct[i][1]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int m = 4 * i + j;
                 request(m + 1, (m + 1) & 1);
-                const uint4(&d)[4] = dg[m & 1];
-                const float4(&tq)[2] = tb2[m & 1];
-                const uint8_t* cr = ctile + r16 * MMA_CPITCH + 32 * j;
-                const uint2 cd = *reinterpret_cast<const uint2*>(cr + 8 * kq);
-                const uint32_t pv = *reinterpret_cast<const uint32_t*>(cr + (kq > 0 ? 8 * kq - 4 : 0));
-                const uint32_t prev = kq > 0 ? pv : 0u;      // a block starts the trellis at state 0
-                uint32_t P0[4], P1[4];
-                planes_of(cd.x, prev, P0);
-                planes_of(cd.y, cd.x, P1);
-                const mma_v4i b0 = {(int)P0[0], (int)P0[1], (int)P0[2], (int)P0[3]};
-                const mma_v4i b1 = {(int)P1[0], (int)P1[1], (int)P1[2], (int)P1[3]};
-                mma_v4i H = {0, 0, 0, 0}, L = {0, 0, 0, 0};
-                H = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(mma_v4i, d[0]), b0, H, 0, 0, 0);
-                L = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(mma_v4i, d[1]), b0, L, 0, 0, 0);
-                H = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(mma_v4i, d[2]), b1, H, 0, 0, 0);
-                L = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(mma_v4i, d[3]), b1, L, 0, 0, 0);
                 // this lane: batch rows 4 kq .. 4 kq + 3 of weight row 16 rt + r16
                 const int blk = 4 * tb + j;
                 const float sw = blk < nbk ? h2f(swt[(16 * rt + r16) * nbk4 + blk]) : 0.0f;   // uniform test
-                const float tx[4] = {tq[0].x, tq[0].z, tq[1].x, tq[1].z};
-                const float ty[4] = {tq[0].y, tq[0].w, tq[1].y, tq[1].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float f = (float)(H[e] * 256 + L[e]);
-                    acc[e] = fmaf(fmaf(f, tx[e], ty[e]), sw, acc[e]);
-                }
+                mma_block(ctile, r16, kq, j, dg[m & 1], tb2[m & 1], sw, acc);
             }
             // a tile's running sums go to the wave's slot of its row tile; they
             // carry on into the next tile of the same row tile (the last store

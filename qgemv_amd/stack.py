@@ -25,13 +25,18 @@ ORDER = ("qkv", "o", "gu", "down")
 
 class Stack:
     def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_Q16,
-                 fused: bool = True, carry: bool = False):
+                 fused: bool = True, carry: bool = False, split_above: int | None = None):
         import torch
         if carry and not fused:
             raise ValueError("carried-state codes run on the fused path only")
         # random bytes are valid paths of both the per-block and the
         # carried-state trellis; carry selects how the stages read them
         self.cflag = L.PG_FLAG_CARRY_STATE if carry else 0
+        # fused path: stages with k above this run as rotation + product
+        # (pg_fwht_rotate_ex, pg_qgemv) instead of one pg_rot_qgemv
+        if split_above is not None and carry:
+            raise ValueError("carried-state codes run on the fused path only")
+        self.split_above = split_above
         self.shapes = synth.merged_shapes(shapes)
         self.raw_shapes = shapes
         self.layers = layers
@@ -85,6 +90,12 @@ class Stack:
                     continue
                 prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
                 n_prev = self.shapes[prev][0]
+                if self.split_above is not None and k > self.split_above:
+                    L.pg_fwht_rotate_ex(self.out[prev], L.PG_F32, n_prev, self.xrot, L.PG_Q16, self.signs[layer][site],
+                                        b, k, L.PG_FLAG_RMSNORM, stream)
+                    L.pg_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.xrot, L.PG_Q16, b,
+                               self.out[site], stream)
+                    continue
                 L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.out[prev], L.PG_F32,
                                n_prev, self.signs[layer][site], L.PG_FLAG_RMSNORM | self.cflag, b, self.out[site],
                                stream)

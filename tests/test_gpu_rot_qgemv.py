@@ -1,5 +1,7 @@
 """GPU parity of the fused stage pg_rot_qgemv (RMS normalisation + rotation +
-product in one launch) against the oracle's fp64 chain of the same steps."""
+product in one launch) against the oracle's fp64 chain of the same steps,
+for both of its kernels: v_dot4 (batch 1..3, activations quantised per 32
+values) and the int8 matrix cores (batch 4..8, per 128-block)."""
 import numpy as np
 import pytest
 
@@ -10,6 +12,18 @@ from qgemv_amd.stack import Stack
 from tests.helpers import TOL, dev, encoded_qwen, host, oracle_chain, rel_err, rel_err_rows
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["auto", "vdot", "mma"])
+def kernel(request, monkeypatch):
+    """Which kernel pg_rot_qgemv runs: its own choice by batch, or one forced
+    through PG_FUSED_KERNEL (the matrix-core kernel takes k <= 4096 only and
+    leaves larger k to the v_dot4 kernel)."""
+    if request.param == "auto":
+        monkeypatch.delenv("PG_FUSED_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("PG_FUSED_KERNEL", request.param)
+    return request.param
 
 
 def _run(codes, scales, x, x_dt, ldx, k, sb, flags):
@@ -23,7 +37,7 @@ def _run(codes, scales, x, x_dt, ldx, k, sb, flags):
 
 
 @pytest.mark.parametrize("name", ["q", "o", "gate", "down"])
-def test_fp16_input_no_norm(name):
+def test_fp16_input_no_norm(name, kernel):
     codes, scales = encoded_qwen(name)
     k = codes.shape[1] * 4
     x = synth.activations_fp16(1, k)
@@ -33,10 +47,10 @@ def test_fp16_input_no_norm(name):
     assert rel_err(y, ref) <= TOL
 
 
-@pytest.mark.parametrize("batch", [1, 2, 3, 8])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("n,k,ldx", [(33, 128, 128), (100, 640, 700), (512, 2560, 6144), (64, 9728, 19456),
                                      (300, 4096, 4096), (40, 16384, 16384), (2000, 2560, 2560)])
-def test_rmsnorm_strided_fp32_input(n, k, ldx, batch):
+def test_rmsnorm_strided_fp32_input(n, k, ldx, batch, kernel):
     rng = np.random.default_rng(n + k + batch)
     codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
     scales = synth.random_scale_bits(n, k, n)
@@ -51,7 +65,7 @@ def test_rmsnorm_strided_fp32_input(n, k, ldx, batch):
 
 
 @pytest.mark.parametrize("batch", [1, 5])
-def test_fp16_input_rmsnorm_and_ragged_rows(batch):
+def test_fp16_input_rmsnorm_and_ragged_rows(batch, kernel):
     rng = np.random.default_rng(11 + batch)
     n, k = 1001, 1152
     codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
@@ -63,7 +77,7 @@ def test_fp16_input_rmsnorm_and_ragged_rows(batch):
     assert np.max(rel_err_rows(y, ref)) <= TOL
 
 
-def test_zero_input_gives_zero_output():
+def test_zero_input_gives_zero_output(kernel):
     n, k = 96, 512
     rng = np.random.default_rng(5)
     codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
@@ -89,9 +103,10 @@ def test_fused_chain_matches_oracle(shapes_fn, layers):
     assert np.array_equal(d2.view(np.uint32), got.view(np.uint32))
 
 
-def test_fused_graph_replays_match_eager():
+@pytest.mark.parametrize("batch", [1, 8])
+def test_fused_graph_replays_match_eager(batch):
     import torch
-    st = Stack(synth.qwen3_4b_shapes(), 3, fused=True)
+    st = Stack(synth.qwen3_4b_shapes(), 3, batch=batch, fused=True)
     eager = host(st.token()).copy()
     st.capture()
     for i in range(4):
