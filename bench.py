@@ -206,12 +206,14 @@ def run_stack(args):
 
 
 def run_qgemm(stream_iters: int = 10):
-    """Prompt path on the matrix cores: pg_qgemm on the Qwen3-4B layer-0
+    """Prompt path on the matrix cores: pg_qgemm_ex on the Qwen3-4B layer-0
     launch groups (random codes and scales as in the stack), X = bf16 N(0,1)
-    rows rotated once by pg_fwht_rotate (bf16 -> bf16), at m = 512 and 4096.
-    Each product is timed alone with HIP events on the launch stream over
-    `stream_iters` back-to-back calls; the fraction is 2 m n k per second over
-    the 2.5 PFLOP/s dense bf16 peak."""
+    rows rotated once by pg_fwht_rotate (bf16 -> bf16), at m = 512 and 4096,
+    with the workspace pg_qgemm_workspace_bytes asks for (allocated before the
+    timed calls; shapes that fill the chip with tiles ask for none and run
+    unsplit).  Each product is timed alone with HIP events on the launch
+    stream over `stream_iters` back-to-back calls, the split sum included;
+    the fraction is 2 m n k per second over the 2.5 PFLOP/s dense bf16 peak."""
     import numpy as np
     import torch
 
@@ -223,7 +225,7 @@ def run_qgemm(stream_iters: int = 10):
     site_no = {"qkv": 0, "o": 1, "gu": 2, "down": 3}
     stream = torch.cuda.current_stream()
     out = {"bound": "mfma", "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16 x bf16 -> f32",
-           "kernel": "k_qgemm_v2 (pg_qgemm)", "workload": "Qwen3-4B layer-0 launch groups qkv/o/gu/down, "
+           "kernel": "k_qgemm_v2 + k_qgemm_sum (pg_qgemm_ex)", "workload": "Qwen3-4B layer-0 launch groups qkv/o/gu/down, "
            "random trellis bitstreams, bf16 N(0,1) rows", "per_m": {}}
     for m in (512, 4096):
         tot_flop = tot_us = 0.0
@@ -237,21 +239,24 @@ def run_qgemm(stream_iters: int = 10):
             sb = torch.from_numpy(synth.site_sign_bits(0, site_no[site], k)).cuda()
             q.pg_fwht_rotate(xb, q.PG_BF16, xr, q.PG_BF16, sb, m, k, 0)
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            wsb = q.pg_qgemm_workspace_bytes(n, k, m)
+            ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device="cuda")
             for _ in range(2):
-                q.pg_qgemm(cd, sc, n, k, xr, m, y)
+                q.pg_qgemm_ex(cd, sc, n, k, xr, m, y, ws, wsb)
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(stream_iters):
-                q.pg_qgemm(cd, sc, n, k, xr, m, y)
+                q.pg_qgemm_ex(cd, sc, n, k, xr, m, y, ws, wsb)
             e1.record(stream)
             torch.cuda.synchronize()
             us = 1e3 * e0.elapsed_time(e1) / stream_iters
             flop = 2.0 * m * n * k
             tf = flop / (us * 1e-6) / 1e12
+            part = (m * n + 3) // 4 * 4 * 4
             per[site] = {"n": n, "k": k, "us": round(us, 2), "tflops": round(tf, 1),
-                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4)}
+                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "k_splits": 1 + wsb // part}
             tot_flop += flop
             tot_us += us
         tf = tot_flop / (tot_us * 1e-6) / 1e12

@@ -246,6 +246,29 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
 int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
              const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
 
+/* pg_qgemm with a caller-owned device workspace, which lets the product
+ * split K when the output tiles alone would leave compute units idle
+ * (small m, or few weight rows against a long k): each split sums a range of
+ * whole 128-blocks, split 0 into y and the others into the workspace, and a
+ * second launch adds the parts to y in split order.
+ *   workspace        device, 16-byte aligned, or NULL (then workspace_bytes
+ *                    must be 0 and the call is pg_qgemm); it may not overlap
+ *                    codes, scales, x_rot_bf16 or y.  Its contents on entry
+ *                    do not matter; on return they are unspecified.
+ *   workspace_bytes  its size; pg_qgemm_workspace_bytes(n, k, m) bytes allow
+ *                    the full split, fewer bytes fewer splits (none below one
+ *                    part of m * n floats, rounded up to 4).
+ * Results may differ from pg_qgemm's in the last bits (another summation
+ * order), but for a given shape, workspace size and device the order is
+ * fixed: repeated calls are bitwise identical. */
+int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                const uint16_t* x_rot_bf16, int64_t m, float* y, void* workspace,
+                size_t workspace_bytes, pg_stream_t stream);
+
+/* Workspace bytes that give pg_qgemm_ex its full split of K for this shape on
+ * the current device (0: it would not split; 0 as well for invalid sizes). */
+size_t pg_qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m);
+
 #ifdef __cplusplus
 }
 #endif

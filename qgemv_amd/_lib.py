@@ -23,7 +23,8 @@ PG_FLAG_CARRY_STATE = 2
 
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
            "pg_encode", "pg_encode_ex", "pg_decode_ex",
-           "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm")
+           "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm",
+           "pg_qgemm_ex", "pg_qgemm_workspace_bytes")
 
 
 class PgError(RuntimeError):
@@ -78,6 +79,10 @@ def lib():
         L.pg_rot_qgemv.argtypes = [vp, vp, i64, i64, vp, i32, i64, vp, u32, i32, vp, vp]
         L.pg_qgemm.restype = i32
         L.pg_qgemm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+        L.pg_qgemm_ex.restype = i32
+        L.pg_qgemm_ex.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, ctypes.c_size_t, vp]
+        L.pg_qgemm_workspace_bytes.restype = ctypes.c_size_t
+        L.pg_qgemm_workspace_bytes.argtypes = [i64, i64, i64]
         _LIB = L
     return _LIB
 
@@ -184,3 +189,13 @@ def pg_rot_qgemv(codes, scales, n: int, k: int, x, x_dtype: int, ldx: int, sign_
 
 def pg_qgemm(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, stream=None) -> None:
     _check(lib().pg_qgemm(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot_bf16), m, _ptr(y), _stream(stream)))
+
+
+def pg_qgemm_ex(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, workspace, workspace_bytes: int,
+                stream=None) -> None:
+    _check(lib().pg_qgemm_ex(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot_bf16), m, _ptr(y), _ptr(workspace),
+                             workspace_bytes, _stream(stream)))
+
+
+def pg_qgemm_workspace_bytes(n: int, k: int, m: int) -> int:
+    return lib().pg_qgemm_workspace_bytes(n, k, m)

@@ -180,6 +180,18 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
 
 int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,
              int64_t m, float* y, pg_stream_t stream) {
+    return pg_qgemm_ex(codes, scales, n, k, x_rot_bf16, m, y, nullptr, 0, stream);
+}
+
+size_t pg_qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m) {
+    if (n < 1 || k < 128 || k % 128 != 0 || k > (int64_t)1 << 24 || n > (int64_t)1 << 30 || m < 1 ||
+        m > ((int64_t)1 << 30))
+        return 0;
+    return pg::qgemm_workspace_bytes(n, k, m);
+}
+
+int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,
+                int64_t m, float* y, void* workspace, size_t workspace_bytes, pg_stream_t stream) {
     pg::clear_error();
     PG_TRY(check_nk(n, k));
     if (m < 1 || m > ((int64_t)1 << 30)) return pg::fail(PG_ERR_INVALID_ARG, "m must be >= 1 (got %lld)", (long long)m);
@@ -187,7 +199,22 @@ int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
     PG_TRY(check_ptr(scales, 2, "scales"));
     PG_TRY(check_ptr(x_rot_bf16, 16, "x_rot_bf16"));
     PG_TRY(check_ptr(y, 16, "y"));
-    return pg::launch_qgemm(codes, scales, n, k, x_rot_bf16, m, y, stream);
+    if (!workspace && workspace_bytes) return pg::fail(PG_ERR_INVALID_ARG, "workspace is null but workspace_bytes > 0");
+    if (workspace) {
+        PG_TRY(check_ptr(workspace, 16, "workspace"));
+        // the workspace may not overlap any operand
+        const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + workspace_bytes;
+        const struct { const void* p; size_t bytes; const char* name; } ops[] = {
+            {codes, (size_t)n * (size_t)(k / 4), "codes"},
+            {scales, (size_t)n * (size_t)(k / 128) * 2, "scales"},
+            {x_rot_bf16, (size_t)m * (size_t)k * 2, "x_rot_bf16"},
+            {y, (size_t)m * (size_t)n * 4, "y"}};
+        for (const auto& o : ops) {
+            const uintptr_t a = (uintptr_t)o.p;
+            if (w0 < a + o.bytes && a < w1) return pg::fail(PG_ERR_INVALID_ARG, "workspace overlaps %s", o.name);
+        }
+    }
+    return pg::launch_qgemm(codes, scales, n, k, x_rot_bf16, m, y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

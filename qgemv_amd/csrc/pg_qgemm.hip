@@ -4,6 +4,8 @@
 //
 // Method: "Pingala-8" landing page, section "How it works" (the trellis
 // decode); bit layout in include/pingala.h.
+#include <algorithm>
+
 #include "pg_device.h"
 
 namespace pg {
@@ -140,6 +142,9 @@ __global__ __launch_bounds__(256) void k_qgemm_v1(const uint8_t* __restrict__ co
 //     planes (planes_of), transposes them to per-group byte order and turns
 //     P = (level + 7) / 2 into bf16 bits with two byte-permute lookups;
 //   - at the end of each 128-block adds scale * (block sum) to the result.
+// Split K: workgroup index t covers tile t % tiles over the 128-blocks
+// [s nbk / S, (s + 1) nbk / S) of split s = t / tiles; split 0 writes y,
+// split s > 0 writes part s - 1 of the workspace (k_qgemm_sum adds them).
 // LDS rows are 128 bytes; 16-byte chunk c of row r sits at c ^ ((r / 2) & 7),
 // so that the 16 rows an operand read touches at once fall on distinct banks.
 constexpr int Q2_BM = 256, Q2_BN = 128, Q2_BK = 64;
@@ -150,7 +155,8 @@ __device__ __forceinline__ int q2_chunk(int r, int c) { return c ^ ((r >> 1) & 7
 __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ codes,
                                                   const uint16_t* __restrict__ scales, int n, int k,
                                                   const uint16_t* __restrict__ x, int m,
-                                                  float* __restrict__ y, int tiles_n, int remap) {
+                                                  float* __restrict__ y, int tiles_n, int remap, int tiles,
+                                                  int splits, float* __restrict__ ws, int64_t pstride) {
     // one object per buffer, and the step loop unrolled by 6 so that every
     // access names its buffer statically: the compiler then sees that the
     // direct copies in flight never touch the buffers being read or written
@@ -159,15 +165,22 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
     __shared__ __attribute__((aligned(16))) uint8_t xs2[Q2_XBYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ws0[Q2_WBYTES];      // levels, 128 rows x 128 B
     __shared__ __attribute__((aligned(16))) uint8_t ws1[Q2_WBYTES];
-    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(m), "s"(y), "s"(tiles_n), "s"(remap));
+    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(m), "s"(y), "s"(tiles_n), "s"(remap),
+                 "s"(tiles), "s"(splits), "s"(ws), "s"(pstride));
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     // tiles of one XCD are consecutive in (n, m) order, so that they share X rows in L2
     int t = blockIdx.x;
     if (remap) t = (t & 7) * (gridDim.x >> 3) + (t >> 3);
+    const int split = t / tiles;
+    t -= split * tiles;
     const int n0 = (t % tiles_n) * Q2_BN, m0 = (t / tiles_n) * Q2_BM;
-    const int kg = k >> 2, nbk = k >> 7, steps = k / Q2_BK;
+    const int kg = k >> 2, nbk = k >> 7;
+    // this split's steps [st0, st_end): whole 128-blocks, so st0 is even
+    const int st0 = 2 * (int)((int64_t)split * nbk / splits);
+    const int st_end = 2 * (int)((int64_t)(split + 1) * nbk / splits);
+    float* __restrict__ out = split == 0 ? y : ws + (int64_t)(split - 1) * pstride;
 
     // X copies: wave w, copy i covers slots (4 w + i) * 64 + lane; slot j is
     // row j / 8, chunk position j % 8, which holds logical chunk q2_chunk(row, j % 8)
@@ -234,10 +247,10 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
         scol[j] = col < n ? col : n - 1;
     }
 
-    // prologue: codes and X of steps 0 and 1, levels of step 0
-    const uint32_t c0 = csrc[0];
-    copy_x(0, xs0);
-    const int s1 = steps > 1 ? 1 : 0;
+    // prologue: codes and X of steps st0 and st0 + 1, levels of step st0
+    const uint32_t c0 = csrc[4 * st0];
+    copy_x(st0, xs0);
+    const int s1 = st0 + 1;                             // a split holds at least one block
     uint32_t c1 = csrc[4 * s1];
     copy_x(s1, xs1);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -257,7 +270,7 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
         uint8_t* wcur = j6 % 2 == 0 ? ws0 : ws1;
         uint8_t* wnext = j6 % 2 == 0 ? ws1 : ws0;
         constexpr bool half2 = (j6 & 1) != 0;                   // second half of a 128-block
-        const int sn = st + 2 < steps ? st + 2 : steps - 1;
+        const int sn = st + 2 < st_end ? st + 2 : st_end - 1;
         const uint32_t c2 = csrc[4 * sn];
         copy_x(sn, xnext2);
         if (!half2)
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
         // copies
         if (half2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(7));
-        if (st + 1 < steps) decode(!half2, c1, wnext);           // levels of step st + 1
+        if (st + 1 < st_end) decode(!half2, c1, wnext);          // levels of step st + 1
         c1 = c2;
         if (half2) {                                            // end of a 128-block
 #pragma unroll
@@ -305,13 +318,13 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
         }
         lds_barrier();                                          // level writes and operand reads done
     };
-    for (int st = 0; st < steps; st += 6) {                     // steps is even (k % 128 == 0)
+    for (int st = st0; st < st_end; st += 6) {                  // whole blocks: an even count of steps
         body(std::integral_constant<int, 0>(), st);
         body(std::integral_constant<int, 1>(), st + 1);
-        if (st + 2 >= steps) break;
+        if (st + 2 >= st_end) break;
         body(std::integral_constant<int, 2>(), st + 2);
         body(std::integral_constant<int, 3>(), st + 3);
-        if (st + 4 >= steps) break;
+        if (st + 4 >= st_end) break;
         body(std::integral_constant<int, 4>(), st + 4);
         body(std::integral_constant<int, 5>(), st + 5);
     }
@@ -325,25 +338,87 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < m) y[(int64_t)row * n + col] = acc[i][j][r];
+                if (row < m) out[(int64_t)row * n + col] = acc[i][j][r];
             }
         }
 }
 
+// y += part 0 + part 1 + ... (parts of pstride floats, 16-byte aligned), in
+// that order for every element: four values per thread, the thread past the
+// last whole quad takes the count % 4 tail.
+__global__ __launch_bounds__(256) void k_qgemm_sum(float* __restrict__ y, const float* __restrict__ ws,
+                                                   int64_t count, int64_t pstride, int parts) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x, nq = count >> 2;
+    if (q < nq) {
+        float4 a = reinterpret_cast<const float4*>(y)[q];
+        for (int p = 0; p < parts; ++p) {
+            const float4 b = reinterpret_cast<const float4*>(ws + (int64_t)p * pstride)[q];
+            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+        }
+        reinterpret_cast<float4*>(y)[q] = a;
+    } else if (q == nq) {
+        for (int64_t i = 4 * nq; i < count; ++i) {
+            float a = y[i];
+            for (int p = 0; p < parts; ++p) a += ws[(int64_t)p * pstride + i];
+            y[i] = a;
+        }
+    }
+}
+
 }  // namespace
 
+// Splits of K for the pipelined kernel (1 = none), from a cost model in
+// microseconds fitted to kernel timings of the Qwen3-4B-shaped launches at
+// m = 512 and 4096 (split counts 1..8 forced): the workgroups run in rounds
+// of one per compute unit (the kernel's LDS holds one workgroup per unit);
+// a round costs 10 us (start, pipeline fill and drain, output stores) plus
+// 2.2 us per 128-block of the split; a split adds the sum launch, 2 us plus
+// S + 1 reads or writes of m n fp32 values at 5 TB/s.  A split is taken when
+// the model gives 8% or more; PG_QGEMM_SPLITS=S forces S (still within the
+// workspace).
+int qgemm_splits(int64_t n, int64_t k, int64_t m, size_t ws_bytes) {
+    const int64_t tiles = ((n + Q2_BN - 1) / Q2_BN) * ((m + Q2_BM - 1) / Q2_BM), nbk = k / 128;
+    const int64_t cus = compute_units(), pstride = (m * n + 3) & ~(int64_t)3;
+    const int64_t fit = 1 + (int64_t)(ws_bytes / ((size_t)pstride * 4));
+    const int64_t smax = std::min<int64_t>(std::min<int64_t>(8, nbk), fit);
+    const char* e = getenv("PG_QGEMM_SPLITS");
+    if (e && atoi(e) >= 1) return (int)std::min<int64_t>(atoi(e), smax);
+    auto cost = [&](int64_t sp) {
+        const double rounds = (double)((tiles * sp + cus - 1) / cus), per = (double)((nbk + sp - 1) / sp);
+        return rounds * (10.0 + 2.2 * per) + (sp > 1 ? 2.0 + (sp + 1) * (double)(m * n) * 4.0 / 5e6 : 0.0);
+    };
+    int64_t best = 1;
+    double cbest = cost(1);
+    for (int64_t sp = 2; sp <= smax; ++sp)
+        if (cost(sp) < cbest) { cbest = cost(sp); best = sp; }
+    return cbest <= 0.92 * cost(1) ? (int)best : 1;
+}
+
+size_t qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m) {
+    const int sp = qgemm_splits(n, k, m, (size_t)-1 / 2);
+    return (size_t)(sp - 1) * (size_t)((m * n + 3) & ~(int64_t)3) * 4;
+}
+
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x,
-                 int64_t m, float* y, pg_stream_t s) {
+                 int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s) {
     const int64_t tn = (n + Q2_BN - 1) / Q2_BN, tm = (m + Q2_BM - 1) / Q2_BM;
     // the pipelined kernel is the product; PG_QGEMM_KERNEL=1 selects the
     // plain one-buffer kernel (kept as a second implementation for tests)
     const char* e = getenv("PG_QGEMM_KERNEL");
     if (!(e && atoi(e) == 1)) {
-        if (tn * tm > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
-        const int remap = (tn * tm) % 8 == 0 ? 1 : 0;
-        hipLaunchKernelGGL(k_qgemm_v2, dim3((unsigned)(tn * tm)), dim3(512), 0, (hipStream_t)s, codes, scales,
-                           (int)n, (int)k, x, (int)m, y, (int)tn, remap);
-        return hip_check(hipGetLastError(), "pg_qgemm launch");
+        const int sp = workspace ? qgemm_splits(n, k, m, ws_bytes) : 1;
+        const int64_t grid = tn * tm * sp, pstride = (m * n + 3) & ~(int64_t)3;
+        if (grid > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
+        const int remap = grid % 8 == 0 ? 1 : 0;
+        hipLaunchKernelGGL(k_qgemm_v2, dim3((unsigned)grid), dim3(512), 0, (hipStream_t)s, codes, scales,
+                           (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)(tn * tm), sp,
+                           static_cast<float*>(workspace), pstride);
+        const int rc = hip_check(hipGetLastError(), "pg_qgemm launch");
+        if (rc != PG_OK || sp == 1) return rc;
+        const int64_t count = m * n, blocks = ((count >> 2) + 1 + 255) / 256;
+        hipLaunchKernelGGL(k_qgemm_sum, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)s, y,
+                           static_cast<const float*>(workspace), count, pstride, sp - 1);
+        return hip_check(hipGetLastError(), "pg_qgemm split sum launch");
     }
     const dim3 grid((unsigned)((n + QG_BN - 1) / QG_BN), (unsigned)((m + QG_BM - 1) / QG_BM));
     if (grid.y > 65535) return fail(PG_ERR_UNSUPPORTED, "m too large");

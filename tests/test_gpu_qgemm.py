@@ -83,3 +83,124 @@ def test_one_hot_column(kernel):
     for i, c in enumerate(cols):
         assert np.array_equal(y[i].astype(np.float64), w[:, c])
     assert not y[len(cols):].any()
+
+
+# ----------------------------------------------------------------- split K
+def _qgemm_ex(codes, scales, xb, ws_bytes=None, guard=0):
+    """pg_qgemm_ex with a workspace of ws_bytes (default: the full split)
+    followed by `guard` float32 values that must stay untouched."""
+    import torch
+    n, kg = codes.shape
+    k = 4 * kg
+    m = xb.shape[0]
+    if ws_bytes is None:
+        ws_bytes = q.pg_qgemm_workspace_bytes(n, k, m)
+    ws = torch.full((ws_bytes // 4 + guard + 4,), 7.0, dtype=torch.float32, device="cuda")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    q.pg_qgemm_ex(dev(codes), dev(scales), n, k, dev(xb), m, y, ws, ws_bytes)
+    torch.cuda.synchronize()
+    if guard:
+        assert (host(ws[ws_bytes // 4:]) == 7.0).all(), "workspace written past workspace_bytes"
+    return host(y)
+
+
+def _case(m, n, k):
+    rng = np.random.default_rng(m * n + k + 1)
+    codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
+    scales = synth.random_scale_bits(n, k, m + n + 1)
+    xb = synth.bf16_activations_bits(m, k, seed=m + 1)
+    return codes, scales, xb
+
+
+@pytest.mark.parametrize("m,n,k", [(100, 256, 2048), (300, 1024, 2560), (1, 5, 640), (512, 2560, 4096)])
+def test_split_k_matches_oracle(m, n, k):
+    """Shapes whose tiles leave compute units idle: pg_qgemm_ex splits K on
+    its own (nonzero workspace) and matches the oracle."""
+    codes, scales, xb = _case(m, n, k)
+    assert q.pg_qgemm_workspace_bytes(n, k, m) > 0
+    y = _qgemm_ex(codes, scales, xb)
+    rows = np.arange(m) if m <= 128 else np.sort(np.random.default_rng(k).choice(m, 64, replace=False))
+    ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb[rows]))
+    assert np.max(rel_err_rows(y[rows], ref)) <= TOL
+
+
+@pytest.mark.parametrize("splits", [2, 3, 8])
+@pytest.mark.parametrize("m,n,k", [(77, 130, 1152), (256, 384, 512), (3, 1, 1024)])
+def test_forced_splits_ragged(m, n, k, splits, monkeypatch):
+    """Split counts forced through PG_QGEMM_SPLITS (capped at the number of
+    128-blocks), on ragged tiles and an m n that is not a multiple of 4 (the
+    sum kernel's scalar tail); the workspace past the parts stays untouched."""
+    monkeypatch.setenv("PG_QGEMM_SPLITS", str(splits))
+    codes, scales, xb = _case(m, n, k)
+    pstride = (m * n + 3) // 4 * 4
+    y = _qgemm_ex(codes, scales, xb, ws_bytes=7 * pstride * 4, guard=64)
+    ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb))
+    assert np.max(rel_err_rows(y, ref)) <= TOL
+
+
+def test_split_k_small_workspace_and_none():
+    """Fewer workspace bytes give fewer splits (one part: two splits) and
+    still the product; no workspace is pg_qgemm, bit for bit."""
+    codes, scales, xb = _case(512, 2560, 4096)
+    m, n = xb.shape[0], codes.shape[0]
+    ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb[:64]))
+    y1 = _qgemm_ex(codes, scales, xb, ws_bytes=m * n * 4, guard=64)
+    assert np.max(rel_err_rows(y1[:64], ref)) <= TOL
+    y0 = _qgemm_ex(codes, scales, xb, ws_bytes=m * n * 4 - 16)   # less than one part: no split
+    assert np.array_equal(y0, _qgemm(codes, scales, xb))
+
+
+def test_split_k_deterministic_and_close_to_unsplit():
+    codes, scales, xb = _case(512, 2560, 9728)
+    a = _qgemm_ex(codes, scales, xb)
+    b = _qgemm_ex(codes, scales, xb)
+    assert np.array_equal(a, b)
+    c = _qgemm(codes, scales, xb)
+    scale = np.max(np.abs(c), axis=1, keepdims=True)
+    assert np.max(np.abs(a - c) / scale) <= 1e-5                 # only the summation order differs
+
+
+def test_split_k_graph_replays():
+    """pg_qgemm_ex (product + split sum, two launches) captured in a HIP graph
+    and replayed three times, eager work between the replays; every replay
+    equals the eager call."""
+    import torch
+    codes, scales, xb = _case(512, 2560, 4096)
+    n, k, m = codes.shape[0], 4 * codes.shape[1], xb.shape[0]
+    cd, sc, xd = dev(codes), dev(scales), dev(xb)
+    wsb = q.pg_qgemm_workspace_bytes(n, k, m)
+    ws = torch.empty((wsb // 4,), dtype=torch.float32, device="cuda")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    q.pg_qgemm_ex(cd, sc, n, k, xd, m, y, ws, wsb)
+    torch.cuda.synchronize()
+    eager = host(y)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        q.pg_qgemm_ex(cd, sc, n, k, xd, m, y, ws, wsb)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.pg_qgemm_ex(cd, sc, n, k, xd, m, y, ws, wsb)
+    for i in range(3):
+        y.fill_(float(i + 1))
+        ws.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), eager), i
+
+
+@pytest.mark.parametrize("m", [512, 4096])
+def test_prompt_shapes_split_sampled_rows(m):
+    """The full-size Qwen3-4B-shaped launches through pg_qgemm_ex with the
+    workspace it asks for (the 2560-row shapes split at m = 512)."""
+    merged = synth.random_layer_merged(0, synth.qwen3_4b_shapes())
+    rng = np.random.default_rng(m + 1)
+    for site, (codes, scales) in merged.items():
+        k = codes.shape[1] * 4
+        xb = synth.bf16_activations_bits(m, k, seed=m + k)
+        y = _qgemm_ex(codes, scales, xb)
+        rows = np.sort(rng.choice(m, 32, replace=False))
+        ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb[rows]))
+        assert np.max(rel_err_rows(y[rows], ref)) <= TOL, site

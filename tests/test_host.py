@@ -54,6 +54,12 @@ def test_codebook_table_matches_oracle():
     lambda: q.pg_qgemv(None, 1 << 20, 8, 256, 1 << 20, 0, 1, 1 << 20, stream=0),            # null
     lambda: q.pg_qgemv((1 << 20) + 4, 1 << 20, 8, 256, 1 << 20, 0, 1, 1 << 20, stream=0),   # misaligned
     lambda: q.pg_qgemm(1 << 20, 1 << 20, 8, 256, 1 << 20, 0, 1 << 20, stream=0),            # m < 1
+    lambda: q.pg_qgemm_ex(1 << 20, 1 << 20, 8, 256, 1 << 20, 4, 1 << 22, None, 64, stream=0),        # null ws
+    lambda: q.pg_qgemm_ex(1 << 20, 1 << 20, 8, 256, 1 << 20, 4, 1 << 22, (1 << 24) + 8, 64, stream=0),  # ws align
+    lambda: q.pg_qgemm_ex(1 << 20, 1 << 20, 8, 256, 1 << 21, 4, 1 << 22, (1 << 22) + 64, 256, stream=0),  # ws on y
+    lambda: q.pg_qgemm_ex(1 << 20, 1 << 20, 8, 256, 1 << 21, 4, 1 << 22, (1 << 21) + 1024, 64, stream=0),  # on x
+    lambda: q.pg_qgemm_ex(1 << 20, 1 << 23, 8, 256, 1 << 21, 4, 1 << 22, 1 << 23, 64, stream=0),      # on scales
+    lambda: q.pg_qgemm_ex(1 << 20, 1 << 20, 8, 256, 1 << 21, 0, 1 << 22, 1 << 23, 64, stream=0),      # m < 1
     lambda: q.pg_decode(1 << 20, (1 << 20) + 1, 8, 256, 1 << 20, stream=0),                 # scales odd
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 20, 0, 1 << 20, 1, 256, 0, stream=0),         # overlap
     lambda: q.pg_fwht_rotate(1 << 20, 0, 1 << 22, 5, 1 << 20, 1, 256, 0, stream=0),         # dtype
@@ -147,3 +153,16 @@ def test_carried_state_encoder_rejects_k_beyond_its_lds_survivors():
     with pytest.raises(q.PgError) as ei:
         q.pg_encode_ex(1 << 20, 8, 32768, 1 << 20, q.PG_FLAG_CARRY_STATE, 1 << 20, 1 << 20, stream=0)
     assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
+
+
+def test_qgemm_workspace_bytes():
+    """Whole parts of m n floats (rounded up to 4), at most 7 of them; none
+    for a shape that fills the chip with tiles, none for invalid sizes."""
+    for n, k, m in [(2560, 4096, 512), (2560, 9728, 512), (5, 640, 1), (130, 1152, 77)]:
+        b = q.pg_qgemm_workspace_bytes(n, k, m)
+        part = (m * n + 3) // 4 * 4 * 4
+        assert b > 0 and b % part == 0 and b // part <= min(7, k // 128 - 1), (n, k, m, b)
+    assert q.pg_qgemm_workspace_bytes(19456, 2560, 4096) == 0
+    assert q.pg_qgemm_workspace_bytes(8, 200, 4) == 0
+    assert q.pg_qgemm_workspace_bytes(8, 256, 0) == 0
+    assert q.pg_qgemm_workspace_bytes(0, 256, 4) == 0
