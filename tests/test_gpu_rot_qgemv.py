@@ -1,7 +1,7 @@
 """GPU parity of the fused stage pg_rot_qgemv (RMS normalisation + rotation +
 product in one launch) against the oracle's fp64 chain of the same steps,
-for both of its kernels: v_dot4 (batch 1..3, activations quantised per 32
-values) and the int8 matrix cores (batch 4..8, per 128-block)."""
+for both of its kernels: v_dot4 (batch 1..2, activations quantised per 32
+values) and the int8 matrix cores (batch 3..8, per 128-block)."""
 import numpy as np
 import pytest
 
