@@ -46,8 +46,9 @@
  *   - Device calls are asynchronous on the caller's hipStream_t (0 = the null
  *     stream) and validate all arguments on the host before any launch; on an
  *     invalid argument nothing is launched.  pg_encode_ref is synchronous.
- *   - codes, x, y and w pointers must be 16-byte aligned; scales and
- *     sign_bits 2-byte and 1-byte aligned.
+ *   - codes, x, y, w and workspace pointers must be 16-byte aligned;
+ *     scales and sign_bits at least 2-byte and 1-byte aligned (a call that
+ *     needs more says so in its comment).
  *   - Errors: PG_OK = 0; negative codes below.  pg_last_error() returns a
  *     per-thread message for the last failing call of that thread.
  *   - Results of pg_decode are bit-exact; products accumulate in fp32.
