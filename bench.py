@@ -211,8 +211,8 @@ def run_qgemm(stream_iters: int = 10):
     launch groups (random codes and scales as in the stack), X = bf16 N(0,1)
     rows rotated once by pg_fwht_rotate (bf16 -> bf16), at m = 512 and 4096,
     with the workspace pg_qgemm_workspace_bytes asks for (allocated before the
-    timed calls; shapes that fill the chip with tiles ask for none and run
-    unsplit).  Each product is timed alone with HIP events on the launch
+    timed calls; shapes whose tiles fill the chip in whole rounds ask for none
+    and run unsplit).  Each product is timed alone with HIP events on the launch
     stream over `stream_iters` back-to-back calls, the split sum included;
     the fraction is 2 m n k per second over the 2.5 PFLOP/s dense bf16 peak."""
     import numpy as np
@@ -255,9 +255,8 @@ def run_qgemm(stream_iters: int = 10):
             us = 1e3 * e0.elapsed_time(e1) / stream_iters
             flop = 2.0 * m * n * k
             tf = flop / (us * 1e-6) / 1e12
-            part = (m * n + 3) // 4 * 4 * 4
             per[site] = {"n": n, "k": k, "us": round(us, 2), "tflops": round(tf, 1),
-                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "k_splits": 1 + wsb // part}
+                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "workspace_bytes": wsb}
             tot_flop += flop
             tot_us += us
         tf = tot_flop / (tot_us * 1e-6) / 1e12

@@ -251,16 +251,19 @@ int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
 
 /* pg_qgemm with a caller-owned device workspace, which lets the product
  * split K when the output tiles alone would leave compute units idle
- * (small m, or few weight rows against a long k): each split sums a range of
- * whole 128-blocks, split 0 into y and the others into the workspace, and a
- * second launch adds the parts to y in split order.
+ * (small m, few weight rows against a long k, or a last round of tiles that
+ * fills only part of the chip): the tiles of the split (all of them, or
+ * those of the last round) are each summed over ranges of whole 128-blocks,
+ * split 0 into y and the others into the workspace, and a second launch adds
+ * the parts to y in split order.
  *   workspace        device, 16-byte aligned, or NULL (then workspace_bytes
  *                    must be 0 and the call is pg_qgemm); it may not overlap
  *                    codes, scales, x_rot_bf16 or y.  Its contents on entry
  *                    do not matter; on return they are unspecified.
  *   workspace_bytes  its size; pg_qgemm_workspace_bytes(n, k, m) bytes allow
- *                    the full split, fewer bytes fewer splits (none below one
- *                    part of m * n floats, rounded up to 4).
+ *                    the split the library picks for the shape, fewer bytes
+ *                    a smaller split or none (each further part takes 128 KiB
+ *                    per split tile of 256 x 128 outputs).
  * Results may differ from pg_qgemm's in the last bits (another summation
  * order), but for a given shape, workspace size and device the order is
  * fixed: repeated calls are bitwise identical. */

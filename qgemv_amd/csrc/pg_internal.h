@@ -43,12 +43,17 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
 // (pg_qgemv_mma.hip) batched product on PG_Q16 activations, matrix cores
 int launch_qgemv_mma(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint8_t* xq,
                      int batch, float* y, pg_stream_t s);
-// (pg_qgemm.hip) the prompt product; with a workspace it may split K
-// (qgemm_splits picks the split count, qgemm_workspace_bytes the bytes that
-// allow its full split)
+// (pg_qgemm.hip) the prompt product; with a workspace it may split K:
+// the first t_full output tiles whole, the others `splits` ways
+// (qgemm_plan picks the plan, qgemm_workspace_bytes the bytes that allow the
+// plan it picks with no workspace limit)
+struct QgPlan {
+    int64_t t_full;
+    int splits;
+};
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const uint16_t* x, int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s);
-int qgemm_splits(int64_t n, int64_t k, int64_t m, size_t ws_bytes);
+QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes);
 size_t qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m);
 // (pg_encode.hip)
 int launch_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,

@@ -142,9 +142,15 @@ __global__ __launch_bounds__(256) void k_qgemm_v1(const uint8_t* __restrict__ co
 //     planes (planes_of), transposes them to per-group byte order and turns
 //     P = (level + 7) / 2 into bf16 bits with two byte-permute lookups;
 //   - at the end of each 128-block adds scale * (block sum) to the result.
-// Split K: workgroup index t covers tile t % tiles over the 128-blocks
-// [s nbk / S, (s + 1) nbk / S) of split s = t / tiles; split 0 writes y,
-// split s > 0 writes part s - 1 of the workspace (k_qgemm_sum adds them).
+// Split K: workgroups 0 .. t_full - 1 take tiles 0 .. t_full - 1 whole; the
+// workgroups after them take the other nrem = tiles - t_full tiles S ways,
+// workgroup t_full + i covering tile t_full + i % nrem over the 128-blocks
+// [s nbk / S, (s + 1) nbk / S) of split s = i / nrem.  Split 0 writes y;
+// split s > 0 writes its 256 x 128 block to part s - 1 of the workspace
+// ([S - 1][nrem][256][128] fp32), which k_qgemm_sum then adds to y.  Each
+// range is XCD-grouped by itself (remap bit 0: the whole tiles, bit 1: the
+// splits), so that the whole tiles are dispatched first and the short split
+// workgroups fill the last round.
 // LDS rows are 128 bytes; 16-byte chunk c of row r sits at c ^ ((r / 2) & 7),
 // so that the 16 rows an operand read touches at once fall on distinct banks.
 constexpr int Q2_BM = 256, Q2_BN = 128, Q2_BK = 64;
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
                                                   const uint16_t* __restrict__ scales, int n, int k,
                                                   const uint16_t* __restrict__ x, int m,
                                                   float* __restrict__ y, int tiles_n, int remap, int tiles,
-                                                  int splits, float* __restrict__ ws, int64_t pstride) {
+                                                  int t_full, int splits, float* __restrict__ ws) {
     // one object per buffer, and the step loop unrolled by 6 so that every
     // access names its buffer statically: the compiler then sees that the
     // direct copies in flight never touch the buffers being read or written
@@ -166,21 +172,39 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
     __shared__ __attribute__((aligned(16))) uint8_t ws0[Q2_WBYTES];      // levels, 128 rows x 128 B
     __shared__ __attribute__((aligned(16))) uint8_t ws1[Q2_WBYTES];
     asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(m), "s"(y), "s"(tiles_n), "s"(remap),
-                 "s"(tiles), "s"(splits), "s"(ws), "s"(pstride));
+                 "s"(tiles), "s"(t_full), "s"(splits), "s"(ws));
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     // tiles of one XCD are consecutive in (n, m) order, so that they share X rows in L2
-    int t = blockIdx.x;
-    if (remap) t = (t & 7) * (gridDim.x >> 3) + (t >> 3);
-    const int split = t / tiles;
-    t -= split * tiles;
+    int t, split = 0, nsplit = 1;
+    const int nrem = tiles - t_full;
+    if ((int)blockIdx.x < t_full) {
+        t = blockIdx.x;
+        if (remap & 1) t = (t & 7) * (t_full >> 3) + (t >> 3);
+    } else {
+        int i = blockIdx.x - t_full;
+        const int cnt = gridDim.x - t_full;
+        if (remap & 2) i = (i & 7) * (cnt >> 3) + (i >> 3);
+        split = i / nrem;
+        t = t_full + (i - split * nrem);
+        nsplit = splits;
+    }
     const int n0 = (t % tiles_n) * Q2_BN, m0 = (t / tiles_n) * Q2_BM;
     const int kg = k >> 2, nbk = k >> 7;
     // this split's steps [st0, st_end): whole 128-blocks, so st0 is even
-    const int st0 = 2 * (int)((int64_t)split * nbk / splits);
-    const int st_end = 2 * (int)((int64_t)(split + 1) * nbk / splits);
-    float* __restrict__ out = split == 0 ? y : ws + (int64_t)(split - 1) * pstride;
+    const int st0 = 2 * (int)((int64_t)split * nbk / nsplit);
+    const int st_end = 2 * (int)((int64_t)(split + 1) * nbk / nsplit);
+    // output: y itself, or this split's tile block of the workspace
+    float* __restrict__ out = y;
+    int64_t ld = n;
+    int rb = 0, cb = 0;
+    if (split > 0) {
+        out = ws + ((int64_t)(split - 1) * nrem + (t - t_full)) * (Q2_BM * Q2_BN);
+        ld = Q2_BN;
+        rb = m0;
+        cb = n0;
+    }
 
     // X copies: wave w, copy i covers slots (4 w + i) * 64 + lane; slot j is
     // row j / 8, chunk position j % 8, which holds logical chunk q2_chunk(row, j % 8)
@@ -338,86 +362,132 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < m) out[(int64_t)row * n + col] = acc[i][j][r];
+                if (row < m) out[(int64_t)(row - rb) * ld + (col - cb)] = acc[i][j][r];
             }
         }
 }
 
-// y += part 0 + part 1 + ... (parts of pstride floats, 16-byte aligned), in
-// that order for every element: four values per thread, the thread past the
-// last whole quad takes the count % 4 tail.
-__global__ __launch_bounds__(256) void k_qgemm_sum(float* __restrict__ y, const float* __restrict__ ws,
-                                                   int64_t count, int64_t pstride, int parts) {
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x, nq = count >> 2;
-    if (q < nq) {
-        float4 a = reinterpret_cast<const float4*>(y)[q];
-        for (int p = 0; p < parts; ++p) {
-            const float4 b = reinterpret_cast<const float4*>(ws + (int64_t)p * pstride)[q];
-            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-        }
-        reinterpret_cast<float4*>(y)[q] = a;
-    } else if (q == nq) {
-        for (int64_t i = 4 * nq; i < count; ++i) {
-            float a = y[i];
-            for (int p = 0; p < parts; ++p) a += ws[(int64_t)p * pstride + i];
-            y[i] = a;
-        }
+// y += part 0 + part 1 + ... over the split tiles: thread q takes values
+// 4 (q % 8192) .. + 3 of tile block q / 8192 (tile t_full + q / 8192, 256 x
+// 128 values, row-major) from every part in part order; values outside y
+// (ragged edges) are skipped.
+__global__ __launch_bounds__(256) void k_qgemm_sum(float* __restrict__ y, const float* __restrict__ ws, int m,
+                                                   int n, int tiles_n, int t_full, int nrem, int parts) {
+    constexpr int TB = Q2_BM * Q2_BN;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)nrem * (TB / 4)) return;
+    const int u = (int)(q / (TB / 4)), e = 4 * (int)(q % (TB / 4));
+    const int t = t_full + u;
+    const int row = (t / tiles_n) * Q2_BM + e / Q2_BN, col = (t % tiles_n) * Q2_BN + e % Q2_BN;
+    if (row >= m || col >= n) return;
+    const float* src = ws + (int64_t)u * TB + e;
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float* yr = y + (int64_t)row * n + col;
+    const bool whole = (n & 3) == 0 && col + 4 <= n;
+    if (whole) {
+        a = *reinterpret_cast<const float4*>(yr);
+    } else {
+        a.x = yr[0];
+        if (col + 1 < n) a.y = yr[1];
+        if (col + 2 < n) a.z = yr[2];
+        if (col + 3 < n) a.w = yr[3];
+    }
+    for (int p = 0; p < parts; ++p) {
+        const float4 b = *reinterpret_cast<const float4*>(src + (int64_t)p * nrem * TB);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    if (whole) {
+        *reinterpret_cast<float4*>(yr) = a;
+    } else {
+        yr[0] = a.x;
+        if (col + 1 < n) yr[1] = a.y;
+        if (col + 2 < n) yr[2] = a.z;
+        if (col + 3 < n) yr[3] = a.w;
     }
 }
 
 }  // namespace
 
-// Splits of K for the pipelined kernel (1 = none), from a cost model in
-// microseconds fitted to kernel timings of the Qwen3-4B-shaped launches at
-// m = 512 and 4096 (split counts 1..8 forced): the workgroups run in rounds
-// of one per compute unit (the kernel's LDS holds one workgroup per unit);
-// a round costs 10 us (start, pipeline fill and drain, output stores) plus
-// 2.2 us per 128-block of the split; a split adds the sum launch, 2 us plus
-// S + 1 reads or writes of m n fp32 values at 5 TB/s.  A split is taken when
-// the model gives 8% or more; PG_QGEMM_SPLITS=S forces S (still within the
-// workspace).
-int qgemm_splits(int64_t n, int64_t k, int64_t m, size_t ws_bytes) {
+// How the pipelined kernel splits K: the first t_full tiles whole, the other
+// tiles `splits` ways (splits = 1: no split, t_full = all tiles).  Chosen by a
+// cost model in microseconds fitted to kernel timings of the Qwen3-4B-shaped
+// launches at m = 512 and 4096 (split counts 1..8 forced): workgroups run in
+// rounds of one per compute unit (the kernel's LDS holds one workgroup per
+// unit); a round costs 10 us (start, pipeline fill and drain, output stores)
+// plus 2.2 us per 128-block of its workgroups; a split adds the sum launch,
+// 2 us plus S + 1 reads or writes of the split tiles' fp32 values at 5 TB/s.
+// The candidates: no split; every tile split S ways; the tiles of the full
+// rounds whole and those of the last, partial round split S ways (run after
+// the full rounds, they fill it).  A split is taken when the model gives 8%
+// or more.  PG_QGEMM_SPLITS=S (every tile) or S:T (tiles T.. only) forces a
+// plan, still within the 128-blocks and the workspace.
+QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes) {
     const int64_t tiles = ((n + Q2_BN - 1) / Q2_BN) * ((m + Q2_BM - 1) / Q2_BM), nbk = k / 128;
-    const int64_t cus = compute_units(), pstride = (m * n + 3) & ~(int64_t)3;
-    const int64_t fit = 1 + (int64_t)(ws_bytes / ((size_t)pstride * 4));
-    const int64_t smax = std::min<int64_t>(std::min<int64_t>(8, nbk), fit);
-    const char* e = getenv("PG_QGEMM_SPLITS");
-    if (e && atoi(e) >= 1) return (int)std::min<int64_t>(atoi(e), smax);
-    auto cost = [&](int64_t sp) {
-        const double rounds = (double)((tiles * sp + cus - 1) / cus), per = (double)((nbk + sp - 1) / sp);
-        return rounds * (10.0 + 2.2 * per) + (sp > 1 ? 2.0 + (sp + 1) * (double)(m * n) * 4.0 / 5e6 : 0.0);
+    const int64_t cus = compute_units();
+    const double tb = (double)Q2_BM * Q2_BN * 4;                   // bytes of a tile block
+    const QgPlan none = {tiles, 1};
+    auto fits = [&](int64_t t_full, int64_t sp) {
+        return sp >= 1 && sp <= std::min<int64_t>(8, nbk) && t_full >= 0 && t_full < tiles &&
+               (double)(sp - 1) * (double)(tiles - t_full) * tb <= (double)ws_bytes;
     };
-    int64_t best = 1;
-    double cbest = cost(1);
-    for (int64_t sp = 2; sp <= smax; ++sp)
-        if (cost(sp) < cbest) { cbest = cost(sp); best = sp; }
-    return cbest <= 0.92 * cost(1) ? (int)best : 1;
+    if (const char* e = getenv("PG_QGEMM_SPLITS")) {
+        long long sp = 0, tf = 0;
+        const int got = sscanf(e, "%lld:%lld", &sp, &tf);
+        if (got >= 1 && sp > 1) {
+            if (got < 2) tf = 0;
+            sp = std::min<long long>(sp, std::min<int64_t>(8, nbk));
+            while (sp > 1 && !fits(tf, sp)) --sp;
+            return sp > 1 ? QgPlan{tf, (int)sp} : none;
+        }
+        if (got >= 1 && sp == 1) return none;
+    }
+    auto rt = [](double blocks) { return 10.0 + 2.2 * blocks; };
+    auto per = [&](int64_t sp) { return (double)((nbk + sp - 1) / sp); };
+    auto sum_cost = [&](int64_t nrem, int64_t sp) { return 2.0 + (double)(sp + 1) * (double)nrem * tb / 5e6; };
+    const double c1 = (double)((tiles + cus - 1) / cus) * rt((double)nbk);
+    QgPlan best = none;
+    double cbest = c1;
+    for (int64_t sp = 2; sp <= 8; ++sp) {
+        if (fits(0, sp)) {                                          // every tile
+            const double c = (double)((tiles * sp + cus - 1) / cus) * rt(per(sp)) + sum_cost(tiles, sp);
+            if (c < cbest) { cbest = c; best = {0, (int)sp}; }
+        }
+        const int64_t full = (tiles / cus) * cus, rem = tiles - full;
+        if (full > 0 && rem > 0 && fits(full, sp)) {                // the last round's tiles
+            const double c = (double)(full / cus) * rt((double)nbk) +
+                             (double)((rem * sp + cus - 1) / cus) * rt(per(sp)) + sum_cost(rem, sp);
+            if (c < cbest) { cbest = c; best = {full, (int)sp}; }
+        }
+    }
+    return cbest <= 0.92 * c1 ? best : none;
 }
 
 size_t qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m) {
-    const int sp = qgemm_splits(n, k, m, (size_t)-1 / 2);
-    return (size_t)(sp - 1) * (size_t)((m * n + 3) & ~(int64_t)3) * 4;
+    const int64_t tiles = ((n + Q2_BN - 1) / Q2_BN) * ((m + Q2_BM - 1) / Q2_BM);
+    const QgPlan p = qgemm_plan(n, k, m, (size_t)-1 / 2);
+    return (size_t)(p.splits - 1) * (size_t)(tiles - p.t_full) * (size_t)(Q2_BM * Q2_BN) * 4;
 }
 
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x,
                  int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s) {
-    const int64_t tn = (n + Q2_BN - 1) / Q2_BN, tm = (m + Q2_BM - 1) / Q2_BM;
+    const int64_t tn = (n + Q2_BN - 1) / Q2_BN, tm = (m + Q2_BM - 1) / Q2_BM, tiles = tn * tm;
     // the pipelined kernel is the product; PG_QGEMM_KERNEL=1 selects the
     // plain one-buffer kernel (kept as a second implementation for tests)
     const char* e = getenv("PG_QGEMM_KERNEL");
     if (!(e && atoi(e) == 1)) {
-        const int sp = workspace ? qgemm_splits(n, k, m, ws_bytes) : 1;
-        const int64_t grid = tn * tm * sp, pstride = (m * n + 3) & ~(int64_t)3;
+        const QgPlan p = workspace ? qgemm_plan(n, k, m, ws_bytes) : QgPlan{tiles, 1};
+        const int64_t nrem = tiles - p.t_full, grid = p.t_full + nrem * p.splits;
         if (grid > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
-        const int remap = grid % 8 == 0 ? 1 : 0;
+        const int remap = (p.t_full % 8 == 0 ? 1 : 0) | ((nrem * p.splits) % 8 == 0 ? 2 : 0);
         hipLaunchKernelGGL(k_qgemm_v2, dim3((unsigned)grid), dim3(512), 0, (hipStream_t)s, codes, scales,
-                           (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)(tn * tm), sp,
-                           static_cast<float*>(workspace), pstride);
+                           (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)tiles, (int)p.t_full, p.splits,
+                           static_cast<float*>(workspace));
         const int rc = hip_check(hipGetLastError(), "pg_qgemm launch");
-        if (rc != PG_OK || sp == 1) return rc;
-        const int64_t count = m * n, blocks = ((count >> 2) + 1 + 255) / 256;
+        if (rc != PG_OK || p.splits == 1) return rc;
+        const int64_t blocks = nrem * (Q2_BM * Q2_BN / 4) / 256;
         hipLaunchKernelGGL(k_qgemm_sum, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)s, y,
-                           static_cast<const float*>(workspace), count, pstride, sp - 1);
+                           static_cast<const float*>(workspace), (int)m, (int)n, (int)tn, (int)p.t_full, (int)nrem,
+                           p.splits - 1);
         return hip_check(hipGetLastError(), "pg_qgemm split sum launch");
     }
     const dim3 grid((unsigned)((n + QG_BN - 1) / QG_BN), (unsigned)((m + QG_BM - 1) / QG_BM));

@@ -124,27 +124,32 @@ def test_split_k_matches_oracle(m, n, k):
     assert np.max(rel_err_rows(y[rows], ref)) <= TOL
 
 
-@pytest.mark.parametrize("splits", [2, 3, 8])
-@pytest.mark.parametrize("m,n,k", [(77, 130, 1152), (256, 384, 512), (3, 1, 1024)])
-def test_forced_splits_ragged(m, n, k, splits, monkeypatch):
-    """Split counts forced through PG_QGEMM_SPLITS (capped at the number of
-    128-blocks), on ragged tiles and an m n that is not a multiple of 4 (the
-    sum kernel's scalar tail); the workspace past the parts stays untouched."""
-    monkeypatch.setenv("PG_QGEMM_SPLITS", str(splits))
+TILE_BYTES = 256 * 128 * 4
+
+
+@pytest.mark.parametrize("plan", ["2", "3", "8", "2:1", "3:5"])
+@pytest.mark.parametrize("m,n,k", [(77, 130, 1152), (256, 384, 512), (3, 1, 1024), (300, 1024, 2560),
+                                   (513, 1030, 1152)])
+def test_forced_splits_ragged(m, n, k, plan, monkeypatch):
+    """Split plans forced through PG_QGEMM_SPLITS: S (every tile split S ways,
+    capped at the number of 128-blocks) or S:T (tiles T.. split, the others
+    whole), on ragged tiles and odd n (the sum kernel's scalar edge); the
+    workspace past the parts stays untouched."""
+    monkeypatch.setenv("PG_QGEMM_SPLITS", plan)
     codes, scales, xb = _case(m, n, k)
-    pstride = (m * n + 3) // 4 * 4
-    y = _qgemm_ex(codes, scales, xb, ws_bytes=7 * pstride * 4, guard=64)
+    tiles = -(-n // 128) * -(-m // 256)
+    y = _qgemm_ex(codes, scales, xb, ws_bytes=7 * tiles * TILE_BYTES, guard=64)
     ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb))
     assert np.max(rel_err_rows(y, ref)) <= TOL
 
 
 def test_split_k_small_workspace_and_none():
     """Fewer workspace bytes give fewer splits (one part: two splits) and
-    still the product; no workspace is pg_qgemm, bit for bit."""
+    still the product; too little for a part is pg_qgemm, bit for bit."""
     codes, scales, xb = _case(512, 2560, 4096)
     m, n = xb.shape[0], codes.shape[0]
     ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb[:64]))
-    y1 = _qgemm_ex(codes, scales, xb, ws_bytes=m * n * 4, guard=64)
+    y1 = _qgemm_ex(codes, scales, xb, ws_bytes=m * n * 4, guard=64)   # 40 tiles: one part
     assert np.max(rel_err_rows(y1[:64], ref)) <= TOL
     y0 = _qgemm_ex(codes, scales, xb, ws_bytes=m * n * 4 - 16)   # less than one part: no split
     assert np.array_equal(y0, _qgemm(codes, scales, xb))

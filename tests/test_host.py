@@ -156,13 +156,15 @@ def test_carried_state_encoder_rejects_k_beyond_its_lds_survivors():
 
 
 def test_qgemm_workspace_bytes():
-    """Whole parts of m n floats (rounded up to 4), at most 7 of them; none
-    for a shape that fills the chip with tiles, none for invalid sizes."""
-    for n, k, m in [(2560, 4096, 512), (2560, 9728, 512), (5, 640, 1), (130, 1152, 77)]:
+    """Whole 256 x 128 fp32 tile blocks, at most 7 per tile; none for a shape
+    whose tiles fill the chip in whole rounds, none for invalid sizes."""
+    tb = 256 * 128 * 4
+    for n, k, m in [(2560, 4096, 512), (2560, 9728, 512), (5, 640, 1), (130, 1152, 77), (2560, 4096, 4096),
+                    (19456, 2560, 512)]:
         b = q.pg_qgemm_workspace_bytes(n, k, m)
-        part = (m * n + 3) // 4 * 4 * 4
-        assert b > 0 and b % part == 0 and b // part <= min(7, k // 128 - 1), (n, k, m, b)
-    assert q.pg_qgemm_workspace_bytes(19456, 2560, 4096) == 0
+        tiles = -(-n // 128) * -(-m // 256)
+        assert b > 0 and b % tb == 0 and b // tb <= min(7, k // 128 - 1) * tiles, (n, k, m, b)
+    assert q.pg_qgemm_workspace_bytes(6144, 2560, 4096) == 0               # 768 tiles: three whole rounds
     assert q.pg_qgemm_workspace_bytes(8, 200, 4) == 0
     assert q.pg_qgemm_workspace_bytes(8, 256, 0) == 0
     assert q.pg_qgemm_workspace_bytes(0, 256, 4) == 0
