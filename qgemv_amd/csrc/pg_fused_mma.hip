@@ -88,6 +88,7 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
     const uint8_t* xr = reinterpret_cast<const uint8_t*>(x) + (int64_t)(rowon ? wave : 0) * ldx * esz;
     float xv[KV][8];
     uint32_t sgb[KV];
+    if (rowon)                                               // waves past the batch load no row
 #pragma unroll
     for (int u = 0; u < KV; ++u) {
         const int g = lane + 64 * u, gc = g < ngr ? g : ngr - 1;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
         }
         sgb[u] = sign_bits[gc];
     }
-    constexpr int SWU = RQ_MAX_ITEMS * 16 / 512;             // weight scales per thread, at most
+    constexpr int SWU = TPW;                                 // weight scales per thread: R nbk4 <= 512 TPW
     const int nsw = R * nbk;
     uint32_t swv[SWU];
 #pragma unroll
@@ -183,36 +184,62 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
     lds_barrier();                                           // LDS only: the code requests stay in flight
 
     // ---- 3. rotation tiles (batch row, quarter mt of the row's blocks), kept
-    // in registers; quarter maxima to the blocks
+    // in registers; quarter maxima to the blocks.  Above batch 4 wave w takes
+    // all four quarters of row w, up to batch 4 two quarters of row w % 4
+    // (2 (w / 4), + 1): a wave reads each block's B operand once for all of
+    // its quarters, whose A operands differ only in sign.
     uint32_t apat[2][4];
     fs_apat(lane, apat);
-    const int jobs = batch * 4;                              // one tile of 32 blocks per row (k <= 4096)
     const int blk = lane & 31;
     const bool bok = blk < nbk;
+    const bool wide = batch > 4;
+    const int brow = wide ? wave : (wave & 3);               // uniform
+    const int mt0 = wide ? 0 : 2 * (wave >> 2);
+    const int nj = brow < batch ? (wide ? 4 : 2) : 0;        // uniform
     f32x16 acc_r[4];
+    auto rotate = [&](auto NJ) {
+        constexpr int J = decltype(NJ)::value;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int job = wave + 8 * jj;
-        if (job < jobs) {                                    // uniform
-            const int b = job >> 2, mt = job & 3;
-            const uint8_t* xb = xh + (size_t)b * xrowb + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
-            acc_r[jj] = fs_rot_tile(xb, bok, mt, apat);
+        for (int jj = 0; jj < J; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_r[jj][r] = 0.0f;
+        const uint8_t* xb = xh + (size_t)brow * xrowb + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
+        uint4 bv[8];                                         // the block's B operands, one LDS wait
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xb + 32 * st);
+            bv[st] = bok ? v : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const uint32_t* av = apat[st & 1];
+#pragma unroll
+            for (int jj = 0; jj < J; ++jj) {
+                const uint32_t fl = (__builtin_popcount((mt0 + jj) & (st >> 1)) & 1) ? 0x80008000u : 0u;
+                const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
+                acc_r[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
+                                                                   __builtin_bit_cast(fs_f16x8, bv[st]), acc_r[jj], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < J; ++jj) {
             float mx = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc_r[jj][r]));
             mx = fmaxf(mx, xor_lane32(mx, lane));
-            if (bok && lane < 32) atomicMax(&bmax[b * nbk + blk], __builtin_bit_cast(uint32_t, mx));
+            if (bok && lane < 32) atomicMax(&bmax[brow * nbk + blk], __builtin_bit_cast(uint32_t, mx));
         }
-    }
+    };
+    if (nj == 4) rotate(std::integral_constant<int, 4>());  // uniform
+    else if (nj == 2) rotate(std::integral_constant<int, 2>());
     lds_barrier();                                           // LDS only: the code requests stay in flight
 
     // ---- 4. digits with the block maxima, over the fp16 blocks (every read
     // of them is done); block sums of q
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-        const int job = wave + 8 * jj;
-        if (job < jobs) {                                    // uniform
-            const int b = job >> 2, mt = job & 3;
+        if (jj < nj) {                                       // uniform
+            const int b = brow, mt = mt0 + jj;
             const float bm = __builtin_bit_cast(float, bmax[b * nbk + (bok ? blk : 0)]);
             const float s = bm > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(bm) : 0.0f;
             // value 16 p + 4 g + j of the block at byte 32 p + 4 j + g (hi), + 16 (lo):
