@@ -119,10 +119,11 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
         swv[u] = scales[(int64_t)row * nbk + (ec - r * nbk)];
     }
     asm volatile("" ::: "memory");
-    const int tpw = (tiles + 7) >> 3;
-    const int first = wave * tpw;
-    const int mine = tiles - first < tpw ? (tiles - first > 0 ? tiles - first : 0) : tpw;
-    auto tile_of = [&](int i) { const int t = first + i; return t < tiles ? t : tiles - 1; };
+    // wave w takes tiles w, w + 8, ... (at most TPW; the waves' counts differ
+    // by one at most); its row tiles never decrease, so a running sum per row
+    // tile is enough
+    const int mine = wave < tiles ? (tiles - wave + 7) >> 3 : 0;     // uniform
+    auto tile_of = [&](int i) { const int t = wave + 8 * i; return t < tiles ? t : tiles - 1; };
     mma_v4u ct[TPW][2];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
