@@ -59,9 +59,31 @@ __device__ __forceinline__ void q16_store(uint8_t* row, int k, int blk, int i, i
     row[off + 16] = (uint8_t)(int8_t)lo;
 }
 
-__global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, int in_dt, void* __restrict__ y,
+// squares of the 4 (fp32) or 8 (fp16, bf16) values of a 16-byte vector, in order
+template <int IDT>
+__device__ __forceinline__ float sq16(const uint4 w) {
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        if constexpr (IDT == PG_F32) {
+            const float f = __builtin_bit_cast(float, v[t]);
+            s += f * f;
+        } else {
+            const float f0 = IDT == PG_F16 ? h2f((uint16_t)(v[t] & 0xffffu)) : bf2f((uint16_t)(v[t] & 0xffffu));
+            const float f1 = IDT == PG_F16 ? h2f((uint16_t)(v[t] >> 16)) : bf2f((uint16_t)(v[t] >> 16));
+            s += f0 * f0;
+            s += f1 * f1;
+        }
+    }
+    return s;
+}
+
+template <int IDT>
+__global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, void* __restrict__ y,
                                               int out_dt, const uint8_t* __restrict__ sign_bits, int k,
-                                              int64_t ldx, uint32_t flags, int64_t q16_stride) {
+                                              int64_t ldx, uint32_t flags, int64_t q16_stride, int vec) {
+    constexpr int in_dt = IDT;
     const int64_t row = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -77,7 +99,29 @@ __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, int in
     float c = load_elem(x, in_dt, xbase + i1);
     const uint32_t sg0 = sign_bits[i0 >> 3], sg1 = sign_bits[i1 >> 3];
     float inv = 1.0f;
-    if (flags & PG_FLAG_RMSNORM) {
+    if ((flags & PG_FLAG_RMSNORM) && vec) {
+        // the whole row's squares, rows 16-byte aligned: 16-byte vectors
+        // t + 256 u, up to 8 per thread in flight at once
+        constexpr int per = IDT == PG_F32 ? 4 : 8;
+        const int nv = k / per;
+        const uint4* xv = reinterpret_cast<const uint4*>((const uint8_t*)x + xbase * (IDT == PG_F32 ? 4 : 2));
+        float ss = 0.0f;
+        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 8) {
+            uint4 w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int v = v0 + 256 * u;
+                w[u] = v < nv ? xv[v] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ss += sq16<IDT>(w[u]);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+        inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+    } else if (flags & PG_FLAG_RMSNORM) {
         // the whole row's squares: up to 64 loads per thread in flight at once
         float ss = 0.0f;
         for (int i0r = threadIdx.x; i0r < k; i0r += 256 * 64) {
@@ -453,8 +497,16 @@ int launch_fwht(const void* x, int in_dt, int64_t ldx, void* y, int out_dt, cons
                 int64_t rows, int64_t k, uint32_t flags, pg_stream_t s) {
     if (rows > 65535) return fail(PG_ERR_UNSUPPORTED, "rows > 65535");
     const dim3 grid((unsigned)((k / 128 + 3) / 4), (unsigned)rows);
-    hipLaunchKernelGGL(k_fwht, grid, dim3(256), 0, (hipStream_t)s, x, in_dt, y, out_dt, sign_bits, (int)k, ldx, flags,
-                       (int64_t)q16_row_bytes(k));
+    // 16-byte loads for the RMS pass where every row starts 16-byte aligned
+    const int vec = (ldx * (in_dt == PG_F32 ? 4 : 2)) % 16 == 0 && (uintptr_t)x % 16 == 0;
+    const int64_t qs = (int64_t)q16_row_bytes(k);
+    hipStream_t st = (hipStream_t)s;
+    if (in_dt == PG_F32)
+        hipLaunchKernelGGL(k_fwht<PG_F32>, grid, dim3(256), 0, st, x, y, out_dt, sign_bits, (int)k, ldx, flags, qs, vec);
+    else if (in_dt == PG_F16)
+        hipLaunchKernelGGL(k_fwht<PG_F16>, grid, dim3(256), 0, st, x, y, out_dt, sign_bits, (int)k, ldx, flags, qs, vec);
+    else
+        hipLaunchKernelGGL(k_fwht<PG_BF16>, grid, dim3(256), 0, st, x, y, out_dt, sign_bits, (int)k, ldx, flags, qs, vec);
     return hip_check(hipGetLastError(), "pg_fwht_rotate launch");
 }
 
