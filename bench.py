@@ -96,11 +96,11 @@ def run_stack(args):
 
     shapes = synth.qwen3_4b_shapes() if args.workload == "qwen36" else synth.llama31_8b_shapes()
     layers = 36 if args.workload == "qwen36" else 32
-    # auto: the v_dot4 fused stage up to batch 2; from batch 3 on the matrix
+    # auto: the v_dot4 fused stage at batch 1; from batch 2 on the matrix
     # cores, whose cost hardly grows with the batch: the fused stage where
     # the batch's rotated activations fit in LDS (k <= 4096), the rotation +
     # product elsewhere (hybrid)
-    path = args.path if args.path != "auto" else ("fused" if args.batch <= 2 or args.carry else "hybrid")
+    path = args.path if args.path != "auto" else ("fused" if args.batch <= 1 or args.carry else "hybrid")
     fused = path in ("fused", "hybrid")
     split_above = 4096 if path == "hybrid" else None
     log(f"building {args.workload}: {layers} layers, batch {args.batch}, {path} path")
@@ -138,12 +138,12 @@ def run_stack(args):
         # every launch of the step is the fused stage kernel: its average
         # duration is the timed region over the launches (gaps included)
         avg_us = 1e3 * gpu_ms / (args.steps * launches_per_step)
-        if args.batch <= 2 or args.carry:
+        if args.batch <= 1 or args.carry:
             kname = "k_rot_qgemv"
             kdesc = "k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
         else:
             kname = "k_rot_qmma"
-            kdesc = ("k_rot_qmma (pg_rot_qgemv at batch 3..8: RMS norm + rotation + int8 matrix-core product) "
+            kdesc = ("k_rot_qmma (pg_rot_qgemv at batch 2..8: RMS norm + rotation + int8 matrix-core product) "
                      "where k <= 4096" + ("; k_fwht + k_qgemv_mma above" if n_split else
                                           "; k_rot_qgemv above" if path == "fused" else ""))
         nlaunch = args.steps * launches_per_step
@@ -337,7 +337,7 @@ def main():
                     help="only run a plain 256 MiB device copy 4 times (HBM-counter calibration) and exit")
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "split", "hybrid"],
                     help="fused: one pg_rot_qgemv per stage; split: pg_fwht_rotate_ex + pg_qgemv per stage; "
-                         "hybrid: fused where k <= 4096, split above; auto: fused up to batch 2, hybrid from batch 3")
+                         "hybrid: fused where k <= 4096, split above; auto: fused at batch 1, hybrid from batch 2")
     ap.add_argument("--batch", type=int, default=1, help="activation rows per step (1..8)")
     ap.add_argument("--carry", action="store_true",
                     help="read the codes as the carried-state variant (state runs on across blocks; fused path)")

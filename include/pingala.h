@@ -231,10 +231,10 @@ int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
  * PG_FLAG_RMSNORM (the rotation runs on fp16 values, exact after the
  * normalisation's fp16 rounding or for fp16 input; PG_ERR_UNSUPPORTED
  * otherwise).  The rotated values are quantised to 16-bit digits with one
- * scale per 32 values at batch 1..2 and per 128-block at batch 3..8 (there
- * the product runs on the matrix cores, for k <= 4096; larger k stays on the
- * batch-1..2 kernel).  PG_FLAG_CARRY_STATE: the codes are of the
- * carried-state variant (batch-1..2 kernel at every batch).  x and y may not overlap.  The
+ * scale per 32 values at batch 1 and per 128-block at batch 2..8 (there the
+ * product runs on the matrix cores, for k <= 4096; larger k stays on the
+ * batch-1 kernel).  PG_FLAG_CARRY_STATE: the codes are of the carried-state
+ * variant (batch-1 kernel at every batch).  x and y may not overlap.  The
  * summation order is fixed: repeated calls are bitwise identical. */
 int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const void* x, int x_dtype, int64_t ldx, const uint8_t* sign_bits,

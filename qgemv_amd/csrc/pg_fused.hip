@@ -59,11 +59,11 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
     if (x_dt == PG_F32 && !(flags & PG_FLAG_RMSNORM))
         return fail(PG_ERR_UNSUPPORTED, "pg_rot_qgemv: fp32 input needs PG_FLAG_RMSNORM (its rotation runs in fp16)");
     hipStream_t st = (hipStream_t)s;
-    // batch 3..8 on the matrix cores where the shape fits (PG_FUSED_KERNEL=vdot
+    // batch 2..8 on the matrix cores where the shape fits (PG_FUSED_KERNEL=vdot
     // keeps the v_dot4 stage, =mma takes the matrix cores at any batch; for tests)
     const char* kern = getenv("PG_FUSED_KERNEL");
     const bool force_v = kern && strcmp(kern, "vdot") == 0, force_m = kern && strcmp(kern, "mma") == 0;
-    if (!(flags & PG_FLAG_CARRY_STATE) && !force_v && (force_m || batch >= 3)) {
+    if (!(flags & PG_FLAG_CARRY_STATE) && !force_v && (force_m || batch >= 2)) {
         const int r = launch_rot_qmma(codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
         if (r != PG_ERR_UNSUPPORTED) return r;
     }

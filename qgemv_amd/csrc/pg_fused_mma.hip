@@ -1,4 +1,4 @@
-// Fused stage of a stack for batch 3..8 on the gfx950 matrix cores: RMS
+// Fused stage of a stack for batch 2..8 on the gfx950 matrix cores: RMS
 // normalisation, the random Hadamard rotation and the product y = W~ . R . n(x)
 // of every batch row in one launch.  The rotation runs on the f16 matrix
 // cores as in k_rot_qgemv; the product is the int8 block step of pg_mma.h,

@@ -1,7 +1,8 @@
 """GPU parity of the fused stage pg_rot_qgemv (RMS normalisation + rotation +
 product in one launch) against the oracle's fp64 chain of the same steps,
-for both of its kernels: v_dot4 (batch 1..2, activations quantised per 32
-values) and the int8 matrix cores (batch 3..8, per 128-block)."""
+for both of its kernels: v_dot4 (batch 1, and any batch when forced,
+activations quantised per 32 values) and the int8 matrix cores (batch 2..8,
+per 128-block)."""
 import numpy as np
 import pytest
 
