@@ -20,16 +20,14 @@ constexpr size_t RQ_LDS_LIMIT = 160 * 1024;
 
 // LDS of one launch
 struct RqLayout {
-    size_t xh, tab, bmax, bsq, yw, swt, ctile, total;
+    size_t xh, tab, yw, swt, ctile, total;
 };
 __host__ __device__ inline RqLayout rq_layout(int k, int R, int batch) {
     const int nbk = k / 128, nbk4 = (nbk + 3) & ~3;
     RqLayout L;
     L.xh = 0;                                                         // [batch][nbk][272]: fp16 blocks, then digits
     L.tab = L.xh + (size_t)batch * nbk * FS_XPITCH;                  // [nbk][16] float2
-    L.bmax = L.tab + (size_t)nbk * 16 * 8;                           // [8][nbk] block maxima (float bits)
-    L.bsq = L.bmax + (size_t)RQ_MAX_BATCH * nbk * 4;                 // [8][nbk] block sums of q
-    L.yw = L.bsq + (size_t)RQ_MAX_BATCH * nbk * 4;                   // [8][R][16] float
+    L.yw = L.tab + (size_t)nbk * 16 * 8;                             // [8][R][16] float
     L.swt = L.yw + (size_t)8 * R * 16 * 4;                           // [R][nbk4] fp16 bits
     L.ctile = L.swt + (((size_t)R * nbk4 * 2 + 15) & ~(size_t)15);   // [8][16][144]
     L.total = L.ctile + (size_t)8 * MMA_TILE_BYTES;
@@ -42,15 +40,13 @@ __host__ __device__ inline RqLayout rq_layout(int k, int R, int batch) {
 //      tiles (16 rows x 4 blocks, as k_qgemv_mma), which stay in flight;
 //   2. wave w sums its row's squares (RMS norm) and stages the normalised,
 //      sign-flipped fp16 blocks in LDS;
-//   3. the rotation tiles (batch row, quarter mt of 32 blocks) on the f16
-//      matrix cores, kept in registers; each quarter's maximum goes to its
-//      block's entry by an LDS max;
-//   4. with every maximum known (barrier, also the end of all staging reads),
-//      q = rint(v * 32512 / block max) as digits hi = floor((q + 128) / 256),
-//      lo = q - 256 hi (signed), written over the fp16 blocks in code-dword
-//      plane order, and the block sums of q by LDS integer adds;
-//   5. the table (2 sx, -7 sx sum q) per (block, batch row);
-//   6. the items of k_qgemv_mma, digits from LDS;
+//   3.-5. wave w < batch, after a barrier: the rotation tiles of row w (all
+//      four quarters of its 32-block tile) on the f16 matrix cores, kept in
+//      registers; the block maxima in registers; q = rint(v * 32512 / block
+//      max) as digits hi = floor((q + 128) / 256), lo = q - 256 hi (signed),
+//      written over the row's fp16 blocks in code-dword plane order; the
+//      block sums of q; the row's table entries (2 sx, -7 sx sum q);
+//   6. after a barrier, the items of k_qgemv_mma, digits from LDS;
 //   7. the waves' sums in wave order.
 // Every reduction has a fixed order or is exact (integer adds, maxima), so
 // the result does not depend on timing.
@@ -73,8 +69,6 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
     const size_t xrowb = (size_t)nbk * FS_XPITCH;            // LDS bytes per batch row of blocks
     uint8_t* xh = lds + Ly.xh;
     float2* tab = reinterpret_cast<float2*>(lds + Ly.tab);
-    uint32_t* bmax = reinterpret_cast<uint32_t*>(lds + Ly.bmax);
-    int* bsq = reinterpret_cast<int*>(lds + Ly.bsq);
     float* yw = reinterpret_cast<float*>(lds + Ly.yw);
     float* ywv = yw + (size_t)wave * R * 16;
     uint16_t* swt = reinterpret_cast<uint16_t*>(lds + Ly.swt);
@@ -141,10 +135,7 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
     asm volatile("" ::: "memory");
 
     // ---- 2. LDS set-up; normalised, sign-flipped fp16 blocks of row `wave`
-    for (int e = tid; e < RQ_MAX_BATCH * nbk; e += 512) {
-        bmax[e] = 0u;
-        bsq[e] = 0;
-    }
+    for (int e = tid; e < nbk * 16; e += 512) tab[e] = make_float2(0.0f, 0.0f);   // batch slots past the batch
 #pragma unroll
     for (int u = 0; u < SWU; ++u) {                          // past the end: the last entry again, same place
         const int e = tid + 512 * u, ec = e < nsw ? e : nsw - 1;
@@ -184,27 +175,23 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
     }
     lds_barrier();                                           // LDS only: the code requests stay in flight
 
-    // ---- 3. rotation tiles (batch row, quarter mt of the row's blocks), kept
-    // in registers; quarter maxima to the blocks.  Above batch 4 wave w takes
-    // all four quarters of row w, up to batch 4 two quarters of row w % 4
-    // (2 (w / 4), + 1): a wave reads each block's B operand once for all of
-    // its quarters, whose A operands differ only in sign.
+    // ---- 3.-5. wave w < batch: the rotation tiles of batch row w, all four
+    // quarters from one read of each block's B operand (their A operands
+    // differ only in sign); the block maxima and sums of q in registers; the
+    // digits written over the row's fp16 blocks (only this wave reads them)
+    // and the row's table entries (2 sx, -7 sx sum q), sx = max 2^-3.5 / 32512
     uint32_t apat[2][4];
     fs_apat(lane, apat);
     const int blk = lane & 31;
     const bool bok = blk < nbk;
-    const bool wide = batch > 4;
-    const int brow = wide ? wave : (wave & 3);               // uniform
-    const int mt0 = wide ? 0 : 2 * (wave >> 2);
-    const int nj = brow < batch ? (wide ? 4 : 2) : 0;        // uniform
-    f32x16 acc_r[4];
-    auto rotate = [&](auto NJ) {
-        constexpr int J = decltype(NJ)::value;
+    if (wave < batch) {                                      // uniform
+        const int b = wave;
+        f32x16 acc_r[4];
 #pragma unroll
-        for (int jj = 0; jj < J; ++jj)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc_r[jj][r] = 0.0f;
-        const uint8_t* xb = xh + (size_t)brow * xrowb + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
+            for (int r = 0; r < 16; ++r) acc_r[mt][r] = 0.0f;
+        const uint8_t* xb = xh + (size_t)b * xrowb + (bok ? blk : 0) * FS_XPITCH + 16 * (lane >> 5);
         uint4 bv[8];                                         // the block's B operands, one LDS wait
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
@@ -215,34 +202,25 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
         for (int st = 0; st < 8; ++st) {
             const uint32_t* av = apat[st & 1];
 #pragma unroll
-            for (int jj = 0; jj < J; ++jj) {
-                const uint32_t fl = (__builtin_popcount((mt0 + jj) & (st >> 1)) & 1) ? 0x80008000u : 0u;
+            for (int mt = 0; mt < 4; ++mt) {
+                const uint32_t fl = (__builtin_popcount(mt & (st >> 1)) & 1) ? 0x80008000u : 0u;
                 const uint4 aw = make_uint4(av[0] ^ fl, av[1] ^ fl, av[2] ^ fl, av[3] ^ fl);
-                acc_r[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
-                                                                   __builtin_bit_cast(fs_f16x8, bv[st]), acc_r[jj], 0, 0, 0);
+                acc_r[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fs_f16x8, aw),
+                                                                   __builtin_bit_cast(fs_f16x8, bv[st]), acc_r[mt], 0, 0, 0);
             }
         }
+        // block maximum: a lane holds 16 values of each quarter of block
+        // lane % 32, the lane pair (l, l + 32) all 128
+        float mx = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < J; ++jj) {
-            float mx = 0.0f;
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc_r[jj][r]));
-            mx = fmaxf(mx, xor_lane32(mx, lane));
-            if (bok && lane < 32) atomicMax(&bmax[brow * nbk + blk], __builtin_bit_cast(uint32_t, mx));
-        }
-    };
-    if (nj == 4) rotate(std::integral_constant<int, 4>());  // uniform
-    else if (nj == 2) rotate(std::integral_constant<int, 2>());
-    lds_barrier();                                           // LDS only: the code requests stay in flight
-
-    // ---- 4. digits with the block maxima, over the fp16 blocks (every read
-    // of them is done); block sums of q
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc_r[mt][r]));
+        mx = fmaxf(mx, xor_lane32(mx, lane));
+        const float s = mx > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(mx) : 0.0f;
+        int qsum = 0;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        if (jj < nj) {                                       // uniform
-            const int b = brow, mt = mt0 + jj;
-            const float bm = __builtin_bit_cast(float, bmax[b * nbk + (bok ? blk : 0)]);
-            const float s = bm > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(bm) : 0.0f;
+        for (int mt = 0; mt < 4; ++mt) {
             // value 16 p + 4 g + j of the block at byte 32 p + 4 j + g (hi), + 16 (lo):
             // accumulator row 8 i + 4 h + r is part 2 mt + i / 2, position 2 (i % 2) + h
             uint8_t* dq = xh + (size_t)b * xrowb + (bok ? blk : 0) * FS_XPITCH + 64 * mt + 4 * (lane >> 5);
@@ -252,7 +230,7 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
                 uint32_t bits[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    bits[r] = __builtin_bit_cast(uint32_t, fmaf(acc_r[jj][4 * i + r], s, 12582912.0f + 128.0f));
+                    bits[r] = __builtin_bit_cast(uint32_t, fmaf(acc_r[mt][4 * i + r], s, 12582912.0f + 128.0f));
                 // the low 16 bits are q + 128: hi = its high byte, lo = its low byte - 128
                 const uint32_t t01 = __builtin_amdgcn_perm(bits[1], bits[0], 0x05040100u);
                 const uint32_t t23 = __builtin_amdgcn_perm(bits[3], bits[2], 0x05040100u);
@@ -266,22 +244,13 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
                     *reinterpret_cast<uint32_t*>(dd + 16) = dl;
                 }
             }
-            int qs = 256 * shi + slo;
-            qs += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, qs), lane));
-            if (bok && lane < 32) atomicAdd(&bsq[b * nbk + blk], qs);
+            qsum += 256 * shi + slo;
         }
-    }
-    lds_barrier();                                           // LDS only: the code requests stay in flight
-
-    // ---- 5. table: (2 sx, -7 sx sum q), sx = max 2^-3.5 / 32512
-    for (int e = tid; e < nbk * 16; e += 512) {
-        const int bk = e >> 4, b = e & 15;
-        float2 t = make_float2(0.0f, 0.0f);
-        if (b < batch) {
-            const float sx = __builtin_bit_cast(float, bmax[b * nbk + bk]) * (0.08838834764831845f / (float)Q16_MAXQ);
-            t = make_float2(2.0f * sx, -7.0f * sx * (float)bsq[b * nbk + bk]);
+        qsum += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, qsum), lane));
+        if (bok && lane < 32) {
+            const float sx = mx * (0.08838834764831845f / (float)Q16_MAXQ);
+            tab[16 * blk + b] = make_float2(2.0f * sx, -7.0f * sx * (float)qsum);
         }
-        tab[e] = t;
     }
     lds_barrier();                                           // LDS only: the code requests stay in flight
 
