@@ -345,8 +345,8 @@ def main():
     ap.add_argument("--no-encode", action="store_true", help="skip the GPU encoder (pg_encode) measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "
-              "(see the sharding notes in the design document); use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: libpingala runs the hot path on a single MI355X "
+              "and has no multi-GPU path; use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

@@ -68,7 +68,7 @@ typedef struct ihipStream_t* pg_stream_t; /* a hipStream_t */
 enum {
     PG_OK = 0,
     PG_ERR_INVALID_ARG = -1,  /* bad size, null or misaligned pointer, bad dtype */
-    PG_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
+    PG_ERR_UNSUPPORTED = -2,  /* valid request the library does not implement */
     PG_ERR_HIP = -3           /* a HIP runtime call or launch failed */
 };
 
