@@ -28,16 +28,20 @@ def test_chain_matches_oracle(shapes_fn, layers, fused):
     assert np.array_equal(d2.view(np.uint32), got.view(np.uint32))
 
 
-@pytest.mark.parametrize("fused", [True, False])
-@pytest.mark.parametrize("batch", [3, 4, 8])
-def test_chain_batched_matches_oracle(batch, fused):
+PATHS = {"fused": dict(fused=True), "split": dict(fused=False), "hybrid": dict(fused=True, split_above=4096)}
+
+
+@pytest.mark.parametrize("path", ["fused", "split", "hybrid"])
+@pytest.mark.parametrize("batch", [2, 3, 4, 8])
+def test_chain_batched_matches_oracle(batch, path):
     """Batched decode, through the fused stage (several activation rows per
-    launch) or the rotation + matrix-core product, against the oracle's
-    chain, row by row."""
+    launch), the rotation + matrix-core product, or both (fused where
+    k <= 4096, the default batched path of the benchmark), against the
+    oracle's chain, row by row."""
     import torch
     from tests.helpers import rel_err_rows
     shapes = synth.llama31_8b_shapes()
-    st = Stack(shapes, 2, batch=batch, fused=fused)
+    st = Stack(shapes, 2, batch=batch, **PATHS[path])
     got = host(st.token())
     torch.cuda.synchronize()
     codes, scales, signs = zip(*[st.host_arrays(l) for l in range(2)])
@@ -46,13 +50,13 @@ def test_chain_batched_matches_oracle(batch, fused):
     assert np.max(rel_err_rows(got, ref)) <= TOL
 
 
-@pytest.mark.parametrize("batch", [1, 8])
-def test_graph_replays_match_eager(batch):
+@pytest.mark.parametrize("batch,path", [(1, "split"), (8, "split"), (2, "hybrid"), (8, "hybrid")])
+def test_graph_replays_match_eager(batch, path):
     """A captured token replays bitwise-identically to the eager token, on
-    every replay, with eager work and synchronisations in between (batch 8:
-    the matrix-core product)."""
+    every replay, with eager work and synchronisations in between (batch
+    2..8: the matrix-core kernels)."""
     import torch
-    st = Stack(synth.qwen3_4b_shapes(), 3, batch=batch, fused=False)
+    st = Stack(synth.qwen3_4b_shapes(), 3, batch=batch, **PATHS[path])
     eager = host(st.token()).copy()
     st.capture()
     for i in range(4):
