@@ -7,7 +7,7 @@ import pytest
 import qgemv_amd as q
 from oracle import p8f
 from qgemv_amd import synth
-from tests.helpers import dev, host, rel_err_rows
+from tests.helpers import TOL, dev, host, rel_err_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +81,29 @@ def test_many_rows_prompt_shape():
     got = _run(b, q.PG_BF16, q.PG_F32, sb, rows, k, 0)
     ref = p8f.rotate(p8f.bf16_bits_to_float(b), sb)
     assert np.max(rel_err_rows(got, ref)) <= 1e-6
+
+
+@pytest.mark.parametrize("in_dt,pad", [("f32", 1), ("f16", 3), ("f32", 4)])
+def test_rmsnorm_rows_any_stride(in_dt, pad):
+    """Rows ldx = k + pad apart (pad 1 or 3: rows not 16-byte aligned, so the
+    sums of squares take element loads; pad 4: 16-byte loads) against the
+    oracle's normalisation and rotation, and against the same rows made
+    contiguous (the 16-byte path)."""
+    import torch
+    rows, k = 4, 2560
+    ldx = k + pad
+    rng = np.random.default_rng(ldx)
+    xs = rng.standard_normal((rows, ldx)).astype(np.float32)
+    dt, npdt = (q.PG_F32, np.float32) if in_dt == "f32" else (q.PG_F16, np.float16)
+    xs = xs.astype(npdt)
+    sb = rng.integers(0, 256, k // 8, dtype=np.uint8)
+    flat = torch.from_numpy(np.ascontiguousarray(xs).reshape(-1)).cuda()
+    y = torch.zeros((rows, k), dtype=torch.float32, device="cuda")
+    q.pg_fwht_rotate_ex(flat, dt, ldx, y, q.PG_F32, dev(sb), rows, k, q.PG_FLAG_RMSNORM)
+    yc = torch.zeros((rows, k), dtype=torch.float32, device="cuda")
+    q.pg_fwht_rotate(dev(np.ascontiguousarray(xs[:, :k])), dt, yc, q.PG_F32, dev(sb), rows, k, q.PG_FLAG_RMSNORM)
+    torch.cuda.synchronize()
+    got, gotc = host(y), host(yc)
+    ref = np.stack([p8f.rotate(p8f.rmsnorm16(xs[r, :k].astype(np.float64)), sb) for r in range(rows)])
+    assert np.max(rel_err_rows(got, ref)) <= TOL
+    assert np.max(np.abs(got - gotc)) <= 1e-3 * np.max(np.abs(gotc))
