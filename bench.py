@@ -1,27 +1,35 @@
 """Benchmark of the Pingala-8 hot path on one MI355X.
 
-Default workload: the 36-layer Qwen3-4B-shaped linear stack at batch 1
+Headline workload: the 36-layer Qwen3-4B-shaped linear stack at batch 1
 (uniform random trellis bitstreams, fp16 U(0.005, 0.05) scales, fp16 N(0,1)
 input fed layer to layer; 965,099,520 coded bytes per token).  One step is
 one token through the whole stack: per layer four launches of the fused
 stage kernel (RMS normalisation + activation rotation + qgemv; qkv and
-gate/up merged), replayed from a HIP graph.  Inputs are resident in HBM before timing starts.
+gate/up merged), replayed from a HIP graph.  Inputs are resident in HBM
+before timing starts.
 
-Printed: one JSON line with the whole-job compressed-weight GB/s
-(bytes per token x tokens per second), tokens per second, the roofline of
-the stage kernel (coded bytes per launch over its average duration, from
-the HIP events around the timed region), the prompt path's matrix-core
-fraction (pg_qgemm on the Qwen3-4B layer shapes at m = 512 and 4096), the
-GPU encoder's throughput on one Qwen3-4B-shaped layer, and the oracle's CPU
-throughput on a bounded sample of the stack workload.
+Printed: one JSON line.  `value` is the whole-job compressed-weight GB/s of
+the headline stack (bytes per token x tokens per second).  `roofline` is the
+stage kernel's: coded bytes per launch over its average launch duration,
+timed with HIP events around every weight-reading launch on the launch
+stream.  Extra keys carry the other measurements: the Llama-3.1-8B-shaped
+stack at batch 1 and 4, the 512 x 2048 layer's microseconds per call (warm
+and cold), each Qwen3-4B matrix's cold GB/s, a streaming-read kernel's HBM
+bandwidth, the prompt path's matrix-core fraction, the GPU encoder, and the
+CPU oracle on one core and on all the host cores given to this process.
 """
 from __future__ import annotations
 
-import argparse
-import json
 import os
-import sys
-import time
+
+# the CPU oracle is timed per core: one BLAS thread per process
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = "1"
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -30,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = "qgemv compressed-weight GB/s (% HBM peak) + linear-stack tok/s at batch 1"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0          # dense bf16
+FP64_OPS_PEAK_T = 39.3             # fp64 vector instructions per second (78.6 TFLOP/s counts an FMA as two)
 
 
 def log(*a):
@@ -58,152 +67,287 @@ def committed_traffic(kernel: str, workload: str):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(seconds: float = 12.0):
+def host_cores() -> int:
+    """Host cores this process may use (capped at 16, the share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+# ------------------------------------------------------------------ CPU oracle
+
+def _oracle_chunk(args):
+    from oracle import p8f
+    codes, scales, x = args
+    t0 = time.perf_counter()
+    p8f.gemv_ref(codes, scales, x)
+    return codes.nbytes + scales.nbytes, time.perf_counter() - t0
+
+
+def cpu_baseline(seconds: float = 12.0, cores: int = 1):
     """The oracle (numpy fp64 decode + product), as it stands, on a bounded
-    sample of the stack: layer-0 launch groups of the Qwen3-4B-shaped stack,
-    repeated until `seconds` have passed.  numpy runs these ops on one
-    thread."""
+    sample of the stack: the layer-0 launch groups of the Qwen3-4B-shaped
+    stack, repeated until `seconds` have passed.  cores = 1: one process;
+    cores > 1: a process pool over 256-row chunks of the same products."""
     import numpy as np
 
-    from oracle import p8f
     from qgemv_amd import synth
 
     merged = synth.random_layer_merged(0, synth.qwen3_4b_shapes())
     x = {s: synth.activations_f32(1, merged[s][0].shape[1] * 4) for s in merged}
-    done_bytes, t0, mats = 0, time.perf_counter(), 0
-    while True:
-        for site in ("o", "qkv", "down", "gu"):
-            codes, scales = merged[site]
-            p8f.gemv_ref(codes, scales, x[site])
-            done_bytes += codes.nbytes + scales.nbytes
-            mats += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{mats} launch-group products of layer 0 (decode + fp64 GEMV, batch 1) in {dt:.1f} s; "
-                      f"{done_bytes} coded bytes"}
+    if cores <= 1:
+        from oracle import p8f
+        done_bytes, t0, mats = 0, time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            for site in ("o", "qkv", "down", "gu"):
+                codes, scales = merged[site]
+                p8f.gemv_ref(codes, scales, x[site])
+                done_bytes += codes.nbytes + scales.nbytes
+                mats += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+        dt = time.perf_counter() - t0
+        return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{mats} launch-group products of layer 0 (decode + fp64 GEMV, batch 1) in {dt:.1f} s "
+                          f"on one core; {done_bytes} coded bytes"}
+    import multiprocessing as mp
+    jobs = []
+    for site in ("o", "qkv", "down", "gu"):
+        codes, scales = merged[site]
+        for r in range(0, codes.shape[0], 256):
+            jobs.append((np.ascontiguousarray(codes[r:r + 256]), np.ascontiguousarray(scales[r:r + 256]), x[site]))
+    ctx = mp.get_context("spawn")                  # workers hold no GPU state
+    done_bytes, rounds = 0, 0
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_chunk, jobs[:cores])                 # start the workers
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for nb, _ in pool.imap_unordered(_oracle_chunk, jobs):
+                done_bytes += nb
+            rounds += 1
+        dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rounds} passes over the layer-0 launch groups (decode + fp64 GEMV, batch 1), 256-row chunks "
+                      f"over a pool of {cores} processes, in {dt:.1f} s; {done_bytes} coded bytes"}
 
 
-def run_stack(args):
+# ----------------------------------------------------------------- GPU stacks
+
+def time_launches(st, stream, reps: int = 10):
+    """Average duration of the weight-reading launches of each site: one HIP
+    graph per site holding that site's product launch of every layer, replayed
+    `reps` times between HIP events on the launch stream (launch-to-launch
+    time of back-to-back launches, dispatch included; no event inside)."""
     import torch
+    per, nlaunch = {}, 0
+    calls = {}
+    for kind, layer, site, call in st.launches():       # the stream current at call time (the capture's)
+        if kind == "product":
+            calls.setdefault(site, []).append(call)
+    for site, cs in calls.items():
+        g = _graph_of(cs)
+        per[site] = 1e3 * _time_graph(g, reps) / len(cs)
+        nlaunch += reps * len(cs)
+        del g
+    torch.cuda.synchronize()
+    return per, nlaunch
 
-    import qgemv_amd as q
-    from qgemv_amd import synth
-    from qgemv_amd.stack import ORDER, Stack
 
-    shapes = synth.qwen3_4b_shapes() if args.workload == "qwen36" else synth.llama31_8b_shapes()
-    layers = 36 if args.workload == "qwen36" else 32
-    # auto: the v_dot4 fused stage at batch 1; from batch 2 on the matrix
-    # cores, whose cost hardly grows with the batch: the fused stage where
-    # the batch's rotated activations fit in LDS (k <= 4096), the rotation +
-    # product elsewhere (hybrid)
-    path = args.path if args.path != "auto" else ("fused" if args.batch <= 1 or args.carry else "hybrid")
-    fused = path in ("fused", "hybrid")
-    split_above = 4096 if path == "hybrid" else None
-    log(f"building {args.workload}: {layers} layers, batch {args.batch}, {path} path")
-    st = Stack(shapes, layers, batch=args.batch, x_dtype=q.PG_Q16, fused=fused, carry=args.carry,
-               split_above=split_above)
+def run_stack(st, steps: int, warmup: int, use_graph: bool = True):
+    """Whole-job timing of `steps` tokens: HIP events on the launch stream
+    around exactly `steps` replays (graph) or eager tokens, synchronised on
+    both sides."""
+    import torch
     stream = torch.cuda.current_stream()
-    use_graph = not args.no_graph
     if use_graph:
         st.capture()
     step = st.replay if use_graph else st.token
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup done (hip graph: {use_graph})")
-    # timed region: exactly `steps` tokens (one step = one pass of the batch
-    # through every layer), HIP events on the launch stream
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    log(f"timed {args.steps} steps: {gpu_ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
+    return max(gpu_ms, wall * 1e3) / steps, gpu_ms, wall * 1e3
 
-    n_split = sum(1 for _, k in st.shapes.values() if split_above is not None and k > split_above)
-    launches_per_step = (4 + n_split if fused else 8) * layers
-    bytes_per_launch = st.bytes_per_token // (4 * layers)
-    if fused:
-        # every launch of the step is the fused stage kernel: its average
-        # duration is the timed region over the launches (gaps included)
-        avg_us = 1e3 * gpu_ms / (args.steps * launches_per_step)
-        if args.batch <= 1 or args.carry:
-            kname = "k_rot_qgemv"
-            kdesc = "k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
-        else:
-            kname = "k_rot_qmma"
-            kdesc = ("k_rot_qmma (pg_rot_qgemv at batch 2..8: RMS norm + rotation + int8 matrix-core product) "
-                     "where k <= 4096" + ("; k_fwht + k_qgemv_mma above" if n_split else
-                                          "; k_rot_qgemv above" if path == "fused" else ""))
-        nlaunch = args.steps * launches_per_step
-    else:
-        # split path: events around every product launch of a separate pass;
-        # a spin kernel queued first holds the GPU while the host enqueues, so
-        # the events time back-to-back GPU work, not the host's launch rate
-        evs = []
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.25))
-        for _ in range(2):
-            for layer in range(layers):
-                for site in ORDER:
-                    n, k = st.shapes[site]
-                    first = site == "qkv" and layer == 0
-                    prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
-                    q.pg_fwht_rotate_ex(st.h0 if first else st.out[prev], q.PG_F16 if first else q.PG_F32,
-                                        k if first else st.shapes[prev][0], st.xrot, q.PG_Q16, st.signs[layer][site],
-                                        args.batch, k, 0 if first else q.PG_FLAG_RMSNORM)
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    q.pg_qgemv(st.codes[layer][site], st.scales[layer][site], n, k, st.xrot, q.PG_Q16, args.batch,
-                               st.out[site])
-                    b.record(stream)
-                    evs.append((a, b))
-        torch.cuda.synchronize()
-        avg_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-        if args.batch == 1:
-            kname = "k_qgemv_q16"
-            kdesc = "k_qgemv_q16 (pg_qgemv on PG_Q16 activations)"
-        else:
-            kname = "k_qgemv_mma"
-            kdesc = "k_qgemv_mma (pg_qgemv on PG_Q16 activations, int8 matrix cores, batch 2..8)"
-        nlaunch = len(evs)
-    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
-    wl = ("qwen3-4b-36L" if args.workload == "qwen36" else "llama3.1-8b-32L") + f"-b{args.batch}"
-    traffic = committed_traffic(kname, wl)
-    tok_s = args.batch * 1e3 / ms_per_step
-    value = st.bytes_per_token * (1e3 / ms_per_step) / 1e9
-    res = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": ("i8xi8->i32 (levels x 16-bit activation digits), f16 MFMA rotation, f32 scales" if fused or
-                  args.batch == 1 else "i8xi8->i32 MFMA (level planes x 16-bit activation digits), f32 scales"),
-        "data": "synthetic",
-        "config": {"workload": f"{'Qwen3-4B' if args.workload == 'qwen36' else 'Llama-3.1-8B'}-shaped "
-                               f"{layers}-layer linear stack, batch {args.batch}, random trellis bitstreams",
-                   "layers": layers, "batch": args.batch, "bytes_per_token": st.bytes_per_token,
-                   "tok_per_s": round(tok_s, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "hip_graphs": use_graph, "launches_per_token": launches_per_step, "path": path,
-                   "format": "carried-state variant" if args.carry else "P8F v1"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_bytes_per_launch": bytes_per_launch, "kernel": kdesc,
-                     "launches": nlaunch, "avg_launch_us": round(avg_us, 3)},
-    }
-    return res
+
+def stack_result(st, ms_per_step: float, batch: int, per_site_us: dict):
+    """Throughput of a stack and its per-launch figures."""
+    bytes_tok = st.bytes_per_token
+    sizes = {s: 0 for s in per_site_us}
+    for layer in range(st.layers):
+        for s in per_site_us:
+            sizes[s] += st.codes[layer][s].numel() + st.scales[layer][s].numel() * 2
+    per = {}
+    for s, us in per_site_us.items():
+        b = sizes[s] // st.layers
+        per[s] = {"n": st.shapes[s][0], "k": st.shapes[s][1], "coded_bytes": b, "us": round(us, 3),
+                  "gbs": round(b / (us * 1e-6) / 1e9, 1)}
+    launches = 4 * st.layers
+    avg_us = sum(per_site_us[s] for s in per_site_us) / len(per_site_us)
+    value = bytes_tok * (1e3 / ms_per_step) / 1e9
+    return {"ms_per_step": round(ms_per_step, 4), "tok_per_s": round(batch * 1e3 / ms_per_step, 2),
+            "gbs": round(value, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "bytes_per_token": bytes_tok, "weight_launches_per_token": launches,
+            "avg_weight_launch_us": round(avg_us, 3), "per_site": per}
+
+
+def build_stack(workload: str, batch: int, path: str, carry: bool):
+    from qgemv_amd import _lib as L
+    from qgemv_amd import synth
+    from qgemv_amd.stack import Stack
+    shapes = synth.qwen3_4b_shapes() if workload == "qwen36" else synth.llama31_8b_shapes()
+    layers = 36 if workload == "qwen36" else 32
+    fused = path in ("fused", "hybrid")
+    split_above = 4096 if path == "hybrid" else None
+    return Stack(shapes, layers, batch=batch, x_dtype=L.PG_Q16, fused=fused, carry=carry, split_above=split_above)
+
+
+def auto_path(batch: int, carry: bool) -> str:
+    # the v_dot4 fused stage at batch 1; from batch 2 on the matrix cores,
+    # whose cost hardly grows with the batch: the fused stage where the
+    # batch's rotated activations fit in LDS (k <= 4096), the rotation +
+    # product elsewhere (hybrid)
+    return "fused" if batch <= 1 or carry else "hybrid"
+
+
+# ------------------------------------------------------- single-matrix timing
+
+def _graph_of(calls):
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls[:2]:
+            c()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    return g
+
+
+def _time_graph(g, reps: int):
+    import torch
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def matrix_timing(codes, scales, n: int, k: int, x, x_dt: int, flags: int, signs, min_bytes: int = 1 << 30,
+                  launches: int = 200):
+    """Microseconds per pg_rot_qgemv call (batch 1) on one matrix: warm (the
+    same copy every call, cache-resident) and cold (cycling through distinct
+    device copies that together hold >= min_bytes, more than four times the
+    256 MB last-level cache)."""
+    import torch
+    import qgemv_amd as q
+    per = codes.numel() + scales.numel() * 2
+    copies = max(1, -(-min_bytes // per))
+    cbig = codes.repeat(copies, 1)          # copy i is rows [i n, (i + 1) n)
+    sbig = scales.repeat(copies, 1)
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    warm = [lambda: q.pg_rot_qgemv(codes, scales, n, k, x, x_dt, k, signs, flags, 1, y)] * launches
+    cold = []
+    for i in range(min(copies, 4096)):
+        ci, si = cbig[i * n:(i + 1) * n], sbig[i * n:(i + 1) * n]
+        cold.append(lambda ci=ci, si=si: q.pg_rot_qgemv(ci, si, n, k, x, x_dt, k, signs, flags, 1, y))
+    while len(cold) < launches:
+        cold = cold + cold
+    gw, gc = _graph_of(warm), _graph_of(cold)
+    us_w = 1e3 * _time_graph(gw, 5) / len(warm)
+    us_c = 1e3 * _time_graph(gc, 2) / len(cold)
+    del cbig, sbig
+    return {"coded_bytes": per, "warm_us": round(us_w, 3), "cold_us": round(us_c, 3),
+            "warm_gbs": round(per / (us_w * 1e-6) / 1e9, 1), "cold_gbs": round(per / (us_c * 1e-6) / 1e9, 1),
+            "cold_copies": copies, "cold_bytes": copies * per}
+
+
+def run_single_layer():
+    """The 512 x 2048 layer (W ~ N(0,1) from seed 0, encoded by pg_encode),
+    batch-1 fp16 input, no normalisation: one pg_rot_qgemv per call."""
+    import torch
+    import qgemv_amd as q
+    from qgemv_amd import synth
+    w = synth.single_layer_weights()
+    n, k = w.shape
+    sb = torch.from_numpy(synth.site_sign_bits(0, 0, k)).cuda()
+    c = torch.empty((n, k // 4), dtype=torch.uint8, device="cuda")
+    s = torch.empty((n, k // 128), dtype=torch.int16, device="cuda")
+    q.pg_encode(torch.from_numpy(w).cuda(), n, k, sb, c, s)
+    x = torch.from_numpy(synth.activations_fp16(1, k)).cuda()
+    r = matrix_timing(c, s, n, k, x, q.PG_F16, 0, sb)
+    r["workload"] = "512 x 2048 layer, N(0,1) weights encoded on the GPU, batch-1 fp16 input, pg_rot_qgemv"
+    return r
+
+
+def run_layer_cold():
+    """Each matrix of one Qwen3-4B-shaped layer (0.02 N(0,1) weights with
+    0.1% outliers x20, encoded by pg_encode), batch-1 fp32 input with the RMS
+    normalisation, timed cold over >= 1 GB of distinct copies."""
+    import torch
+    import qgemv_amd as q
+    from qgemv_amd import synth
+    out = {}
+    x32 = None
+    for name in synth.MATS:
+        w = synth.qwen_layer_weights(name)
+        n, k = w.shape
+        sb = torch.from_numpy(synth.site_sign_bits(0, synth.SITE_OF[name], k)).cuda()
+        c = torch.empty((n, k // 4), dtype=torch.uint8, device="cuda")
+        s = torch.empty((n, k // 128), dtype=torch.int16, device="cuda")
+        q.pg_encode(torch.from_numpy(w).cuda(), n, k, sb, c, s)
+        x32 = torch.from_numpy(synth.activations_f32(1, k)).cuda()
+        r = matrix_timing(c, s, n, k, x32, q.PG_F32, q.PG_FLAG_RMSNORM, sb)
+        out[name] = {"n": n, "k": k, **r}
+        del c, s
+    return out
+
+
+def run_hbm_read(nbytes: int = 4 << 30, reps: int = 5):
+    """pg_hbm_read over a 4 GiB buffer: the bandwidth a plain streaming read
+    reaches, checked against the XOR of the buffer."""
+    import numpy as np
+    import torch
+    import qgemv_amd as q
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.random_()
+    ref = int(np.bitwise_xor.reduce(buf[: 1 << 24].cpu().numpy().view(np.uint32)))
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q.pg_hbm_read(buf[: 1 << 24], 1 << 26, out)
+    torch.cuda.synchronize()
+    ok = (int(out.item()) & 0xFFFFFFFF) == ref
+    stream = torch.cuda.current_stream()
+    q.pg_hbm_read(buf, nbytes, out)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        q.pg_hbm_read(buf, nbytes, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    return {"kernel": "k_hbm_read (pg_hbm_read)", "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "xor_check": ok}
 
 
 def run_qgemm(stream_iters: int = 10):
@@ -273,7 +417,9 @@ def run_encode():
     the host reference encoder (pg_encode_ref, all host cores) on 64 rows of
     each as the CPU figure.  The search scores 128 points of 4 values in each
     of 4 cosets per group of 4 weights: 4 x 128 x 11 / 4 = 1408 fp64
-    operations per weight, the encoder's algorithmic work."""
+    operations per weight (none fused), the encoder's algorithmic work, set
+    against the fp64 instruction rate (78.6 TFLOP/s counts an FMA as two
+    operations; the encoder issues none, so its peak is 39.3 T operations/s)."""
     import numpy as np
     import torch
 
@@ -304,7 +450,7 @@ def run_encode():
         hc = np.zeros((rows, k // 4), np.uint8)
         hs = np.zeros((rows, k // 128), np.uint16)
         t0 = time.perf_counter()
-        q.pg_encode_ref(np.ascontiguousarray(w[:rows]), rows, k, sb, hc, hs, 0)
+        q.pg_encode_ref(np.ascontiguousarray(w[:rows]), rows, k, sb, hc, hs, host_cores())
         cpu_s += time.perf_counter() - t0
         cpu_w += rows * k
         if not np.array_equal(c[:rows].cpu().numpy(), hc):
@@ -313,13 +459,14 @@ def run_encode():
         tot_w += n * k
         tot_ms += ms
     gws = tot_w / tot_ms / 1e6
-    tflops = 1408.0 * gws * 1e9 / 1e12
+    tops = 1408.0 * gws * 1e9 / 1e12
     log(f"encode: {gws:.2f} Gweights/s on the GPU")
     return {"kernel": "k_encode (pg_encode)", "workload": "Qwen3-4B-shaped layer, 7 matrices, "
             f"{int(tot_w)} weights", "ms": round(tot_ms, 3), "gweights_per_s": round(gws, 2),
-            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": 78.6, "unit": "TFLOP/s (fp64)",
-                         "frac": round(tflops / 78.6, 4), "flop_per_weight": 1408},
-            "cpu_reference": {"mweights_per_s": round(cpu_w / cpu_s / 1e6, 2), "threads": os.cpu_count(),
+            "roofline": {"bound": "alu", "achieved": round(tops, 2), "peak": FP64_OPS_PEAK_T,
+                         "unit": "T fp64 operations/s (no FMA)", "frac": round(tops / FP64_OPS_PEAK_T, 4),
+                         "ops_per_weight": 1408},
+            "cpu_reference": {"mweights_per_s": round(cpu_w / cpu_s / 1e6, 2), "threads": host_cores(),
                               "kind": "pg_encode_ref (host C++, bit-identical output)",
                               "sample": "64 rows of each matrix"},
             "matrices": per}
@@ -341,8 +488,11 @@ def main():
     ap.add_argument("--batch", type=int, default=1, help="activation rows per step (1..8)")
     ap.add_argument("--carry", action="store_true",
                     help="read the codes as the carried-state variant (state runs on across blocks; fused path)")
+    ap.add_argument("--only-stack", action="store_true", help="only the headline stack (for profiling runs)")
     ap.add_argument("--no-qgemm", action="store_true", help="skip the prompt-path (pg_qgemm) measurement")
     ap.add_argument("--no-encode", action="store_true", help="skip the GPU encoder (pg_encode) measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the Llama stack, single-matrix, HBM-read and all-core CPU measurements")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: libpingala runs the hot path on a single MI355X "
@@ -361,7 +511,82 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": 256 << 20, "bytes_written": 256 << 20,
                           "launches": 4}), flush=True)
         return
-    res = run_stack(args)
+    if args.only_stack:
+        args.no_qgemm = args.no_encode = args.no_extra = args.no_cpu_baseline = True
+
+    # ---- the headline stack
+    path = args.path if args.path != "auto" else auto_path(args.batch, args.carry)
+    log(f"building {args.workload}: batch {args.batch}, {path} path")
+    st = build_stack(args.workload, args.batch, path, args.carry)
+    stream = torch.cuda.current_stream()
+    ms, gpu_ms, wall_ms = run_stack(st, args.steps, args.warmup, use_graph=not args.no_graph)
+    log(f"timed {args.steps} steps: {gpu_ms:.2f} ms (events), {wall_ms:.2f} ms (wall)")
+    per_site_us, nlaunch = time_launches(st, stream)
+    head = stack_result(st, ms, args.batch, per_site_us)
+    fused_b1 = path == "fused" and args.batch <= 1
+    if fused_b1 and not args.carry:
+        kname, kdesc = "k_rot_qgemv1", "k_rot_qgemv1 (pg_rot_qgemv at batch 1: RMS norm + rotation + qgemv, one launch per stage)"
+    elif path == "fused":
+        kname, kdesc = "k_rot_qgemv", "k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
+    elif path == "hybrid":
+        kname, kdesc = "k_rot_qmma", ("k_rot_qmma (pg_rot_qgemv at batch 2..8, int8 matrix cores) where k <= 4096, "
+                                      "k_qgemv_mma after k_fwht above")
+    else:
+        kname = "k_qgemv_q16" if args.batch == 1 else "k_qgemv_mma"
+        kdesc = f"{kname} (pg_qgemv on PG_Q16 activations, after k_fwht)"
+    wl = ("qwen3-4b-36L" if args.workload == "qwen36" else "llama3.1-8b-32L") + f"-b{args.batch}"
+    bytes_per_launch = st.bytes_per_token // head["weight_launches_per_token"]
+    avg_us = head["avg_weight_launch_us"]
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    res = {
+        "metric": METRIC, "value": head["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8xi8->i32 (levels x 16-bit activation digits), f32 rotation and scales",
+        "data": "synthetic",
+        "config": {"workload": f"{'Qwen3-4B' if args.workload == 'qwen36' else 'Llama-3.1-8B'}-shaped "
+                               f"{st.layers}-layer linear stack, batch {args.batch}, random trellis bitstreams",
+                   "layers": st.layers, "batch": args.batch, "bytes_per_token": st.bytes_per_token,
+                   "tok_per_s": head["tok_per_s"], "pct_hbm_peak": head["pct_hbm_peak"],
+                   "hip_graphs": not args.no_graph, "path": path,
+                   "format": "carried-state variant" if args.carry else "P8F v1"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(kname, wl),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes_per_launch": bytes_per_launch, "kernel": kdesc,
+                     "launches_timed": nlaunch, "avg_launch_us": avg_us,
+                     "timing": "per site, a HIP graph of that site's launch in every layer, replayed between "
+                               "HIP events on the launch stream; launch-to-launch duration",
+                     "per_site": head["per_site"]},
+        "stack": head,
+    }
+    log(f"stack: {head['ms_per_step']} ms/step, {head['gbs']} GB/s, {avg_us} us per weight launch")
+    del st
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        log("timing the streaming-read ceiling (pg_hbm_read)")
+        res["hbm_read"] = run_hbm_read()
+        if args.workload == "qwen36" and args.batch == 1:
+            log("timing the Llama-3.1-8B-shaped stack at batch 1 and 4")
+            ll = {}
+            base = build_stack("llama32", 1, "fused", False)
+            for b in (1, 4):
+                s2 = base if b == 1 else base.with_batch(b)
+                if b > 1:
+                    s2.fused, s2.split_above = True, 4096       # the batched (hybrid) path
+                ms2, _, _ = run_stack(s2, max(5, args.steps // 2), args.warmup)
+                per2, _ = time_launches(s2, stream, reps=5)
+                ll[f"b{b}"] = {"path": "fused" if b == 1 else "hybrid", **stack_result(s2, ms2, b, per2)}
+                log(f"llama32 b{b}: {ll[f'b{b}']['ms_per_step']} ms/step")
+                del s2
+            del base
+            torch.cuda.empty_cache()
+            res["llama32"] = ll
+            log("timing the 512 x 2048 layer warm and cold")
+            res["single_layer"] = run_single_layer()
+            log("timing each Qwen3-4B matrix cold")
+            res["layer_cold"] = run_layer_cold()
+            torch.cuda.empty_cache()
     if not args.no_qgemm:
         log("timing the prompt path (pg_qgemm)")
         res["qgemm"] = run_qgemm()
@@ -371,6 +596,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline()
+        if not args.no_extra:
+            res["cpu_all_cores"] = cpu_baseline(seconds=10.0, cores=host_cores())
     print(json.dumps(res), flush=True)
 
 

@@ -275,6 +275,20 @@ int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t
  * the current device (0: it would not split; 0 as well for invalid sizes). */
 size_t pg_qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m);
 
+/* Measurement helper, not part of the method: the HBM bandwidth a plain
+ * streaming kernel reaches on this device, as the practical ceiling next to
+ * the vendor peak (the batch-1 product is meant to stream its compressed
+ * bytes at HBM speed: article "8 open models...", section "What 2-bit
+ * keeps", one pass over all weights per token).
+ *   p        device, 16-byte aligned, `bytes` readable bytes
+ *   bytes    a positive multiple of 16
+ *   xor_out  device u32, 4-byte aligned, not inside [p, p + bytes): the XOR of
+ *            all 32-bit words of the range is XOR-ed into *xor_out (so a
+ *            caller that zeroes it first gets exactly that XOR; the value
+ *            checks that every byte was read).
+ * Asynchronous on `stream`. */
+int pg_hbm_read(const void* p, size_t bytes, uint32_t* xor_out, pg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ PG_FLAG_CARRY_STATE = 2
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
            "pg_encode", "pg_encode_ex", "pg_decode_ex",
            "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm",
-           "pg_qgemm_ex", "pg_qgemm_workspace_bytes")
+           "pg_qgemm_ex", "pg_qgemm_workspace_bytes", "pg_hbm_read")
 
 
 class PgError(RuntimeError):
@@ -83,6 +83,8 @@ def lib():
         L.pg_qgemm_ex.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, ctypes.c_size_t, vp]
         L.pg_qgemm_workspace_bytes.restype = ctypes.c_size_t
         L.pg_qgemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.pg_hbm_read.restype = i32
+        L.pg_hbm_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
         _LIB = L
     return _LIB
 
@@ -199,3 +201,9 @@ def pg_qgemm_ex(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, workspace,
 
 def pg_qgemm_workspace_bytes(n: int, k: int, m: int) -> int:
     return lib().pg_qgemm_workspace_bytes(n, k, m)
+
+
+def pg_hbm_read(p, nbytes: int, xor_out, stream=None) -> None:
+    """Streaming read of nbytes (multiple of 16) at device buffer p; the XOR of
+    its 32-bit words is XOR-ed into the device u32 xor_out."""
+    _check(lib().pg_hbm_read(_ptr(p), nbytes, _ptr(xor_out), _stream(stream)))

@@ -217,4 +217,15 @@ int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t
     return pg::launch_qgemm(codes, scales, n, k, x_rot_bf16, m, y, workspace, workspace_bytes, stream);
 }
 
+int pg_hbm_read(const void* p, size_t bytes, uint32_t* xor_out, pg_stream_t stream) {
+    pg::clear_error();
+    if (bytes == 0 || bytes % 16 != 0)
+        return pg::fail(PG_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 (got %zu)", bytes);
+    PG_TRY(check_ptr(p, 16, "p"));
+    PG_TRY(check_ptr(xor_out, 4, "xor_out"));
+    const uintptr_t a = (uintptr_t)p, o = (uintptr_t)xor_out;
+    if (o < a + bytes && a < o + 4) return pg::fail(PG_ERR_INVALID_ARG, "xor_out overlaps p");
+    return pg::launch_hbm_read(p, (int64_t)bytes, xor_out, stream);
+}
+
 }  // extern "C"

@@ -105,6 +105,16 @@ __device__ __forceinline__ int wave_sum_i(int v) {
     v += __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, v), lane));
     return v;
 }
+__device__ __forceinline__ int wave_xor(int v) {
+    const int lane = threadIdx.x & 63;
+    v ^= xor_lane_i<1>(v, lane);
+    v ^= xor_lane_i<2>(v, lane);
+    v ^= xor_lane_i<4>(v, lane);
+    v ^= xor_lane_i<8>(v, lane);
+    v ^= __builtin_bit_cast(int, xor_lane16(__builtin_bit_cast(float, v), lane));
+    v ^= __builtin_bit_cast(int, xor_lane32(__builtin_bit_cast(float, v), lane));
+    return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
     const int lane = threadIdx.x & 63;
     v = fmaxf(v, xor_lane<1>(v, lane));

@@ -555,6 +555,11 @@ int launch_fused_all(const FusedShape& S, const uint8_t* codes, const uint16_t* 
 int launch_rot_qmma(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x, int x_dt,
                     int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y, hipStream_t st);
 
+// batch 1 on P8F v1 codes (pg_fused1.hip): the stage with the rotation in
+// registers; PG_ERR_UNSUPPORTED (message set) when the shape does not fit it
+int launch_rot_qgemv1(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x, int x_dt,
+                      const uint8_t* sign_bits, uint32_t flags, float* y, hipStream_t st);
+
 // the carried-state instances (pg_fused_carry.hip, compiled on their own)
 int launch_fused_carry(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                        const void* x, int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch,

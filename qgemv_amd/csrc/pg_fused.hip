@@ -67,6 +67,12 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
         const int r = launch_rot_qmma(codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
         if (r != PG_ERR_UNSUPPORTED) return r;
     }
+    // batch 1 on P8F v1 codes: the register-rotation stage where the
+    // rotation is at most one round per wave (k <= 4096); larger k keeps the
+    // matrix-core rotation below, which is faster there (k = 9728: 8.5 against
+    // 9.1 us per launch)
+    if (batch == 1 && !(flags & PG_FLAG_CARRY_STATE) && k <= 4096)
+        return launch_rot_qgemv1(codes, scales, n, k, x, x_dt, sign_bits, flags, y, st);
     if (flags & PG_FLAG_CARRY_STATE)
         return launch_fused_carry(S, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
     return launch_fused_all<false>(S, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);

@@ -55,6 +55,8 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
                  const uint16_t* x, int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s);
 QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes);
 size_t qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m);
+// (pg_kernels.hip) streaming read of `bytes` (a multiple of 16) at p
+int launch_hbm_read(const void* p, int64_t bytes, uint32_t* out, pg_stream_t s);
 // (pg_encode.hip)
 int launch_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
                   uint16_t* scales, pg_stream_t s);

@@ -482,7 +482,40 @@ __global__ __launch_bounds__(512) void k_qgemv_q16(const uint8_t* __restrict__ c
     }
 }
 
+// ----------------------------------------------------------- streaming read
+// The HBM ceiling a plain streaming kernel reaches: every thread reads 16-byte
+// words in a grid-stride sweep with four requests in flight and XORs them;
+// each workgroup folds its XOR into *out with one atomic (XOR does not depend
+// on the order, so the result is exact and checkable).
+__global__ __launch_bounds__(256) void k_hbm_read(const uint4* __restrict__ p, int64_t n16, uint32_t* out) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = p[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    acc = (uint32_t)wave_xor(acc);
+    __shared__ uint32_t red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicXor(out, red[0] ^ red[1] ^ red[2] ^ red[3]);
+}
+
 }  // namespace
+
+int launch_hbm_read(const void* p, int64_t bytes, uint32_t* out, pg_stream_t s) {
+    const int64_t n16 = bytes / 16;
+    int64_t grid = (int64_t)compute_units() * 32;
+    if (grid > (n16 + 255) / 256) grid = (n16 + 255) / 256;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(k_hbm_read, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)s, (const uint4*)p, n16, out);
+    return hip_check(hipGetLastError(), "pg_hbm_read launch");
+}
 
 int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w,
                   bool carry, pg_stream_t s) {

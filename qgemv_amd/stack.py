@@ -72,53 +72,62 @@ class Stack:
         h = shapes["q"][1]
         self.h0 = torch.from_numpy(synth.activations_fp16(b, h)).to(device)
 
+    def with_batch(self, batch: int, device: str = "cuda") -> "Stack":
+        """A stack over the same device weights with its own activation and
+        output buffers for `batch` rows."""
+        import copy
+
+        import torch
+        other = copy.copy(self)
+        other.batch = batch
+        kmax = max(k for _, k in self.shapes.values())
+        if self.x_dtype == L.PG_Q16:
+            other.xrot = torch.zeros((batch, L.pg_q16_row_bytes(kmax)), dtype=torch.uint8, device=device)
+        else:
+            xt = torch.float32 if self.x_dtype == L.PG_F32 else torch.float16
+            other.xrot = torch.empty((batch, kmax), dtype=xt, device=device)
+        other.out = {site: torch.empty((batch, n), dtype=torch.float32, device=device)
+                     for site, (n, _) in self.shapes.items()}
+        other.h0 = torch.from_numpy(synth.activations_fp16(batch, self.raw_shapes["q"][1])).to(device)
+        other.graph = None
+        return other
+
+    def launches(self, stream=None, h_in=None):
+        """One token as a list of (kind, layer, site, call): kind "product"
+        for a launch that reads the site's weights (pg_rot_qgemv or
+        pg_qgemv), "rotate" for pg_fwht_rotate_ex; call() issues it."""
+        b = self.batch
+        out = []
+        for layer in range(self.layers):
+            for site in ORDER:
+                n, k = self.shapes[site]
+                c, s, g = self.codes[layer][site], self.scales[layer][site], self.signs[layer][site]
+                y = self.out[site]
+                first = site == "qkv" and layer == 0
+                prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
+                if first:
+                    src, src_dt, ldx, flags = (h_in if h_in is not None else self.h0), L.PG_F16, k, 0
+                else:
+                    src, src_dt, ldx, flags = self.out[prev], L.PG_F32, self.shapes[prev][0], L.PG_FLAG_RMSNORM
+                split = not self.fused or (self.split_above is not None and k > self.split_above and not first)
+                if split:
+                    xd = self.x_dtype if not self.fused else L.PG_Q16
+                    out.append(("rotate", layer, site,
+                                lambda src=src, src_dt=src_dt, ldx=ldx, g=g, k=k, flags=flags, xd=xd:
+                                L.pg_fwht_rotate_ex(src, src_dt, ldx, self.xrot, xd, g, b, k, flags, stream)))
+                    out.append(("product", layer, site,
+                                lambda c=c, s=s, n=n, k=k, y=y, xd=xd:
+                                L.pg_qgemv(c, s, n, k, self.xrot, xd, b, y, stream)))
+                else:
+                    out.append(("product", layer, site,
+                                lambda c=c, s=s, n=n, k=k, src=src, src_dt=src_dt, ldx=ldx, g=g, flags=flags, y=y:
+                                L.pg_rot_qgemv(c, s, n, k, src, src_dt, ldx, g, flags | self.cflag, b, y, stream)))
+        return out
+
     def token(self, stream=None, h_in=None):
         """Run one token through all layers; returns the last layer's d."""
-        if self.fused:
-            return self._token_fused(stream, h_in)
-        return self._token_split(stream, h_in)
-
-    def _token_fused(self, stream=None, h_in=None):
-        b = self.batch
-        for layer in range(self.layers):
-            for site in ORDER:
-                n, k = self.shapes[site]
-                if site == "qkv" and layer == 0:
-                    src = h_in if h_in is not None else self.h0
-                    L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, src, L.PG_F16, k,
-                                   self.signs[layer][site], self.cflag, b, self.out[site], stream)
-                    continue
-                prev = {"qkv": "down", "o": "qkv", "gu": "o", "down": "gu"}[site]
-                n_prev = self.shapes[prev][0]
-                if self.split_above is not None and k > self.split_above:
-                    L.pg_fwht_rotate_ex(self.out[prev], L.PG_F32, n_prev, self.xrot, L.PG_Q16, self.signs[layer][site],
-                                        b, k, L.PG_FLAG_RMSNORM, stream)
-                    L.pg_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.xrot, L.PG_Q16, b,
-                               self.out[site], stream)
-                    continue
-                L.pg_rot_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.out[prev], L.PG_F32,
-                               n_prev, self.signs[layer][site], L.PG_FLAG_RMSNORM | self.cflag, b, self.out[site],
-                               stream)
-        return self.out["down"]
-
-    def _token_split(self, stream=None, h_in=None):
-        b = self.batch
-        for layer in range(self.layers):
-            for site in ORDER:
-                n, k = self.shapes[site]
-                if site == "qkv":
-                    if layer == 0:
-                        src, src_dt, flags, ldx = (h_in if h_in is not None else self.h0), L.PG_F16, 0, k
-                    else:
-                        src, src_dt, flags, ldx = self.out["down"], L.PG_F32, L.PG_FLAG_RMSNORM, self.shapes["down"][0]
-                else:
-                    prev = {"o": "qkv", "gu": "o", "down": "gu"}[site]
-                    src, src_dt, flags, ldx = self.out[prev], L.PG_F32, L.PG_FLAG_RMSNORM, self.shapes[prev][0]
-                # the first k columns of each row of the previous output are the input
-                L.pg_fwht_rotate_ex(src, src_dt, ldx, self.xrot, self.x_dtype, self.signs[layer][site], b, k, flags,
-                                    stream)
-                L.pg_qgemv(self.codes[layer][site], self.scales[layer][site], n, k, self.xrot, self.x_dtype,
-                           b, self.out[site], stream)
+        for _, _, _, call in self.launches(stream, h_in):
+            call()
         return self.out["down"]
 
     def capture(self):

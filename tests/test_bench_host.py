@@ -19,9 +19,9 @@ def test_refuses_more_than_one_gpu():
 
 
 def test_committed_traffic_matches_the_summary_and_its_sources():
-    path = os.path.join(ROOT, "profiles", "k_rot_qgemv__qwen3-4b-36L-b1__hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", "k_rot_qgemv1__qwen3-4b-36L-b1__hbm_traffic.md")
     want = [int(line.split(": ")[1]) for line in open(path) if line.startswith("traffic_bytes_per_launch:")]
-    assert bench.committed_traffic("k_rot_qgemv", "qwen3-4b-36L-b1") == want[0]
+    assert bench.committed_traffic("k_rot_qgemv1", "qwen3-4b-36L-b1") == want[0]
     assert bench.committed_traffic("no_such_kernel", "no-workload") is None
 
 
@@ -30,18 +30,18 @@ def test_committed_traffic_is_null_once_a_source_changes(tmp_path, monkeypatch):
     summary's hash no longer matches and no traffic is reported."""
     prof = tmp_path / "profiles"
     prof.mkdir()
-    src = open(os.path.join(ROOT, "profiles", "k_rot_qgemv__qwen3-4b-36L-b1__hbm_traffic.md")).read()
-    (prof / "k_rot_qgemv__w__hbm_traffic.md").write_text(src)
+    src = open(os.path.join(ROOT, "profiles", "k_rot_qgemv1__qwen3-4b-36L-b1__hbm_traffic.md")).read()
+    (prof / "k_rot_qgemv1__w__hbm_traffic.md").write_text(src)
     files = [line.split(": ", 1)[1].split() for line in src.splitlines() if line.startswith("kernel_source:")][0]
     for f in files:
         dst = tmp_path / f
         dst.parent.mkdir(parents=True, exist_ok=True)
         dst.write_bytes(open(os.path.join(ROOT, f), "rb").read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.committed_traffic("k_rot_qgemv", "w") is not None
+    assert bench.committed_traffic("k_rot_qgemv1", "w") is not None
     with open(tmp_path / files[0], "ab") as fh:
         fh.write(b"\n")
-    assert bench.committed_traffic("k_rot_qgemv", "w") is None
+    assert bench.committed_traffic("k_rot_qgemv1", "w") is None
 
 
 def test_cpu_baseline_fields():
