@@ -122,3 +122,73 @@ def test_encode_matrix_row_layout():
             blk = wr[r, 128 * b:128 * b + 128][None]
             assert scales[r, b] == p8f.block_scale_bits(blk)[0]
             assert codes[r, 32 * b:32 * b + 32].tolist() == p8f.viterbi_encode(blk, scales[r, b:b + 1])[0].tolist()
+
+
+def _golden_ties():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "viterbi_tie_example.json")) as f:
+        return json.load(f)
+
+
+def test_viterbi_tie_rule_hand_example():
+    """T1: two minimum paths meet in one state at the last step; the rule
+    keeps the predecessor s'>>1 (derived by hand in the fixture)."""
+    t = _golden_ties()["tie"]
+    w = np.array(t["w_rot"], dtype=np.float64)[None]
+    sb = p8f.float_to_fp16_bits(np.array([t["scale"]]))
+    codes = p8f.viterbi_encode(w, sb)
+    assert codes[0].tolist() == t["codes"]
+    assert p8f.block_distortion(w, codes, sb)[0] == t["distortion"]
+    other = np.array([t["codes_other_predecessor"]], dtype=np.uint8)
+    assert p8f.block_distortion(w, other, sb)[0] == t["distortion"]       # a tie, not a worse path
+
+
+def _ordered_search(w, s_val, g):
+    """All 2^G branch paths; per group the nearest point of the branch's
+    coset (ascending bytes, strict <, so the smaller byte wins ties),
+    distortions summed in group order.  Among the minimum paths: the
+    smaller end state, then going back from the end the oldest branch bit
+    of each step's predecessor state 0 before 1 (the documented
+    predecessor rule: s'>>1 before (s'>>1)|4), i.e. (u[G-4], ..., u[0])
+    compared lexicographically."""
+    pts = {}
+    for z0 in (0, 1):
+        for z1 in (0, 1):
+            s = z0 << 1
+            pts[(z0, z1)] = [(b, p8f.decode_group(b, s)) for b in range(256) if (b & 1) == z1]
+    best = None
+    for path in range(1 << g):
+        u = [(path >> (g - 1 - t)) & 1 for t in range(g)]
+        st, tot, codes = 0, 0.0, []
+        for t in range(g):
+            z0, z1 = p8f.z0_of_state(st), p8f.z1_of_branch(st, u[t])
+            bm, bb = None, None
+            for b, lv in pts[(z0, z1)]:
+                d = [w[4 * t + j] - s_val * lv[j] for j in range(4)]
+                m = ((d[0] * d[0] + d[1] * d[1]) + d[2] * d[2]) + d[3] * d[3]
+                if bm is None or m < bm:
+                    bm, bb = m, b
+            tot += bm
+            codes.append((bb & 0xFE) | u[t])
+            st = p8f.next_state(st, u[t])
+        key = (tot, st, tuple(u[t] for t in range(g - 4, -1, -1)))
+        if best is None or key < best[0]:
+            best = (key, codes)
+    return best[1]
+
+
+@pytest.mark.parametrize("g", [4, 5, 6])
+def test_viterbi_tie_rule_equals_ordered_exhaustive_search(g):
+    """Integer-valued blocks at unit scale tie often; the Viterbi output
+    equals the path an exhaustive search picks by the documented order."""
+    rng = np.random.default_rng(70 + g)
+    one = p8f.float_to_fp16_bits(np.array([1.0]))
+    ties = 0
+    for i in range(12 if g < 6 else 4):
+        w = rng.choice([0.0, 1.0, -1.0, 2.0, -2.0, 4.0], 4 * g) if i else np.array(
+            _golden_ties()["tie"]["w_rot"] + [0.0] * (4 * (g - 4)), dtype=np.float64)
+        codes = p8f.viterbi_encode(w[None], one)[0].tolist()
+        assert codes == _ordered_search(w, 1.0, g)
+        ties += 1
+    assert ties > 0

@@ -70,6 +70,18 @@ def test_rmsnorm16_closed_forms():
     assert np.array_equal(out, out.astype(np.float16).astype(np.float64))
 
 
+def test_rmsnorm16_eps_hand_examples():
+    """N1, N2: constant rows small enough that eps (1e-6) decides the fp16
+    result (values derived by hand in the fixture)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "viterbi_tie_example.json")) as f:
+        cases = json.load(f)["rmsnorm"]
+    for c in cases:
+        out = p8f.rmsnorm16(np.full((1, c["length"]), c["value"]))
+        assert np.all(out == c["out"]), (c["id"], out[0, 0])
+
+
 def test_bf16_rounding_helper():
     vals = np.array([1.0, 1.00390625, 1.005859375, -2.5, 3.0e-3], dtype=np.float32)
     bits = p8f.bf16_rne_bits(vals)
