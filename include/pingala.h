@@ -271,6 +271,19 @@ int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t
                 const uint16_t* x_rot_bf16, int64_t m, float* y, void* workspace,
                 size_t workspace_bytes, pg_stream_t stream);
 
+/* pg_qgemm_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the split workspace is the library's own scratch, a device
+ * array of 32 MiB that each GPU the library runs on holds until the
+ * process ends.  Same arguments as pg_qgemm; same result as pg_qgemm_ex with
+ * a workspace of pg_qgemm_workspace_bytes(n, k, m) bytes (bitwise).
+ * PG_ERR_UNSUPPORTED (nothing launched) when the shape needs more than the
+ * scratch holds.  Calls no allocating routine.  Every call on a GPU shares
+ * that GPU's scratch: calls that may overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller. */
+int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                     const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
+
 /* Workspace bytes that give pg_qgemm_ex its full split of K for this shape on
  * the current device (0: it would not split; 0 as well for invalid sizes). */
 size_t pg_qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m);

@@ -24,7 +24,8 @@ PG_FLAG_CARRY_STATE = 2
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
            "pg_encode", "pg_encode_ex", "pg_decode_ex",
            "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm",
-           "pg_qgemm_ex", "pg_qgemm_workspace_bytes", "pg_hbm_read")
+           "pg_qgemm_ex", "pg_qgemm_workspace_bytes", "pg_hbm_read",
+           "pg_qgemm_noalloc")
 
 
 class PgError(RuntimeError):
@@ -83,6 +84,8 @@ def lib():
         L.pg_qgemm_ex.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, ctypes.c_size_t, vp]
         L.pg_qgemm_workspace_bytes.restype = ctypes.c_size_t
         L.pg_qgemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.pg_qgemm_noalloc.restype = i32
+        L.pg_qgemm_noalloc.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
         L.pg_hbm_read.restype = i32
         L.pg_hbm_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
         _LIB = L
@@ -207,3 +210,8 @@ def pg_hbm_read(p, nbytes: int, xor_out, stream=None) -> None:
     """Streaming read of nbytes (multiple of 16) at device buffer p; the XOR of
     its 32-bit words is XOR-ed into the device u32 xor_out."""
     _check(lib().pg_hbm_read(_ptr(p), nbytes, _ptr(xor_out), _stream(stream)))
+
+
+def pg_qgemm_noalloc(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, stream=None) -> None:
+    """pg_qgemm_ex on the library's own split workspace (no allocation)."""
+    _check(lib().pg_qgemm_noalloc(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot_bf16), m, _ptr(y), _stream(stream)))

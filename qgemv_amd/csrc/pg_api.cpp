@@ -217,6 +217,26 @@ int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t
     return pg::launch_qgemm(codes, scales, n, k, x_rot_bf16, m, y, workspace, workspace_bytes, stream);
 }
 
+int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,
+                     int64_t m, float* y, pg_stream_t stream) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    if (m < 1 || m > ((int64_t)1 << 30)) return pg::fail(PG_ERR_INVALID_ARG, "m must be >= 1 (got %lld)", (long long)m);
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    PG_TRY(check_ptr(x_rot_bf16, 16, "x_rot_bf16"));
+    PG_TRY(check_ptr(y, 16, "y"));
+    const size_t need = pg::qgemm_workspace_bytes(n, k, m);
+    if (need > pg::QGEMM_SCRATCH_BYTES)
+        return pg::fail(PG_ERR_UNSUPPORTED,
+                        "pg_qgemm_noalloc: n=%lld k=%lld m=%lld needs %zu bytes of split workspace, the library's "
+                        "scratch holds %zu; use pg_qgemm_ex with a caller workspace",
+                        (long long)n, (long long)k, (long long)m, need, pg::QGEMM_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0) PG_TRY(pg::qgemm_scratch(&ws));
+    return pg::launch_qgemm(codes, scales, n, k, x_rot_bf16, m, y, ws, need, stream);
+}
+
 int pg_hbm_read(const void* p, size_t bytes, uint32_t* xor_out, pg_stream_t stream) {
     pg::clear_error();
     if (bytes == 0 || bytes % 16 != 0)

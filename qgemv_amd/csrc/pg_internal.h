@@ -54,6 +54,9 @@ struct QgPlan {
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const uint16_t* x, int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s);
 QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes);
+// the library's own split-K workspace on the current device (pg_qgemm_noalloc)
+constexpr size_t QGEMM_SCRATCH_BYTES = (size_t)32 << 20;
+int qgemm_scratch(void** out);
 size_t qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m);
 // (pg_kernels.hip) streaming read of `bytes` (a multiple of 16) at p
 int launch_hbm_read(const void* p, int64_t bytes, uint32_t* out, pg_stream_t s);

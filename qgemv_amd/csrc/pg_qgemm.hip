@@ -5,6 +5,7 @@
 // Method: "Pingala-8" landing page, section "How it works" (the trellis
 // decode); bit layout in include/pingala.h.
 #include <algorithm>
+#include <mutex>
 
 #include "pg_device.h"
 
@@ -494,6 +495,36 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
     if (grid.y > 65535) return fail(PG_ERR_UNSUPPORTED, "m too large");
     hipLaunchKernelGGL(k_qgemm_v1, grid, dim3(256), 0, (hipStream_t)s, codes, scales, (int)n, (int)k, x, (int)m, y);
     return hip_check(hipGetLastError(), "pg_qgemm launch");
+}
+
+// ---------------------------------------------------- allocation-free variant
+// The split-K workspace of pg_qgemm_noalloc: a device array in the library's
+// code object, one copy per GPU the library runs on, held until the process
+// ends.  In host code `scratch` is only a stand-in for the symbol; its device
+// address is looked up once per device (hipGetSymbolAddress) and only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[QGEMM_SCRATCH_BYTES];
+
+namespace {
+std::mutex scratch_mu;
+void* scratch_addr[64] = {};
+}  // namespace
+
+int qgemm_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PG_ERR_HIP, "pg_qgemm_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(PG_ERR_UNSUPPORTED, "pg_qgemm_noalloc: device %d out of range", dev);
+    std::lock_guard<std::mutex> lk(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PG_ERR_HIP, "pg_qgemm_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return PG_OK;
 }
 
 }  // namespace pg
