@@ -76,7 +76,18 @@ enum { PG_F32 = 0, PG_F16 = 1, PG_BF16 = 2,     /* element types of x / y */
        PG_Q16 = 3 };                               /* rotated activations, 16-bit fixed point */
 
 enum { PG_FLAG_RMSNORM = 1u,                    /* pg_fwht_rotate / pg_rot_qgemv flags */
-       PG_FLAG_CARRY_STATE = 2u };               /* codes of the carried-state variant (below) */
+       PG_FLAG_CARRY_STATE = 2u,                 /* codes of the carried-state variant (below) */
+       PG_FLAG_KERNEL_VDOT = 4u,                 /* kernel choice, for tests and tuning (below) */
+       PG_FLAG_KERNEL_MMA = 8u };
+
+/* Kernel choice.  Each product has kernels that compute the same values
+ * (within the stated tolerances): products on the v_dot4 vector
+ * instructions and products on the int8 matrix cores.  Without a choice
+ * flag the library picks by batch and shape; PG_FLAG_KERNEL_VDOT or
+ * PG_FLAG_KERNEL_MMA (at most one) selects a kernel, so that tests can check
+ * each against the oracle and a tuning sweep can time each.  Where the
+ * selected kernel does not take the shape, the call falls back to the
+ * library's own choice.  The library reads no environment variable. */
 
 /* Carried-state variant of the format (the small-state coset-trellis design
  * space of the landing page, section "Paper"): the same bytes, scales and
@@ -174,9 +185,12 @@ int pg_decode_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
  *   y        device [rows][k] of out_dtype (PG_F32 / PG_F16 / PG_BF16), or
  *            rows * pg_q16_row_bytes(k) bytes for PG_Q16
  *   sign_bits device u8 [k/8]
- *   flags    PG_FLAG_RMSNORM: first replace each row v by
- *            fp16_RNE(v / sqrt(mean(v^2) + 1e-6)) (fp32 math), as the
- *            normalisation between the layers of a linear stack.
+ *   flags    PG_FLAG_RMSNORM: first replace each row v by n(v), the
+ *            normalisation between the layers of a linear stack:
+ *              S = sum of v^2 over the row (fp32, order unspecified),
+ *              inv = rsq(fma(S, rk, 1e-6)), rk = 1/k rounded to fp32,
+ *              rsq the hardware reciprocal square root (<= 1 ulp),
+ *              n(v) = fp16_RNE(v * inv)   (every kernel computes this)
  * x and y may not overlap.  fp32 arithmetic; fp16/bf16 outputs round to
  * nearest even. */
 int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype,
@@ -209,13 +223,21 @@ int pg_fwht_rotate_ex(const void* x, int in_dtype, int64_t ldx, void* y, int out
 int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
              const void* x_rot, int x_dtype, int batch, float* y, pg_stream_t stream);
 
+/* pg_qgemv with kernel-choice flags (PG_Q16 input only; 0 is pg_qgemv):
+ * PG_FLAG_KERNEL_VDOT keeps the v_dot4 kernel at every batch,
+ * PG_FLAG_KERNEL_MMA takes the matrix cores at every batch. */
+int pg_qgemv_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                const void* x_rot, int x_dtype, int batch, uint32_t flags, float* y, pg_stream_t stream);
+
 /* One stage of a linear stack in a single launch: the RMS normalisation and
  * the run-time rotation of the activations (landing page, section "How it
  * works": a random Hadamard rotation is applied before coding, so the
  * activations take the same rotation) are the product's prologue:
  *   y[b] = W~ . R . n(x[b][0:k])
- * with n(v) = fp16_RNE(v / sqrt(mean(v^2) + 1e-6)) under PG_FLAG_RMSNORM
- * (fp32 math, mean over the k values), n(v) = v otherwise, R the input
+ * with n(v) the normalisation of pg_fwht_rotate under PG_FLAG_RMSNORM
+ * (fp16_RNE(v * rsq(fma(S, 1/k, 1e-6))), S the row's sum of squares;
+ * within rounding of fp16_RNE(v / sqrt(mean(v^2) + 1e-6))), n(v) = v
+ * otherwise, R the input
  * site's rotation (as pg_fwht_rotate), and the rotated activations carried
  * at 16-bit precision (error <= 2^-16 of the largest value of each 32
  * consecutive rotated values).
@@ -233,8 +255,11 @@ int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
  * otherwise).  The rotated values are quantised to 16-bit digits with one
  * scale per 32 values at batch 1 and per 128-block at batch 2..8 (there the
  * product runs on the matrix cores, for k <= 4096; larger k stays on the
- * batch-1 kernel).  PG_FLAG_CARRY_STATE: the codes are of the carried-state
- * variant (batch-1 kernel at every batch).  x and y may not overlap.  The
+ * batch-1 kernels).  PG_FLAG_CARRY_STATE: the codes are of the carried-state
+ * variant (v_dot4 kernel at every batch).  PG_FLAG_KERNEL_VDOT: the v_dot4
+ * products with the rotation on the matrix cores at every batch;
+ * PG_FLAG_KERNEL_MMA: the int8 matrix-core products at every batch where
+ * k <= 4096.  x and y may not overlap.  The
  * summation order is fixed: repeated calls are bitwise identical. */
 int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const void* x, int x_dtype, int64_t ldx, const uint8_t* sign_bits,
@@ -283,6 +308,17 @@ int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t
  * other host threads) race and must be serialised by the caller. */
 int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                      const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
+
+/* pg_qgemm_ex with its kernel and split plan given, for tests and tuning:
+ *   kernel  0: the pipelined 256 x 128-tile kernel (what pg_qgemm_ex runs);
+ *           1: the one-buffer 128 x 128-tile kernel (never splits)
+ *   splits  0: the library's plan; S >= 1: tiles first_split .. split S ways
+ *           (tiles before it whole), S capped by the 128-blocks of k, by 8
+ *           and by the workspace
+ * Other arguments as pg_qgemm_ex. */
+int pg_qgemm_tune(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                  const uint16_t* x_rot_bf16, int64_t m, float* y, void* workspace, size_t workspace_bytes,
+                  int kernel, int splits, int64_t first_split, pg_stream_t stream);
 
 /* Workspace bytes that give pg_qgemm_ex its full split of K for this shape on
  * the current device (0: it would not split; 0 as well for invalid sizes). */

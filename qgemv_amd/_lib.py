@@ -20,12 +20,14 @@ PG_OK, PG_ERR_INVALID_ARG, PG_ERR_UNSUPPORTED, PG_ERR_HIP = 0, -1, -2, -3
 PG_F32, PG_F16, PG_BF16, PG_Q16 = 0, 1, 2, 3
 PG_FLAG_RMSNORM = 1
 PG_FLAG_CARRY_STATE = 2
+PG_FLAG_KERNEL_VDOT = 4
+PG_FLAG_KERNEL_MMA = 8
 
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
            "pg_encode", "pg_encode_ex", "pg_decode_ex",
            "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm",
            "pg_qgemm_ex", "pg_qgemm_workspace_bytes", "pg_hbm_read",
-           "pg_qgemm_noalloc")
+           "pg_qgemm_noalloc", "pg_qgemv_ex", "pg_qgemm_tune")
 
 
 class PgError(RuntimeError):
@@ -84,6 +86,10 @@ def lib():
         L.pg_qgemm_ex.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, ctypes.c_size_t, vp]
         L.pg_qgemm_workspace_bytes.restype = ctypes.c_size_t
         L.pg_qgemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.pg_qgemv_ex.restype = i32
+        L.pg_qgemv_ex.argtypes = [vp, vp, i64, i64, vp, i32, i32, u32, vp, vp]
+        L.pg_qgemm_tune.restype = i32
+        L.pg_qgemm_tune.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, ctypes.c_size_t, i32, i32, i64, vp]
         L.pg_qgemm_noalloc.restype = i32
         L.pg_qgemm_noalloc.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
         L.pg_hbm_read.restype = i32
@@ -108,6 +114,48 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _esz(dtype: int) -> int:
+    return 4 if dtype == PG_F32 else 2
+
+
+def _need(t, nbytes: int, name: str) -> None:
+    """Check a buffer handed to the library as a device pointer: a torch
+    tensor must be a contiguous GPU tensor of at least nbytes bytes (a raw
+    integer address is passed through unchecked; the library validates
+    alignment and null pointers).  Raises ValueError before any call."""
+    if t is None or isinstance(t, int):
+        return
+    if isinstance(t, np.ndarray):
+        raise ValueError(f"{name}: a device buffer is required, got a numpy array")
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name}: tensor is not on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor is not contiguous")
+    have = t.numel() * t.element_size()
+    if nbytes > 0 and have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, the call needs {nbytes}")
+
+
+def _weights(codes, scales, n: int, k: int) -> None:
+    if n > 0 and k > 0:
+        _need(codes, n * (k // 4), "codes")
+        _need(scales, n * (k // 128) * 2, "scales")
+
+
+def _xbytes(dtype: int, rows: int, ldx: int, k: int) -> int:
+    if rows < 1 or k < 1:
+        return 0
+    if dtype == PG_Q16:
+        return rows * (q16_row_bytes_host(k))
+    return ((rows - 1) * ldx + k) * _esz(dtype)
+
+
+def q16_row_bytes_host(k: int) -> int:
+    """Bytes of one PG_Q16 row (the layout in include/pingala.h)."""
+    raw = 2 * k + k // 32 + k // 16
+    return (raw + 63) & ~63
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -115,6 +163,12 @@ def _stream(stream):
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _qgemm_need(codes, scales, n, k, x, m, y) -> None:
+    _weights(codes, scales, n, k)
+    _need(x, max(m, 0) * max(k, 0) * 2, "x_rot_bf16")
+    _need(y, max(m, 0) * max(n, 0) * 4, "y")
 
 
 def pg_version() -> int:
@@ -152,52 +206,78 @@ def pg_encode_ref(w: np.ndarray, n: int, k: int, sign_bits: np.ndarray, codes: n
 def pg_encode(w, n: int, k: int, sign_bits, codes, scales, stream=None) -> None:
     """Device buffers: w f32 [n][k], sign_bits u8 [k/8], codes u8 [n][k/4]
     out, scales 16-bit [n][k/128] out (fp16 bits)."""
+    _need(w, max(n, 0) * max(k, 0) * 4, "w")
+    _need(sign_bits, max(k, 0) // 8, "sign_bits")
+    _weights(codes, scales, n, k)
     _check(lib().pg_encode(_ptr(w), n, k, _ptr(sign_bits), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def pg_encode_ex(w, n: int, k: int, sign_bits, flags: int, codes, scales, stream=None) -> None:
     """pg_encode with format flags (PG_FLAG_CARRY_STATE: the carried-state variant)."""
+    _need(w, max(n, 0) * max(k, 0) * 4, "w")
+    _need(sign_bits, max(k, 0) // 8, "sign_bits")
+    _weights(codes, scales, n, k)
     _check(lib().pg_encode_ex(_ptr(w), n, k, _ptr(sign_bits), flags, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def pg_decode_ex(codes, scales, n: int, k: int, flags: int, w_rot, stream=None) -> None:
     """pg_decode with format flags (PG_FLAG_CARRY_STATE: the carried-state variant)."""
+    _weights(codes, scales, n, k)
+    _need(w_rot, max(n, 0) * max(k, 0) * 4, "w_rot")
     _check(lib().pg_decode_ex(_ptr(codes), _ptr(scales), n, k, flags, _ptr(w_rot), _stream(stream)))
 
 
 def pg_decode(codes, scales, n: int, k: int, w_rot, stream=None) -> None:
+    _weights(codes, scales, n, k)
+    _need(w_rot, max(n, 0) * max(k, 0) * 4, "w_rot")
     _check(lib().pg_decode(_ptr(codes), _ptr(scales), n, k, _ptr(w_rot), _stream(stream)))
 
 
 def pg_fwht_rotate(x, in_dtype: int, y, out_dtype: int, sign_bits, rows: int, k: int, flags: int = 0,
                    stream=None) -> None:
+    _need(x, _xbytes(in_dtype, rows, k, k), "x")
+    _need(y, _xbytes(out_dtype, rows, k, k), "y")
+    _need(sign_bits, max(k, 0) // 8, "sign_bits")
     _check(lib().pg_fwht_rotate(_ptr(x), in_dtype, _ptr(y), out_dtype, _ptr(sign_bits), rows, k, flags,
                                 _stream(stream)))
 
 
 def pg_fwht_rotate_ex(x, in_dtype: int, ldx: int, y, out_dtype: int, sign_bits, rows: int, k: int, flags: int = 0,
                       stream=None) -> None:
+    _need(x, _xbytes(in_dtype, rows, ldx, k), "x")
+    _need(y, _xbytes(out_dtype, rows, k, k), "y")
+    _need(sign_bits, max(k, 0) // 8, "sign_bits")
     _check(lib().pg_fwht_rotate_ex(_ptr(x), in_dtype, ldx, _ptr(y), out_dtype, _ptr(sign_bits), rows, k, flags,
                                    _stream(stream)))
 
 
 def pg_qgemv(codes, scales, n: int, k: int, x_rot, x_dtype: int, batch: int, y, stream=None) -> None:
+    _weights(codes, scales, n, k)
+    _need(x_rot, _xbytes(x_dtype, batch, k, k), "x_rot")
+    _need(y, max(batch, 0) * max(n, 0) * 4, "y")
     _check(lib().pg_qgemv(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot), x_dtype, batch, _ptr(y),
                           _stream(stream)))
 
 
 def pg_rot_qgemv(codes, scales, n: int, k: int, x, x_dtype: int, ldx: int, sign_bits, flags: int, batch: int, y,
                  stream=None) -> None:
+    _weights(codes, scales, n, k)
+    _need(x, _xbytes(x_dtype, batch, ldx, k), "x")
+    _need(sign_bits, max(k, 0) // 8, "sign_bits")
+    _need(y, max(batch, 0) * max(n, 0) * 4, "y")
     _check(lib().pg_rot_qgemv(_ptr(codes), _ptr(scales), n, k, _ptr(x), x_dtype, ldx, _ptr(sign_bits), flags,
                               batch, _ptr(y), _stream(stream)))
 
 
 def pg_qgemm(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, stream=None) -> None:
+    _qgemm_need(codes, scales, n, k, x_rot_bf16, m, y)
     _check(lib().pg_qgemm(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot_bf16), m, _ptr(y), _stream(stream)))
 
 
 def pg_qgemm_ex(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, workspace, workspace_bytes: int,
                 stream=None) -> None:
+    _qgemm_need(codes, scales, n, k, x_rot_bf16, m, y)
+    _need(workspace, workspace_bytes, "workspace")
     _check(lib().pg_qgemm_ex(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot_bf16), m, _ptr(y), _ptr(workspace),
                              workspace_bytes, _stream(stream)))
 
@@ -209,9 +289,30 @@ def pg_qgemm_workspace_bytes(n: int, k: int, m: int) -> int:
 def pg_hbm_read(p, nbytes: int, xor_out, stream=None) -> None:
     """Streaming read of nbytes (multiple of 16) at device buffer p; the XOR of
     its 32-bit words is XOR-ed into the device u32 xor_out."""
+    _need(p, nbytes, "p")
+    _need(xor_out, 4, "xor_out")
     _check(lib().pg_hbm_read(_ptr(p), nbytes, _ptr(xor_out), _stream(stream)))
 
 
 def pg_qgemm_noalloc(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, stream=None) -> None:
     """pg_qgemm_ex on the library's own split workspace (no allocation)."""
+    _qgemm_need(codes, scales, n, k, x_rot_bf16, m, y)
     _check(lib().pg_qgemm_noalloc(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot_bf16), m, _ptr(y), _stream(stream)))
+
+
+def pg_qgemv_ex(codes, scales, n: int, k: int, x_rot, x_dtype: int, batch: int, flags: int, y, stream=None) -> None:
+    """pg_qgemv with kernel-choice flags (PG_FLAG_KERNEL_VDOT / PG_FLAG_KERNEL_MMA)."""
+    _weights(codes, scales, n, k)
+    _need(x_rot, _xbytes(x_dtype, batch, k, k), "x_rot")
+    _need(y, max(batch, 0) * max(n, 0) * 4, "y")
+    _check(lib().pg_qgemv_ex(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot), x_dtype, batch, flags, _ptr(y),
+                             _stream(stream)))
+
+
+def pg_qgemm_tune(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, workspace, workspace_bytes: int, kernel: int,
+                  splits: int, first_split: int, stream=None) -> None:
+    """pg_qgemm_ex with its kernel (0 pipelined, 1 one-buffer) and split plan given."""
+    _qgemm_need(codes, scales, n, k, x_rot_bf16, m, y)
+    _need(workspace, workspace_bytes, "workspace")
+    _check(lib().pg_qgemm_tune(_ptr(codes), _ptr(scales), n, k, _ptr(x_rot_bf16), m, _ptr(y), _ptr(workspace),
+                               workspace_bytes, kernel, splits, first_split, _stream(stream)))

@@ -143,17 +143,27 @@ int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype, const ui
     return pg_fwht_rotate_ex(x, in_dtype, k, y, out_dtype, sign_bits, rows, k, flags, stream);
 }
 
-int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x_rot,
-             int x_dtype, int batch, float* y, pg_stream_t stream) {
+int pg_qgemv_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x_rot,
+                int x_dtype, int batch, uint32_t flags, float* y, pg_stream_t stream) {
     pg::clear_error();
     PG_TRY(check_nk(n, k));
     if (batch < 1 || batch > 8) return pg::fail(PG_ERR_INVALID_ARG, "batch must be 1..8 (got %d)", batch);
     PG_TRY(check_dtype(x_dtype, "x_dtype", false, true));
+    if (flags & ~(uint32_t)(PG_FLAG_KERNEL_VDOT | PG_FLAG_KERNEL_MMA))
+        return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if ((flags & PG_FLAG_KERNEL_VDOT) && (flags & PG_FLAG_KERNEL_MMA))
+        return pg::fail(PG_ERR_INVALID_ARG, "PG_FLAG_KERNEL_VDOT and PG_FLAG_KERNEL_MMA exclude each other");
+    if (flags && x_dtype != PG_Q16) return pg::fail(PG_ERR_INVALID_ARG, "kernel choice needs PG_Q16 input");
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 2, "scales"));
     PG_TRY(check_ptr(x_rot, 16, "x_rot"));
     PG_TRY(check_ptr(y, 16, "y"));
-    return pg::launch_qgemv(codes, scales, n, k, x_rot, x_dtype, batch, y, stream);
+    return pg::launch_qgemv(codes, scales, n, k, x_rot, x_dtype, batch, flags, y, stream);
+}
+
+int pg_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x_rot,
+             int x_dtype, int batch, float* y, pg_stream_t stream) {
+    return pg_qgemv_ex(codes, scales, n, k, x_rot, x_dtype, batch, 0, y, stream);
 }
 
 int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x, int x_dtype,
@@ -163,8 +173,10 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
     if (batch < 1 || batch > 8) return pg::fail(PG_ERR_INVALID_ARG, "batch must be 1..8 (got %d)", batch);
     PG_TRY(check_dtype(x_dtype, "x_dtype", false, false));
     if (ldx < k) return pg::fail(PG_ERR_INVALID_ARG, "ldx (%lld) < k (%lld)", (long long)ldx, (long long)k);
-    if (flags & ~(PG_FLAG_RMSNORM | PG_FLAG_CARRY_STATE))
+    if (flags & ~(uint32_t)(PG_FLAG_RMSNORM | PG_FLAG_CARRY_STATE | PG_FLAG_KERNEL_VDOT | PG_FLAG_KERNEL_MMA))
         return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if ((flags & PG_FLAG_KERNEL_VDOT) && (flags & PG_FLAG_KERNEL_MMA))
+        return pg::fail(PG_ERR_INVALID_ARG, "PG_FLAG_KERNEL_VDOT and PG_FLAG_KERNEL_MMA exclude each other");
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 4, "scales"));
     PG_TRY(check_ptr(x, 16, "x"));
@@ -190,11 +202,16 @@ size_t pg_qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m) {
     return pg::qgemm_workspace_bytes(n, k, m);
 }
 
-int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,
-                int64_t m, float* y, void* workspace, size_t workspace_bytes, pg_stream_t stream) {
+int pg_qgemm_tune(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,
+                  int64_t m, float* y, void* workspace, size_t workspace_bytes, int kernel, int splits,
+                  int64_t first_split, pg_stream_t stream) {
     pg::clear_error();
     PG_TRY(check_nk(n, k));
     if (m < 1 || m > ((int64_t)1 << 30)) return pg::fail(PG_ERR_INVALID_ARG, "m must be >= 1 (got %lld)", (long long)m);
+    if (kernel != 0 && kernel != 1) return pg::fail(PG_ERR_INVALID_ARG, "kernel must be 0 or 1 (got %d)", kernel);
+    if (splits < 0 || first_split < 0)
+        return pg::fail(PG_ERR_INVALID_ARG, "splits and first_split must be >= 0 (got %d, %lld)", splits,
+                        (long long)first_split);
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 2, "scales"));
     PG_TRY(check_ptr(x_rot_bf16, 16, "x_rot_bf16"));
@@ -214,7 +231,13 @@ int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t
             if (w0 < a + o.bytes && a < w1) return pg::fail(PG_ERR_INVALID_ARG, "workspace overlaps %s", o.name);
         }
     }
-    return pg::launch_qgemm(codes, scales, n, k, x_rot_bf16, m, y, workspace, workspace_bytes, stream);
+    return pg::launch_qgemm(codes, scales, n, k, x_rot_bf16, m, y, workspace, workspace_bytes, stream, kernel, splits,
+                            first_split);
+}
+
+int pg_qgemm_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,
+                int64_t m, float* y, void* workspace, size_t workspace_bytes, pg_stream_t stream) {
+    return pg_qgemm_tune(codes, scales, n, k, x_rot_bf16, m, y, workspace, workspace_bytes, 0, 0, 0, stream);
 }
 
 int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,

@@ -128,6 +128,12 @@ __device__ __forceinline__ float wave_max(float v) {
 
 constexpr int Q16_MAXQ = 32512;
 
+// The stack normalisation's factor for a row of k values whose squares sum
+// to ss (rk = 1/k rounded to fp32): the hardware reciprocal square root of
+// fma(ss, rk, 1e-6).  Every kernel that normalises calls this, so that n(v) =
+// fp16_RNE(v * rms_inv(ss, rk)) has one definition.
+__device__ __forceinline__ float rms_inv(float ss, float rk) { return __builtin_amdgcn_rsqf(fmaf(ss, rk, 1e-6f)); }
+
 // (a & m) | c and a ^ b ^ c, one gfx950 three-input bit operation each
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
     return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);

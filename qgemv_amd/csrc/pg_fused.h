@@ -166,6 +166,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     uint32_t* cprev = reinterpret_cast<uint32_t*>(wsum + (size_t)BT * W);  // [64 teams][16 row slots]: last
                                                                            // code dword of each team's chunks
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
+    const float rk = 1.0f / (float)k;                 // computed before any wait
     constexpr bool carry = CARRY;                      // codes of the carried-state variant
 
     // this lane's column of chunks and its rows
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
             if (norm) {
                 float tot = 0.0f;
                 for (int w = 0; w < W; ++w) tot += wsum[b * W + w];
-                inv = __builtin_amdgcn_rsqf(tot * __builtin_amdgcn_rcpf((float)k) + 1e-6f);
+                inv = rms_inv(tot, rk);
             }
     #pragma unroll
             for (int u = 0; u < XG; ++u) {

@@ -1,7 +1,5 @@
 // Launch side of the fused stage (pg_fused.h): the launch shape and the
 // P8F v1 instances; the carried-state ones are in pg_fused_carry.hip.
-#include <string.h>
-
 #include "pg_fused.h"
 
 namespace pg {
@@ -11,11 +9,6 @@ namespace pg {
 int fused_shape(int64_t n, int64_t k, int batch, FusedShape* out) {
     FusedShape S;
     S.W = 8;                                           // the kernel assumes 512 threads
-    int R_req = 0;
-    if (const char* e = getenv("PG_FUSED_ROWS")) {     // rows per workgroup, for tuning sweeps
-        const int r2 = atoi(e);
-        if (r2 > 0) R_req = r2;
-    }
     const int nchunk = (int)(k / 64), nbk = (int)(k / 128);
     S.CG = (nchunk + 7) / 8;
     if (S.CG > 8 * S.W) return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
@@ -25,7 +18,7 @@ int fused_shape(int64_t n, int64_t k, int batch, FusedShape* out) {
         return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for pg_rot_qgemv", (long long)k);
     (void)nbk;
     const int64_t cus = compute_units();
-    int64_t R = R_req > 0 ? R_req : (n + cus - 1) / cus;
+    int64_t R = (n + cus - 1) / cus;
     if (R > 16 * S.RP) R = 16 * S.RP;                      // at most 16 rows per lane
     if (R > n) R = n;
     S.R = (int)R;
@@ -59,11 +52,12 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
     if (x_dt == PG_F32 && !(flags & PG_FLAG_RMSNORM))
         return fail(PG_ERR_UNSUPPORTED, "pg_rot_qgemv: fp32 input needs PG_FLAG_RMSNORM (its rotation runs in fp16)");
     hipStream_t st = (hipStream_t)s;
-    // batch 2..8 on the matrix cores where the shape fits (PG_FUSED_KERNEL=vdot
-    // keeps the v_dot4 stage, =mma takes the matrix cores at any batch; for tests)
-    const char* kern = getenv("PG_FUSED_KERNEL");
-    const bool force_v = kern && strcmp(kern, "vdot") == 0, force_m = kern && strcmp(kern, "mma") == 0;
-    if (!(flags & PG_FLAG_CARRY_STATE) && !force_v && (force_m || batch >= 2)) {
+    // batch 2..8 on the matrix cores where the shape fits (PG_FLAG_KERNEL_VDOT
+    // keeps the v_dot4 stage, PG_FLAG_KERNEL_MMA takes the matrix cores at
+    // any batch)
+    const bool carry = (flags & PG_FLAG_CARRY_STATE) != 0;
+    const bool force_v = (flags & PG_FLAG_KERNEL_VDOT) != 0, force_m = (flags & PG_FLAG_KERNEL_MMA) != 0;
+    if (!carry && !force_v && (force_m || batch >= 2)) {
         const int r = launch_rot_qmma(codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
         if (r != PG_ERR_UNSUPPORTED) return r;
     }
@@ -71,7 +65,7 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
     // rotation is at most one round per wave (k <= 4096); larger k keeps the
     // matrix-core rotation below, which is faster there (k = 9728: 8.5 against
     // 9.1 us per launch)
-    if (batch == 1 && !(flags & PG_FLAG_CARRY_STATE) && k <= 4096)
+    if (batch == 1 && !carry && !force_v && k <= 4096)
         return launch_rot_qgemv1(codes, scales, n, k, x, x_dt, sign_bits, flags, y, st);
     if (flags & PG_FLAG_CARRY_STATE)
         return launch_fused_carry(S, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);

@@ -65,6 +65,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
     float* part = reinterpret_cast<float*>(dig + fused_row_bytes(k));          // [R][CG] team sums
     float* wsum = part + R * CG;                                               // [W] sums of squares
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
+    const float rk = 1.0f / (float)k;                 // computed before any wait
 
     // ---- 1. requests: the lane's x values and sign words of every round,
     // then its code chunks and scales (memory operations of a wave complete
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
         float tot = 0.0f;
 #pragma unroll
         for (int w = 0; w < W; ++w) tot += wsum[w];
-        inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+        inv = rms_inv(tot, rk);
     }
 
     // ---- 3. rotation rounds: n(x) rounded to fp16 and sign-flipped, the

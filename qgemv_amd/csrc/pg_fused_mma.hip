@@ -74,6 +74,7 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
     uint16_t* swt = reinterpret_cast<uint16_t*>(lds + Ly.swt);
     uint8_t* ctile = lds + Ly.ctile + (size_t)wave * MMA_TILE_BYTES;
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
+    const float rk = 1.0f / (float)k;                 // computed before any wait
     constexpr int esz = XDT == PG_F32 ? 4 : 2;
 
     // ---- 1. requests (past the end: repeats of valid addresses)
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
 #pragma unroll
                     for (int t = 0; t < 8; ++t) ss += xv[u][t] * xv[u][t];
             ss = wave_sum(ss);
-            inv = __builtin_amdgcn_rsqf(ss * __builtin_amdgcn_rcpf((float)k) + 1e-6f);
+            inv = rms_inv(ss, rk);
         }
 #pragma unroll
         for (int u = 0; u < KV; ++u) {

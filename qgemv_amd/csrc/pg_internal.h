@@ -36,7 +36,7 @@ int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64
 int launch_fwht(const void* x, int in_dt, int64_t ldx, void* y, int out_dt, const uint8_t* sign_bits,
                 int64_t rows, int64_t k, uint32_t flags, pg_stream_t s);
 int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
-                 const void* x, int x_dt, int batch, float* y, pg_stream_t s);
+                 const void* x, int x_dt, int batch, uint32_t kflags, float* y, pg_stream_t s);
 int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
                      int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
                      pg_stream_t s);
@@ -52,8 +52,10 @@ struct QgPlan {
     int splits;
 };
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
-                 const uint16_t* x, int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s);
+                 const uint16_t* x, int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s,
+                 int kernel = 0, int splits = 0, int64_t first_split = 0);
 QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes);
+QgPlan qgemm_forced(int64_t n, int64_t k, int64_t m, size_t ws_bytes, int splits, int64_t t_full);
 // the library's own split-K workspace on the current device (pg_qgemm_noalloc)
 constexpr size_t QGEMM_SCRATCH_BYTES = (size_t)32 << 20;
 int qgemm_scratch(void** out);

@@ -6,8 +6,6 @@
 // Ungerboeck trellis over groups of 4 weights, the state carried from group
 // to group choosing the value set of the next group, plus a random Hadamard
 // rotation.  Bit layout: format P8F v1 as stated in include/pingala.h.
-#include <string.h>
-
 #include "pg_device.h"
 
 namespace pg {
@@ -92,6 +90,7 @@ __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, void* 
     const int64_t xbase = row * ldx;                          // row of x (ldx elements apart)
     const int64_t base = row * (int64_t)k;                    // row of an fp output
     __shared__ float red[4];
+    const float rk = 1.0f / (float)k;
     // this wave's block first (its loads overlap the normalisation pass)
     const bool active = blk < nblk;
     const int i0 = (active ? blk : 0) * 128 + lane, i1 = i0 + 64;
@@ -120,7 +119,7 @@ __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, void* 
         if (lane == 0) red[wave] = ss;
         __syncthreads();
         const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-        inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+        inv = rms_inv(tot, rk);
     } else if (flags & PG_FLAG_RMSNORM) {
         // the whole row's squares: up to 64 loads per thread in flight at once
         float ss = 0.0f;
@@ -138,7 +137,7 @@ __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, void* 
         if (lane == 0) red[wave] = ss;
         __syncthreads();
         const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-        inv = 1.0f / sqrtf(tot / (float)k + 1e-6f);
+        inv = rms_inv(tot, rk);
     }
     if (!active) return;
     const float cnorm = 0.08838834764831845f;   // 2^-3.5
@@ -564,13 +563,12 @@ int launch_q16_bs(int R, int W, const uint8_t* codes, const uint16_t* scales, in
 }  // namespace
 
 int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
-                 int x_dt, int batch, float* y, pg_stream_t s) {
+                 int x_dt, int batch, uint32_t kflags, float* y, pg_stream_t s) {
     if (x_dt == PG_Q16) {
         // batch 2..8: the matrix-core kernel, whose vector work per weight
-        // does not grow with the batch (PG_QGEMV_KERNEL=q16 keeps the
-        // v_dot4 kernel, =mma takes the matrix cores at any batch; for tests)
-        const char* kern = getenv("PG_QGEMV_KERNEL");
-        const bool force_q16 = kern && strcmp(kern, "q16") == 0, force_mma = kern && strcmp(kern, "mma") == 0;
+        // does not grow with the batch (PG_FLAG_KERNEL_VDOT keeps the v_dot4
+        // kernel, PG_FLAG_KERNEL_MMA takes the matrix cores at any batch)
+        const bool force_q16 = (kflags & PG_FLAG_KERNEL_VDOT) != 0, force_mma = (kflags & PG_FLAG_KERNEL_MMA) != 0;
         if (force_mma || (!force_q16 && batch >= 2))
             return launch_qgemv_mma(codes, scales, n, k, (const uint8_t*)x, batch, y, s);
         const int stride = (int)q16_row_bytes(k);
@@ -581,8 +579,6 @@ int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
         const int64_t wgs = (n + 7) / 8;
         int W = 1;
         while (W < 8 && wgs * W < 2048 && (k / 64) >= 16 * W) W *= 2;
-        const char* env = getenv("PG_QGEMV_SHAPE");          // development override "R,W"
-        if (env) { int a = 0, b = 0; if (sscanf(env, "%d,%d", &a, &b) == 2 && (a == 1 || a == 2) && (b == 1 || b == 2 || b == 4 || b == 8)) { R = a; W = b; } }
         // batch rows per pass: the staged activations fit the LDS budget
         const size_t budget = 96 * 1024;
         int bs = 1;

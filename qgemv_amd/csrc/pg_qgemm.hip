@@ -420,8 +420,7 @@ __global__ __launch_bounds__(256) void k_qgemm_sum(float* __restrict__ y, const 
 // The candidates: no split; every tile split S ways; the tiles of the full
 // rounds whole and those of the last, partial round split S ways (run after
 // the full rounds, they fill it).  A split is taken when the model gives 8%
-// or more.  PG_QGEMM_SPLITS=S (every tile) or S:T (tiles T.. only) forces a
-// plan, still within the 128-blocks and the workspace.
+// or more.
 QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes) {
     const int64_t tiles = ((n + Q2_BN - 1) / Q2_BN) * ((m + Q2_BM - 1) / Q2_BM), nbk = k / 128;
     const int64_t cus = compute_units();
@@ -431,17 +430,6 @@ QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes) {
         return sp >= 1 && sp <= std::min<int64_t>(8, nbk) && t_full >= 0 && t_full < tiles &&
                (double)(sp - 1) * (double)(tiles - t_full) * tb <= (double)ws_bytes;
     };
-    if (const char* e = getenv("PG_QGEMM_SPLITS")) {
-        long long sp = 0, tf = 0;
-        const int got = sscanf(e, "%lld:%lld", &sp, &tf);
-        if (got >= 1 && sp > 1) {
-            if (got < 2) tf = 0;
-            sp = std::min<long long>(sp, std::min<int64_t>(8, nbk));
-            while (sp > 1 && !fits(tf, sp)) --sp;
-            return sp > 1 ? QgPlan{tf, (int)sp} : none;
-        }
-        if (got >= 1 && sp == 1) return none;
-    }
     auto rt = [](double blocks) { return 10.0 + 2.2 * blocks; };
     auto per = [&](int64_t sp) { return (double)((nbk + sp - 1) / sp); };
     auto sum_cost = [&](int64_t nrem, int64_t sp) { return 2.0 + (double)(sp + 1) * (double)nrem * tb / 5e6; };
@@ -463,6 +451,17 @@ QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes) {
     return cbest <= 0.92 * c1 ? best : none;
 }
 
+// A given plan (pg_qgemm_tune): tiles t_full.. split `splits` ways, the split
+// count lowered until it fits the 128-blocks, 8 and the workspace.
+QgPlan qgemm_forced(int64_t n, int64_t k, int64_t m, size_t ws_bytes, int splits, int64_t t_full) {
+    const int64_t tiles = ((n + Q2_BN - 1) / Q2_BN) * ((m + Q2_BM - 1) / Q2_BM), nbk = k / 128;
+    const double tb = (double)Q2_BM * Q2_BN * 4;
+    if (t_full < 0 || t_full >= tiles) return QgPlan{tiles, 1};
+    int64_t sp = std::min<int64_t>(splits, std::min<int64_t>(8, nbk));
+    while (sp > 1 && (double)(sp - 1) * (double)(tiles - t_full) * tb > (double)ws_bytes) --sp;
+    return sp > 1 ? QgPlan{t_full, (int)sp} : QgPlan{tiles, 1};
+}
+
 size_t qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m) {
     const int64_t tiles = ((n + Q2_BN - 1) / Q2_BN) * ((m + Q2_BM - 1) / Q2_BM);
     const QgPlan p = qgemm_plan(n, k, m, (size_t)-1 / 2);
@@ -470,13 +469,15 @@ size_t qgemm_workspace_bytes(int64_t n, int64_t k, int64_t m) {
 }
 
 int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x,
-                 int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s) {
+                 int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s, int kernel, int splits,
+                 int64_t first_split) {
     const int64_t tn = (n + Q2_BN - 1) / Q2_BN, tm = (m + Q2_BM - 1) / Q2_BM, tiles = tn * tm;
-    // the pipelined kernel is the product; PG_QGEMM_KERNEL=1 selects the
-    // plain one-buffer kernel (kept as a second implementation for tests)
-    const char* e = getenv("PG_QGEMM_KERNEL");
-    if (!(e && atoi(e) == 1)) {
-        const QgPlan p = workspace ? qgemm_plan(n, k, m, ws_bytes) : QgPlan{tiles, 1};
+    // the pipelined kernel is the product; kernel 1 is the plain one-buffer
+    // kernel (kept as a second implementation, for tests)
+    if (kernel != 1) {
+        const QgPlan p = !workspace ? QgPlan{tiles, 1}
+                         : splits >= 1 ? qgemm_forced(n, k, m, ws_bytes, splits, first_split)
+                                       : qgemm_plan(n, k, m, ws_bytes);
         const int64_t nrem = tiles - p.t_full, grid = p.t_full + nrem * p.splits;
         if (grid > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
         const int remap = (p.t_full % 8 == 0 ? 1 : 0) | ((nrem * p.splits) % 8 == 0 ? 2 : 0);

@@ -243,10 +243,6 @@ int launch_qgemv_mma(const uint8_t* codes, const uint16_t* scales, int64_t n, in
         return fail(PG_ERR_UNSUPPORTED, "k=%lld too large for the batched PG_Q16 path", (long long)k);
     int64_t per = (n + cus - 1) / cus;
     int64_t R = 16 * ((per + 15) / 16);
-    if (const char* e = getenv("PG_MMA_ROWS")) {             // rows per workgroup, for tuning sweeps
-        const int r2 = atoi(e);
-        if (r2 >= 16) R = 16 * (r2 / 16);
-    }
     if (R > 128) R = 128;                                    // 8 waves x R x 64 B of partial sums
     while (R > 16 && (R / 16) * nbk4 > MMA_MAX_ITEMS) R -= 16;
     const int tpw = (int)(((R / 16) * (nbk4 / 4) + 7) / 8);

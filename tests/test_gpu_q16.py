@@ -17,15 +17,17 @@ from tests.helpers import TOL, dev, encoded_qwen, encoded_single, host, rel_err_
 pytestmark = pytest.mark.gpu
 
 
+_KFLAGS = {"auto": 0, "q16": q.PG_FLAG_KERNEL_VDOT, "mma": q.PG_FLAG_KERNEL_MMA}
+_kflag = [0]
+
+
 @pytest.fixture(params=["auto", "q16", "mma"])
-def kernel(request, monkeypatch):
-    """Which PG_Q16 product kernel pg_qgemv runs: its own choice by batch,
-    or one forced through PG_QGEMV_KERNEL."""
-    if request.param == "auto":
-        monkeypatch.delenv("PG_QGEMV_KERNEL", raising=False)
-    else:
-        monkeypatch.setenv("PG_QGEMV_KERNEL", request.param)
-    return request.param
+def kernel(request):
+    """Which PG_Q16 product kernel pg_qgemv_ex runs: its own choice by batch,
+    or one selected by PG_FLAG_KERNEL_VDOT / PG_FLAG_KERNEL_MMA."""
+    _kflag[0] = _KFLAGS[request.param]
+    yield request.param
+    _kflag[0] = 0
 
 
 def _rotate_q16(x_np, in_dt, sb, rows, k, flags=0):
@@ -40,7 +42,7 @@ def _qgemv_q16(codes, scales, buf, batch):
     import torch
     n, kg = codes.shape
     y = torch.empty((batch, n), dtype=torch.float32, device="cuda")
-    q.pg_qgemv(dev(codes), dev(scales), n, 4 * kg, dev(buf), q.PG_Q16, batch, y)
+    q.pg_qgemv_ex(dev(codes), dev(scales), n, 4 * kg, dev(buf), q.PG_Q16, batch, _kflag[0], y)
     torch.cuda.synchronize()
     return host(y)
 

@@ -18,21 +18,25 @@ def _qgemm(codes, scales, xb):
     k = 4 * kg
     m = xb.shape[0]
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-    q.pg_qgemm(dev(codes), dev(scales), n, k, dev(xb), m, y)
+    if _kernel[0] is None:
+        q.pg_qgemm(dev(codes), dev(scales), n, k, dev(xb), m, y)
+    else:
+        q.pg_qgemm_tune(dev(codes), dev(scales), n, k, dev(xb), m, y, None, 0, _kernel[0], 0, 0)
     torch.cuda.synchronize()
     return host(y)
 
 
+_kernel = [None]
+
+
 @pytest.fixture(params=["auto", "1", "2"])
-def kernel(request, monkeypatch):
-    """Which product kernel pg_qgemm runs: its own choice by grid size, or
-    one forced through PG_QGEMM_KERNEL (the 128x128 tile or the pipelined
-    256x128 tile)."""
-    if request.param == "auto":
-        monkeypatch.delenv("PG_QGEMM_KERNEL", raising=False)
-    else:
-        monkeypatch.setenv("PG_QGEMM_KERNEL", request.param)
-    return request.param
+def kernel(request):
+    """Which product kernel runs: pg_qgemm's own, or one selected through
+    pg_qgemm_tune (1: the 128x128-tile one-buffer kernel, 2: the pipelined
+    256x128-tile kernel, which pg_qgemm runs)."""
+    _kernel[0] = {"auto": None, "1": 1, "2": 0}[request.param]
+    yield request.param
+    _kernel[0] = None
 
 
 @pytest.mark.parametrize("m,n,k", [(128, 128, 128), (256, 384, 512), (77, 130, 640), (1, 5, 256), (300, 1024, 2560),
@@ -86,9 +90,10 @@ def test_one_hot_column(kernel):
 
 
 # ----------------------------------------------------------------- split K
-def _qgemm_ex(codes, scales, xb, ws_bytes=None, guard=0):
+def _qgemm_ex(codes, scales, xb, ws_bytes=None, guard=0, plan=None):
     """pg_qgemm_ex with a workspace of ws_bytes (default: the full split)
-    followed by `guard` float32 values that must stay untouched."""
+    followed by `guard` float32 values that must stay untouched; with a plan
+    "S" or "S:T", pg_qgemm_tune with that split."""
     import torch
     n, kg = codes.shape
     k = 4 * kg
@@ -97,7 +102,11 @@ def _qgemm_ex(codes, scales, xb, ws_bytes=None, guard=0):
         ws_bytes = q.pg_qgemm_workspace_bytes(n, k, m)
     ws = torch.full((ws_bytes // 4 + guard + 4,), 7.0, dtype=torch.float32, device="cuda")
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-    q.pg_qgemm_ex(dev(codes), dev(scales), n, k, dev(xb), m, y, ws, ws_bytes)
+    if plan is None:
+        q.pg_qgemm_ex(dev(codes), dev(scales), n, k, dev(xb), m, y, ws, ws_bytes)
+    else:
+        sp, _, t = plan.partition(":")
+        q.pg_qgemm_tune(dev(codes), dev(scales), n, k, dev(xb), m, y, ws, ws_bytes, 0, int(sp), int(t or 0))
     torch.cuda.synchronize()
     if guard:
         assert (host(ws[ws_bytes // 4:]) == 7.0).all(), "workspace written past workspace_bytes"
@@ -130,15 +139,14 @@ TILE_BYTES = 256 * 128 * 4
 @pytest.mark.parametrize("plan", ["2", "3", "8", "2:1", "3:5"])
 @pytest.mark.parametrize("m,n,k", [(77, 130, 1152), (256, 384, 512), (3, 1, 1024), (300, 1024, 2560),
                                    (513, 1030, 1152)])
-def test_forced_splits_ragged(m, n, k, plan, monkeypatch):
-    """Split plans forced through PG_QGEMM_SPLITS: S (every tile split S ways,
+def test_forced_splits_ragged(m, n, k, plan):
+    """Split plans given to pg_qgemm_tune: S (every tile split S ways,
     capped at the number of 128-blocks) or S:T (tiles T.. split, the others
     whole), on ragged tiles and odd n (the sum kernel's scalar edge); the
     workspace past the parts stays untouched."""
-    monkeypatch.setenv("PG_QGEMM_SPLITS", plan)
     codes, scales, xb = _case(m, n, k)
     tiles = -(-n // 128) * -(-m // 256)
-    y = _qgemm_ex(codes, scales, xb, ws_bytes=7 * tiles * TILE_BYTES, guard=64)
+    y = _qgemm_ex(codes, scales, xb, ws_bytes=7 * tiles * TILE_BYTES, guard=64, plan=plan)
     ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb))
     assert np.max(rel_err_rows(y, ref)) <= TOL
 

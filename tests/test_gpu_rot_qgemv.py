@@ -15,16 +15,21 @@ from tests.helpers import TOL, dev, encoded_qwen, host, oracle_chain, rel_err, r
 pytestmark = pytest.mark.gpu
 
 
+_KFLAGS = {"auto": 0, "vdot": q.PG_FLAG_KERNEL_VDOT, "mma": q.PG_FLAG_KERNEL_MMA}
+_kflag = [0]
+
+
 @pytest.fixture(params=["auto", "vdot", "mma"])
-def kernel(request, monkeypatch):
-    """Which kernel pg_rot_qgemv runs: its own choice by batch, or one forced
-    through PG_FUSED_KERNEL (the matrix-core kernel takes k <= 4096 only and
-    leaves larger k to the v_dot4 kernel)."""
-    if request.param == "auto":
-        monkeypatch.delenv("PG_FUSED_KERNEL", raising=False)
-    else:
-        monkeypatch.setenv("PG_FUSED_KERNEL", request.param)
-    return request.param
+def kernel(request):
+    """Which kernel pg_rot_qgemv runs: its own choice by batch (the
+    register-rotation stage at batch 1 for k <= 4096, the matrix-core stage
+    from batch 2), the v_dot4 stage with the matrix-core rotation at every
+    batch (PG_FLAG_KERNEL_VDOT), or the matrix-core stage at every batch
+    (PG_FLAG_KERNEL_MMA; it takes k <= 4096 only and leaves larger k to the
+    library's choice)."""
+    _kflag[0] = _KFLAGS[request.param]
+    yield request.param
+    _kflag[0] = 0
 
 
 def _run(codes, scales, x, x_dt, ldx, k, sb, flags):
@@ -32,7 +37,7 @@ def _run(codes, scales, x, x_dt, ldx, k, sb, flags):
     n = codes.shape[0]
     b = x.shape[0]
     y = torch.empty((b, n), dtype=torch.float32, device="cuda")
-    q.pg_rot_qgemv(dev(codes), dev(scales), n, k, dev(x), x_dt, ldx, dev(sb), flags, b, y)
+    q.pg_rot_qgemv(dev(codes), dev(scales), n, k, dev(x), x_dt, ldx, dev(sb), flags | _kflag[0], b, y)
     torch.cuda.synchronize()
     return host(y)
 

@@ -68,7 +68,13 @@ def test_codebook_table_matches_oracle():
     lambda: q.pg_fwht_rotate_ex(1 << 20, 0, 4096, (1 << 20) + 4 * 4096 + 16, 0, 1 << 20, 2, 256, 0,
                                 stream=0),                                                   # overlap, 2nd row
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 255, 1 << 20, 1, 1, 1 << 24, stream=0),  # ldx < k
-    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 4, 1, 1 << 24, stream=0),  # flags
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 16, 1, 1 << 24, stream=0),  # flags
+    lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, 1 << 20, 13, 1, 1 << 24, stream=0),  # vdot+mma
+    lambda: q.pg_qgemv_ex(1 << 20, 1 << 20, 8, 256, 1 << 20, 3, 2, 12, 1 << 24, stream=0),  # vdot+mma
+    lambda: q.pg_qgemv_ex(1 << 20, 1 << 20, 8, 256, 1 << 20, 0, 2, 4, 1 << 24, stream=0),   # choice, fp32 x
+    lambda: q.pg_qgemv_ex(1 << 20, 1 << 20, 8, 256, 1 << 20, 3, 2, 1, 1 << 24, stream=0),   # flags
+    lambda: q.pg_qgemm_tune(1 << 20, 1 << 20, 8, 256, 1 << 21, 4, 1 << 22, None, 0, 2, 0, 0, stream=0),   # kernel
+    lambda: q.pg_qgemm_tune(1 << 20, 1 << 20, 8, 256, 1 << 21, 4, 1 << 22, None, 0, 0, -1, 0, stream=0),  # splits
     lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 256, 4, 1 << 24, stream=0),                  # flags
     lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 200, 2, 1 << 24, stream=0),                  # k % 128
     lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 256, 2, (1 << 24) + 4, stream=0),            # w align
@@ -168,3 +174,53 @@ def test_qgemm_workspace_bytes():
     assert q.pg_qgemm_workspace_bytes(8, 200, 4) == 0
     assert q.pg_qgemm_workspace_bytes(8, 256, 0) == 0
     assert q.pg_qgemm_workspace_bytes(0, 256, 4) == 0
+
+
+class _FakeDeviceTensor:
+    """Stands in for a GPU tensor in the binding's checks (no GPU here)."""
+
+    def __init__(self, nbytes, contiguous=True):
+        self._n, self._c, self.is_cuda = nbytes, contiguous, True
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        return 1 << 20
+
+
+@pytest.mark.parametrize("bad,what", [
+    (lambda t: q.pg_decode(t(256 * 64 - 1), t(256 * 4), 256, 256, t(256 * 256 * 4)), "codes"),
+    (lambda t: q.pg_decode(t(256 * 64), t(256 * 4 - 2), 256, 256, t(256 * 256 * 4)), "scales"),
+    (lambda t: q.pg_decode(t(256 * 64), t(256 * 4), 256, 256, t(256 * 256 * 4 - 4)), "w_rot"),
+    (lambda t: q.pg_rot_qgemv(t(64 * 64), t(64 * 4), 64, 256, t((300 + 256) * 4 - 4), 0, 300, t(32), 1, 2, t(2 * 64 * 4)),
+     "x"),
+    (lambda t: q.pg_rot_qgemv(t(64 * 64), t(64 * 4), 64, 256, t(300 * 4 + 256 * 4), 0, 300, t(31), 1, 2,
+                              t(2 * 64 * 4)), "sign_bits"),
+    (lambda t: q.pg_qgemv(t(64 * 64), t(64 * 4), 64, 256, t(2 * q.pg_q16_row_bytes(256) - 1), 3, 2, t(2 * 64 * 4)),
+     "x_rot"),
+    (lambda t: q.pg_qgemm_ex(t(64 * 64), t(64 * 4), 64, 256, t(8 * 256 * 2), 8, t(8 * 64 * 4), t(100), 128),
+     "workspace"),
+    (lambda t: q.pg_fwht_rotate(t(4 * 256 * 2), 1, t(4 * 256 * 4 - 1), 0, t(32), 4, 256), "y"),
+    (lambda t: q.pg_decode(t(256 * 64, contiguous=False), t(256 * 4), 256, 256, t(256 * 256 * 4)), "codes"),
+])
+def test_binding_checks_device_buffers_before_the_call(bad, what):
+    """Undersized, non-contiguous or host buffers raise ValueError in the
+    binding, before the library is called (so no kernel can run past a
+    caller's buffer)."""
+    with pytest.raises(ValueError, match=what):
+        bad(_FakeDeviceTensor)
+
+
+def test_binding_refuses_host_tensors_for_device_arguments():
+    import torch
+    with pytest.raises(ValueError, match="not on the GPU"):
+        q.pg_decode(torch.zeros(64, dtype=torch.uint8), 1 << 20, 1, 256, 1 << 20)
+    with pytest.raises(ValueError, match="numpy"):
+        q.pg_decode(np.zeros(64, np.uint8), 1 << 20, 1, 256, 1 << 20)
