@@ -489,6 +489,8 @@ def main():
     ap.add_argument("--carry", action="store_true",
                     help="read the codes as the carried-state variant (state runs on across blocks; fused path)")
     ap.add_argument("--only-stack", action="store_true", help="only the headline stack (for profiling runs)")
+    ap.add_argument("--only-qgemm", action="store_true",
+                    help="only the prompt-path products, printed as one JSON line (for profiling runs)")
     ap.add_argument("--no-qgemm", action="store_true", help="skip the prompt-path (pg_qgemm) measurement")
     ap.add_argument("--no-encode", action="store_true", help="skip the GPU encoder (pg_encode) measurement")
     ap.add_argument("--no-extra", action="store_true",
@@ -510,6 +512,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": 256 << 20, "bytes_written": 256 << 20,
                           "launches": 4}), flush=True)
+        return
+    if args.only_qgemm:
+        log("timing the prompt path (pg_qgemm)")
+        print(json.dumps({"qgemm": run_qgemm()}), flush=True)
         return
     if args.only_stack:
         args.no_qgemm = args.no_encode = args.no_extra = args.no_cpu_baseline = True
