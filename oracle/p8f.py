@@ -642,3 +642,76 @@ def encode_matrix_carry(w: np.ndarray, sign_bits: np.ndarray, c: float = SCALE_C
     for r in range(n):
         codes[r] = viterbi_encode_row_carry(wr[r], scales[r]).reshape(-1)
     return codes, scales
+
+
+# ------------------------------------- variant: table-driven codebook
+# The landing page's "Paper" section places the format in the small-state
+# coset-trellis design space.  Its two halves are separable: the trellis
+# fixes the branch bit of a byte (u = bit 0) and the state that follows, the
+# codebook fixes the 4-D point a byte names in a state.  A table T[s][byte]
+# of four int8 levels (units of the block scale, 8 x 256 x 4 bytes) holds any
+# such codebook: P8F v1's closed-form rule is one table (codebook_table), a
+# non-uniform or learned value set another.  Trellis, scales, block length
+# and rotation stay as in P8F v1; the state restarts at 0 in every block
+# unless carry is asked for.
+def decode_block_levels_table(codes, table) -> list[int]:
+    """Definition of the table decode: one scalar walk over one block's code
+    bytes from state 0; each group's four levels are T[s][byte]."""
+    t = np.asarray(table, dtype=np.int8).reshape(8, 256, 4)
+    s = 0
+    out: list[int] = []
+    for byte in codes:
+        byte = int(byte)
+        out.extend(int(v) for v in t[s, byte])
+        s = next_state(s, byte & 1)
+    return out
+
+
+def trellis_states(codes: np.ndarray, carry: bool = False) -> np.ndarray:
+    """The state each code byte of codes [..., K/4] is read in: its block's
+    (with carry: its row's) three previous branch bits, the newest at bit 0,
+    zero before the start.  Pinned against the scalar walks in the tests."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lead, g = c.shape[:-1], c.shape[-1]
+    if g % GROUPS_PER_BLOCK:
+        raise ValueError("K/4 must be a multiple of 32")
+    if carry:
+        u = (c & 1).reshape(lead + (1, g)).astype(np.int32)
+    else:
+        u = (c & 1).reshape(lead + (g // GROUPS_PER_BLOCK, GROUPS_PER_BLOCK)).astype(np.int32)
+    s = np.zeros_like(u)
+    for d in (1, 2, 3):                      # branch bit d groups back -> state bit d - 1
+        s[..., d:] |= u[..., :-d] << (d - 1)
+    return s.reshape(lead + (g,))
+
+
+def decode_levels_table(codes: np.ndarray, table: np.ndarray, carry: bool = False) -> np.ndarray:
+    """Levels of codes [..., K/4] under the table T [8][256][4] int8: the
+    group read in state s as byte c takes T[s][c].  Returns int8 [..., K]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    t = np.asarray(table, dtype=np.int8).reshape(8, 256, 4)
+    s = trellis_states(c, carry)
+    return t[s, c].reshape(c.shape[:-1] + (c.shape[-1] * 4,))
+
+
+def decode_weights_table(codes: np.ndarray, scales_u16: np.ndarray, table: np.ndarray,
+                         carry: bool = False) -> np.ndarray:
+    """Rotated-domain weights s * T-level as fp64 [..., K] (exact in fp32 as
+    well: an 11-bit scale times an 8-bit level)."""
+    lv = decode_levels_table(codes, table, carry).astype(np.float64)
+    s = fp16_bits_to_float(scales_u16)
+    k = lv.shape[-1]
+    return (lv.reshape(lv.shape[:-1] + (k // BLOCK, BLOCK)) * s[..., None]).reshape(lv.shape)
+
+
+def gemv_table_ref(codes: np.ndarray, scales_u16: np.ndarray, table: np.ndarray, x_rot: np.ndarray,
+                   carry: bool = False) -> np.ndarray:
+    """y[b][n] = sum_blk s[n][blk] * sum_{k in blk} T-level[n][k] * x~[b][k] in
+    fp64, x_rot [B][K].  Returns fp64 [B][N]."""
+    lv = decode_levels_table(codes, table, carry).astype(np.float64)
+    n, k = lv.shape
+    x = np.asarray(x_rot, dtype=np.float64).reshape(-1, k)
+    s = fp16_bits_to_float(scales_u16)
+    part = np.einsum("nbk,mbk->mnb", lv.reshape(n, k // BLOCK, BLOCK),
+                     x.reshape(x.shape[0], k // BLOCK, BLOCK))
+    return np.einsum("mnb,nb->mn", part, s)

@@ -95,6 +95,20 @@ def random_codes(n: int, k: int, seed: int) -> np.ndarray:
     return np.random.default_rng(seed).integers(0, 256, (n, k // 4), dtype=np.uint8)
 
 
+def random_codebook_table(seed: int, dist: str = "uniform") -> np.ndarray:
+    """A swappable codebook for the table-driven variant: int8 [8][256][4]
+    (four levels per state and code byte).  "uniform": every int8 value
+    equally likely, -128 and 127 included; "gauss": round(N(0, 24^2))
+    clipped to [-127, 127], a non-uniform value set of the kind a learned
+    codebook has."""
+    rng = np.random.default_rng(seed)
+    if dist == "uniform":
+        return rng.integers(-128, 128, (8, 256, 4), dtype=np.int16).astype(np.int8)
+    if dist == "gauss":
+        return np.clip(np.rint(rng.normal(0.0, 24.0, (8, 256, 4))), -127, 127).astype(np.int8)
+    raise ValueError(f"unknown table distribution {dist!r}")
+
+
 def random_scale_bits(n: int, k: int, seed: int, lo: float = 0.005, hi: float = 0.05) -> np.ndarray:
     """fp16 bits of U(lo, hi) scales [N][K/128] (numpy's float16 cast rounds
     to nearest even)."""
