@@ -715,3 +715,167 @@ def gemv_table_ref(codes: np.ndarray, scales_u16: np.ndarray, table: np.ndarray,
     part = np.einsum("nbk,mbk->mnb", lv.reshape(n, k // BLOCK, BLOCK),
                      x.reshape(x.shape[0], k // BLOCK, BLOCK))
     return np.einsum("mnb,nb->mn", part, s)
+
+
+# ------------------------------------- variant: rate-2/3 trellis, 8 cosets
+# The landing page's "Where the name comes from" section: eight states over
+# short patterns, labels in Ungerboeck's manner; "Paper" names the family a
+# small-state coset trellis.  P8F v1 spends one branch bit per group (rate
+# 1/2 over 4 cosets of 128 points); this variant spends two (rate 2/3, four
+# branches per state) over 8 cosets of 64 points of the same 512-point set
+# (four coordinates, levels 4 p + 2 z0 - 7 with p = 2 e + b), still 8 bits a
+# group.  The set is split in Ungerboeck's way along the chain
+# A0|A1 (z0: the value set) / D4 parity (z1 = b0^b1^b2^b3) / the RZ4 split
+# (z2 = b0^b1).  Byte bits 0, 1 are the branch u = (u0, u1); bits 2, 3 are
+# b0, b2 (b1 = b0 ^ z2, b3 = b2 ^ z1 ^ z2); bits 4..7 are e0..e3.  The state
+# is a shift register of the branch bits, s' = ((s << 2) | u) & 7, 0 at each
+# block start.  Ungerboeck's rules fix the labels: the four branches that
+# leave a state, and the four that enter one, take the four cosets of one
+# value set, z0 = bit 0 of s, and (z1, z2) = (u0 ^ bit 1 of s, u1 ^ bit 2 of
+# s) gives both groups of four distinct cosets.
+def next_state_r23(s: int, u: int) -> int:
+    return ((s << 2) | u) & 7
+
+
+def coset_r23(s: int, u: int) -> tuple[int, int, int]:
+    """(z0, z1, z2) of the branch u out of state s."""
+    return s & 1, (u & 1) ^ ((s >> 1) & 1), ((u >> 1) & 1) ^ ((s >> 2) & 1)
+
+
+def decode_group_r23(byte: int, s: int) -> list[int]:
+    """Four integer levels of one code byte read in state s (rate 2/3)."""
+    z0, z1, z2 = coset_r23(s, byte & 3)
+    b0, b2 = (byte >> 2) & 1, (byte >> 3) & 1
+    b = [b0, b0 ^ z2, b2, b2 ^ z1 ^ z2]
+    return [4 * (2 * ((byte >> (4 + j)) & 1) + b[j]) + 2 * z0 - 7 for j in range(4)]
+
+
+def decode_block_levels_r23(codes) -> list[int]:
+    """Definition of the rate-2/3 decode: one scalar walk over one block's
+    bytes from state 0."""
+    s = 0
+    out: list[int] = []
+    for byte in codes:
+        byte = int(byte)
+        out.extend(decode_group_r23(byte, s))
+        s = next_state_r23(s, byte & 3)
+    return out
+
+
+def coset_of_levels(grp) -> tuple[int, int, int]:
+    """(z0, z1, z2) of a 4-D point of the 512-point set (levels odd, |l| <= 7,
+    all four in one value set); ValueError otherwise."""
+    lv = [int(v) for v in grp]
+    if any(v not in (-7, -5, -3, -1, 1, 3, 5, 7) for v in lv):
+        raise ValueError("level outside the 8-level alphabet")
+    z0s = {((v + 7) // 2) % 2 for v in lv}
+    if len(z0s) != 1:
+        raise ValueError("the four levels are not in one value set")
+    z0 = z0s.pop()
+    b = [((v + 7 - 2 * z0) // 4) % 2 for v in lv]
+    return z0, b[0] ^ b[1] ^ b[2] ^ b[3], b[0] ^ b[1]
+
+
+def levels_trellis_valid_r23(levels) -> bool:
+    """A level sequence (one block) is a rate-2/3 path: every group's coset
+    is one that a branch out of the current state carries; the branch it
+    takes is then unique and fixes the next state."""
+    lv = np.asarray(levels, dtype=np.int64).reshape(-1, 4)
+    s = 0
+    for grp in lv:
+        try:
+            z = coset_of_levels(grp)
+        except ValueError:
+            return False
+        us = [u for u in range(4) if coset_r23(s, u) == z]
+        if len(us) != 1:
+            return False
+        s = next_state_r23(s, us[0])
+    return True
+
+
+def _coset_points_r23():
+    """For each coset (z0, z1, z2): its 64 points as (bytes without the
+    branch bits, levels [64][4]), the byte's bits 2..7 ascending."""
+    out = {}
+    for z0 in range(2):
+        for z1 in range(2):
+            for z2 in range(2):
+                # a state and branch that carry this coset: s = z0 (bits 1, 2 zero), u = (z1, z2)
+                s, u = z0, z1 | (z2 << 1)
+                assert coset_r23(s, u) == (z0, z1, z2)
+                bytes_ = np.array([(hi << 2) | u for hi in range(64)], dtype=np.int64)
+                pts = np.array([decode_group_r23(int(c), s) for c in bytes_], dtype=np.float64)
+                out[(z0, z1, z2)] = (bytes_ >> 2, pts)
+    return out
+
+
+def viterbi_encode_r23(w_rot: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Minimum-squared-error rate-2/3 path per block: w_rot [nb, 4G] fp64,
+    scale_bits [nb] u16.  Per group and coset the nearest of its 64 points by
+    brute force (lowest byte on ties); then a Viterbi over 8 states from state
+    0 with a free end state (predecessors tried in increasing state and
+    branch order, strict improvement, lowest final state).  A zero-scale
+    block codes as bytes 0 (the all-zero branch sequence, any point)."""
+    w = np.asarray(w_rot, dtype=np.float64)
+    nb, g = w.shape[0], w.shape[1] // 4
+    sv = fp16_bits_to_float(np.asarray(scale_bits, dtype=np.uint16))
+    cos = _coset_points_r23()
+    out = np.zeros((nb, g), dtype=np.uint8)
+    for b in range(nb):
+        if sv[b] == 0:
+            continue
+        near = {}
+        for z, (hi, pts) in cos.items():
+            d = w[b].reshape(g, 1, 4) - sv[b] * pts[None, :, :]
+            dist = np.sum(d * d, axis=2)                 # [g, 64]
+            i = np.argmin(dist, axis=1)                  # first minimum: lowest byte
+            near[z] = (dist[np.arange(g), i], hi[i])
+        metric = np.full(8, np.inf)
+        metric[0] = 0.0
+        back = np.zeros((g, 8, 2), dtype=np.int64)       # (previous state, byte)
+        for t in range(g):
+            new = np.full(8, np.inf)
+            for sp in range(8):
+                if metric[sp] == np.inf:
+                    continue
+                for u in range(4):
+                    z = coset_r23(sp, u)
+                    tot = metric[sp] + near[z][0][t]
+                    sn = next_state_r23(sp, u)
+                    if tot < new[sn]:
+                        new[sn] = tot
+                        back[t, sn] = (sp, (int(near[z][1][t]) << 2) | u)
+            metric = new
+        st = int(np.argmin(metric))
+        for t in range(g - 1, -1, -1):
+            out[b, t] = back[t, st, 1]
+            st = int(back[t, st, 0])
+    return out
+
+
+def block_distortion_r23(w_rot: np.ndarray, codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Squared error per block of the rate-2/3 decode of codes [nb, G]."""
+    w = np.asarray(w_rot, dtype=np.float64)
+    sv = fp16_bits_to_float(np.asarray(scale_bits, dtype=np.uint16))
+    out = np.zeros(w.shape[0])
+    for b in range(w.shape[0]):
+        lv = np.array(decode_block_levels_r23(codes[b]), dtype=np.float64)
+        d = w[b] - sv[b] * lv
+        out[b] = float(np.sum(d * d))
+    return out
+
+
+def exhaustive_encode_r23(w_rot_row: np.ndarray, scale_bits: int) -> float:
+    """Minimum distortion over every byte string of a short block (256^G
+    strings, G <= 3), each decoded by the scalar walk: the brute-force
+    optimum that the Viterbi must reach."""
+    w = np.asarray(w_rot_row, dtype=np.float64)
+    g = w.shape[0] // 4
+    sv = float(fp16_bits_to_float(np.array([scale_bits], dtype=np.uint16))[0])
+    best = np.inf
+    for idx in range(256 ** g):
+        codes = [(idx >> (8 * t)) & 255 for t in range(g)]
+        d = w - sv * np.array(decode_block_levels_r23(codes), dtype=np.float64)
+        best = min(best, float(np.sum(d * d)))
+    return best
