@@ -124,8 +124,10 @@ size_t pg_q16_row_bytes(int64_t k);
 /* Message of the calling thread's last failed call ("" if none). */
 const char* pg_last_error(void);
 
-/* Test hook: the decode table the kernels use, out[s][c][j] = level_j of
- * byte c read in state s (int8 [8][256][4], host memory). */
+/* P8F v1's codebook written out as a table: out[s][c][j] = level_j of
+ * byte c read in state s (int8 [8][256][4], host memory).  Given to
+ * pg_decode_table / pg_rot_qgemv_table it reproduces P8F v1 (the other
+ * entry points compute the same levels from the byte's bits). */
 int pg_codebook_table(int8_t* out);
 
 /* Host (CPU) reference encoder, synchronous.  Follows the "How it works"
@@ -178,6 +180,21 @@ int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k
  * codes of the carried-state variant.  Bit-exact. */
 int pg_decode_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, uint32_t flags,
                  float* w_rot, pg_stream_t stream);
+
+/* Table-driven codebook variant (landing page, section "Paper": the format
+ * is a small-state coset trellis; the trellis and the codebook separate).
+ * The trellis is P8F v1's (branch bit u = bit 0 of the byte, state = the
+ * last three branch bits, 0 at each 128-block start, or run on along the
+ * row with PG_FLAG_CARRY_STATE); the codebook is a caller-supplied table:
+ *   table    device int8 [8][256][4], 16-byte aligned: table[s][c][j] is
+ *            level j (units of the block scale) of the group read in state s
+ *            as byte c.  Any int8 values: a non-uniform or learned value set,
+ *            or P8F v1's own (pg_codebook_table).  Read only; the caller owns
+ *            it and may change it between calls.
+ * Decode to rotated-domain fp32 weights, w = fp32(scale) * level (exact).
+ * flags 0 or PG_FLAG_CARRY_STATE.  Other arguments as pg_decode. */
+int pg_decode_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const int8_t* table,
+                    uint32_t flags, float* w_rot, pg_stream_t stream);
 
 /* Run-time activation rotation ("How it works": the random Hadamard
  * rotation; the activations take the same rotation as the weight rows):
@@ -264,6 +281,21 @@ int pg_qgemv_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t
 int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                  const void* x, int x_dtype, int64_t ldx, const uint8_t* sign_bits,
                  uint32_t flags, int batch, float* y, pg_stream_t stream);
+
+/* The fused stage of pg_rot_qgemv at batch 1 through a codebook table (as
+ * pg_decode_table): y = W~ . R . n(x) with W~'s levels read from table.
+ *   codes, scales, sign_bits, x (first k values), y, x_dtype: as pg_rot_qgemv
+ *   at batch 1; table as pg_decode_table
+ *   flags    PG_FLAG_RMSNORM, PG_FLAG_CARRY_STATE (state run on along rows)
+ * The rotated activations are quantised to 16-bit digits per 32 values as
+ * pg_rot_qgemv at batch 1; each 32-value partial sum of level * digit is
+ * exact in int32 and rounded once to fp32.  With P8F v1's table the output
+ * is bitwise that of pg_rot_qgemv at batch 1 (k <= 4096, where that takes
+ * the same stage).  k <= 16384 (PG_ERR_UNSUPPORTED beyond); PG_F32 input
+ * needs PG_FLAG_RMSNORM.  x and y may not overlap.  Fixed summation order. */
+int pg_rot_qgemv_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
+                       int x_dtype, const uint8_t* sign_bits, const int8_t* table, uint32_t flags, float* y,
+                       pg_stream_t stream);
 
 /* Prompt-processing product for m activation rows (landing page, section
  * "Results": prompt reading is the mat-mat path):

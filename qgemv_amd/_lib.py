@@ -27,7 +27,7 @@ EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_erro
            "pg_encode", "pg_encode_ex", "pg_decode_ex",
            "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm",
            "pg_qgemm_ex", "pg_qgemm_workspace_bytes", "pg_hbm_read",
-           "pg_qgemm_noalloc", "pg_qgemv_ex", "pg_qgemm_tune")
+           "pg_qgemm_noalloc", "pg_qgemv_ex", "pg_qgemm_tune", "pg_decode_table", "pg_rot_qgemv_table")
 
 
 class PgError(RuntimeError):
@@ -70,6 +70,10 @@ def lib():
         L.pg_encode_ex.argtypes = [vp, i64, i64, vp, u32, vp, vp, vp]
         L.pg_decode_ex.restype = i32
         L.pg_decode_ex.argtypes = [vp, vp, i64, i64, u32, vp, vp]
+        L.pg_decode_table.restype = i32
+        L.pg_decode_table.argtypes = [vp, vp, i64, i64, vp, u32, vp, vp]
+        L.pg_rot_qgemv_table.restype = i32
+        L.pg_rot_qgemv_table.argtypes = [vp, vp, i64, i64, vp, i32, vp, vp, u32, vp, vp]
         L.pg_decode.restype = i32
         L.pg_decode.argtypes = [vp, vp, i64, i64, vp, vp]
         L.pg_fwht_rotate.restype = i32
@@ -227,6 +231,17 @@ def pg_decode_ex(codes, scales, n: int, k: int, flags: int, w_rot, stream=None) 
     _check(lib().pg_decode_ex(_ptr(codes), _ptr(scales), n, k, flags, _ptr(w_rot), _stream(stream)))
 
 
+TABLE_BYTES = 8 * 256 * 4     # int8 [8][256][4] codebook table
+
+
+def pg_decode_table(codes, scales, n: int, k: int, table, flags: int, w_rot, stream=None) -> None:
+    """Decode through a codebook table (device int8 [8][256][4])."""
+    _weights(codes, scales, n, k)
+    _need(table, TABLE_BYTES, "table")
+    _need(w_rot, max(n, 0) * max(k, 0) * 4, "w_rot")
+    _check(lib().pg_decode_table(_ptr(codes), _ptr(scales), n, k, _ptr(table), flags, _ptr(w_rot), _stream(stream)))
+
+
 def pg_decode(codes, scales, n: int, k: int, w_rot, stream=None) -> None:
     _weights(codes, scales, n, k)
     _need(w_rot, max(n, 0) * max(k, 0) * 4, "w_rot")
@@ -267,6 +282,18 @@ def pg_rot_qgemv(codes, scales, n: int, k: int, x, x_dtype: int, ldx: int, sign_
     _need(y, max(batch, 0) * max(n, 0) * 4, "y")
     _check(lib().pg_rot_qgemv(_ptr(codes), _ptr(scales), n, k, _ptr(x), x_dtype, ldx, _ptr(sign_bits), flags,
                               batch, _ptr(y), _stream(stream)))
+
+
+def pg_rot_qgemv_table(codes, scales, n: int, k: int, x, x_dtype: int, sign_bits, table, flags: int, y,
+                       stream=None) -> None:
+    """The batch-1 fused stage through a codebook table."""
+    _weights(codes, scales, n, k)
+    _need(x, _xbytes(x_dtype, 1, k, k), "x")
+    _need(sign_bits, max(k, 0) // 8, "sign_bits")
+    _need(table, TABLE_BYTES, "table")
+    _need(y, max(n, 0) * 4, "y")
+    _check(lib().pg_rot_qgemv_table(_ptr(codes), _ptr(scales), n, k, _ptr(x), x_dtype, _ptr(sign_bits), _ptr(table),
+                                    flags, _ptr(y), _stream(stream)))
 
 
 def pg_qgemm(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, stream=None) -> None:

@@ -108,6 +108,18 @@ int pg_decode_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
     return pg::launch_decode(codes, scales, n, k, w_rot, (flags & PG_FLAG_CARRY_STATE) != 0, stream);
 }
 
+int pg_decode_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const int8_t* table,
+                    uint32_t flags, float* w_rot, pg_stream_t stream) {
+    pg::clear_error();
+    if (flags & ~PG_FLAG_CARRY_STATE) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    PG_TRY(check_nk(n, k));
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    PG_TRY(check_ptr(table, 16, "table"));
+    PG_TRY(check_ptr(w_rot, 16, "w_rot"));
+    return pg::launch_decode_table(codes, scales, n, k, table, (flags & PG_FLAG_CARRY_STATE) != 0, w_rot, stream);
+}
+
 int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w_rot,
               pg_stream_t stream) {
     pg::clear_error();
@@ -188,6 +200,26 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
     const size_t yb = (size_t)batch * n * 4, xb = (size_t)batch * ldx * (x_dtype == PG_F32 ? 4 : 2);
     if (xa < ya + yb && ya < xa + xb) return pg::fail(PG_ERR_INVALID_ARG, "x and y overlap");
     return pg::launch_rot_qgemv(codes, scales, n, k, x, x_dtype, ldx, sign_bits, flags, batch, y, stream);
+}
+
+int pg_rot_qgemv_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
+                       int x_dtype, const uint8_t* sign_bits, const int8_t* table, uint32_t flags, float* y,
+                       pg_stream_t stream) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    PG_TRY(check_dtype(x_dtype, "x_dtype", false, false));
+    if (flags & ~(uint32_t)(PG_FLAG_RMSNORM | PG_FLAG_CARRY_STATE))
+        return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 4, "scales"));
+    PG_TRY(check_ptr(x, 16, "x"));
+    PG_TRY(check_ptr(sign_bits, 4, "sign_bits"));
+    PG_TRY(check_ptr(table, 16, "table"));
+    PG_TRY(check_ptr(y, 4, "y"));
+    const uintptr_t ya = (uintptr_t)y, xa = (uintptr_t)x;
+    const size_t yb = (size_t)n * 4, xb = (size_t)k * (x_dtype == PG_F32 ? 4 : 2);
+    if (xa < ya + yb && ya < xa + xb) return pg::fail(PG_ERR_INVALID_ARG, "x and y overlap");
+    return pg::launch_rot_qgemv_table(codes, scales, n, k, x, x_dtype, sign_bits, table, flags, y, stream);
 }
 
 int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const uint16_t* x_rot_bf16,

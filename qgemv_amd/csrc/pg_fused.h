@@ -561,6 +561,13 @@ int launch_rot_qmma(const uint8_t* codes, const uint16_t* scales, int64_t n, int
 int launch_rot_qgemv1(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x, int x_dt,
                       const uint8_t* sign_bits, uint32_t flags, float* y, hipStream_t st);
 
+// batch 1 through a codebook table (pg_fused1.hip): the same stage with the
+// table-driven decode, k <= 16384; PG_ERR_UNSUPPORTED (message set) when the
+// shape does not fit it
+int launch_rot_qgemv1_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
+                            int x_dt, const uint8_t* sign_bits, const int8_t* table, uint32_t flags, float* y,
+                            hipStream_t st);
+
 // the carried-state instances (pg_fused_carry.hip, compiled on their own)
 int launch_fused_carry(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                        const void* x, int x_dt, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch,

@@ -72,4 +72,12 @@ int launch_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, in
     return launch_fused_all<false>(S, codes, scales, n, k, x, x_dt, ldx, sign_bits, flags, batch, y, st);
 }
 
+int launch_rot_qgemv_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const void* x,
+                           int x_dt, const uint8_t* sign_bits, const int8_t* table, uint32_t flags, float* y,
+                           pg_stream_t s) {
+    if (x_dt == PG_F32 && !(flags & PG_FLAG_RMSNORM))
+        return fail(PG_ERR_UNSUPPORTED, "pg_rot_qgemv_table: fp32 input needs PG_FLAG_RMSNORM (its rotation runs in fp16)");
+    return launch_rot_qgemv1_table(codes, scales, n, k, x, x_dt, sign_bits, table, flags, y, (hipStream_t)s);
+}
+
 }  // namespace pg

@@ -1,10 +1,14 @@
-// Batch-1 fused stage of a stack for gfx950 (MI355X, wave64), P8F v1 codes:
+// Batch-1 fused stage of a stack for gfx950 (MI355X, wave64):
 // y = W~ . R . n(x) in one launch, with the activation rotation computed in
 // registers (butterflies inside the lane and across lanes) instead of
-// staging fp16 blocks in LDS for the matrix cores.
+// staging fp16 blocks in LDS for the matrix cores.  Two decodes share it:
+// P8F v1's closed-form bit planes, and the table-driven codebook (the 8 x 256
+// points of four int8 levels staged in LDS, one lookup per group).
 //
 // Method: "Pingala-8" landing page, section "How it works" (trellis decode
-// and random Hadamard rotation).  Bit layout: include/pingala.h.
+// and random Hadamard rotation); the table variant is the codebook half of
+// the small-state coset trellis of section "Paper".  Bit layout:
+// include/pingala.h.
 #pragma once
 #include "pg_fused.h"
 
@@ -19,17 +23,30 @@ struct Fused1Shape {
 };
 
 // PG_ERR_UNSUPPORTED (message set) when the shape does not fit the kernel
-int fused1_shape(int64_t n, int64_t k, Fused1Shape* out);
+// with at most umax rotation rounds (and the codebook table in LDS if asked)
+int fused1_shape(int64_t n, int64_t k, int umax, bool table, Fused1Shape* out);
 
 namespace {
 
-constexpr int F1_UMAX = 1;   // rotation rounds per wave: k <= 4096 with 8 waves
+constexpr int F1_UMAX = 1;       // rotation rounds per wave of the closed-form stage: k <= 4096 with 8 waves
+constexpr int F1T_UMAX = 4;      // and of the table stage: k <= 16384
+constexpr int F1T_TABLE_BYTES = 8 * 256 * 4;
 
-// LDS of one launch: the digits row of the rotated activations (per 32-value
-// quarter its scale and its sum of q after the digits), the team sums and the
-// per-wave sums of squares
-__host__ inline size_t fused1_lds_bytes(int k, const Fused1Shape& S) {
-    return (size_t)fused_row_bytes(k) + (size_t)S.R * S.CG * 4 + (size_t)S.W * 4;
+// LDS of one launch: [the codebook table,] the digits row of the rotated
+// activations (per 32-value quarter its scale and its sum of q after the
+// digits), the team sums and the per-wave sums of squares
+__host__ inline size_t fused1_lds_bytes(int k, const Fused1Shape& S, bool table) {
+    return (table ? (size_t)F1T_TABLE_BYTES : 0) + (size_t)fused_row_bytes(k) + (size_t)S.R * S.CG * 4 +
+           (size_t)S.W * 4;
+}
+
+// 4 x 4 byte transpose across the lanes of a quad: lane j holds byte g of row
+// j on entry and byte j of row g on return (two DPP exchanges, two permutes)
+__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t o, int lane) {
+    uint32_t p = (uint32_t)xor_lane_i<1>((int)o, lane);
+    o = __builtin_amdgcn_perm(p, o, (lane & 1) ? 0x03070105u : 0x06020400u);
+    p = (uint32_t)xor_lane_i<2>((int)o, lane);
+    return __builtin_amdgcn_perm(p, o, (lane & 2) ? 0x03020706u : 0x05040100u);
 }
 
 // The rotation's lane roles.  Four 128-blocks per wave and round: lane
@@ -43,16 +60,29 @@ __host__ inline size_t fused1_lds_bytes(int k, const Fused1Shape& S) {
 // the block): its digits leave in two dword stores.  The 32 values of a
 // quarter (mh fixed) sit in one quad, whose maximum and sum of q take two
 // DPP steps.
-template <int XDT, int RS>
+//
+// TAB = 1, the table-driven codebook: the digits are balanced (q = 256 hi +
+// lo with both signed bytes, hi = (q + 128) >> 8) and stored group-major
+// (one dword holds the four weights of one group, as a table point does),
+// after a 4 x 4 byte transpose across the quad.  A group read in state s as
+// byte c takes the point T[s][c] from the LDS copy of the table; its dot
+// products with the digits are two v_dot4_i32_i8.  The state of each byte of
+// a code dword comes from the branch bits of the three bytes before it
+// (funnel shifts of the dword and its predecessor); flags PG_FLAG_CARRY_STATE
+// continues the state from the previous 64-value chunk of the row, whose
+// last code dword every lane loads itself.
+template <int XDT, int RS, int TAB, int UMAX>
 __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ codes,
                                                      const uint16_t* __restrict__ scales, int n, int k,
                                                      const void* __restrict__ x,
-                                                     const uint8_t* __restrict__ sign_bits, uint32_t flags,
+                                                     const uint8_t* __restrict__ sign_bits,
+                                                     const uint32_t* __restrict__ table, uint32_t flags,
                                                      float* __restrict__ y, int R, int CG, int RP, int U) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
     // one scalar load burst for every argument (see k_rot_qgemv)
-    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(sign_bits), "s"(flags), "s"(y),
-                 "s"(R), "s"(CG), "s"(RP), "s"(U));
+    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(sign_bits), "s"(table), "s"(flags),
+                 "s"(y), "s"(R), "s"(CG), "s"(RP), "s"(U));
+    uint8_t* lds = lds_all + (TAB ? F1T_TABLE_BYTES : 0);                    // the table, if any, sits first
     constexpr int W = 8;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -65,6 +95,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
     float* part = reinterpret_cast<float*>(dig + fused_row_bytes(k));          // [R][CG] team sums
     float* wsum = part + R * CG;                                               // [W] sums of squares
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
+    const bool carry = TAB && (flags & PG_FLAG_CARRY_STATE) != 0;
     const float rk = 1.0f / (float)k;                 // computed before any wait
 
     // ---- 1. requests: the lane's x values and sign words of every round,
@@ -72,10 +103,10 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
     // in order, so waiting until only the code requests are outstanding
     // means x has arrived)
     const int rj = lane & 3, rbb = (lane >> 2) & 3, rmh = lane >> 4;
-    uint32_t xr[F1_UMAX][8];
-    uint32_t sw[F1_UMAX];
+    uint32_t xr[UMAX][8];
+    uint32_t sw[UMAX];
 #pragma unroll
-    for (int u = 0; u < F1_UMAX; ++u) {
+    for (int u = 0; u < UMAX; ++u) {
         if (u < U) {
             const int blk = 4 * (wave + W * u) + rbb;
             const int bc = blk < nbk ? blk : nbk - 1;          // clamped: every lane issues the same loads
@@ -102,6 +133,21 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
         rok[j] = col_ok && r < R && row0 + r < n;
         rowj[j] = rok[j] ? row0 + r : (row0 < n ? row0 : n - 1);
     }
+    // the table (16 bytes per thread) and, for carried state, the code dword
+    // before each of the lane's chunks: requested before the codes, so the
+    // wait below covers them
+    uint4 tv = {0u, 0u, 0u, 0u};
+    uint32_t pq[RS];
+#pragma unroll
+    for (int j = 0; j < RS; ++j) pq[j] = 0u;
+    if constexpr (TAB) {
+        tv = reinterpret_cast<const uint4*>(table)[tid];
+        if (carry && cc > 0) {
+#pragma unroll
+            for (int j = 0; j < RS; ++j)
+                pq[j] = *reinterpret_cast<const uint32_t*>(codes + (int64_t)rowj[j] * kg + 16 * cc - 4);
+        }
+    }
     asm volatile("" ::: "memory");
     uint4 q[RS];
     uint32_t wsr[RS];
@@ -112,7 +158,8 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
         wsr[j] = scales[(int64_t)row * nbk + (cc >> 1)];
     }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * RS));      // x and sign words have arrived
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * RS));      // x, sign words (and table, carried dwords) have arrived
+    if constexpr (TAB) reinterpret_cast<uint4*>(lds_all)[tid] = tv;   // read after the barriers below
 
     // ---- 2. the RMS factor: sum of squares over the lane's valid blocks,
     // wave sums, the waves' sums added in wave order by every thread
@@ -120,7 +167,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
     if (norm) {
         float ss = 0.0f;
 #pragma unroll
-        for (int u = 0; u < F1_UMAX; ++u) {
+        for (int u = 0; u < UMAX; ++u) {
             if (u < U && 4 * (wave + W * u) + rbb < nbk) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -143,7 +190,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
     const float sg1 = (lane & 1) ? -1.0f : 1.0f, sg2 = (lane & 2) ? -1.0f : 1.0f;
     const float sg16 = (lane & 16) ? -1.0f : 1.0f, sg32 = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int u = 0; u < F1_UMAX; ++u) {
+    for (int u = 0; u < UMAX; ++u) {
         if (u >= U || 4 * (wave + W * u) >= nbk) break;   // wave-uniform: no block left for this wave
         const int blk = 4 * (wave + W * u) + rbb;
         const bool ok = blk < nbk;
@@ -176,7 +223,9 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = fmaf(sg32, v[i], xor_lane32(v[i], lane));
         // quarter mh of the block: its maximum over the quad, q = rint(v * 32512 / max)
-        // as the low 16 bits of fma(v, s, 1.5 * 2^23)
+        // as the low 16 bits of fma(v, s, 1.5 * 2^23) (of q + 128 with 128
+        // added to the constant, for the balanced digits: rounding to an
+        // integer commutes with adding an even integer)
         float mx = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
@@ -187,11 +236,13 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
         int qs = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            bits[i] = __builtin_bit_cast(uint32_t, fmaf(v[i], s, 12582912.0f));
-            qs += (int)(int16_t)(bits[i] & 0xffffu);
+            bits[i] = __builtin_bit_cast(uint32_t, fmaf(v[i], s, TAB ? 12583040.0f : 12582912.0f));
+            if constexpr (!TAB) qs += (int)(int16_t)(bits[i] & 0xffffu);
         }
-        qs += xor_lane_i<1>(qs, lane);
-        qs += xor_lane_i<2>(qs, lane);
+        if constexpr (!TAB) {
+            qs += xor_lane_i<1>(qs, lane);
+            qs += xor_lane_i<2>(qs, lane);
+        }
         if (ok) {
             // chunk 2 blk + mh / 2; code dword m0 + 2 (mh % 2) of it; plane j
             uint8_t* d = dig + (2 * blk + (rmh >> 1)) * FS_PITCH + 64 * (rmh & 1) + 4 * rj;
@@ -199,12 +250,19 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
             for (int m0 = 0; m0 < 2; ++m0) {
                 const uint32_t t01 = __builtin_amdgcn_perm(bits[4 * m0 + 1], bits[4 * m0], 0x05040100u);
                 const uint32_t t23 = __builtin_amdgcn_perm(bits[4 * m0 + 3], bits[4 * m0 + 2], 0x05040100u);
-                *reinterpret_cast<uint32_t*>(d + 32 * m0) = __builtin_amdgcn_perm(t23, t01, 0x07050301u);       // floor(q / 256)
-                *reinterpret_cast<uint32_t*>(d + 32 * m0 + 16) = __builtin_amdgcn_perm(t23, t01, 0x06040200u);  // q mod 256
+                uint32_t dh = __builtin_amdgcn_perm(t23, t01, 0x07050301u);   // floor(q / 256); balanced: (q + 128) >> 8
+                uint32_t dl = __builtin_amdgcn_perm(t23, t01, 0x06040200u);   // q mod 256; balanced: its signed byte
+                if constexpr (TAB) {
+                    dl ^= 0x80808080u;
+                    dh = quad_transpose_bytes(dh, lane);
+                    dl = quad_transpose_bytes(dl, lane);
+                }
+                *reinterpret_cast<uint32_t*>(d + 32 * m0) = dh;
+                *reinterpret_cast<uint32_t*>(d + 32 * m0 + 16) = dl;
             }
             if (rj == 0) {
                 sxq[4 * blk + rmh] = mx * (0.08838834764831845f / (float)Q16_MAXQ);   // 2^-3.5 max / 32512
-                sqq[4 * blk + rmh] = qs;
+                if constexpr (!TAB) sqq[4 * blk + rmh] = qs;
             }
         }
     }
@@ -222,9 +280,56 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
         }
         const uint32_t left_mask = (c & 1) ? ~0u : 0u;   // odd chunks continue the left lane's block
         const float sx0 = sxq[2 * cc], sx1 = sxq[2 * cc + 1];
-        const int sq0 = sqq[2 * cc], sq1 = sqq[2 * cc + 1];
         float tq[RS];
         int hi[RS], lo[RS];
+        if constexpr (TAB) {
+            const uint32_t* tab = reinterpret_cast<const uint32_t*>(lds_all);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (m == 0 || m == 2)
+#pragma unroll
+                    for (int j = 0; j < RS; ++j) { hi[j] = 0; lo[j] = 0; }
+                const uint8_t* dg = dig + cc * FS_PITCH + 32 * m;
+                const uint4 xh4 = *reinterpret_cast<const uint4*>(dg);
+                const uint4 xl4 = *reinterpret_cast<const uint4*>(dg + 16);
+                const uint32_t xh[4] = {xh4.x, xh4.y, xh4.z, xh4.w}, xl[4] = {xl4.x, xl4.y, xl4.z, xl4.w};
+#pragma unroll
+                for (int j = 0; j < RS; ++j) {
+                    const uint32_t w4[4] = {qb[j].x, qb[j].y, qb[j].z, qb[j].w};
+                    uint32_t prev;
+                    if (m > 0)
+                        prev = w4[m - 1];
+                    else if (carry)
+                        prev = pq[j];
+                    else
+                        prev = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb[j].w, 0x111, 0xf, 0xf, true) & left_mask;
+                    const uint32_t w = w4[m];
+                    // state of byte b: branch bits of bytes b-1, b-2, b-3 at its bits 0, 1, 2
+                    uint32_t st = __builtin_amdgcn_alignbit(w, prev, 24) & 0x01010101u;
+                    st |= __builtin_amdgcn_alignbit(w, prev, 15) & 0x02020202u;
+                    st |= __builtin_amdgcn_alignbit(w, prev, 6) & 0x04040404u;
+                    int h = hi[j], l = lo[j];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        // table index s * 256 + byte: the byte, then its state, as bytes 0 and 1
+                        const uint32_t idx = __builtin_amdgcn_perm(st, w, 0x0c0c0400u + 0x0101u * g);
+                        const uint32_t pt = tab[idx];
+                        h = __builtin_amdgcn_sdot4((int)pt, (int)xh[g], h, false);
+                        l = __builtin_amdgcn_sdot4((int)pt, (int)xl[g], l, false);
+                    }
+                    hi[j] = h;
+                    lo[j] = l;
+                }
+                // quarter done: sum level * q = 256 hi + lo
+                if (m == 1)
+#pragma unroll
+                    for (int j = 0; j < RS; ++j) tq[j] = sx0 * (float)(hi[j] * 256 + lo[j]);
+                if (m == 3)
+#pragma unroll
+                    for (int j = 0; j < RS; ++j) tq[j] += sx1 * (float)(hi[j] * 256 + lo[j]);
+            }
+        } else {
+        const int sq0 = sqq[2 * cc], sq1 = sqq[2 * cc + 1];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             if (m == 0 || m == 2)
@@ -262,6 +367,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
 #pragma unroll
                 for (int j = 0; j < RS; ++j) tq[j] += sx1 * (float)(2 * (hi[j] * 256 + lo[j]) - 7 * sq1);
         }
+        }
 #pragma unroll
         for (int j = 0; j < RS; ++j) {
             float v = rok[j] ? h2f((uint16_t)wb[j]) * tq[j] : 0.0f;
@@ -282,20 +388,23 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
     }
 }
 
-template <int XDT, int RS>
+template <int XDT, int RS, int TAB, int UMAX>
 int launch_fused1_t(const Fused1Shape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
-                    const void* x, const uint8_t* sign_bits, uint32_t flags, float* y, hipStream_t st) {
+                    const void* x, const uint8_t* sign_bits, const uint32_t* table, uint32_t flags, float* y,
+                    hipStream_t st) {
     const dim3 grid((unsigned)((n + S.R - 1) / S.R));
-    hipLaunchKernelGGL((k_rot_qgemv1<XDT, RS>), grid, dim3(64 * S.W), fused1_lds_bytes((int)k, S), st, codes, scales,
-                       (int)n, (int)k, x, sign_bits, flags, y, S.R, S.CG, S.RP, S.U);
-    return hip_check(hipGetLastError(), "pg_rot_qgemv launch");
+    hipLaunchKernelGGL((k_rot_qgemv1<XDT, RS, TAB, UMAX>), grid, dim3(64 * S.W), fused1_lds_bytes((int)k, S, TAB != 0),
+                       st, codes, scales, (int)n, (int)k, x, sign_bits, table, flags, y, S.R, S.CG, S.RP, S.U);
+    return hip_check(hipGetLastError(), TAB ? "pg_rot_qgemv_table launch" : "pg_rot_qgemv launch");
 }
 
 // rows per lane as exact as possible: every row slot costs a full decode
-template <int XDT>
+template <int XDT, int TAB, int UMAX>
 int launch_fused1_rs(const Fused1Shape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
-                     const void* x, const uint8_t* sign_bits, uint32_t flags, float* y, hipStream_t st) {
-#define PG_F1(RS_) return launch_fused1_t<XDT, RS_>(S, codes, scales, n, k, x, sign_bits, flags, y, st)
+                     const void* x, const uint8_t* sign_bits, const uint32_t* table, uint32_t flags, float* y,
+                     hipStream_t st) {
+#define PG_F1(RS_) \
+    return launch_fused1_t<XDT, RS_, TAB, UMAX>(S, codes, scales, n, k, x, sign_bits, table, flags, y, st)
     if (S.RS <= 1) PG_F1(1);
     if (S.RS <= 2) PG_F1(2);
     if (S.RS <= 3) PG_F1(3);

@@ -80,9 +80,22 @@ int main() {
           PG_ERR_INVALID_ARG);
     CHECK(pg_hbm_read(p, 100, (uint32_t*)(p + 4096), st) == PG_ERR_INVALID_ARG);
     CHECK(pg_hbm_read(p, 4096, (uint32_t*)(p + 64), st) == PG_ERR_INVALID_ARG);             // out inside the range
+    const int8_t* tb = (const int8_t*)(p + 8192);
+    CHECK(pg_decode_table(p, (uint16_t*)p, 4, 256, tb, PG_FLAG_RMSNORM, (float*)(p + 16384), st) == PG_ERR_INVALID_ARG);
+    CHECK(pg_decode_table(p, (uint16_t*)p, 4, 256, tb + 4, 0, (float*)(p + 16384), st) == PG_ERR_INVALID_ARG);
+    CHECK(pg_rot_qgemv_table(p, (uint16_t*)p, 8, 256, p, PG_BF16, p, tb, 0, (float*)(p + 16384), st) ==
+          PG_ERR_INVALID_ARG);
+    CHECK(pg_rot_qgemv_table(p, (uint16_t*)p, 8, 256, p, PG_F16, p, tb, PG_FLAG_KERNEL_MMA, (float*)(p + 16384), st) ==
+          PG_ERR_INVALID_ARG);
+    CHECK(pg_rot_qgemv_table(p, (uint16_t*)p, 8, 256, p + 16384, PG_F16, p, tb, 0, (float*)(p + 16384), st) ==
+          PG_ERR_INVALID_ARG);                                                                  // x, y overlap
     CHECK(std::strlen(pg_last_error()) > 0);
     // a valid request reaches the (stubbed) launcher
     CHECK(pg_decode(p, (uint16_t*)p, 4, 256, (float*)(p + 16384), st) == PG_ERR_UNSUPPORTED);
+    CHECK(pg_decode_table(p, (uint16_t*)p, 4, 256, tb, PG_FLAG_CARRY_STATE, (float*)(p + 16384), st) ==
+          PG_ERR_UNSUPPORTED);
+    CHECK(pg_rot_qgemv_table(p, (uint16_t*)p, 8, 256, p + 4096, PG_F16, p, tb, PG_FLAG_RMSNORM, (float*)(p + 16384),
+                             st) == PG_ERR_UNSUPPORTED);
 
     // messages are per thread
     std::string other;

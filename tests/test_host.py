@@ -88,6 +88,16 @@ def test_codebook_table_matches_oracle():
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 1, 260, 1 << 20, 1, 1, 1 << 24, stream=0),  # row align
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, (1 << 22) + 8, 0, 256, 1 << 20, 1, 1, 1 << 24, stream=0),
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, (1 << 20) + 2, 1, 1, 1 << 24, stream=0),
+    lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 1, 1 << 24, stream=0),             # flags
+    lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 256, (1 << 22) + 4, 0, 1 << 24, stream=0),       # table align
+    lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 200, 1 << 22, 0, 1 << 24, stream=0),             # k
+    lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 256, 0, 0, 1 << 24, stream=0),                   # null table
+    lambda: q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 1 << 20, 1 << 18, 4, 1 << 24, stream=0),  # flags
+    lambda: q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 2, 1 << 20, 1 << 18, 1, 1 << 24, stream=0),  # dtype
+    lambda: q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 1 << 20, (1 << 18) + 8, 1, 1 << 24,
+                                 stream=0),                                                            # table align
+    lambda: q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 1 << 20, 1 << 18, 1, (1 << 22) + 64,
+                                 stream=0),                                                            # x, y overlap
 ])
 def test_invalid_arguments_fail_before_launch(call):
     # the pointers are never dereferenced: validation rejects the call first
@@ -146,6 +156,18 @@ def test_encode_ref_rejects_bad_arguments():
 def test_rot_qgemv_rejects_k_beyond_its_register_staging():
     with pytest.raises(q.PgError) as ei:
         q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 32768, 1 << 22, 0, 32768, 1 << 20, 1, 1, 1 << 28, stream=0)
+    assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
+
+
+def test_table_stage_rejects_k_beyond_its_rotation_rounds():
+    with pytest.raises(q.PgError) as ei:
+        q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 32768, 1 << 22, 0, 1 << 20, 1 << 18, 1, 1 << 28, stream=0)
+    assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
+
+
+def test_table_stage_rejects_fp32_input_without_normalisation():
+    with pytest.raises(q.PgError) as ei:
+        q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, q.PG_F32, 1 << 20, 1 << 18, 0, 1 << 24, stream=0)
     assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
 
 
@@ -209,6 +231,11 @@ class _FakeDeviceTensor:
      "workspace"),
     (lambda t: q.pg_fwht_rotate(t(4 * 256 * 2), 1, t(4 * 256 * 4 - 1), 0, t(32), 4, 256), "y"),
     (lambda t: q.pg_decode(t(256 * 64, contiguous=False), t(256 * 4), 256, 256, t(256 * 256 * 4)), "codes"),
+    (lambda t: q.pg_decode_table(t(256 * 64), t(256 * 4), 256, 256, t(8191), 0, t(256 * 256 * 4)), "table"),
+    (lambda t: q.pg_rot_qgemv_table(t(64 * 64), t(64 * 4), 64, 256, t(256 * 2 - 2), 1, t(32), t(8192), 1,
+                                    t(64 * 4)), "x"),
+    (lambda t: q.pg_rot_qgemv_table(t(64 * 64), t(64 * 4), 64, 256, t(256 * 2), 1, t(32), t(8192), 1, t(63 * 4)),
+     "y"),
 ])
 def test_binding_checks_device_buffers_before_the_call(bad, what):
     """Undersized, non-contiguous or host buffers raise ValueError in the
