@@ -201,7 +201,19 @@ def stack_result(st, ms_per_step: float, batch: int, per_site_us: dict):
             "avg_weight_launch_us": round(avg_us, 3), "per_site": per}
 
 
-def build_stack(workload: str, batch: int, path: str, carry: bool):
+def codebook_tensor(table: str):
+    """Device codebook table for the table-driven path: "v1" is P8F v1's own
+    (pg_codebook_table), "gauss" a seeded rounded-Gaussian int8 table."""
+    import numpy as np
+    import torch
+
+    import qgemv_amd as q
+    from qgemv_amd import synth
+    t = q.pg_codebook_table() if table == "v1" else synth.random_codebook_table(22, "gauss")
+    return torch.from_numpy(np.ascontiguousarray(t)).cuda()
+
+
+def build_stack(workload: str, batch: int, path: str, carry: bool, table: str = "none"):
     from qgemv_amd import _lib as L
     from qgemv_amd import synth
     from qgemv_amd.stack import Stack
@@ -209,7 +221,26 @@ def build_stack(workload: str, batch: int, path: str, carry: bool):
     layers = 36 if workload == "qwen36" else 32
     fused = path in ("fused", "hybrid")
     split_above = 4096 if path == "hybrid" else None
-    return Stack(shapes, layers, batch=batch, x_dtype=L.PG_Q16, fused=fused, carry=carry, split_above=split_above)
+    tab = codebook_tensor(table) if table != "none" else None
+    return Stack(shapes, layers, batch=batch, x_dtype=L.PG_Q16, fused=fused, carry=carry, split_above=split_above,
+                 table=tab)
+
+
+def run_table_stacks(steps: int, warmup: int):
+    """The Qwen3-4B-shaped 36-layer stack at batch 1 with every launch group
+    through a codebook table in LDS (pg_rot_qgemv_table): P8F v1's own table
+    and a rounded-Gaussian one, each timed as the headline."""
+    import torch
+    out = {}
+    for table in ("v1", "gauss"):
+        st = build_stack("qwen36", 1, "fused", False, table)
+        ms, _, _ = run_stack(st, steps, warmup)
+        per, _ = time_launches(st, torch.cuda.current_stream(), reps=5)
+        out[table] = {"kernel": "k_rot_qgemv1<TAB=1> (pg_rot_qgemv_table)", **stack_result(st, ms, 1, per)}
+        log(f"table {table}: {out[table]['ms_per_step']} ms/step, {out[table]['gbs']} GB/s")
+        del st
+        torch.cuda.empty_cache()
+    return out
 
 
 def auto_path(batch: int, carry: bool) -> str:
@@ -489,6 +520,8 @@ def main():
     ap.add_argument("--carry", action="store_true",
                     help="read the codes as the carried-state variant (state runs on across blocks; fused path)")
     ap.add_argument("--only-stack", action="store_true", help="only the headline stack (for profiling runs)")
+    ap.add_argument("--table", default="none", choices=["none", "v1", "gauss"],
+                    help="run the headline stack through a codebook table (pg_rot_qgemv_table; batch 1)")
     ap.add_argument("--only-qgemm", action="store_true",
                     help="only the prompt-path products, printed as one JSON line (for profiling runs)")
     ap.add_argument("--no-qgemm", action="store_true", help="skip the prompt-path (pg_qgemm) measurement")
@@ -523,14 +556,19 @@ def main():
     # ---- the headline stack
     path = args.path if args.path != "auto" else auto_path(args.batch, args.carry)
     log(f"building {args.workload}: batch {args.batch}, {path} path")
-    st = build_stack(args.workload, args.batch, path, args.carry)
+    if args.table != "none" and (args.batch != 1 or path != "fused"):
+        print("--table runs the fused batch-1 path only", file=sys.stderr)
+        sys.exit(2)
+    st = build_stack(args.workload, args.batch, path, args.carry, args.table)
     stream = torch.cuda.current_stream()
     ms, gpu_ms, wall_ms = run_stack(st, args.steps, args.warmup, use_graph=not args.no_graph)
     log(f"timed {args.steps} steps: {gpu_ms:.2f} ms (events), {wall_ms:.2f} ms (wall)")
     per_site_us, nlaunch = time_launches(st, stream)
     head = stack_result(st, ms, args.batch, per_site_us)
     fused_b1 = path == "fused" and args.batch <= 1
-    if fused_b1 and not args.carry:
+    if args.table != "none":
+        kname, kdesc = "k_rot_qgemv1", f"k_rot_qgemv1<TAB=1> (pg_rot_qgemv_table, {args.table} codebook table in LDS)"
+    elif fused_b1 and not args.carry:
         kname, kdesc = "k_rot_qgemv1", "k_rot_qgemv1 (pg_rot_qgemv at batch 1: RMS norm + rotation + qgemv, one launch per stage)"
     elif path == "fused":
         kname, kdesc = "k_rot_qgemv", "k_rot_qgemv (pg_rot_qgemv: RMS norm + rotation + qgemv, one launch per stage)"
@@ -541,6 +579,8 @@ def main():
         kname = "k_qgemv_q16" if args.batch == 1 else "k_qgemv_mma"
         kdesc = f"{kname} (pg_qgemv on PG_Q16 activations, after k_fwht)"
     wl = ("qwen3-4b-36L" if args.workload == "qwen36" else "llama3.1-8b-32L") + f"-b{args.batch}"
+    if args.table != "none":
+        wl += f"-table-{args.table}"
     bytes_per_launch = st.bytes_per_token // head["weight_launches_per_token"]
     avg_us = head["avg_weight_launch_us"]
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
@@ -555,7 +595,8 @@ def main():
                    "layers": st.layers, "batch": args.batch, "bytes_per_token": st.bytes_per_token,
                    "tok_per_s": head["tok_per_s"], "pct_hbm_peak": head["pct_hbm_peak"],
                    "hip_graphs": not args.no_graph, "path": path,
-                   "format": "carried-state variant" if args.carry else "P8F v1"},
+                   "format": ("carried-state variant" if args.carry else "P8F v1") +
+                             (f", {args.table} codebook table" if args.table != "none" else "")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(kname, wl),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
@@ -588,6 +629,8 @@ def main():
             del base
             torch.cuda.empty_cache()
             res["llama32"] = ll
+            log("timing the stack through codebook tables (pg_rot_qgemv_table)")
+            res["table"] = run_table_stacks(max(5, args.steps // 2), args.warmup)
             log("timing the 512 x 2048 layer warm and cold")
             res["single_layer"] = run_single_layer()
             log("timing each Qwen3-4B matrix cold")

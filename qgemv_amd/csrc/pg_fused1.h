@@ -304,10 +304,12 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
                     else
                         prev = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb[j].w, 0x111, 0xf, 0xf, true) & left_mask;
                     const uint32_t w = w4[m];
-                    // state of byte b: branch bits of bytes b-1, b-2, b-3 at its bits 0, 1, 2
-                    uint32_t st = __builtin_amdgcn_alignbit(w, prev, 24) & 0x01010101u;
-                    st |= __builtin_amdgcn_alignbit(w, prev, 15) & 0x02020202u;
-                    st |= __builtin_amdgcn_alignbit(w, prev, 6) & 0x04040404u;
+                    // state of byte b: branch bits of bytes b-1, b-2, b-3 at its bits 0, 1, 2;
+                    // with only the branch bits kept, the three shifted copies
+                    // land on disjoint bits and need no masks
+                    const uint32_t uw = w & 0x01010101u, up = prev & 0x01010101u;
+                    const uint32_t st = __builtin_amdgcn_alignbit(uw, up, 24) | __builtin_amdgcn_alignbit(uw, up, 15) |
+                                        __builtin_amdgcn_alignbit(uw, up, 6);
                     int h = hi[j], l = lo[j];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {

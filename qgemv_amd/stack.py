@@ -13,7 +13,9 @@ input is fp16 and is not normalised.  k, v and u are computed and stored but
 not consumed.  The fused path (default) runs each group as one
 pg_rot_qgemv launch (normalisation + rotation + product, batch 1..8); the
 split path runs pg_fwht_rotate_ex then pg_qgemv (batch 1..8; from batch 2 on
-pg_qgemv's products run on the matrix cores).
+pg_qgemv's products run on the matrix cores).  With a codebook table (batch 1,
+fused) every group runs as one pg_rot_qgemv_table launch, the codes read
+through that table.
 """
 from __future__ import annotations
 
@@ -25,8 +27,12 @@ ORDER = ("qkv", "o", "gu", "down")
 
 class Stack:
     def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_Q16,
-                 fused: bool = True, carry: bool = False, split_above: int | None = None):
+                 fused: bool = True, carry: bool = False, split_above: int | None = None, table=None):
         import torch
+        if table is not None and (not fused or batch != 1 or split_above is not None):
+            raise ValueError("a codebook table runs on the fused batch-1 path only")
+        # device int8 [8][256][4] codebook, or None for P8F v1's closed form
+        self.table = table
         if carry and not fused:
             raise ValueError("carried-state codes run on the fused path only")
         # random bytes are valid paths of both the per-block and the
@@ -118,6 +124,11 @@ class Stack:
                     out.append(("product", layer, site,
                                 lambda c=c, s=s, n=n, k=k, y=y, xd=xd:
                                 L.pg_qgemv(c, s, n, k, self.xrot, xd, b, y, stream)))
+                elif self.table is not None:
+                    out.append(("product", layer, site,
+                                lambda c=c, s=s, n=n, k=k, src=src, src_dt=src_dt, g=g, flags=flags, y=y:
+                                L.pg_rot_qgemv_table(c, s, n, k, src, src_dt, g, self.table, flags | self.cflag, y,
+                                                     stream)))
                 else:
                     out.append(("product", layer, site,
                                 lambda c=c, s=s, n=n, k=k, src=src, src_dt=src_dt, ldx=ldx, g=g, flags=flags, y=y:

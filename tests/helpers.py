@@ -65,10 +65,11 @@ def encoded_qwen(name: str):
     return _cached(f"qwen_{name}", run)
 
 
-def oracle_chain(codes, scales, signs, shapes, h0, layers, carry=False):
+def oracle_chain(codes, scales, signs, shapes, h0, layers, carry=False, table=None):
     """The stack driver's chain (qgemv_amd.stack) written with the oracle's
     fp64 functions: rotate, RMS-normalise with fp16 rounding, product
-    (carry: codes of the carried-state variant)."""
+    (carry: codes of the carried-state variant; table: levels read through
+    that codebook table)."""
     from qgemv_amd.stack import ORDER
     merged = synth.merged_shapes(shapes)
     h = np.asarray(h0, dtype=np.float64)
@@ -82,7 +83,10 @@ def oracle_chain(codes, scales, signs, shapes, h0, layers, carry=False):
                 prev = {"o": "qkv", "gu": "o", "down": "gu"}[site]
                 src = p8f.rmsnorm16(out[prev][:, :k])
             xr = p8f.rotate(src[:, :k], signs[layer][site])
-            out[site] = p8f.gemv_ref(codes[layer][site], scales[layer][site], xr, carry)
+            if table is None:
+                out[site] = p8f.gemv_ref(codes[layer][site], scales[layer][site], xr, carry)
+            else:
+                out[site] = p8f.gemv_table_ref(codes[layer][site], scales[layer][site], table, xr, carry)
     return out["down"]
 
 

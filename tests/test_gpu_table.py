@@ -14,7 +14,8 @@ import pytest
 import qgemv_amd as q
 from oracle import p8f
 from qgemv_amd import synth
-from tests.helpers import TOL, dev, host, rel_err_rows
+from qgemv_amd.stack import Stack
+from tests.helpers import TOL, dev, host, oracle_chain, rel_err, rel_err_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -139,3 +140,21 @@ def test_stage_table_zero_input():
     assert np.all(_stage_table(codes, scales, k, np.zeros((1, k), np.float16), q.PG_F16, sb, t, 0) == 0.0)
     assert np.all(_stage_table(codes, scales, k, np.zeros((1, k), np.float32), q.PG_F32, sb, t,
                                q.PG_FLAG_RMSNORM) == 0.0)
+
+
+@pytest.mark.parametrize("shapes_fn,carry", [(synth.qwen3_4b_shapes, False), (synth.llama31_8b_shapes, True)])
+def test_table_stack_chain_matches_oracle(shapes_fn, carry):
+    """Two layers of the stack with every launch group through a
+    rounded-Gaussian table (down at k = 9728 / 14336 included), against the
+    oracle's chain with the same table; replays bitwise repeatable."""
+    import torch
+    t = synth.random_codebook_table(24, "gauss")
+    shapes = shapes_fn()
+    st = Stack(shapes, 2, fused=True, carry=carry, table=dev(t))
+    got = host(st.token()).copy()
+    torch.cuda.synchronize()
+    codes, scales, signs = zip(*[st.host_arrays(l) for l in range(2)])
+    ref = oracle_chain(list(codes), list(scales), list(signs), shapes, host(st.h0).astype(np.float64), 2,
+                       carry=carry, table=t)
+    assert rel_err(got, ref) <= TOL
+    assert np.array_equal(host(st.token()).view(np.uint32), got.view(np.uint32))
