@@ -879,3 +879,94 @@ def exhaustive_encode_r23(w_rot_row: np.ndarray, scale_bits: int) -> float:
         d = w - sv * np.array(decode_block_levels_r23(codes), dtype=np.float64)
         best = min(best, float(np.sum(d * d)))
     return best
+
+
+# ------------------------------------------- LDLQ with a proxy Hessian
+# The landing page's "How it works" section names LDLQ as the compressor's
+# rounding: each coded unit's error is passed on, through the Hessian of the
+# layer's inputs, to the units not yet coded.  Here the unit is the 128-block
+# (the trellis restarts per block, so a block's codes are final only when its
+# Viterbi ends): with H~ = R H R^T the Hessian in the rotated basis, and
+# H~ = U D U^T (U unit upper block-triangular, D block-diagonal, blocks of
+# 128), block j is coded against the target
+#     T_j = W~_j + sum_{c < 128 j} (W~ - What)[:, c] * U[c, block j]
+# (its scale from T_j by the usual rule), so that the proxy loss
+# tr(E H~ E^T), E = What - W~, equals sum_j tr(eta_j D_j eta_j^T) with eta_j
+# = What_j - T_j the block's own rounding error.  H = I gives U = I and the
+# plain encoder.  The feedback sum runs over c in increasing order, one
+# rounding per product and per addition (fp64), the order the library's
+# encoders use.
+def rotate_hessian(h: np.ndarray, sign_bits: np.ndarray) -> np.ndarray:
+    """H~ = R H R^T for the block rotation R of the input site (fp64)."""
+    hr = rotate(np.asarray(h, dtype=np.float64), sign_bits)     # H R^T
+    return rotate(np.ascontiguousarray(hr.T), sign_bits)        # R (H R^T)^T R^T = R H R^T (H symmetric)
+
+
+def block_udu(h: np.ndarray, block: int = BLOCK):
+    """H = U D U^T for symmetric positive definite H [k][k]: U unit upper
+    block-triangular, D block-diagonal (blocks of `block`), by eliminating
+    the blocks from the last one up.  Returns (U, D)."""
+    a = np.array(h, dtype=np.float64, copy=True)
+    k = a.shape[0]
+    nb = k // block
+    u = np.eye(k)
+    d = np.zeros((k, k))
+    for j in range(nb - 1, -1, -1):
+        sl = slice(j * block, (j + 1) * block)
+        dj = a[sl, sl].copy()
+        np.linalg.cholesky(dj)                          # raises unless positive definite
+        d[sl, sl] = dj
+        if j:
+            pre = slice(0, j * block)
+            x = np.linalg.solve(dj, a[pre, sl].T).T     # U[pre, block j] = H[pre, j] D_j^-1
+            u[pre, sl] = x
+            a[pre, pre] = a[pre, pre] - x @ a[pre, sl].T
+    return u, d
+
+
+def ldlq_encode_rotated(w_rot: np.ndarray, h_rot: np.ndarray, block: int = BLOCK, c: float = SCALE_C):
+    """Block LDLQ over rotated weights W~ [N][K] with the rotated Hessian
+    H~ [K][K]: per block in order the target T_j (feedback summed as stated
+    above), its scale, its minimum-squared-error trellis path.  `block` may
+    be shortened (a multiple of 4) for tests on tiny blocks.  Returns codes
+    u8 [N][K/4], scale bits u16 [N][K/block] and the rounding errors
+    eta [N][K] (What - T per block)."""
+    w = np.asarray(w_rot, dtype=np.float64)
+    n, k = w.shape
+    nb, g = k // block, block // 4
+    u, _ = block_udu(h_rot, block)
+    codes = np.zeros((n, k // 4), dtype=np.uint8)
+    scales = np.zeros((n, nb), dtype=np.uint16)
+    err = np.zeros((n, k))               # W~ - What of the blocks coded so far
+    eta = np.zeros((n, k))
+    for j in range(nb):
+        sl = slice(j * block, (j + 1) * block)
+        acc = np.zeros((n, block))
+        for cp in range(j * block):
+            acc = acc + err[:, cp:cp + 1] * u[cp, sl][None, :]
+        t = w[:, sl] + acc
+        sb = block_scale_bits(t, c)
+        cj = viterbi_encode(t, sb)
+        codes[:, j * g:(j + 1) * g] = cj
+        scales[:, j] = sb
+        lv = np.array([decode_block_levels(cj[r]) for r in range(n)], dtype=np.float64)
+        what = fp16_bits_to_float(sb)[:, None] * lv
+        err[:, sl] = w[:, sl] - what
+        eta[:, sl] = what - t
+    return codes, scales, eta
+
+
+def encode_matrix_ldlq(w: np.ndarray, sign_bits: np.ndarray, hessian: np.ndarray, c: float = SCALE_C):
+    """Offline compression with LDLQ: W [N][K] (fp32 values), the layer
+    inputs' proxy Hessian H [K][K] (symmetric positive definite, original
+    basis).  Returns codes u8 [N][K/4] and scale bits u16 [N][K/128]."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    wr = rotate(w, sign_bits)
+    codes, scales, _ = ldlq_encode_rotated(wr, rotate_hessian(hessian, sign_bits), BLOCK, c)
+    return codes, scales
+
+
+def proxy_loss(w_rot: np.ndarray, what: np.ndarray, h_rot: np.ndarray) -> float:
+    """tr(E H~ E^T) with E = What - W~ (fp64)."""
+    e = np.asarray(what, dtype=np.float64) - np.asarray(w_rot, dtype=np.float64)
+    return float(np.sum((e @ h_rot) * e))
