@@ -137,7 +137,7 @@ int pg_codebook_table(int8_t* out);
  *   sign_bits  host u8 [k/8], the input site's random signs
  *   codes      host u8 [n][k/4] out
  *   scales     host u16 [n][k/128] out (fp16 bits)
- *   n_threads  worker threads (<= 0: hardware concurrency)
+ *   n_threads  worker threads (<= 0: the hardware concurrency, at most 16)
  * Per row: rotate each 128-block in fp64; scale = fp16_RNE(min(0.29 * rms,
  * 65504)) with the squares summed in index order (0 if the block is zero);
  * Viterbi over the 32 groups from state 0 with a free end state, the branch
@@ -160,6 +160,39 @@ int pg_encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits
  * Buffers are the caller's; nothing is allocated.  n * k / 128 < 2^31. */
 int pg_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
               uint16_t* scales, pg_stream_t stream);
+
+/* LDLQ encoding with a proxy Hessian (landing page, "How it works": the
+ * compressor rounds with LDLQ, passing each coded unit's error through the
+ * Hessian on to the units not yet coded).  The unit is the 128-block:
+ *   H~ = R H R^T (the site's block rotation on both sides) = U D U^T, U unit
+ *   upper block-triangular, D block-diagonal (blocks of 128), factored on
+ *   the host in fp64;
+ *   block b of each row is coded (scale rule and Viterbi as pg_encode_ref)
+ *   against t = v + sum_{c < 128 b} e_c * (U - I)[c][128 b + i], summed in
+ *   increasing c with one rounding per product and per sum, where v are the
+ *   block's rotated weights and e = W~ - What of the blocks already coded.
+ * H = I (or any H without terms across blocks after rotation) gives
+ * pg_encode_ref's codes.
+ *   hessian  host fp64 [k][k], symmetric positive definite, in the original
+ *            (unrotated) input basis, e.g. the mean of x x^T over calibration
+ *            inputs; PG_ERR_INVALID_ARG if not finite, not symmetric (to
+ *            1e-12 of its largest entry) or not positive definite
+ * k <= 16384 (PG_ERR_UNSUPPORTED beyond): the feedback matrix is held as
+ * k x k fp64.  Other arguments as pg_encode_ref.  Synchronous. */
+int pg_encode_ref_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* hessian,
+                       uint8_t* codes, uint16_t* scales, int n_threads);
+
+/* The LDLQ encoder on the GPU: codes and scales bit-identical to
+ * pg_encode_ref_ldlq's.  The factorisation runs on the host (shared with
+ * pg_encode_ref_ldlq); the library then allocates k x k + n x k fp64 device
+ * buffers for the feedback matrix and the coded blocks' errors, launches one
+ * kernel per 128-block on `stream` (one workgroup per row: rotation, the
+ * feedback sum in the stated order, the block encoder of pg_encode, the
+ * block's errors), and frees them before returning.  Synchronous.
+ *   w, sign_bits, codes, scales: device, as pg_encode
+ *   hessian  host fp64 [k][k], as pg_encode_ref_ldlq */
+int pg_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* hessian,
+                   uint8_t* codes, uint16_t* scales, pg_stream_t stream);
 
 /* pg_encode with format flags: 0 is pg_encode (format P8F v1);
  * PG_FLAG_CARRY_STATE codes the carried-state variant with one Viterbi

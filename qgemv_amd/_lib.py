@@ -27,7 +27,8 @@ EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_erro
            "pg_encode", "pg_encode_ex", "pg_decode_ex",
            "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm",
            "pg_qgemm_ex", "pg_qgemm_workspace_bytes", "pg_hbm_read",
-           "pg_qgemm_noalloc", "pg_qgemv_ex", "pg_qgemm_tune", "pg_decode_table", "pg_rot_qgemv_table")
+           "pg_qgemm_noalloc", "pg_qgemv_ex", "pg_qgemm_tune", "pg_decode_table", "pg_rot_qgemv_table",
+           "pg_encode_ref_ldlq", "pg_encode_ldlq")
 
 
 class PgError(RuntimeError):
@@ -66,6 +67,10 @@ def lib():
         L.pg_encode_ref.argtypes = [vp, i64, i64, vp, vp, vp, i32]
         L.pg_encode.restype = i32
         L.pg_encode.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+        L.pg_encode_ref_ldlq.restype = i32
+        L.pg_encode_ref_ldlq.argtypes = [vp, i64, i64, vp, vp, vp, vp, i32]
+        L.pg_encode_ldlq.restype = i32
+        L.pg_encode_ldlq.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.pg_encode_ex.restype = i32
         L.pg_encode_ex.argtypes = [vp, i64, i64, vp, u32, vp, vp, vp]
         L.pg_decode_ex.restype = i32
@@ -205,6 +210,40 @@ def pg_encode_ref(w: np.ndarray, n: int, k: int, sign_bits: np.ndarray, codes: n
         if not a.flags["C_CONTIGUOUS"]:
             raise ValueError("host buffers must be C-contiguous")
     _check(lib().pg_encode_ref(_ptr(w), n, k, _ptr(sign_bits), _ptr(codes), _ptr(scales), n_threads))
+
+
+def _host_hessian(hessian, k: int):
+    if not isinstance(hessian, np.ndarray) or hessian.dtype != np.float64 or not hessian.flags["C_CONTIGUOUS"]:
+        raise ValueError("hessian: a C-contiguous float64 numpy array is required")
+    if k > 0 and hessian.size < k * k:
+        raise ValueError(f"hessian: {hessian.size} values, {k * k} needed")
+
+
+def pg_encode_ref_ldlq(w: np.ndarray, n: int, k: int, sign_bits: np.ndarray, hessian: np.ndarray,
+                       codes: np.ndarray, scales: np.ndarray, n_threads: int = 0) -> None:
+    """LDLQ reference encoder.  Host buffers (numpy, C-contiguous): w f32
+    [n][k], sign_bits u8 [k/8], hessian f64 [k][k], codes u8 [n][k/4] out,
+    scales u16 [n][k/128] out."""
+    for a, nbytes, name in ((w, n * k * 4, "w"), (sign_bits, k // 8, "sign_bits"), (codes, n * (k // 4), "codes"),
+                            (scales, n * (k // 128) * 2, "scales")):
+        if not isinstance(a, np.ndarray) or not a.flags["C_CONTIGUOUS"]:
+            raise ValueError(f"{name}: a C-contiguous numpy array is required")
+        if n > 0 and k > 0 and a.nbytes < nbytes:
+            raise ValueError(f"{name}: {a.nbytes} bytes, {nbytes} needed")
+    _host_hessian(hessian, k)
+    _check(lib().pg_encode_ref_ldlq(_ptr(w), n, k, _ptr(sign_bits), _ptr(hessian), _ptr(codes), _ptr(scales),
+                                    n_threads))
+
+
+def pg_encode_ldlq(w, n: int, k: int, sign_bits, hessian: np.ndarray, codes, scales, stream=None) -> None:
+    """LDLQ encoder on the GPU: w, sign_bits, codes, scales device buffers
+    as pg_encode; hessian host f64 [k][k] (numpy).  Synchronous."""
+    _need(w, max(n, 0) * max(k, 0) * 4, "w")
+    _need(sign_bits, max(k, 0) // 8, "sign_bits")
+    _weights(codes, scales, n, k)
+    _host_hessian(hessian, k)
+    _check(lib().pg_encode_ldlq(_ptr(w), n, k, _ptr(sign_bits), _ptr(hessian), _ptr(codes), _ptr(scales),
+                                _stream(stream)))
 
 
 def pg_encode(w, n: int, k: int, sign_bits, codes, scales, stream=None) -> None:

@@ -3,6 +3,8 @@
 // launches anything when an argument is invalid.
 #include <cstdint>
 
+#include <vector>
+
 #include "pg_internal.h"
 
 namespace {
@@ -81,6 +83,34 @@ int pg_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, ui
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 2, "scales"));
     return pg::launch_encode(w, n, k, sign_bits, codes, scales, stream);
+}
+
+int pg_encode_ref_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* hessian,
+                       uint8_t* codes, uint16_t* scales, int n_threads) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    if (k > 16384) return pg::fail(PG_ERR_UNSUPPORTED, "pg_encode_ref_ldlq: k <= 16384 (the feedback matrix is k^2 fp64)");
+    PG_TRY(check_ptr(w, 4, "w"));
+    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    PG_TRY(check_ptr(hessian, 8, "hessian"));
+    PG_TRY(check_ptr(codes, 1, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    std::vector<double> fb((size_t)(k * k));
+    PG_TRY(pg::ldlq_feedback(hessian, k, sign_bits, n_threads, fb.data()));
+    return pg::encode_ref_ldlq(w, n, k, sign_bits, fb.data(), codes, scales, n_threads);
+}
+
+int pg_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* hessian,
+                   uint8_t* codes, uint16_t* scales, pg_stream_t stream) {
+    pg::clear_error();
+    PG_TRY(check_nk(n, k));
+    if (k > 16384) return pg::fail(PG_ERR_UNSUPPORTED, "pg_encode_ldlq: k <= 16384 (the feedback matrix is k^2 fp64)");
+    PG_TRY(check_ptr(w, 4, "w"));
+    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    PG_TRY(check_ptr(hessian, 8, "hessian"));
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    return pg::run_encode_ldlq(w, n, k, sign_bits, hessian, codes, scales, stream);
 }
 
 int pg_encode_ex(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint32_t flags, uint8_t* codes,

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "pg_internal.h"
 
 namespace pg {
@@ -163,6 +165,151 @@ __global__ __launch_bounds__(128) void k_encode(const float* __restrict__ w, int
     }
 }
 
+// LDLQ variant (landing page, "How it works": LDLQ rounding): one launch per
+// 128-block b, one workgroup per row.  Thread i rotates weight i of the
+// block as above (v_i), adds the feedback of the blocks already coded,
+//   t_i = v_i + sum_{c < 128 b} err[row][c] * fb[c][128 b + i]
+// (increasing c, one rounding per product and per sum, as the host
+// reference), and the block is coded against t by the steps above; then
+// thread i decodes its own weight from the chosen bytes and stores
+// err[row][128 b + i] = v_i - s * level_i for the next blocks.
+__global__ __launch_bounds__(128) void k_encode_ldlq(const float* __restrict__ w, int n, int k,
+                                                     const uint8_t* __restrict__ sign_bits,
+                                                     const double* __restrict__ fb, double* __restrict__ err,
+                                                     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                     int b) {
+#pragma clang fp contract(off)
+    __shared__ double v[128];
+    __shared__ double bm[32][4];
+    __shared__ int barg[32][4];
+    __shared__ double metric[8];
+    __shared__ int8_t prv[32][8];
+    __shared__ uint8_t byt[32][8];
+    __shared__ uint8_t out[32];
+    __shared__ uint32_t sbits;
+    const int tid = threadIdx.x;
+    const int nb = k >> 7;
+    const int row = blockIdx.x;
+    const int64_t kk = (int64_t)b * 128 + tid;
+
+    // ---- 1. rotation (as k_encode)
+    double x = (double)w[(int64_t)row * k + kk];
+    if ((sign_bits[kk >> 3] >> (kk & 7)) & 1) x = -x;
+    v[tid] = x;
+    __syncthreads();
+    for (int h = 1; h < 128; h <<= 1) {
+        const int j = (tid / h) * 2 * h + (tid % h);
+        double a = 0.0, c = 0.0;
+        if (tid < 64) { a = v[j]; c = v[j + h]; }
+        __syncthreads();
+        if (tid < 64) { v[j] = a + c; v[j + h] = a - c; }
+        __syncthreads();
+    }
+    const double vr = v[tid] * 0x1.6a09e667f3bcdp-4;
+
+    // ---- LDLQ feedback of the coded blocks: the loads run ahead, the sum in order
+    {
+        const double* e = err + (int64_t)row * k;
+        const double* f = fb + kk;
+        double acc = 0.0;
+        const int m = 128 * b;
+        int c = 0;
+        for (; c + 8 <= m; c += 8) {
+            double p[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) p[q] = e[c + q] * f[(int64_t)(c + q) * k];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc = acc + p[q];
+        }
+        for (; c < m; ++c) acc = acc + e[c] * f[(int64_t)c * k];
+        __syncthreads();
+        v[tid] = vr + acc;
+    }
+    __syncthreads();
+
+    // ---- 2. scale from the RMS of the target
+    if (tid == 0) {
+        double acc = 0.0;
+        for (int i = 0; i < 128; ++i) acc = acc + v[i] * v[i];
+        const double rms = sqrt(acc / 128.0);
+        const double sc = 0.29 * rms;
+        const double val = 65504.0 < sc ? 65504.0 : sc;
+        sbits = enc_half_rne(val);
+        scales[(int64_t)row * nb + b] = (uint16_t)sbits;
+    }
+    __syncthreads();
+    const double s = enc_half_to_double((uint16_t)sbits);
+
+    // ---- 3. branch metrics (as k_encode)
+    {
+        const int t = tid >> 2, cs = tid & 3, z0 = cs >> 1, z1 = cs & 1;
+        const double w0 = v[4 * t], w1 = v[4 * t + 1], w2 = v[4 * t + 2], w3 = v[4 * t + 3];
+        double best = __builtin_inf();
+        int arg = 0;
+        for (int i = 0; i < 128; ++i) {
+            const int b0 = i & 1, b1 = (i >> 1) & 1, b2 = (i >> 2) & 1, b3 = z1 ^ b0 ^ b1 ^ b2;
+            const double p0 = (double)(4 * (2 * ((i >> 3) & 1) + b0) + 2 * z0 - 7);
+            const double p1 = (double)(4 * (2 * ((i >> 4) & 1) + b1) + 2 * z0 - 7);
+            const double p2 = (double)(4 * (2 * ((i >> 5) & 1) + b2) + 2 * z0 - 7);
+            const double p3 = (double)(4 * (2 * ((i >> 6) & 1) + b3) + 2 * z0 - 7);
+            const double d0 = w0 - s * p0, d1 = w1 - s * p1, d2 = w2 - s * p2, d3 = w3 - s * p3;
+            const double m = ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
+            if (m < best) { best = m; arg = i; }
+        }
+        bm[t][cs] = best;
+        barg[t][cs] = arg;
+    }
+    if (tid < 8) metric[tid] = tid == 0 ? 0.0 : __builtin_inf();
+    __syncthreads();
+
+    // ---- 4. add-compare-select and traceback (as k_encode)
+    for (int t = 0; t < 32; ++t) {
+        double nxt = __builtin_inf();
+        if (tid < 8) {
+            const int sn = tid, u = sn & 1;
+            int pv = 0, by = 0;
+            for (int c = 0; c < 2; ++c) {
+                const int ps = c == 0 ? sn >> 1 : (sn >> 1) | 4;
+                const int z0 = (ps >> 1) & 1, z1 = u ^ (ps & 1) ^ ((ps >> 2) & 1);
+                const double tot = metric[ps] + bm[t][2 * z0 + z1];
+                if (tot < nxt) { nxt = tot; pv = ps; by = (barg[t][2 * z0 + z1] << 1) | u; }
+            }
+            prv[t][sn] = (int8_t)pv;
+            byt[t][sn] = (uint8_t)by;
+        }
+        __syncthreads();
+        if (tid < 8) metric[tid] = nxt;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        int st = 0;
+        for (int q = 1; q < 8; ++q)
+            if (metric[q] < metric[st]) st = q;
+        for (int t = 31; t >= 0; --t) {
+            out[t] = s == 0.0 ? 0 : byt[t][st];             // a zero scale codes every group as byte 0
+            st = prv[t][st];
+        }
+        uint32_t* dst = reinterpret_cast<uint32_t*>(codes + (int64_t)row * (k >> 2) + 32 * b);
+        for (int i = 0; i < 8; ++i)
+            dst[i] = (uint32_t)out[4 * i] | ((uint32_t)out[4 * i + 1] << 8) | ((uint32_t)out[4 * i + 2] << 16) |
+                     ((uint32_t)out[4 * i + 3] << 24);
+    }
+    __syncthreads();
+
+    // ---- 5. the error of this weight: state from the three bytes before its group
+    {
+        const int t = tid >> 2, j = tid & 3;
+        int st = 0;
+        for (int q = t - 3; q < t; ++q)
+            if (q >= 0) st = ((st << 1) | (out[q] & 1)) & 7;
+        const int c = out[t], u = c & 1, z0 = (st >> 1) & 1, z1 = u ^ (st & 1) ^ ((st >> 2) & 1);
+        const int bb0 = (c >> 1) & 1, bb1 = (c >> 2) & 1, bb2 = (c >> 3) & 1;
+        const int bj = j == 0 ? bb0 : j == 1 ? bb1 : j == 2 ? bb2 : (z1 ^ bb0 ^ bb1 ^ bb2);
+        const int lvl = 4 * (2 * ((c >> (4 + j)) & 1) + bj) + 2 * z0 - 7;
+        err[(int64_t)row * k + kk] = vr - s * (double)lvl;
+    }
+}
+
 // Carried-state variant: one workgroup per row walks its blocks in order,
 // each block rotated, scaled and scored as above, the path metrics carried
 // from block to block; the survivors of all 32 nb steps stay in LDS (2 bytes
@@ -279,6 +426,48 @@ int launch_encode_carry(const float* w, int64_t n, int64_t k, const uint8_t* sig
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PG_ERR_HIP, "pg_encode_ex launch: %s", hipGetErrorString(e));
     return PG_OK;
+}
+
+int launch_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* fb,
+                       double* err, uint8_t* codes, uint16_t* scales, pg_stream_t s) {
+    if (n > 0x7fffffff) return fail(PG_ERR_UNSUPPORTED, "pg_encode_ldlq: too many rows");
+    for (int64_t b = 0; b < k / 128; ++b) {
+        hipLaunchKernelGGL(k_encode_ldlq, dim3((unsigned)n), dim3(128), 0, (hipStream_t)s, w, (int)n, (int)k,
+                           sign_bits, fb, err, codes, scales, (int)b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(PG_ERR_HIP, "pg_encode_ldlq launch: %s", hipGetErrorString(e));
+    }
+    return PG_OK;
+}
+
+// pg_encode_ldlq: sign bits to the host, the feedback matrix factored there
+// (ldlq_feedback, shared with pg_encode_ref_ldlq), copied up with an error
+// buffer, one launch per block, then everything freed; returns when done.
+int run_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* hessian,
+                    uint8_t* codes, uint16_t* scales, pg_stream_t s) {
+    hipStream_t st = (hipStream_t)s;
+    std::vector<uint8_t> sb((size_t)(k / 8));
+    hipError_t e = hipMemcpyAsync(sb.data(), sign_bits, sb.size(), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(PG_ERR_HIP, "pg_encode_ldlq: reading sign_bits: %s", hipGetErrorString(e));
+    std::vector<double> fb((size_t)(k * k));
+    int rc = ldlq_feedback(hessian, k, sb.data(), 0, fb.data());
+    if (rc != PG_OK) return rc;
+    double* fb_d = nullptr;
+    double* err_d = nullptr;
+    e = hipMalloc((void**)&fb_d, sizeof(double) * (size_t)(k * k));
+    if (e == hipSuccess) e = hipMalloc((void**)&err_d, sizeof(double) * (size_t)(n * k));
+    if (e == hipSuccess) e = hipMemcpyAsync(fb_d, fb.data(), sizeof(double) * fb.size(), hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) {
+        rc = fail(PG_ERR_HIP, "pg_encode_ldlq: %s", hipGetErrorString(e));
+    } else {
+        rc = launch_encode_ldlq(w, n, k, sign_bits, fb_d, err_d, codes, scales, s);
+        e = hipStreamSynchronize(st);
+        if (rc == PG_OK && e != hipSuccess) rc = fail(PG_ERR_HIP, "pg_encode_ldlq: %s", hipGetErrorString(e));
+    }
+    if (fb_d) (void)hipFree(fb_d);
+    if (err_d) (void)hipFree(err_d);
+    return rc;
 }
 
 int launch_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,

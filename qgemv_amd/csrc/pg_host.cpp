@@ -184,13 +184,166 @@ void encode_block(const double* w, uint16_t scale_bits, const CosetPoints& P, ui
     if (s == 0.0) std::memset(out, 0, 32);
 }
 
+// level_j of every weight of one block from its 32 code bytes (state 0 at the start)
+void decode_block_levels(const uint8_t* c, double* lv) {
+    int st = 0;
+    for (int t = 0; t < 32; ++t) {
+        int l[4];
+        group_levels(st, c[t], l);
+        for (int j = 0; j < 4; ++j) lv[4 * t + j] = (double)l[j];
+        st = ((st << 1) | (c[t] & 1)) & 7;
+    }
+}
+
+// run f(r) for r in [0, count) on up to n_threads threads
+template <class F>
+void parallel_rows(int64_t count, int n_threads, F f) {
+    if (n_threads <= 0) n_threads = (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
+    n_threads = (int)std::max<int64_t>(1, std::min<int64_t>(n_threads, count));
+    std::atomic<int64_t> next{0};
+    auto worker = [&]() {
+        for (;;) {
+            const int64_t r = next.fetch_add(1);
+            if (r >= count) break;
+            f(r);
+        }
+    };
+    std::vector<std::thread> pool;
+    for (int t = 1; t < n_threads; ++t) pool.emplace_back(worker);
+    worker();
+    for (auto& th : pool) th.join();
+}
+
 }  // namespace
+
+// LDLQ feedback (landing page, "How it works": LDLQ rounding).  H~ = R H R^T
+// (the block rotation on both sides), then H~ = U D U^T with U unit upper
+// block-triangular and D block-diagonal (blocks of 128), eliminating blocks
+// from the last one up: U[<j, j] = H[<j, j] D_j^-1 through a Cholesky of D_j,
+// then H[<j, <j] -= U[<j, j] H[<j, j]^T.  fb receives U - I (k x k,
+// row-major; only blocks above the diagonal are non-zero).
+int ldlq_feedback(const double* hessian, int64_t k, const uint8_t* sign_bits, int n_threads, double* fb) {
+    const int64_t nb = k / 128;
+    for (int64_t i = 0; i < k * k; ++i)
+        if (!std::isfinite(hessian[i])) return fail(PG_ERR_INVALID_ARG, "hessian holds a non-finite value");
+    double amax = 0.0;
+    for (int64_t i = 0; i < k * k; ++i) amax = std::max(amax, std::fabs(hessian[i]));
+    for (int64_t r = 0; r < k; ++r)
+        for (int64_t c = r + 1; c < k; ++c)
+            if (std::fabs(hessian[r * k + c] - hessian[c * k + r]) > 1e-12 * amax)
+                return fail(PG_ERR_INVALID_ARG, "hessian is not symmetric (entries %lld, %lld)", (long long)r,
+                            (long long)c);
+    std::vector<double> a((size_t)(k * k)), tmp((size_t)(k * k));
+    // H R^T: every row's blocks rotated; then the same on the transpose
+    parallel_rows(k, n_threads, [&](int64_t r) {
+        std::memcpy(&tmp[(size_t)(r * k)], hessian + r * k, sizeof(double) * (size_t)k);
+        for (int64_t b = 0; b < nb; ++b) rotate_block(&tmp[(size_t)(r * k + b * 128)], sign_bits, b * 128);
+    });
+    parallel_rows(k, n_threads, [&](int64_t r) {
+        for (int64_t c = 0; c < k; ++c) a[(size_t)(r * k + c)] = tmp[(size_t)(c * k + r)];
+        for (int64_t b = 0; b < nb; ++b) rotate_block(&a[(size_t)(r * k + b * 128)], sign_bits, b * 128);
+    });
+    std::fill(fb, fb + k * k, 0.0);
+    std::vector<double> chol(128 * 128);
+    for (int64_t j = nb - 1; j >= 1; --j) {
+        const int64_t j0 = j * 128;
+        // Cholesky of D_j = a[j0.., j0..]: chol lower triangular
+        for (int p = 0; p < 128; ++p) {
+            for (int q = 0; q <= p; ++q) {
+                double v = a[(size_t)((j0 + p) * k + j0 + q)];
+                for (int t = 0; t < q; ++t) v -= chol[p * 128 + t] * chol[q * 128 + t];
+                if (p == q) {
+                    if (!(v > 0.0)) return fail(PG_ERR_INVALID_ARG, "hessian is not positive definite");
+                    chol[p * 128 + p] = std::sqrt(v);
+                } else {
+                    chol[p * 128 + q] = v / chol[q * 128 + q];
+                }
+            }
+        }
+        // rows above: D_j x = a[r, block j]^T, x = U[r, block j]
+        parallel_rows(j0, n_threads, [&](int64_t r) {
+            double y[128];
+            const double* h = &a[(size_t)(r * k + j0)];
+            for (int p = 0; p < 128; ++p) {
+                double v = h[p];
+                for (int t = 0; t < p; ++t) v -= chol[p * 128 + t] * y[t];
+                y[p] = v / chol[p * 128 + p];
+            }
+            double* x = fb + r * k + j0;
+            for (int p = 127; p >= 0; --p) {
+                double v = y[p];
+                for (int t = p + 1; t < 128; ++t) v -= chol[t * 128 + p] * x[t];
+                x[p] = v / chol[p * 128 + p];
+            }
+        });
+        // Schur complement of the rows and columns above block j
+        parallel_rows(j0, n_threads, [&](int64_t r) {
+            const double* x = fb + r * k + j0;
+            for (int64_t c = 0; c <= r; ++c) {
+                const double* h = &a[(size_t)(c * k + j0)];
+                double v = 0.0;
+                for (int q = 0; q < 128; ++q) v += x[q] * h[q];
+                a[(size_t)(r * k + c)] -= v;
+            }
+        });
+        parallel_rows(j0, n_threads, [&](int64_t r) {
+            for (int64_t c = r + 1; c < j0; ++c) a[(size_t)(r * k + c)] = a[(size_t)(c * k + r)];
+        });
+    }
+    // the first block's D must be positive definite too
+    for (int p = 0; p < 128; ++p)
+        for (int q = 0; q <= p; ++q) {
+            double v = a[(size_t)(p * k + q)];
+            for (int t = 0; t < q; ++t) v -= chol[p * 128 + t] * chol[q * 128 + t];
+            if (p == q) {
+                if (!(v > 0.0)) return fail(PG_ERR_INVALID_ARG, "hessian is not positive definite");
+                chol[p * 128 + p] = std::sqrt(v);
+            } else {
+                chol[p * 128 + q] = v / chol[q * 128 + q];
+            }
+        }
+    return PG_OK;
+}
+
+// Reference LDLQ encoder: per row, blocks in order; block b's target is
+// t_c = v_c + sum_{c' < 128 b} e_c' * fb[c'][128 b + c] (increasing c', one
+// rounding per product and per sum), v the rotated weights and e = v - What
+// of the blocks already coded; scale rule and Viterbi as encode_ref.
+int encode_ref_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* fb,
+                    uint8_t* codes, uint16_t* scales, int n_threads) {
+    static const CosetPoints P;
+    const int64_t nb = k / 128;
+    parallel_rows(n, n_threads, [&](int64_t r) {
+        std::vector<double> e((size_t)k), v(128), t(128), lv(128);
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int i = 0; i < 128; ++i) v[i] = (double)w[r * k + b * 128 + i];
+            rotate_block(v.data(), sign_bits, b * 128);
+            for (int i = 0; i < 128; ++i) {
+                double acc = 0.0;
+                for (int64_t cp = 0; cp < b * 128; ++cp) acc = acc + e[(size_t)cp] * fb[cp * k + b * 128 + i];
+                t[i] = v[i] + acc;
+            }
+            double acc = 0.0;
+            for (int i = 0; i < 128; ++i) acc = acc + t[i] * t[i];
+            const double rms = std::sqrt(acc / 128.0);
+            const double val = std::min(kScaleC * rms, 65504.0);
+            const uint16_t sb = double_to_half_rne(val);
+            scales[r * nb + b] = sb;
+            uint8_t* cb = codes + r * (k / 4) + b * 32;
+            encode_block(t.data(), sb, P, cb);
+            decode_block_levels(cb, lv.data());
+            const double s = half_to_double(sb);
+            for (int i = 0; i < 128; ++i) e[(size_t)(b * 128 + i)] = v[i] - s * lv[i];
+        }
+    });
+    return PG_OK;
+}
 
 int encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
                uint16_t* scales, int n_threads) {
     static const CosetPoints P;
     const int64_t nb = k / 128;
-    if (n_threads <= 0) n_threads = (int)std::max(1u, std::thread::hardware_concurrency());
+    if (n_threads <= 0) n_threads = (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
     n_threads = (int)std::min<int64_t>(n_threads, n);
     std::atomic<int64_t> next_row{0};
     auto worker = [&]() {

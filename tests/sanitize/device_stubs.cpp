@@ -43,4 +43,7 @@ int launch_encode(const float*, int64_t, int64_t, const uint8_t*, uint8_t*, uint
 int launch_encode_carry(const float*, int64_t, int64_t, const uint8_t*, uint8_t*, uint16_t*, pg_stream_t) {
     return no_device("pg_encode_ex");
 }
+int run_encode_ldlq(const float*, int64_t, int64_t, const uint8_t*, const double*, uint8_t*, uint16_t*, pg_stream_t) {
+    return no_device("pg_encode_ldlq");
+}
 }  // namespace pg
