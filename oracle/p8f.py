@@ -667,48 +667,56 @@ def decode_block_levels_table(codes, table) -> list[int]:
     return out
 
 
-def trellis_states(codes: np.ndarray, carry: bool = False) -> np.ndarray:
-    """The state each code byte of codes [..., K/4] is read in: its block's
-    (with carry: its row's) three previous branch bits, the newest at bit 0,
-    zero before the start.  Pinned against the scalar walks in the tests."""
+def trellis_states(codes: np.ndarray, carry: bool = False, rate23: bool = False) -> np.ndarray:
+    """The state each code byte of codes [..., K/4] is read in, zero before
+    the block's (with carry: the row's) start.  P8F v1: the three previous
+    branch bits, the newest at bit 0.  Rate 2/3 (the variant below): the
+    previous byte's two branch bits at bits 0, 1 and the branch bit u0 of
+    the byte before it at bit 2 (s' = ((s << 2) | u) & 7 unrolled).  Pinned
+    against the scalar walks in the tests."""
     c = np.asarray(codes, dtype=np.uint8)
     lead, g = c.shape[:-1], c.shape[-1]
     if g % GROUPS_PER_BLOCK:
         raise ValueError("K/4 must be a multiple of 32")
-    if carry:
-        u = (c & 1).reshape(lead + (1, g)).astype(np.int32)
+    shape = lead + (1, g) if carry else lead + (g // GROUPS_PER_BLOCK, GROUPS_PER_BLOCK)
+    c = c.reshape(shape).astype(np.int32)
+    s = np.zeros_like(c)
+    if rate23:
+        s[..., 1:] |= c[..., :-1] & 3
+        s[..., 2:] |= (c[..., :-2] & 1) << 2
     else:
-        u = (c & 1).reshape(lead + (g // GROUPS_PER_BLOCK, GROUPS_PER_BLOCK)).astype(np.int32)
-    s = np.zeros_like(u)
-    for d in (1, 2, 3):                      # branch bit d groups back -> state bit d - 1
-        s[..., d:] |= u[..., :-d] << (d - 1)
+        u = c & 1
+        for d in (1, 2, 3):                  # branch bit d groups back -> state bit d - 1
+            s[..., d:] |= u[..., :-d] << (d - 1)
     return s.reshape(lead + (g,))
 
 
-def decode_levels_table(codes: np.ndarray, table: np.ndarray, carry: bool = False) -> np.ndarray:
+def decode_levels_table(codes: np.ndarray, table: np.ndarray, carry: bool = False,
+                        rate23: bool = False) -> np.ndarray:
     """Levels of codes [..., K/4] under the table T [8][256][4] int8: the
-    group read in state s as byte c takes T[s][c].  Returns int8 [..., K]."""
+    group read in state s as byte c takes T[s][c]; the states follow P8F
+    v1's trellis, or the rate-2/3 one.  Returns int8 [..., K]."""
     c = np.asarray(codes, dtype=np.uint8)
     t = np.asarray(table, dtype=np.int8).reshape(8, 256, 4)
-    s = trellis_states(c, carry)
+    s = trellis_states(c, carry, rate23)
     return t[s, c].reshape(c.shape[:-1] + (c.shape[-1] * 4,))
 
 
 def decode_weights_table(codes: np.ndarray, scales_u16: np.ndarray, table: np.ndarray,
-                         carry: bool = False) -> np.ndarray:
+                         carry: bool = False, rate23: bool = False) -> np.ndarray:
     """Rotated-domain weights s * T-level as fp64 [..., K] (exact in fp32 as
     well: an 11-bit scale times an 8-bit level)."""
-    lv = decode_levels_table(codes, table, carry).astype(np.float64)
+    lv = decode_levels_table(codes, table, carry, rate23).astype(np.float64)
     s = fp16_bits_to_float(scales_u16)
     k = lv.shape[-1]
     return (lv.reshape(lv.shape[:-1] + (k // BLOCK, BLOCK)) * s[..., None]).reshape(lv.shape)
 
 
 def gemv_table_ref(codes: np.ndarray, scales_u16: np.ndarray, table: np.ndarray, x_rot: np.ndarray,
-                   carry: bool = False) -> np.ndarray:
+                   carry: bool = False, rate23: bool = False) -> np.ndarray:
     """y[b][n] = sum_blk s[n][blk] * sum_{k in blk} T-level[n][k] * x~[b][k] in
     fp64, x_rot [B][K].  Returns fp64 [B][N]."""
-    lv = decode_levels_table(codes, table, carry).astype(np.float64)
+    lv = decode_levels_table(codes, table, carry, rate23).astype(np.float64)
     n, k = lv.shape
     x = np.asarray(x_rot, dtype=np.float64).reshape(-1, k)
     s = fp16_bits_to_float(scales_u16)
@@ -748,6 +756,16 @@ def decode_group_r23(byte: int, s: int) -> list[int]:
     b0, b2 = (byte >> 2) & 1, (byte >> 3) & 1
     b = [b0, b0 ^ z2, b2, b2 ^ z1 ^ z2]
     return [4 * (2 * ((byte >> (4 + j)) & 1) + b[j]) + 2 * z0 - 7 for j in range(4)]
+
+
+def codebook_table_r23() -> np.ndarray:
+    """T[s][byte] = the four levels of `byte` read in state s (rate 2/3, int8):
+    with the rate-2/3 states, the table decode reproduces this variant."""
+    t = np.zeros((8, 256, 4), dtype=np.int8)
+    for s in range(8):
+        for byte in range(256):
+            t[s, byte] = decode_group_r23(byte, s)
+    return t
 
 
 def decode_block_levels_r23(codes) -> list[int]:

@@ -173,3 +173,29 @@ def test_full_block_viterbi_beats_greedy():
         s = p8f.next_state_r23(s, best & 3)
     assert vit <= p8f.block_distortion_r23(w, np.array([greedy], dtype=np.uint8), sb)[0] + 1e-12
     assert p8f.levels_trellis_valid_r23(p8f.decode_block_levels_r23(codes[0]))
+
+
+@pytest.mark.parametrize("carry", [False, True])
+def test_table_decode_with_rate23_states_equals_the_scalar_walk(carry):
+    """The rate-2/3 variant through the table decode: its own table with the
+    rate-2/3 state rule equals the defining scalar walk (per block, or along
+    the row with carried state); a random table follows the same states."""
+    rng = np.random.default_rng(111)
+    codes = rng.integers(0, 256, (6, 96), dtype=np.uint8)            # three blocks per row
+    got = p8f.decode_levels_table(codes, p8f.codebook_table_r23(), carry=carry, rate23=True)
+    for r in range(6):
+        if carry:
+            want = p8f.decode_block_levels_r23(codes[r])
+        else:
+            want = sum((p8f.decode_block_levels_r23(codes[r, 32 * b:32 * b + 32]) for b in range(3)), [])
+        assert got[r].tolist() == want
+    t = rng.integers(-128, 128, (8, 256, 4)).astype(np.int8)
+    st = p8f.trellis_states(codes, carry, rate23=True)
+    for r in range(2):
+        s = 0
+        for j in range(96):
+            if j % 32 == 0 and not carry:
+                s = 0
+            assert st[r, j] == s
+            s = p8f.next_state_r23(s, int(codes[r, j]) & 3)
+    assert np.array_equal(p8f.decode_levels_table(codes, t, carry, True).reshape(6, 96, 4), t[st, codes])
