@@ -203,13 +203,17 @@ def stack_result(st, ms_per_step: float, batch: int, per_site_us: dict):
 
 def codebook_tensor(table: str):
     """Device codebook table for the table-driven path: "v1" is P8F v1's own
-    (pg_codebook_table), "gauss" a seeded rounded-Gaussian int8 table."""
+    (pg_codebook_table), "gauss" a seeded rounded-Gaussian int8 table, "r23"
+    the rate-2/3 variant's own (read on its trellis)."""
     import numpy as np
     import torch
 
     import qgemv_amd as q
     from qgemv_amd import synth
-    t = q.pg_codebook_table() if table == "v1" else synth.random_codebook_table(22, "gauss")
+    if table == "r23":
+        t = q.pg_codebook_table_ex(q.PG_FLAG_RATE23)
+    else:
+        t = q.pg_codebook_table() if table == "v1" else synth.random_codebook_table(22, "gauss")
     return torch.from_numpy(np.ascontiguousarray(t)).cuda()
 
 
@@ -223,16 +227,17 @@ def build_stack(workload: str, batch: int, path: str, carry: bool, table: str = 
     split_above = 4096 if path == "hybrid" else None
     tab = codebook_tensor(table) if table != "none" else None
     return Stack(shapes, layers, batch=batch, x_dtype=L.PG_Q16, fused=fused, carry=carry, split_above=split_above,
-                 table=tab)
+                 table=tab, rate23=table == "r23")
 
 
 def run_table_stacks(steps: int, warmup: int):
     """The Qwen3-4B-shaped 36-layer stack at batch 1 with every launch group
     through a codebook table in LDS (pg_rot_qgemv_table): P8F v1's own table
-    and a rounded-Gaussian one, each timed as the headline."""
+    and a rounded-Gaussian one, and the rate-2/3 trellis with its own table,
+    each timed as the headline."""
     import torch
     out = {}
-    for table in ("v1", "gauss"):
+    for table in ("v1", "gauss", "r23"):
         st = build_stack("qwen36", 1, "fused", False, table)
         ms, _, _ = run_stack(st, steps, warmup)
         per, _ = time_launches(st, torch.cuda.current_stream(), reps=5)
@@ -520,7 +525,7 @@ def main():
     ap.add_argument("--carry", action="store_true",
                     help="read the codes as the carried-state variant (state runs on across blocks; fused path)")
     ap.add_argument("--only-stack", action="store_true", help="only the headline stack (for profiling runs)")
-    ap.add_argument("--table", default="none", choices=["none", "v1", "gauss"],
+    ap.add_argument("--table", default="none", choices=["none", "v1", "gauss", "r23"],
                     help="run the headline stack through a codebook table (pg_rot_qgemv_table; batch 1)")
     ap.add_argument("--only-qgemm", action="store_true",
                     help="only the prompt-path products, printed as one JSON line (for profiling runs)")

@@ -78,7 +78,8 @@ enum { PG_F32 = 0, PG_F16 = 1, PG_BF16 = 2,     /* element types of x / y */
 enum { PG_FLAG_RMSNORM = 1u,                    /* pg_fwht_rotate / pg_rot_qgemv flags */
        PG_FLAG_CARRY_STATE = 2u,                 /* codes of the carried-state variant (below) */
        PG_FLAG_KERNEL_VDOT = 4u,                 /* kernel choice, for tests and tuning (below) */
-       PG_FLAG_KERNEL_MMA = 8u };
+       PG_FLAG_KERNEL_MMA = 8u,
+       PG_FLAG_RATE23 = 16u };                   /* rate-2/3 trellis, through a codebook table (below) */
 
 /* Kernel choice.  Each product has kernels that compute the same values
  * (within the stated tolerances): products on the v_dot4 vector
@@ -95,6 +96,17 @@ enum { PG_FLAG_RMSNORM = 1u,                    /* pg_fwht_rotate / pg_rot_qgemv
  * next along a row instead of restarting at 0; a zero-scale block is 32
  * zero bytes.  Calls that take PG_FLAG_CARRY_STATE read (or write) codes of
  * this variant: pg_decode_ex, pg_encode_ex and pg_rot_qgemv. */
+
+/* Rate-2/3 trellis (landing page, section "Where the name comes from": 8
+ * states over short patterns, Ungerboeck-style labels): two branch bits per
+ * group (byte bits 0, 1) and the state step s' = ((s << 2) | u) & 7, so the
+ * state of a group is the previous byte's two branch bits (bits 0, 1) and
+ * bit 0 of the byte before it (bit 2).  Its codebook is given as a table:
+ * pg_codebook_table_ex(PG_FLAG_RATE23) writes the variant's own (the 512
+ * points of P8F v1 in 8 cosets of 64: z0 = bit 0 of s picks the value set,
+ * z1 = u0 ^ bit 1 of s the D4 parity, z2 = u1 ^ bit 2 of s the split
+ * b0 ^ b1; bits 2, 3 are b0, b2, b1 = b0 ^ z2, b3 = b2 ^ z1 ^ z2, bits 4..7
+ * are e0..e3).  pg_decode_table and pg_rot_qgemv_table take the flag. */
 
 #define PG_FORMAT_VERSION 1
 #define PG_LIB_VERSION 1
@@ -129,6 +141,11 @@ const char* pg_last_error(void);
  * pg_decode_table / pg_rot_qgemv_table it reproduces P8F v1 (the other
  * entry points compute the same levels from the byte's bits). */
 int pg_codebook_table(int8_t* out);
+
+/* A format's codebook as a table, [8][256][4] int8, host memory: flags 0
+ * is pg_codebook_table; PG_FLAG_RATE23 the rate-2/3 variant's (with
+ * PG_FLAG_RATE23 on the table calls it reproduces that variant). */
+int pg_codebook_table_ex(uint32_t flags, int8_t* out);
 
 /* Host (CPU) reference encoder, synchronous.  Follows the "How it works"
  * description (rotation, then sequential trellis coding; the LDLQ Hessian is
@@ -225,7 +242,9 @@ int pg_decode_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
  *            or P8F v1's own (pg_codebook_table).  Read only; the caller owns
  *            it and may change it between calls.
  * Decode to rotated-domain fp32 weights, w = fp32(scale) * level (exact).
- * flags 0 or PG_FLAG_CARRY_STATE.  Other arguments as pg_decode. */
+ * flags: PG_FLAG_CARRY_STATE (state run on along the row), PG_FLAG_RATE23
+ * (the states of the rate-2/3 trellis instead of P8F v1's).  Other
+ * arguments as pg_decode. */
 int pg_decode_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const int8_t* table,
                     uint32_t flags, float* w_rot, pg_stream_t stream);
 
@@ -319,7 +338,8 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
  * pg_decode_table): y = W~ . R . n(x) with W~'s levels read from table.
  *   codes, scales, sign_bits, x (first k values), y, x_dtype: as pg_rot_qgemv
  *   at batch 1; table as pg_decode_table
- *   flags    PG_FLAG_RMSNORM, PG_FLAG_CARRY_STATE (state run on along rows)
+ *   flags    PG_FLAG_RMSNORM, PG_FLAG_CARRY_STATE (state run on along rows),
+ *            PG_FLAG_RATE23 (the rate-2/3 trellis's states)
  * The rotated activations are quantised to 16-bit digits per 32 values as
  * pg_rot_qgemv at batch 1; each 32-value partial sum of level * digit is
  * exact in int32 and rounded once to fp32.  With P8F v1's table the output

@@ -22,13 +22,14 @@ PG_FLAG_RMSNORM = 1
 PG_FLAG_CARRY_STATE = 2
 PG_FLAG_KERNEL_VDOT = 4
 PG_FLAG_KERNEL_MMA = 8
+PG_FLAG_RATE23 = 16
 
 EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_error", "pg_codebook_table", "pg_encode_ref",
            "pg_encode", "pg_encode_ex", "pg_decode_ex",
            "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm",
            "pg_qgemm_ex", "pg_qgemm_workspace_bytes", "pg_hbm_read",
            "pg_qgemm_noalloc", "pg_qgemv_ex", "pg_qgemm_tune", "pg_decode_table", "pg_rot_qgemv_table",
-           "pg_encode_ref_ldlq", "pg_encode_ldlq")
+           "pg_encode_ref_ldlq", "pg_encode_ldlq", "pg_codebook_table_ex")
 
 
 class PgError(RuntimeError):
@@ -63,6 +64,8 @@ def lib():
         L.pg_last_error.argtypes = []
         L.pg_codebook_table.restype = i32
         L.pg_codebook_table.argtypes = [vp]
+        L.pg_codebook_table_ex.restype = i32
+        L.pg_codebook_table_ex.argtypes = [u32, vp]
         L.pg_encode_ref.restype = i32
         L.pg_encode_ref.argtypes = [vp, i64, i64, vp, vp, vp, i32]
         L.pg_encode.restype = i32
@@ -199,6 +202,14 @@ def pg_last_error() -> str:
 def pg_codebook_table() -> np.ndarray:
     out = np.zeros((8, 256, 4), dtype=np.int8)
     _check(lib().pg_codebook_table(out.ctypes.data))
+    return out
+
+
+def pg_codebook_table_ex(flags: int) -> np.ndarray:
+    """A format's codebook as a table (flags 0: P8F v1; PG_FLAG_RATE23: the
+    rate-2/3 variant)."""
+    out = np.zeros((8, 256, 4), dtype=np.int8)
+    _check(lib().pg_codebook_table_ex(flags, out.ctypes.data))
     return out
 
 

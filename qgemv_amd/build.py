@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libpingala.so")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["pg_host.cpp", "pg_api.cpp"]
-HIP_SOURCES = ["pg_kernels.hip", "pg_fused.hip", "pg_fused1.hip", "pg_fused_carry.hip", "pg_fused_mma.hip", "pg_qgemm.hip", "pg_qgemv_mma.hip", "pg_encode.hip"]
+HIP_SOURCES = ["pg_kernels.hip", "pg_fused.hip", "pg_fused1.hip", "pg_fused1_r23.hip", "pg_fused_carry.hip", "pg_fused_mma.hip", "pg_qgemm.hip", "pg_qgemv_mma.hip", "pg_encode.hip"]
 
 
 def _hipcc() -> str:

@@ -63,6 +63,15 @@ int pg_codebook_table(int8_t* out) {
     return PG_OK;
 }
 
+int pg_codebook_table_ex(uint32_t flags, int8_t* out) {
+    pg::clear_error();
+    if (flags & ~PG_FLAG_RATE23) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    PG_TRY(check_ptr(out, 1, "out"));
+    if (flags & PG_FLAG_RATE23) pg::build_codebook_r23(out);
+    else pg::build_codebook(out);
+    return PG_OK;
+}
+
 int pg_encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
                   uint16_t* scales, int n_threads) {
     pg::clear_error();
@@ -141,13 +150,15 @@ int pg_decode_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
 int pg_decode_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const int8_t* table,
                     uint32_t flags, float* w_rot, pg_stream_t stream) {
     pg::clear_error();
-    if (flags & ~PG_FLAG_CARRY_STATE) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if (flags & ~(uint32_t)(PG_FLAG_CARRY_STATE | PG_FLAG_RATE23))
+        return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     PG_TRY(check_nk(n, k));
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 2, "scales"));
     PG_TRY(check_ptr(table, 16, "table"));
     PG_TRY(check_ptr(w_rot, 16, "w_rot"));
-    return pg::launch_decode_table(codes, scales, n, k, table, (flags & PG_FLAG_CARRY_STATE) != 0, w_rot, stream);
+    return pg::launch_decode_table(codes, scales, n, k, table, (flags & PG_FLAG_CARRY_STATE) != 0,
+                                   (flags & PG_FLAG_RATE23) != 0, w_rot, stream);
 }
 
 int pg_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w_rot,
@@ -238,7 +249,7 @@ int pg_rot_qgemv_table(const uint8_t* codes, const uint16_t* scales, int64_t n, 
     pg::clear_error();
     PG_TRY(check_nk(n, k));
     PG_TRY(check_dtype(x_dtype, "x_dtype", false, false));
-    if (flags & ~(uint32_t)(PG_FLAG_RMSNORM | PG_FLAG_CARRY_STATE))
+    if (flags & ~(uint32_t)(PG_FLAG_RMSNORM | PG_FLAG_CARRY_STATE | PG_FLAG_RATE23))
         return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     PG_TRY(check_ptr(codes, 16, "codes"));
     PG_TRY(check_ptr(scales, 4, "scales"));

@@ -26,6 +26,11 @@ struct Fused1Shape {
 // with at most umax rotation rounds (and the codebook table in LDS if asked)
 int fused1_shape(int64_t n, int64_t k, int umax, bool table, Fused1Shape* out);
 
+// the rate-2/3 table instances (pg_fused1_r23.hip, compiled on their own)
+int launch_table_r23(const Fused1Shape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                     const void* x, int x_dt, const uint8_t* sign_bits, const uint32_t* table, uint32_t flags,
+                     float* y, hipStream_t st);
+
 namespace {
 
 constexpr int F1_UMAX = 1;       // rotation rounds per wave of the closed-form stage: k <= 4096 with 8 waves
@@ -61,7 +66,9 @@ __device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t o, int lane) {
 // quarter (mh fixed) sit in one quad, whose maximum and sum of q take two
 // DPP steps.
 //
-// TAB = 1, the table-driven codebook: the digits are balanced (q = 256 hi +
+// TAB = 1, the table-driven codebook (TAB = 2: the same on the rate-2/3
+// trellis, whose state is the previous byte's two branch bits and bit 0 of
+// the byte before): the digits are balanced (q = 256 hi +
 // lo with both signed bytes, hi = (q + 128) >> 8) and stored group-major
 // (one dword holds the four weights of one group, as a table point does),
 // after a 4 x 4 byte transpose across the quad.  A group read in state s as
@@ -304,12 +311,20 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
                     else
                         prev = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb[j].w, 0x111, 0xf, 0xf, true) & left_mask;
                     const uint32_t w = w4[m];
-                    // state of byte b: branch bits of bytes b-1, b-2, b-3 at its bits 0, 1, 2;
-                    // with only the branch bits kept, the three shifted copies
-                    // land on disjoint bits and need no masks
-                    const uint32_t uw = w & 0x01010101u, up = prev & 0x01010101u;
-                    const uint32_t st = __builtin_amdgcn_alignbit(uw, up, 24) | __builtin_amdgcn_alignbit(uw, up, 15) |
-                                        __builtin_amdgcn_alignbit(uw, up, 6);
+                    uint32_t st;
+                    if constexpr (TAB == 1) {
+                        // state of byte b: branch bits of bytes b-1, b-2, b-3 at its bits 0, 1, 2;
+                        // with only the branch bits kept, the three shifted copies
+                        // land on disjoint bits and need no masks
+                        const uint32_t uw = w & 0x01010101u, up = prev & 0x01010101u;
+                        st = __builtin_amdgcn_alignbit(uw, up, 24) | __builtin_amdgcn_alignbit(uw, up, 15) |
+                             __builtin_amdgcn_alignbit(uw, up, 6);
+                    } else {
+                        // rate 2/3: byte b-1's two branch bits at bits 0, 1, bit 0 of byte b-2 at bit 2
+                        const uint32_t w2 = w & 0x03030303u, p2 = prev & 0x03030303u;
+                        const uint32_t w1 = w & 0x01010101u, p1 = prev & 0x01010101u;
+                        st = __builtin_amdgcn_alignbit(w2, p2, 24) | __builtin_amdgcn_alignbit(w1, p1, 14);
+                    }
                     int h = hi[j], l = lo[j];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {

@@ -48,6 +48,7 @@ int launch_rot_qgemv1_table(const uint8_t* codes, const uint16_t* scales, int64_
     const int rc = fused1_shape(n, k, F1T_UMAX, true, &S);
     if (rc != PG_OK) return rc;
     const uint32_t* t = reinterpret_cast<const uint32_t*>(table);
+    if (flags & PG_FLAG_RATE23) return launch_table_r23(S, codes, scales, n, k, x, x_dt, sign_bits, t, flags, y, st);
     if (S.U <= 1) {
         if (x_dt == PG_F32) return launch_fused1_rs<PG_F32, 1, 1>(S, codes, scales, n, k, x, sign_bits, t, flags, y, st);
         return launch_fused1_rs<PG_F16, 1, 1>(S, codes, scales, n, k, x, sign_bits, t, flags, y, st);

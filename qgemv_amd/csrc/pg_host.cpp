@@ -50,6 +50,25 @@ void group_levels(int s, int c, int out[4]) {
     }
 }
 
+// level_j of byte c read in state s, rate-2/3 trellis (include/pingala.h):
+// z0 = bit 0 of s, z1 = u0 ^ bit 1 of s, z2 = u1 ^ bit 2 of s; b0, b2 from
+// bits 2, 3, b1 = b0 ^ z2, b3 = b2 ^ z1 ^ z2; e from bits 4..7
+void group_levels_r23(int s, int c, int out[4]) {
+    const int z0 = s & 1, z1 = (c & 1) ^ ((s >> 1) & 1), z2 = ((c >> 1) & 1) ^ ((s >> 2) & 1);
+    const int b0 = (c >> 2) & 1, b2 = (c >> 3) & 1;
+    const int b[4] = {b0, b0 ^ z2, b2, b2 ^ z1 ^ z2};
+    for (int j = 0; j < 4; ++j) out[j] = 4 * (2 * ((c >> (4 + j)) & 1) + b[j]) + 2 * z0 - 7;
+}
+
+void build_codebook_r23(int8_t* out /* [8][256][4] */) {
+    for (int s = 0; s < 8; ++s)
+        for (int c = 0; c < 256; ++c) {
+            int lv[4];
+            group_levels_r23(s, c, lv);
+            for (int j = 0; j < 4; ++j) out[(s * 256 + c) * 4 + j] = (int8_t)lv[j];
+        }
+}
+
 void build_codebook(int8_t* out /* [8][256][4] */) {
     for (int s = 0; s < 8; ++s)
         for (int c = 0; c < 256; ++c) {

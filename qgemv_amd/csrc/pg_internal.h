@@ -23,6 +23,7 @@ inline size_t q16_row_bytes(int64_t k) {
 // format helpers (pg_host.cpp)
 void group_levels(int s, int c, int out[4]);
 void build_codebook(int8_t* out /* [8][256][4] */);
+void build_codebook_r23(int8_t* out /* [8][256][4] */);
 uint16_t double_to_half_rne(double v);
 double half_to_double(uint16_t h);
 int encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
@@ -39,7 +40,7 @@ int encode_ref_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bi
 int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, float* w,
                   bool carry, pg_stream_t s);
 int launch_decode_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const int8_t* table,
-                        bool carry, float* w, pg_stream_t s);
+                        bool carry, bool rate23, float* w, pg_stream_t s);
 int launch_fwht(const void* x, int in_dt, int64_t ldx, void* y, int out_dt, const uint8_t* sign_bits,
                 int64_t rows, int64_t k, uint32_t flags, pg_stream_t s);
 int launch_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,

@@ -41,13 +41,14 @@ __global__ void k_decode(const uint8_t* __restrict__ codes, const uint16_t* __re
 
 // Decode through a codebook table T[s][byte] (four int8 levels per entry):
 // the workgroup stages the 8 KB table in LDS, then each thread decodes
-// groups as k_decode does, one table lookup per group.
+// groups as k_decode does, one table lookup per group; the state follows
+// P8F v1's trellis or the rate-2/3 one.
 constexpr int DT_GROUPS = 16;                 // groups per thread
 
 __global__ __launch_bounds__(256) void k_decode_table(const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales, int64_t total_groups,
-                                                      int kg, int carry, const uint4* __restrict__ table,
-                                                      float* __restrict__ w) {
+                                                      int kg, int carry, int rate23,
+                                                      const uint4* __restrict__ table, float* __restrict__ w) {
     __shared__ uint4 tab[512];
     tab[threadIdx.x] = table[threadIdx.x];
     tab[threadIdx.x + 256] = table[threadIdx.x + 256];
@@ -62,10 +63,14 @@ __global__ __launch_bounds__(256) void k_decode_table(const uint8_t* __restrict_
         const int tb = carry ? t : (t & 31);
         const uint8_t* rp = codes + row * kg;
         const uint32_t c = rp[t];
-        const uint32_t u1 = tb >= 1 ? (rp[t - 1] & 1u) : 0u;
-        const uint32_t u2 = tb >= 2 ? (rp[t - 2] & 1u) : 0u;
-        const uint32_t u3 = tb >= 3 ? (rp[t - 3] & 1u) : 0u;
-        const uint32_t pt = t32[((u1 | (u2 << 1) | (u3 << 2)) << 8) | c];
+        uint32_t st;
+        if (rate23) {                             // previous byte's two branch bits, u0 of the one before
+            st = (tb >= 1 ? (rp[t - 1] & 3u) : 0u) | (tb >= 2 ? (rp[t - 2] & 1u) << 2 : 0u);
+        } else {                                  // the three previous branch bits
+            st = (tb >= 1 ? (rp[t - 1] & 1u) : 0u) | (tb >= 2 ? (rp[t - 2] & 1u) << 1 : 0u) |
+                 (tb >= 3 ? (rp[t - 3] & 1u) << 2 : 0u);
+        }
+        const uint32_t pt = t32[(st << 8) | c];
         const float s = h2f(scales[row * (kg / 32) + (t >> 5)]);
         float4 o;
         o.x = s * (float)(int8_t)(pt & 0xffu);
@@ -563,12 +568,12 @@ int launch_decode(const uint8_t* codes, const uint16_t* scales, int64_t n, int64
 }
 
 int launch_decode_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k, const int8_t* table,
-                        bool carry, float* w, pg_stream_t s) {
+                        bool carry, bool rate23, float* w, pg_stream_t s) {
     const int64_t total = n * (k / 4);
     const int64_t blocks = (total + 256 * DT_GROUPS - 1) / (256 * DT_GROUPS);
     if (blocks > 0x7fffffff) return fail(PG_ERR_UNSUPPORTED, "pg_decode_table: too many groups");
     hipLaunchKernelGGL(k_decode_table, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)s, codes, scales, total,
-                       (int)(k / 4), carry ? 1 : 0, reinterpret_cast<const uint4*>(table), w);
+                       (int)(k / 4), carry ? 1 : 0, rate23 ? 1 : 0, reinterpret_cast<const uint4*>(table), w);
     return hip_check(hipGetLastError(), "pg_decode_table launch");
 }
 

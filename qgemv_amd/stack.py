@@ -27,17 +27,21 @@ ORDER = ("qkv", "o", "gu", "down")
 
 class Stack:
     def __init__(self, shapes, layers: int, batch: int = 1, device: str = "cuda", x_dtype: int = L.PG_Q16,
-                 fused: bool = True, carry: bool = False, split_above: int | None = None, table=None):
+                 fused: bool = True, carry: bool = False, split_above: int | None = None, table=None,
+                 rate23: bool = False):
         import torch
         if table is not None and (not fused or batch != 1 or split_above is not None):
             raise ValueError("a codebook table runs on the fused batch-1 path only")
-        # device int8 [8][256][4] codebook, or None for P8F v1's closed form
+        # device int8 [8][256][4] codebook, or None for P8F v1's closed form;
+        # rate23: the codes follow the rate-2/3 trellis (read through the table)
+        if rate23 and table is None:
+            raise ValueError("the rate-2/3 trellis is read through a codebook table")
         self.table = table
         if carry and not fused:
             raise ValueError("carried-state codes run on the fused path only")
         # random bytes are valid paths of both the per-block and the
         # carried-state trellis; carry selects how the stages read them
-        self.cflag = L.PG_FLAG_CARRY_STATE if carry else 0
+        self.cflag = (L.PG_FLAG_CARRY_STATE if carry else 0) | (L.PG_FLAG_RATE23 if rate23 else 0)
         # fused path: stages with k above this run as rotation + product
         # (pg_fwht_rotate_ex, pg_qgemv) instead of one pg_rot_qgemv
         if split_above is not None and carry:

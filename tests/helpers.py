@@ -65,7 +65,7 @@ def encoded_qwen(name: str):
     return _cached(f"qwen_{name}", run)
 
 
-def oracle_chain(codes, scales, signs, shapes, h0, layers, carry=False, table=None):
+def oracle_chain(codes, scales, signs, shapes, h0, layers, carry=False, table=None, rate23=False):
     """The stack driver's chain (qgemv_amd.stack) written with the oracle's
     fp64 functions: rotate, RMS-normalise with fp16 rounding, product
     (carry: codes of the carried-state variant; table: levels read through
@@ -86,7 +86,7 @@ def oracle_chain(codes, scales, signs, shapes, h0, layers, carry=False, table=No
             if table is None:
                 out[site] = p8f.gemv_ref(codes[layer][site], scales[layer][site], xr, carry)
             else:
-                out[site] = p8f.gemv_table_ref(codes[layer][site], scales[layer][site], table, xr, carry)
+                out[site] = p8f.gemv_table_ref(codes[layer][site], scales[layer][site], table, xr, carry, rate23)
     return out["down"]
 
 

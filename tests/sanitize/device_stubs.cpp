@@ -12,7 +12,8 @@ int no_device(const char* what) { return fail(PG_ERR_UNSUPPORTED, "%s: no device
 int launch_decode(const uint8_t*, const uint16_t*, int64_t, int64_t, float*, bool, pg_stream_t) {
     return no_device("pg_decode");
 }
-int launch_decode_table(const uint8_t*, const uint16_t*, int64_t, int64_t, const int8_t*, bool, float*, pg_stream_t) {
+int launch_decode_table(const uint8_t*, const uint16_t*, int64_t, int64_t, const int8_t*, bool, bool, float*,
+                        pg_stream_t) {
     return no_device("pg_decode_table");
 }
 int launch_rot_qgemv_table(const uint8_t*, const uint16_t*, int64_t, int64_t, const void*, int, const uint8_t*,

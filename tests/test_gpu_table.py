@@ -49,20 +49,28 @@ def _stage_v1(codes, scales, k, x, x_dt, sb, flags):
 
 def _tables():
     return {"v1": (q.pg_codebook_table(), p8f.codebook_table()),
+            "r23": (q.pg_codebook_table_ex(q.PG_FLAG_RATE23), p8f.codebook_table_r23()),
             "uniform": (synth.random_codebook_table(21, "uniform"),) * 2,
             "gauss": (synth.random_codebook_table(22, "gauss"),) * 2}
 
 
-@pytest.mark.parametrize("tname", ["v1", "uniform", "gauss"])
+# table and trellis: each table read on P8F v1's trellis, the rate-2/3
+# variant's own table on its trellis, and a random table on the rate-2/3
+# trellis
+_CASES = [("v1", False), ("uniform", False), ("gauss", False), ("r23", True), ("gauss", True)]
+
+
+@pytest.mark.parametrize("tname,r23", _CASES)
 @pytest.mark.parametrize("carry", [False, True])
 @pytest.mark.parametrize("n,k", [(37, 640), (300, 4096), (3, 16384)])
-def test_decode_table_bit_exact(n, k, carry, tname):
+def test_decode_table_bit_exact(n, k, carry, tname, r23):
     gpu_t, ora_t = _tables()[tname]
     rng = np.random.default_rng(n + k)
     codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
     scales = synth.random_scale_bits(n, k, n)
-    got = _decode_table(codes, scales, k, gpu_t, q.PG_FLAG_CARRY_STATE if carry else 0)
-    want = p8f.decode_weights_table(codes, scales, ora_t, carry).astype(np.float32)
+    fl = (q.PG_FLAG_CARRY_STATE if carry else 0) | (q.PG_FLAG_RATE23 if r23 else 0)
+    got = _decode_table(codes, scales, k, gpu_t, fl)
+    want = p8f.decode_weights_table(codes, scales, ora_t, carry, r23).astype(np.float32)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
@@ -95,20 +103,20 @@ def test_stage_with_v1_table_is_bitwise_the_closed_form_stage(n, k, x_dt):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("tname", ["v1", "uniform", "gauss"])
+@pytest.mark.parametrize("tname,r23", _CASES)
 @pytest.mark.parametrize("carry", [False, True])
 @pytest.mark.parametrize("n,k", [(33, 128), (100, 640), (512, 2560), (64, 9728), (300, 4096), (40, 16384),
                                  (2000, 2560), (1001, 1152)])
-def test_stage_table_matches_oracle(n, k, carry, tname):
+def test_stage_table_matches_oracle(n, k, carry, tname, r23):
     gpu_t, ora_t = _tables()[tname]
     rng = np.random.default_rng(n + 3 * k + carry)
     codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
     scales = synth.random_scale_bits(n, k, n)
     x = (rng.standard_normal((1, k)) * 7.0).astype(np.float32)
     sb = rng.integers(0, 256, k // 8, dtype=np.uint8)
-    fl = q.PG_FLAG_RMSNORM | (q.PG_FLAG_CARRY_STATE if carry else 0)
+    fl = q.PG_FLAG_RMSNORM | (q.PG_FLAG_CARRY_STATE if carry else 0) | (q.PG_FLAG_RATE23 if r23 else 0)
     y = _stage_table(codes, scales, k, x, q.PG_F32, sb, gpu_t, fl)
-    ref = p8f.gemv_table_ref(codes, scales, ora_t, p8f.rotate(p8f.rmsnorm16(x.astype(np.float64)), sb), carry)
+    ref = p8f.gemv_table_ref(codes, scales, ora_t, p8f.rotate(p8f.rmsnorm16(x.astype(np.float64)), sb), carry, r23)
     assert np.max(rel_err_rows(y, ref)) <= TOL
     y2 = _stage_table(codes, scales, k, x, q.PG_F32, sb, gpu_t, fl)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
@@ -142,19 +150,44 @@ def test_stage_table_zero_input():
                                q.PG_FLAG_RMSNORM) == 0.0)
 
 
-@pytest.mark.parametrize("shapes_fn,carry", [(synth.qwen3_4b_shapes, False), (synth.llama31_8b_shapes, True)])
-def test_table_stack_chain_matches_oracle(shapes_fn, carry):
-    """Two layers of the stack with every launch group through a
-    rounded-Gaussian table (down at k = 9728 / 14336 included), against the
+@pytest.mark.parametrize("shapes_fn,carry,r23", [(synth.qwen3_4b_shapes, False, False),
+                                               (synth.llama31_8b_shapes, True, False),
+                                               (synth.qwen3_4b_shapes, False, True)])
+def test_table_stack_chain_matches_oracle(shapes_fn, carry, r23):
+    """Two layers of the stack with every launch group through a table (down
+    at k = 9728 / 14336 included): a rounded-Gaussian one on P8F v1's
+    trellis, or the rate-2/3 variant's own on its trellis; against the
     oracle's chain with the same table; replays bitwise repeatable."""
     import torch
-    t = synth.random_codebook_table(24, "gauss")
+    if r23:
+        t, t_or = q.pg_codebook_table_ex(q.PG_FLAG_RATE23), p8f.codebook_table_r23()
+    else:
+        t = t_or = synth.random_codebook_table(24, "gauss")
     shapes = shapes_fn()
-    st = Stack(shapes, 2, fused=True, carry=carry, table=dev(t))
+    st = Stack(shapes, 2, fused=True, carry=carry, table=dev(t), rate23=r23)
     got = host(st.token()).copy()
     torch.cuda.synchronize()
     codes, scales, signs = zip(*[st.host_arrays(l) for l in range(2)])
     ref = oracle_chain(list(codes), list(scales), list(signs), shapes, host(st.h0).astype(np.float64), 2,
-                       carry=carry, table=t)
+                       carry=carry, table=t_or, rate23=r23)
     assert rel_err(got, ref) <= TOL
     assert np.array_equal(host(st.token()).view(np.uint32), got.view(np.uint32))
+
+
+def test_rate23_stage_and_decode_agree():
+    """The rate-2/3 variant's own table: the fused stage's product equals the
+    product of the GPU's decoded weights with the oracle's rotated input, to
+    the stage's tolerance (two GPU paths through the same trellis)."""
+    import torch
+    n, k = 257, 1536
+    rng = np.random.default_rng(31)
+    codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
+    scales = synth.random_scale_bits(n, k, 32)
+    x = synth.activations_fp16(1, k, seed=33)
+    sb = rng.integers(0, 256, k // 8, dtype=np.uint8)
+    t = q.pg_codebook_table_ex(q.PG_FLAG_RATE23)
+    y = _stage_table(codes, scales, k, x, q.PG_F16, sb, t, q.PG_FLAG_RATE23)
+    w = _decode_table(codes, scales, k, t, q.PG_FLAG_RATE23).astype(np.float64)
+    ref = w @ p8f.rotate(x.astype(np.float64), sb)[0]
+    assert np.max(rel_err_rows(y, ref[None, :])) <= TOL
+    torch.cuda.synchronize()

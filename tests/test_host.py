@@ -41,6 +41,16 @@ def test_codebook_table_matches_oracle():
     assert np.array_equal(q.pg_codebook_table(), p8f.codebook_table())
 
 
+def test_codebook_tables_by_format_match_oracle():
+    """pg_codebook_table_ex: 0 is P8F v1's table, PG_FLAG_RATE23 the rate-2/3
+    variant's, each equal to the oracle's table of that format."""
+    assert np.array_equal(q.pg_codebook_table_ex(0), p8f.codebook_table())
+    assert np.array_equal(q.pg_codebook_table_ex(q.PG_FLAG_RATE23), p8f.codebook_table_r23())
+    with pytest.raises(q.PgError) as ei:
+        q.pg_codebook_table_ex(q.PG_FLAG_CARRY_STATE)
+    assert ei.value.code == q._lib.PG_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("call", [
     lambda: q.pg_encode(1 << 20, 8, 200, 1 << 20, 1 << 20, 1 << 20, stream=0),                # k % 128
     lambda: q.pg_encode(1 << 20, 0, 256, 1 << 20, 1 << 20, 1 << 20, stream=0),                # n < 1
@@ -89,10 +99,12 @@ def test_codebook_table_matches_oracle():
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, (1 << 22) + 8, 0, 256, 1 << 20, 1, 1, 1 << 24, stream=0),
     lambda: q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 256, (1 << 20) + 2, 1, 1, 1 << 24, stream=0),
     lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 1, 1 << 24, stream=0),             # flags
+    lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 32, 1 << 24, stream=0),            # flags
     lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 256, (1 << 22) + 4, 0, 1 << 24, stream=0),       # table align
     lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 200, 1 << 22, 0, 1 << 24, stream=0),             # k
     lambda: q.pg_decode_table(1 << 20, 1 << 20, 8, 256, 0, 0, 1 << 24, stream=0),                   # null table
     lambda: q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 1 << 20, 1 << 18, 4, 1 << 24, stream=0),  # flags
+    lambda: q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 1 << 20, 1 << 18, 32, 1 << 24, stream=0),
     lambda: q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 2, 1 << 20, 1 << 18, 1, 1 << 24, stream=0),  # dtype
     lambda: q.pg_rot_qgemv_table(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 1 << 20, (1 << 18) + 8, 1, 1 << 24,
                                  stream=0),                                                            # table align
