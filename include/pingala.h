@@ -396,7 +396,9 @@ int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, in
 
 /* pg_qgemm_ex with its kernel and split plan given, for tests and tuning:
  *   kernel  0: the pipelined 256 x 128-tile kernel (what pg_qgemm_ex runs);
- *           1: the one-buffer 128 x 128-tile kernel (never splits)
+ *           1: the one-buffer 128 x 128-tile kernel (never splits);
+ *           2: the pipelined tile with separate producer waves (copies and
+ *              decode) and consumer waves (matrix cores); same plans
  *   splits  0: the library's plan; S >= 1: tiles first_split .. split S ways
  *           (tiles before it whole), S capped by the 128-blocks of k, by 8
  *           and by the workspace

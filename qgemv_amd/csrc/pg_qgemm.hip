@@ -368,6 +368,233 @@ __global__ __launch_bounds__(512) void k_qgemm_v2(const uint8_t* __restrict__ co
         }
 }
 
+// Warp-specialised prompt product: the tile, buffers, decode and split-K
+// plan of k_qgemm_v2, with the work split by role.  Waves 0..7 (consumers)
+// only read operands from LDS, run the matrix cores and apply the per-block
+// scales; waves 8..11 (producers) issue the X copies of step s + 2 and the
+// code loads, and decode the levels of step s + 1 (two code dwords per
+// thread).  One barrier per step, so between barriers the consumers' matrix
+// work on step s runs beside the producers' copies and decode on the other
+// waves of the same SIMDs.  The producers wait for their own copies (vmcnt)
+// before the barrier; the consumers issue no copies, so none of their LDS
+// reads waits for one.
+__global__ __launch_bounds__(768) void k_qgemm_v3(const uint8_t* __restrict__ codes,
+                                                  const uint16_t* __restrict__ scales, int n, int k,
+                                                  const uint16_t* __restrict__ x, int m,
+                                                  float* __restrict__ y, int tiles_n, int remap, int tiles,
+                                                  int t_full, int splits, float* __restrict__ ws) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs0[Q2_XBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t xs1[Q2_XBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t xs2[Q2_XBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ws0[Q2_WBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ws1[Q2_WBYTES];
+    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(m), "s"(y), "s"(tiles_n), "s"(remap),
+                 "s"(tiles), "s"(t_full), "s"(splits), "s"(ws));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    int t, split = 0, nsplit = 1;
+    const int nrem = tiles - t_full;
+    if ((int)blockIdx.x < t_full) {
+        t = blockIdx.x;
+        if (remap & 1) t = (t & 7) * (t_full >> 3) + (t >> 3);
+    } else {
+        int i = blockIdx.x - t_full;
+        const int cnt = gridDim.x - t_full;
+        if (remap & 2) i = (i & 7) * (cnt >> 3) + (i >> 3);
+        split = i / nrem;
+        t = t_full + (i - split * nrem);
+        nsplit = splits;
+    }
+    const int n0 = (t % tiles_n) * Q2_BN, m0 = (t / tiles_n) * Q2_BM;
+    const int kg = k >> 2, nbk = k >> 7;
+    const int st0 = 2 * (int)((int64_t)split * nbk / nsplit);
+    const int st_end = 2 * (int)((int64_t)(split + 1) * nbk / nsplit);
+
+    if (wave >= 8) {
+        // ---------------------------------------------------------- producers
+        const int pw = wave - 8, pt = tid - 512;
+        const uint16_t* xtile = x + (int64_t)m0 * k;
+        int xoff[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = (8 * pw + i) * 64 + lane;
+            const int r = j >> 3, c = q2_chunk(r, j & 7);
+            const int gr = m0 + r < m ? r : m - 1 - m0;
+            xoff[i] = gr * k + 8 * c;
+        }
+        auto copy_x = [&](int st, uint8_t* dst) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                __builtin_amdgcn_global_load_lds(xtile + xoff[i] + st * Q2_BK, dst + (8 * pw + i) * 1024, 16, 0, 0);
+        };
+        // code dwords: rows pt / 4 and pt / 4 + 64 of the tile, dword pt % 4 of the step
+        const int nr = pt >> 2, dm = pt & 3;
+        const int wrow0 = n0 + nr < n ? n0 + nr : n - 1;
+        const int wrow1 = n0 + nr + 64 < n ? n0 + nr + 64 : n - 1;
+        const uint32_t* csrc0 = reinterpret_cast<const uint32_t*>(codes + (int64_t)wrow0 * kg) + dm;
+        const uint32_t* csrc1 = reinterpret_cast<const uint32_t*>(codes + (int64_t)wrow1 * kg) + dm;
+        uint32_t dprev[2] = {0u, 0u};
+        auto decode = [&](bool second_half, uint32_t d, int h, uint8_t* wdst) {
+            const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0x111, 0xf, 0xf, true);          // lane - 1
+            const uint32_t back = (uint32_t)__builtin_amdgcn_mov_dpp((int)dprev[h], 0x103, 0xf, 0xf, true);   // lane + 3
+            const uint32_t dp = dm != 0 ? left : (second_half ? back : 0u);
+            dprev[h] = d;
+            uint32_t P[4];
+            planes_of(d, dp, P);
+            const uint32_t t0 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
+            const uint32_t u0 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
+            const uint32_t t1 = __builtin_amdgcn_perm(P[1], P[0], 0x07030602u);
+            const uint32_t u1 = __builtin_amdgcn_perm(P[3], P[2], 0x07030602u);
+            const uint32_t Q[4] = {__builtin_amdgcn_perm(u0, t0, 0x05040100u), __builtin_amdgcn_perm(u0, t0, 0x07060302u),
+                                   __builtin_amdgcn_perm(u1, t1, 0x05040100u), __builtin_amdgcn_perm(u1, t1, 0x07060302u)};
+            uint32_t o[8];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t lo = __builtin_amdgcn_perm(0xE0A04080u, 0x8040A0E0u, Q[g]);
+                const uint32_t hi = __builtin_amdgcn_perm(0x4040403Fu, 0xBFC0C0C0u, Q[g]);
+                o[2 * g] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+                o[2 * g + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+            }
+            const int rr = nr + 64 * h;
+            uint8_t* row = wdst + rr * 128;
+            *reinterpret_cast<uint4*>(row + 16 * q2_chunk(rr, 2 * dm)) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(row + 16 * q2_chunk(rr, 2 * dm + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+        };
+        // prologue: codes and X of steps st0 and st0 + 1, levels of step st0
+        const uint32_t a0 = csrc0[4 * st0], b0 = csrc1[4 * st0];
+        copy_x(st0, xs0);
+        const int s1 = st0 + 1;
+        uint32_t a1 = csrc0[4 * s1], b1 = csrc1[4 * s1];
+        copy_x(s1, xs1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        decode(false, a0, 0, ws0);
+        decode(false, b0, 1, ws0);
+        lds_barrier();
+        auto body = [&](auto J, int st) {
+            constexpr int j6 = decltype(J)::value;
+            uint8_t* xnext2 = j6 % 3 == 0 ? xs2 : j6 % 3 == 1 ? xs0 : xs1;
+            uint8_t* wnext = j6 % 2 == 0 ? ws1 : ws0;
+            constexpr bool half2 = (j6 & 1) != 0;
+            const int sn = st + 2 < st_end ? st + 2 : st_end - 1;
+            const uint32_t a2 = csrc0[4 * sn], b2 = csrc1[4 * sn];
+            copy_x(sn, xnext2);
+            // all but this step's 10 requests have landed: the codes and X copies of step st + 1
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
+            if (st + 1 < st_end) {
+                decode(!half2, a1, 0, wnext);
+                decode(!half2, b1, 1, wnext);
+            }
+            a1 = a2;
+            b1 = b2;
+            lds_barrier();
+        };
+        for (int st = st0; st < st_end; st += 6) {
+            body(std::integral_constant<int, 0>(), st);
+            body(std::integral_constant<int, 1>(), st + 1);
+            if (st + 2 >= st_end) break;
+            body(std::integral_constant<int, 2>(), st + 2);
+            body(std::integral_constant<int, 3>(), st + 3);
+            if (st + 4 >= st_end) break;
+            body(std::integral_constant<int, 4>(), st + 4);
+            body(std::integral_constant<int, 5>(), st + 5);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));               // the repeated copies past the end
+        return;
+    }
+
+    // -------------------------------------------------------------- consumers
+    const int wm = wave >> 1, wn = wave & 1;
+    float* __restrict__ out = y;
+    int64_t ld = n;
+    int rb = 0, cb = 0;
+    if (split > 0) {
+        out = ws + ((int64_t)(split - 1) * nrem + (t - t_full)) * (Q2_BM * Q2_BN);
+        ld = Q2_BN;
+        rb = m0;
+        cb = n0;
+    }
+    f32x16 acc[2][2], bacc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { acc[i][j][r] = 0.0f; bacc[i][j][r] = 0.0f; }
+    int scol[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+        scol[j] = col < n ? col : n - 1;
+    }
+    uint32_t sc_cur[2] = {0, 0};
+    lds_barrier();                                              // the producers' prologue
+    auto body = [&](auto J, int st) {
+        constexpr int j6 = decltype(J)::value;
+        uint8_t* xcur = j6 % 3 == 0 ? xs0 : j6 % 3 == 1 ? xs1 : xs2;
+        uint8_t* wcur = j6 % 2 == 0 ? ws0 : ws1;
+        constexpr bool half2 = (j6 & 1) != 0;
+        if (!half2)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sc_cur[j] = scales[(int64_t)scol[j] * nbk + (st >> 1)];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int c = 2 * kk + (lane >> 5);
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 64 * wm + 32 * i + (lane & 31);
+                a[i] = *reinterpret_cast<const bf16x8*>(xcur + r * 128 + 16 * q2_chunk(r, c));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = 64 * wn + 32 * j + (lane & 31);
+                b[j] = *reinterpret_cast<const bf16x8*>(wcur + r * 128 + 16 * q2_chunk(r, c));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    bacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], bacc[i][j], 0, 0, 0);
+        }
+        if (half2) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float sc = h2f((uint16_t)sc_cur[j]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        acc[i][j][r] += sc * bacc[i][j][r];
+                        bacc[i][j][r] = 0.0f;
+                    }
+            }
+        }
+        lds_barrier();
+    };
+    for (int st = st0; st < st_end; st += 6) {
+        body(std::integral_constant<int, 0>(), st);
+        body(std::integral_constant<int, 1>(), st + 1);
+        if (st + 2 >= st_end) break;
+        body(std::integral_constant<int, 2>(), st + 2);
+        body(std::integral_constant<int, 3>(), st + 3);
+        if (st + 4 >= st_end) break;
+        body(std::integral_constant<int, 4>(), st + 4);
+        body(std::integral_constant<int, 5>(), st + 5);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+            if (col >= n) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row < m) out[(int64_t)(row - rb) * ld + (col - cb)] = acc[i][j][r];
+            }
+        }
+}
+
 // y += part 0 + part 1 + ... over the split tiles: thread q takes values
 // 4 (q % 8192) .. + 3 of tile block q / 8192 (tile t_full + q / 8192, 256 x
 // 128 values, row-major) from every part in part order; values outside y
@@ -481,9 +708,14 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
         const int64_t nrem = tiles - p.t_full, grid = p.t_full + nrem * p.splits;
         if (grid > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
         const int remap = (p.t_full % 8 == 0 ? 1 : 0) | ((nrem * p.splits) % 8 == 0 ? 2 : 0);
-        hipLaunchKernelGGL(k_qgemm_v2, dim3((unsigned)grid), dim3(512), 0, (hipStream_t)s, codes, scales,
-                           (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)tiles, (int)p.t_full, p.splits,
-                           static_cast<float*>(workspace));
+        if (kernel == 2)
+            hipLaunchKernelGGL(k_qgemm_v3, dim3((unsigned)grid), dim3(768), 0, (hipStream_t)s, codes, scales,
+                               (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)tiles, (int)p.t_full, p.splits,
+                               static_cast<float*>(workspace));
+        else
+            hipLaunchKernelGGL(k_qgemm_v2, dim3((unsigned)grid), dim3(512), 0, (hipStream_t)s, codes, scales,
+                               (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)tiles, (int)p.t_full, p.splits,
+                               static_cast<float*>(workspace));
         const int rc = hip_check(hipGetLastError(), "pg_qgemm launch");
         if (rc != PG_OK || p.splits == 1) return rc;
         const int64_t blocks = nrem * (Q2_BM * Q2_BN / 4) / 256;

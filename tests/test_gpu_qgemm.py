@@ -29,12 +29,13 @@ def _qgemm(codes, scales, xb):
 _kernel = [None]
 
 
-@pytest.fixture(params=["auto", "1", "2"])
+@pytest.fixture(params=["auto", "1", "2", "3"])
 def kernel(request):
     """Which product kernel runs: pg_qgemm's own, or one selected through
     pg_qgemm_tune (1: the 128x128-tile one-buffer kernel, 2: the pipelined
-    256x128-tile kernel, which pg_qgemm runs)."""
-    _kernel[0] = {"auto": None, "1": 1, "2": 0}[request.param]
+    256x128-tile kernel, which pg_qgemm runs, 3: the same tile with producer
+    and consumer waves)."""
+    _kernel[0] = {"auto": None, "1": 1, "2": 0, "3": 2}[request.param]
     yield request.param
     _kernel[0] = None
 
@@ -90,7 +91,7 @@ def test_one_hot_column(kernel):
 
 
 # ----------------------------------------------------------------- split K
-def _qgemm_ex(codes, scales, xb, ws_bytes=None, guard=0, plan=None):
+def _qgemm_ex(codes, scales, xb, ws_bytes=None, guard=0, plan=None, kern=0):
     """pg_qgemm_ex with a workspace of ws_bytes (default: the full split)
     followed by `guard` float32 values that must stay untouched; with a plan
     "S" or "S:T", pg_qgemm_tune with that split."""
@@ -106,7 +107,7 @@ def _qgemm_ex(codes, scales, xb, ws_bytes=None, guard=0, plan=None):
         q.pg_qgemm_ex(dev(codes), dev(scales), n, k, dev(xb), m, y, ws, ws_bytes)
     else:
         sp, _, t = plan.partition(":")
-        q.pg_qgemm_tune(dev(codes), dev(scales), n, k, dev(xb), m, y, ws, ws_bytes, 0, int(sp), int(t or 0))
+        q.pg_qgemm_tune(dev(codes), dev(scales), n, k, dev(xb), m, y, ws, ws_bytes, kern, int(sp), int(t or 0))
     torch.cuda.synchronize()
     if guard:
         assert (host(ws[ws_bytes // 4:]) == 7.0).all(), "workspace written past workspace_bytes"
@@ -136,17 +137,18 @@ def test_split_k_matches_oracle(m, n, k):
 TILE_BYTES = 256 * 128 * 4
 
 
+@pytest.mark.parametrize("kern", [0, 2])
 @pytest.mark.parametrize("plan", ["2", "3", "8", "2:1", "3:5"])
 @pytest.mark.parametrize("m,n,k", [(77, 130, 1152), (256, 384, 512), (3, 1, 1024), (300, 1024, 2560),
                                    (513, 1030, 1152)])
-def test_forced_splits_ragged(m, n, k, plan):
+def test_forced_splits_ragged(m, n, k, plan, kern):
     """Split plans given to pg_qgemm_tune: S (every tile split S ways,
     capped at the number of 128-blocks) or S:T (tiles T.. split, the others
     whole), on ragged tiles and odd n (the sum kernel's scalar edge); the
     workspace past the parts stays untouched."""
     codes, scales, xb = _case(m, n, k)
     tiles = -(-n // 128) * -(-m // 256)
-    y = _qgemm_ex(codes, scales, xb, ws_bytes=7 * tiles * TILE_BYTES, guard=64, plan=plan)
+    y = _qgemm_ex(codes, scales, xb, ws_bytes=7 * tiles * TILE_BYTES, guard=64, plan=plan, kern=kern)
     ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb))
     assert np.max(rel_err_rows(y, ref)) <= TOL
 
