@@ -988,3 +988,83 @@ def proxy_loss(w_rot: np.ndarray, what: np.ndarray, h_rot: np.ndarray) -> float:
     """tr(E H~ E^T) with E = What - W~ (fp64)."""
     e = np.asarray(what, dtype=np.float64) - np.asarray(w_rot, dtype=np.float64)
     return float(np.sum((e @ h_rot) * e))
+
+
+# ------------------------------------------- encoder through a codebook table
+def viterbi_encode_table(w_rot: np.ndarray, scale_bits: np.ndarray, table: np.ndarray,
+                         rate23: bool = False) -> np.ndarray:
+    """Minimum-squared-error path per block through a codebook table, on P8F
+    v1's trellis or the rate-2/3 one.  w_rot [nb, 4G] fp64, scale_bits [nb]
+    u16, table [8][256][4] int8.  For every group, state p and byte c the
+    distortion ((d0^2 + d1^2) + d2^2) + d3^2 with d_j = w_j - s * T[p][c][j];
+    for every state and branch u (the byte's branch bits) the first byte of
+    least distortion in increasing byte order; then add-compare-select from
+    state 0, each next state's predecessors tried in increasing order with
+    strict improvement, the first best end state, traceback.  A zero scale
+    codes every group as byte 0.  On P8F v1's own table this is
+    viterbi_encode, on the rate-2/3 variant's own table viterbi_encode_r23."""
+    w = np.asarray(w_rot, dtype=np.float64)
+    nb, g = w.shape[0], w.shape[1] // 4
+    sv = fp16_bits_to_float(np.asarray(scale_bits, dtype=np.uint16))
+    t = np.asarray(table, dtype=np.int8).reshape(8, 256, 4).astype(np.float64)
+    nbr = 4 if rate23 else 2
+    umask = nbr - 1
+    by_u = [np.array([c for c in range(256) if (c & umask) == u], dtype=np.int64) for u in range(nbr)]
+    nxt = next_state_r23 if rate23 else next_state
+    out = np.zeros((nb, g), dtype=np.uint8)
+    for b in range(nb):
+        if sv[b] == 0:
+            continue
+        d = w[b].reshape(g, 1, 1, 4) - sv[b] * t[None, :, :, :]            # [g, 8, 256, 4]
+        sq = d * d
+        dist = ((sq[..., 0] + sq[..., 1]) + sq[..., 2]) + sq[..., 3]        # [g, 8, 256]
+        best_d = np.zeros((g, 8, nbr))
+        best_c = np.zeros((g, 8, nbr), dtype=np.int64)
+        for u in range(nbr):
+            sub = dist[:, :, by_u[u]]
+            i = np.argmin(sub, axis=2)                                        # first minimum
+            best_d[:, :, u] = np.take_along_axis(sub, i[..., None], axis=2)[..., 0]
+            best_c[:, :, u] = by_u[u][i]
+        metric = np.full(8, np.inf)
+        metric[0] = 0.0
+        back = np.zeros((g, 8, 2), dtype=np.int64)
+        for step in range(g):
+            new = np.full(8, np.inf)
+            for p in range(8):                                                # increasing predecessor
+                for u in range(nbr):
+                    sn = nxt(p, u)
+                    tot = metric[p] + best_d[step, p, u]
+                    if tot < new[sn]:
+                        new[sn] = tot
+                        back[step, sn] = (p, best_c[step, p, u])
+            metric = new
+        st = int(np.argmin(metric))
+        for step in range(g - 1, -1, -1):
+            out[b, step] = back[step, st, 1]
+            st = int(back[step, st, 0])
+    return out
+
+
+def block_distortion_table(w_rot: np.ndarray, codes: np.ndarray, scale_bits: np.ndarray, table: np.ndarray,
+                           rate23: bool = False) -> np.ndarray:
+    """Squared error per block of codes [nb, G] decoded through the table."""
+    w = np.asarray(w_rot, dtype=np.float64)
+    g = np.asarray(codes).shape[1]
+    pad = (-g) % GROUPS_PER_BLOCK
+    c = np.concatenate([np.asarray(codes, dtype=np.uint8), np.zeros((len(codes), pad), np.uint8)], axis=1)
+    lv = decode_levels_table(c, table, rate23=rate23).astype(np.float64)[:, :4 * g]
+    d = w - fp16_bits_to_float(np.asarray(scale_bits, dtype=np.uint16))[:, None] * lv
+    return np.sum(d * d, axis=1)
+
+
+def encode_matrix_table(w: np.ndarray, sign_bits: np.ndarray, table: np.ndarray, rate23: bool = False,
+                        c: float = SCALE_C):
+    """Offline compression through a codebook table: rotate, the usual scale
+    rule, viterbi_encode_table per block.  Returns codes u8 [N][K/4] and
+    scale bits u16 [N][K/128]."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    n, k = w.shape
+    wr = rotate(w, sign_bits).reshape(-1, BLOCK)
+    sb = block_scale_bits(wr, c)
+    codes = viterbi_encode_table(wr, sb, table, rate23)
+    return codes.reshape(n, k // 4), sb.reshape(n, k // BLOCK)

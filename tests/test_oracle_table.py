@@ -149,3 +149,93 @@ def test_uniform_table_covers_int8_range():
     assert t.min() == -128 and t.max() == 127
     g = synth.random_codebook_table(1, "gauss")
     assert g.min() >= -127 and g.max() <= 127 and len(np.unique(g)) > 60
+
+
+# ------------------------------------------------ encoder through a table
+def _brute_min(w, sb, table, rate23):
+    """Least distortion over all 65536 strings of a 2-group block."""
+    sv = float(np.array([sb], dtype=np.uint16).view(np.float16)[0])
+    t = np.asarray(table, dtype=np.float64)
+    nxt = p8f.next_state_r23 if rate23 else p8f.next_state
+    umask = 3 if rate23 else 1
+    best = np.inf
+    for c0 in range(256):
+        d0 = w[:4] - sv * t[0, c0]
+        s1 = nxt(0, c0 & umask)
+        d1 = w[None, 4:] - sv * t[s1]                       # all second bytes at once
+        tot = float(np.sum(d0 * d0)) + np.sum(d1 * d1, axis=1)
+        best = min(best, float(np.min(tot)))
+    return best
+
+
+@pytest.mark.parametrize("rate23", [False, True])
+@pytest.mark.parametrize("seed", range(3))
+def test_table_encoder_equals_exhaustive_search(rate23, seed):
+    rng = np.random.default_rng(200 + seed)
+    t = synth.random_codebook_table(30 + seed, "gauss")
+    w = rng.standard_normal(8) * 3.0
+    sb = int(np.float16(0.21 + 0.05 * seed).view(np.uint16))
+    codes = p8f.viterbi_encode_table(w[None, :], np.array([sb], np.uint16), t, rate23)
+    got = p8f.block_distortion_table(w[None, :], codes, np.array([sb], np.uint16), t, rate23)[0]
+    assert abs(got - _brute_min(w, sb, t, rate23)) <= 1e-9 * max(1.0, got)
+
+
+def test_table_encoder_on_own_tables_is_the_plain_encoders():
+    """P8F v1's table on its trellis gives viterbi_encode's codes, the
+    rate-2/3 variant's table on its trellis viterbi_encode_r23's (same tie
+    rules), including a zero-scale block."""
+    rng = np.random.default_rng(210)
+    w = rng.standard_normal((9, 128))
+    w[4] = 0.0
+    sb = p8f.block_scale_bits(w)
+    assert np.array_equal(p8f.viterbi_encode_table(w, sb, p8f.codebook_table()), p8f.viterbi_encode(w, sb))
+    assert np.array_equal(p8f.viterbi_encode_table(w, sb, p8f.codebook_table_r23(), True),
+                          p8f.viterbi_encode_r23(w, sb))
+
+
+def test_table_encoder_on_a_byte_permuted_table():
+    """Permuting the bytes (branch bits kept) permutes the code book only:
+    the least distortion is the same."""
+    pi = np.array([(c & 1) | (_bitrev7(c >> 1) << 1) for c in range(256)], dtype=np.uint8)
+    tp = p8f.codebook_table()[:, pi, :]
+    rng = np.random.default_rng(211)
+    w = rng.standard_normal((5, 128))
+    sb = p8f.block_scale_bits(w)
+    c0 = p8f.viterbi_encode(w, sb)
+    cp = p8f.viterbi_encode_table(w, sb, tp)
+    assert np.allclose(p8f.block_distortion_table(w, cp, sb, tp), p8f.block_distortion(w, c0, sb), rtol=1e-12)
+
+
+def test_nonuniform_table_encoding_lowers_gaussian_mse():
+    """Diagnostic (parity unpinned: the pages give no codebook values): on
+    Gaussian weights a table whose eight levels follow the Gaussian's shape
+    codes with less error than the uniform v1 levels at the same scale rule
+    (scales from the usual rule, so both tables see the same scales)."""
+    phi = {-7: -9, -5: -6, -3: -3, -1: -1, 1: 1, 3: 3, 5: 6, 7: 9}
+    v1 = p8f.codebook_table()
+    t = np.vectorize(lambda v: phi[int(v)])(v1).astype(np.int8)
+    rng = np.random.default_rng(212)
+    w = rng.standard_normal((24, 128))
+    sb = p8f.block_scale_bits(w, c=0.29 * 7 / 9)
+    e_t = np.mean(p8f.block_distortion_table(w, p8f.viterbi_encode_table(w, sb, t), sb, t))
+    sb1 = p8f.block_scale_bits(w)
+    e_1 = np.mean(p8f.block_distortion(w, p8f.viterbi_encode(w, sb1), sb1))
+    assert 0 < e_t < e_1            # 12.56 against 13.58 on this seed
+
+
+def test_table_encoder_tie_rules_on_the_hand_example():
+    """The hand-derived tie example (tests/golden/viterbi_tie_example.json,
+    T1: two paths of equal distortion, several equally near points) through
+    P8F v1's table: the table encoder picks the codes derived by hand, so its
+    predecessor, byte and end-state tie rules are viterbi_encode's."""
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "viterbi_tie_example.json")))["tie"]
+    w = np.array([ex["w_rot"]], dtype=np.float64)
+    sb = np.array([np.float16(ex["scale"]).view(np.uint16)], dtype=np.uint16)
+    codes = p8f.viterbi_encode_table(w, sb, p8f.codebook_table())
+    assert codes[0].tolist() == ex["codes"]
+    # T2: equally near bytes within a coset, the smaller byte wins
+    ex2 = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "viterbi_tie_example.json")))["tie_bytes"]
+    w2 = np.array([ex2["w_rot"]], dtype=np.float64)
+    sb2 = np.array([np.float16(ex2["scale"]).view(np.uint16)], dtype=np.uint16)
+    assert p8f.viterbi_encode_table(w2, sb2, p8f.codebook_table())[0].tolist() == ex2["codes"]
+    assert p8f.viterbi_encode(w2, sb2)[0].tolist() == ex2["codes"]
