@@ -211,6 +211,28 @@ int pg_encode_ref_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign
 int pg_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* hessian,
                    uint8_t* codes, uint16_t* scales, pg_stream_t stream);
 
+/* Encoders through a codebook table (the table-driven variant, landing
+ * page section "Paper"; codes are then read back with pg_decode_table /
+ * pg_rot_qgemv_table and the same table and flags).  Rotation and scale rule
+ * as pg_encode_ref; per 128-block a Viterbi search over the table: for every
+ * group, state p and byte c the distortion ((d0^2 + d1^2) + d2^2) + d3^2,
+ * d_j = w_j - s * table[p][c][j] (fp64, no fused multiply-add); per state
+ * and branch the first byte of least distortion (the branch is byte bit 0,
+ * or bits 0..1 with PG_FLAG_RATE23); add-compare-select from state 0, each
+ * next state's predecessors in increasing order with strict improvement,
+ * the first best end state; a zero scale codes every group as byte 0.  On
+ * P8F v1's own table the codes are pg_encode_ref's.
+ *   table  int8 [8][256][4]: host memory for pg_encode_ref_table, device
+ *          memory (16-byte aligned) for pg_encode_table
+ *   flags  0 or PG_FLAG_RATE23
+ * pg_encode_table is the same search on the GPU, bit-identical, one
+ * workgroup per 128-block, asynchronous on `stream`.  Other arguments as
+ * pg_encode_ref / pg_encode. */
+int pg_encode_ref_table(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const int8_t* table,
+                        uint32_t flags, uint8_t* codes, uint16_t* scales, int n_threads);
+int pg_encode_table(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const int8_t* table,
+                    uint32_t flags, uint8_t* codes, uint16_t* scales, pg_stream_t stream);
+
 /* pg_encode with format flags: 0 is pg_encode (format P8F v1);
  * PG_FLAG_CARRY_STATE codes the carried-state variant with one Viterbi
  * search per row over all of its blocks (state carried on, per-block scales

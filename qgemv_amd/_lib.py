@@ -29,7 +29,8 @@ EXPORTS = ("pg_version", "pg_footprint_bytes", "pg_q16_row_bytes", "pg_last_erro
            "pg_decode", "pg_fwht_rotate", "pg_fwht_rotate_ex", "pg_qgemv", "pg_rot_qgemv", "pg_qgemm",
            "pg_qgemm_ex", "pg_qgemm_workspace_bytes", "pg_hbm_read",
            "pg_qgemm_noalloc", "pg_qgemv_ex", "pg_qgemm_tune", "pg_decode_table", "pg_rot_qgemv_table",
-           "pg_encode_ref_ldlq", "pg_encode_ldlq", "pg_codebook_table_ex")
+           "pg_encode_ref_ldlq", "pg_encode_ldlq", "pg_codebook_table_ex",
+           "pg_encode_ref_table", "pg_encode_table")
 
 
 class PgError(RuntimeError):
@@ -72,6 +73,10 @@ def lib():
         L.pg_encode.argtypes = [vp, i64, i64, vp, vp, vp, vp]
         L.pg_encode_ref_ldlq.restype = i32
         L.pg_encode_ref_ldlq.argtypes = [vp, i64, i64, vp, vp, vp, vp, i32]
+        L.pg_encode_ref_table.restype = i32
+        L.pg_encode_ref_table.argtypes = [vp, i64, i64, vp, vp, u32, vp, vp, i32]
+        L.pg_encode_table.restype = i32
+        L.pg_encode_table.argtypes = [vp, i64, i64, vp, vp, u32, vp, vp, vp]
         L.pg_encode_ldlq.restype = i32
         L.pg_encode_ldlq.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.pg_encode_ex.restype = i32
@@ -255,6 +260,31 @@ def pg_encode_ldlq(w, n: int, k: int, sign_bits, hessian: np.ndarray, codes, sca
     _host_hessian(hessian, k)
     _check(lib().pg_encode_ldlq(_ptr(w), n, k, _ptr(sign_bits), _ptr(hessian), _ptr(codes), _ptr(scales),
                                 _stream(stream)))
+
+
+def pg_encode_ref_table(w: np.ndarray, n: int, k: int, sign_bits: np.ndarray, table: np.ndarray, flags: int,
+                        codes: np.ndarray, scales: np.ndarray, n_threads: int = 0) -> None:
+    """Host encoder through a codebook table (numpy buffers, C-contiguous):
+    table int8 [8][256][4]; flags 0 or PG_FLAG_RATE23."""
+    for a, nbytes, name in ((w, n * k * 4, "w"), (sign_bits, k // 8, "sign_bits"), (table, 8192, "table"),
+                            (codes, n * (k // 4), "codes"), (scales, n * (k // 128) * 2, "scales")):
+        if not isinstance(a, np.ndarray) or not a.flags["C_CONTIGUOUS"]:
+            raise ValueError(f"{name}: a C-contiguous numpy array is required")
+        if n > 0 and k > 0 and a.nbytes < nbytes:
+            raise ValueError(f"{name}: {a.nbytes} bytes, {nbytes} needed")
+    _check(lib().pg_encode_ref_table(_ptr(w), n, k, _ptr(sign_bits), _ptr(table), flags, _ptr(codes), _ptr(scales),
+                                     n_threads))
+
+
+def pg_encode_table(w, n: int, k: int, sign_bits, table, flags: int, codes, scales, stream=None) -> None:
+    """GPU encoder through a codebook table (device buffers as pg_encode;
+    table device int8 [8][256][4])."""
+    _need(w, max(n, 0) * max(k, 0) * 4, "w")
+    _need(sign_bits, max(k, 0) // 8, "sign_bits")
+    _need(table, TABLE_BYTES, "table")
+    _weights(codes, scales, n, k)
+    _check(lib().pg_encode_table(_ptr(w), n, k, _ptr(sign_bits), _ptr(table), flags, _ptr(codes), _ptr(scales),
+                                 _stream(stream)))
 
 
 def pg_encode(w, n: int, k: int, sign_bits, codes, scales, stream=None) -> None:

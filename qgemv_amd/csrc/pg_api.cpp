@@ -122,6 +122,32 @@ int pg_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bit
     return pg::run_encode_ldlq(w, n, k, sign_bits, hessian, codes, scales, stream);
 }
 
+int pg_encode_ref_table(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const int8_t* table,
+                        uint32_t flags, uint8_t* codes, uint16_t* scales, int n_threads) {
+    pg::clear_error();
+    if (flags & ~PG_FLAG_RATE23) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    PG_TRY(check_nk(n, k));
+    PG_TRY(check_ptr(w, 4, "w"));
+    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    PG_TRY(check_ptr(table, 1, "table"));
+    PG_TRY(check_ptr(codes, 1, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    return pg::encode_ref_table(w, n, k, sign_bits, table, (flags & PG_FLAG_RATE23) != 0, codes, scales, n_threads);
+}
+
+int pg_encode_table(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const int8_t* table,
+                    uint32_t flags, uint8_t* codes, uint16_t* scales, pg_stream_t stream) {
+    pg::clear_error();
+    if (flags & ~PG_FLAG_RATE23) return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    PG_TRY(check_nk(n, k));
+    PG_TRY(check_ptr(w, 4, "w"));
+    PG_TRY(check_ptr(sign_bits, 1, "sign_bits"));
+    PG_TRY(check_ptr(table, 16, "table"));
+    PG_TRY(check_ptr(codes, 16, "codes"));
+    PG_TRY(check_ptr(scales, 2, "scales"));
+    return pg::launch_encode_table(w, n, k, sign_bits, table, (flags & PG_FLAG_RATE23) != 0, codes, scales, stream);
+}
+
 int pg_encode_ex(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint32_t flags, uint8_t* codes,
                  uint16_t* scales, pg_stream_t stream) {
     pg::clear_error();

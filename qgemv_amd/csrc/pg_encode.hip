@@ -310,6 +310,125 @@ __global__ __launch_bounds__(128) void k_encode_ldlq(const float* __restrict__ w
     }
 }
 
+// Through a codebook table (P8F v1's trellis or the rate-2/3 one), the
+// host reference's encode_block_table step for step: one 128-thread
+// workgroup per 128-block copies the 8 KB table to LDS, rotates and scales
+// the block as k_encode does; thread i scores every byte of state p = i % 8
+// against groups i / 8 and 16 + i / 8 (first byte of least distortion per
+// branch); threads 0..7 run the add-compare-select (predecessors in
+// increasing order), thread 0 traces back.
+__global__ __launch_bounds__(128) void k_encode_table(const float* __restrict__ w, int n, int k,
+                                                      const uint8_t* __restrict__ sign_bits,
+                                                      const uint4* __restrict__ table, int r23,
+                                                      uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+#pragma clang fp contract(off)
+    __shared__ uint4 tab[512];
+    __shared__ double v[128];
+    __shared__ double bd[32][8][4];
+    __shared__ uint8_t bc[32][8][4];
+    __shared__ double metric[8];
+    __shared__ int8_t prv[32][8];
+    __shared__ uint8_t byt[32][8];
+    __shared__ uint32_t sbits;
+    const int tid = threadIdx.x;
+    const int nb = k >> 7;
+    const int row = blockIdx.x / nb, b = blockIdx.x - row * nb;
+    const int64_t kk = (int64_t)b * 128 + tid;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tab[tid + 128 * i] = table[tid + 128 * i];
+
+    double x = (double)w[(int64_t)row * k + kk];
+    if ((sign_bits[kk >> 3] >> (kk & 7)) & 1) x = -x;
+    v[tid] = x;
+    __syncthreads();
+    for (int h = 1; h < 128; h <<= 1) {
+        const int j = (tid / h) * 2 * h + (tid % h);
+        double a = 0.0, c = 0.0;
+        if (tid < 64) { a = v[j]; c = v[j + h]; }
+        __syncthreads();
+        if (tid < 64) { v[j] = a + c; v[j + h] = a - c; }
+        __syncthreads();
+    }
+    v[tid] = v[tid] * 0x1.6a09e667f3bcdp-4;
+    __syncthreads();
+    if (tid == 0) {
+        double acc = 0.0;
+        for (int i = 0; i < 128; ++i) acc = acc + v[i] * v[i];
+        const double rms = sqrt(acc / 128.0);
+        const double sc = 0.29 * rms;
+        const double val = 65504.0 < sc ? 65504.0 : sc;
+        sbits = enc_half_rne(val);
+        scales[(int64_t)row * nb + b] = (uint16_t)sbits;
+    }
+    __syncthreads();
+    const double s = enc_half_to_double((uint16_t)sbits);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + (int64_t)row * (k >> 2) + 32 * b);
+    if (s == 0.0) {                                  // a zero scale codes every group as byte 0
+        if (tid < 8) dst[tid] = 0u;
+        return;
+    }
+    const int nbr = r23 ? 4 : 2, um = nbr - 1;
+    const int8_t* T = reinterpret_cast<const int8_t*>(tab);
+    for (int h = 0; h < 2; ++h) {
+        const int t = (tid >> 3) + 16 * h, p = tid & 7;
+        const double w0 = v[4 * t], w1 = v[4 * t + 1], w2 = v[4 * t + 2], w3 = v[4 * t + 3];
+        double best[4] = {__builtin_inf(), __builtin_inf(), __builtin_inf(), __builtin_inf()};
+        int arg[4] = {0, 0, 0, 0};
+        for (int c = 0; c < 256; ++c) {
+            const int8_t* L = T + (p * 256 + c) * 4;
+            const double d0 = w0 - s * (double)L[0], d1 = w1 - s * (double)L[1];
+            const double d2 = w2 - s * (double)L[2], d3 = w3 - s * (double)L[3];
+            const double m = ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
+            const int u = c & um;
+            if (m < best[u]) { best[u] = m; arg[u] = c; }
+        }
+        for (int u = 0; u < nbr; ++u) {
+            bd[t][p][u] = best[u];
+            bc[t][p][u] = (uint8_t)arg[u];
+        }
+    }
+    if (tid < 8) metric[tid] = tid == 0 ? 0.0 : __builtin_inf();
+    __syncthreads();
+    for (int t = 0; t < 32; ++t) {
+        double nxt = __builtin_inf();
+        if (tid < 8) {
+            const int sn = tid;
+            int pv = 0, by = 0;
+            for (int p = 0; p < 8; ++p) {
+                // the branch from p into sn, if there is one
+                int u;
+                if (r23) {
+                    if ((p & 1) != (sn >> 2)) continue;
+                    u = sn & 3;
+                } else {
+                    if ((p & 3) != (sn >> 1)) continue;
+                    u = sn & 1;
+                }
+                const double tot = metric[p] + bd[t][p][u];
+                if (tot < nxt) { nxt = tot; pv = p; by = bc[t][p][u]; }
+            }
+            prv[t][sn] = (int8_t)pv;
+            byt[t][sn] = (uint8_t)by;
+        }
+        __syncthreads();
+        if (tid < 8) metric[tid] = nxt;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        int st = 0;
+        for (int q = 1; q < 8; ++q)
+            if (metric[q] < metric[st]) st = q;
+        uint8_t out[32];
+        for (int t = 31; t >= 0; --t) {
+            out[t] = byt[t][st];
+            st = prv[t][st];
+        }
+        for (int i = 0; i < 8; ++i)
+            dst[i] = (uint32_t)out[4 * i] | ((uint32_t)out[4 * i + 1] << 8) | ((uint32_t)out[4 * i + 2] << 16) |
+                     ((uint32_t)out[4 * i + 3] << 24);
+    }
+}
+
 // Carried-state variant: one workgroup per row walks its blocks in order,
 // each block rotated, scaled and scored as above, the path metrics carried
 // from block to block; the survivors of all 32 nb steps stay in LDS (2 bytes
@@ -468,6 +587,17 @@ int run_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bi
     if (fb_d) (void)hipFree(fb_d);
     if (err_d) (void)hipFree(err_d);
     return rc;
+}
+
+int launch_encode_table(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const int8_t* table,
+                        bool r23, uint8_t* codes, uint16_t* scales, pg_stream_t s) {
+    const int64_t blocks = n * (k / 128);
+    if (blocks > 0x7fffffff) return fail(PG_ERR_UNSUPPORTED, "pg_encode_table: too many blocks (%lld)", (long long)blocks);
+    hipLaunchKernelGGL(k_encode_table, dim3((unsigned)blocks), dim3(128), 0, (hipStream_t)s, w, (int)n, (int)k,
+                       sign_bits, reinterpret_cast<const uint4*>(table), r23 ? 1 : 0, codes, scales);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PG_ERR_HIP, "pg_encode_table launch: %s", hipGetErrorString(e));
+    return PG_OK;
 }
 
 int launch_encode(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,

@@ -235,6 +235,86 @@ void parallel_rows(int64_t count, int n_threads, F f) {
 
 }  // namespace
 
+// Viterbi through a codebook table (P8F v1's trellis, or the rate-2/3 one):
+// for every group, state p and byte c the distortion ((d0^2 + d1^2) + d2^2)
+// + d3^2 with d_j = w_j - s * T[p][c][j]; per state and branch u (the byte's
+// branch bits) the first byte of least distortion; add-compare-select from
+// state 0 with each next state's predecessors in increasing order, strict
+// improvement, the first best end state; a zero scale codes byte 0.
+void encode_block_table(const double* w, uint16_t scale_bits, const int8_t* table, bool r23, uint8_t* out) {
+    const double s = half_to_double(scale_bits);
+    if (s == 0.0) {
+        std::memset(out, 0, 32);
+        return;
+    }
+    const int nbr = r23 ? 4 : 2, um = nbr - 1;
+    static thread_local double bd[32][8][4];
+    static thread_local uint8_t bc[32][8][4];
+    for (int t = 0; t < 32; ++t)
+        for (int p = 0; p < 8; ++p) {
+            for (int u = 0; u < nbr; ++u) bd[t][p][u] = INFINITY;
+            for (int c = 0; c < 256; ++c) {
+                const int8_t* L = table + (p * 256 + c) * 4;
+                const double d0 = w[4 * t + 0] - s * (double)L[0];
+                const double d1 = w[4 * t + 1] - s * (double)L[1];
+                const double d2 = w[4 * t + 2] - s * (double)L[2];
+                const double d3 = w[4 * t + 3] - s * (double)L[3];
+                const double m = ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
+                const int u = c & um;
+                if (m < bd[t][p][u]) {
+                    bd[t][p][u] = m;
+                    bc[t][p][u] = (uint8_t)c;
+                }
+            }
+        }
+    double metric[8], next[8];
+    int8_t prev[32][8];
+    uint8_t byte[32][8];
+    for (int st = 0; st < 8; ++st) metric[st] = INFINITY;
+    metric[0] = 0.0;
+    for (int t = 0; t < 32; ++t) {
+        for (int sn = 0; sn < 8; ++sn) next[sn] = INFINITY;
+        for (int p = 0; p < 8; ++p)
+            for (int u = 0; u < nbr; ++u) {
+                const int sn = r23 ? ((p << 2) | u) & 7 : ((p << 1) | u) & 7;
+                const double tot = metric[p] + bd[t][p][u];
+                if (tot < next[sn]) {
+                    next[sn] = tot;
+                    prev[t][sn] = (int8_t)p;
+                    byte[t][sn] = bc[t][p][u];
+                }
+            }
+        std::memcpy(metric, next, sizeof(metric));
+    }
+    int st = 0;
+    for (int q = 1; q < 8; ++q)
+        if (metric[q] < metric[st]) st = q;
+    for (int t = 31; t >= 0; --t) {
+        out[t] = byte[t][st];
+        st = prev[t][st];
+    }
+}
+
+int encode_ref_table(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const int8_t* table,
+                     bool r23, uint8_t* codes, uint16_t* scales, int n_threads) {
+    const int64_t nb = k / 128;
+    parallel_rows(n, n_threads, [&](int64_t r) {
+        std::vector<double> v(128);
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int i = 0; i < 128; ++i) v[i] = (double)w[r * k + b * 128 + i];
+            rotate_block(v.data(), sign_bits, b * 128);
+            double acc = 0.0;
+            for (int i = 0; i < 128; ++i) acc = acc + v[i] * v[i];
+            const double rms = std::sqrt(acc / 128.0);
+            const double val = std::min(kScaleC * rms, 65504.0);
+            const uint16_t sb = double_to_half_rne(val);
+            scales[r * nb + b] = sb;
+            encode_block_table(v.data(), sb, table, r23, codes + r * (k / 4) + b * 32);
+        }
+    });
+    return PG_OK;
+}
+
 // LDLQ feedback (landing page, "How it works": LDLQ rounding).  H~ = R H R^T
 // (the block rotation on both sides), then H~ = U D U^T with U unit upper
 // block-triangular and D block-diagonal (blocks of 128), eliminating blocks

@@ -28,6 +28,9 @@ uint16_t double_to_half_rne(double v);
 double half_to_double(uint16_t h);
 int encode_ref(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, uint8_t* codes,
                uint16_t* scales, int n_threads);
+// the encoder through a codebook table (pg_host.cpp), P8F v1's or the rate-2/3 trellis
+int encode_ref_table(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const int8_t* table,
+                     bool r23, uint8_t* codes, uint16_t* scales, int n_threads);
 // LDLQ (pg_host.cpp): the feedback matrix U - I of the rotated Hessian
 // (k x k fp64, host), and the reference encoder that uses it
 int ldlq_feedback(const double* hessian, int64_t k, const uint8_t* sign_bits, int n_threads, double* fb);
@@ -82,6 +85,8 @@ int launch_encode_carry(const float* w, int64_t n, int64_t k, const uint8_t* sig
 // fp64 [n][k] scratch; one launch per block in order
 int launch_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* fb,
                        double* err, uint8_t* codes, uint16_t* scales, pg_stream_t s);
+int launch_encode_table(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const int8_t* table,
+                        bool r23, uint8_t* codes, uint16_t* scales, pg_stream_t s);
 // pg_encode_ldlq's device side: factor on the host, allocate, launch, free
 int run_encode_ldlq(const float* w, int64_t n, int64_t k, const uint8_t* sign_bits, const double* hessian,
                     uint8_t* codes, uint16_t* scales, pg_stream_t s);

@@ -47,4 +47,8 @@ int launch_encode_carry(const float*, int64_t, int64_t, const uint8_t*, uint8_t*
 int run_encode_ldlq(const float*, int64_t, int64_t, const uint8_t*, const double*, uint8_t*, uint16_t*, pg_stream_t) {
     return no_device("pg_encode_ldlq");
 }
+int launch_encode_table(const float*, int64_t, int64_t, const uint8_t*, const int8_t*, bool, uint8_t*, uint16_t*,
+                        pg_stream_t) {
+    return no_device("pg_encode_table");
+}
 }  // namespace pg
