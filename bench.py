@@ -497,6 +497,32 @@ def run_encode():
     gws = tot_w / tot_ms / 1e6
     tops = 1408.0 * gws * 1e9 / 1e12
     log(f"encode: {gws:.2f} Gweights/s on the GPU")
+    # the encoder through a codebook table on the q matrix: every byte of every
+    # state scored, 8 x 256 x 15 / 4 = 7680 fp64 operations per weight
+    w = synth.qwen_layer_weights("q")
+    n, k = w.shape
+    wd = torch.from_numpy(w).cuda()
+    sbd = torch.from_numpy(synth.site_sign_bits(0, 0, k)).cuda()
+    c = torch.empty((n, k // 4), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((n, k // 128), dtype=torch.int16, device="cuda")
+    tables = {"gauss table, P8F v1 trellis": (torch.from_numpy(synth.random_codebook_table(22, "gauss")).cuda(), 0),
+              "rate-2/3 table and trellis": (torch.from_numpy(q.pg_codebook_table_ex(q.PG_FLAG_RATE23)).cuda(),
+                                             q.PG_FLAG_RATE23)}
+    tab_res = {}
+    for label, (tt, fl) in tables.items():
+        q.pg_encode_table(wd, n, k, sbd, tt, fl, c, sc)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        q.pg_encode_table(wd, n, k, sbd, tt, fl, c, sc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        g = n * k / ms / 1e6
+        tab_res[label] = {"ms": round(ms, 3), "gweights_per_s": round(g, 3),
+                          "t_ops_per_s": round(7680.0 * g / 1e3, 2)}
+    log(f"table encode: {tab_res}")
     return {"kernel": "k_encode (pg_encode)", "workload": "Qwen3-4B-shaped layer, 7 matrices, "
             f"{int(tot_w)} weights", "ms": round(tot_ms, 3), "gweights_per_s": round(gws, 2),
             "roofline": {"bound": "alu", "achieved": round(tops, 2), "peak": FP64_OPS_PEAK_T,
@@ -505,7 +531,9 @@ def run_encode():
             "cpu_reference": {"mweights_per_s": round(cpu_w / cpu_s / 1e6, 2), "threads": host_cores(),
                               "kind": "pg_encode_ref (host C++, bit-identical output)",
                               "sample": "64 rows of each matrix"},
-            "matrices": per}
+            "matrices": per,
+            "table_encoder": {"kernel": "k_encode_table (pg_encode_table)", "workload": "Qwen3-4B q matrix 4096 x 2560",
+                              "ops_per_weight": 7680, **tab_res}}
 
 
 def main():
