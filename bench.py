@@ -386,15 +386,17 @@ def run_hbm_read(nbytes: int = 4 << 30, reps: int = 5):
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "xor_check": ok}
 
 
-def run_qgemm(stream_iters: int = 10):
+def run_qgemm(stream_iters: int = 10, rounds_n: int = 5):
     """Prompt path on the matrix cores: pg_qgemm_ex on the Qwen3-4B layer-0
     launch groups (random codes and scales as in the stack), X = bf16 N(0,1)
     rows rotated once by pg_fwht_rotate (bf16 -> bf16), at m = 512 and 4096,
     with the workspace pg_qgemm_workspace_bytes asks for (allocated before the
     timed calls; shapes whose tiles fill the chip in whole rounds ask for none
     and run unsplit).  Each product is timed alone with HIP events on the launch
-    stream over `stream_iters` back-to-back calls, the split sum included;
-    the fraction is 2 m n k per second over the 2.5 PFLOP/s dense bf16 peak."""
+    stream: after 3 warm-up calls, `rounds_n` rounds of `stream_iters`
+    back-to-back calls (the split sum included), the median round per call
+    (the first calls of a shape run slower while the clocks settle); the
+    fraction is 2 m n k per second over the 2.5 PFLOP/s dense bf16 peak."""
     import numpy as np
     import torch
 
@@ -406,7 +408,7 @@ def run_qgemm(stream_iters: int = 10):
     site_no = {"qkv": 0, "o": 1, "gu": 2, "down": 3}
     stream = torch.cuda.current_stream()
     out = {"bound": "mfma", "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16 x bf16 -> f32",
-           "kernel": "k_qgemm_v2 + k_qgemm_sum (pg_qgemm_ex)", "workload": "Qwen3-4B layer-0 launch groups qkv/o/gu/down, "
+           "kernel": "k_qgemm_v2 (+ k_qgemm_sum when split) (pg_qgemm_ex)", "workload": "Qwen3-4B layer-0 launch groups qkv/o/gu/down, "
            "random trellis bitstreams, bf16 N(0,1) rows", "per_m": {}}
     for m in (512, 4096):
         tot_flop = tot_us = 0.0
@@ -422,20 +424,24 @@ def run_qgemm(stream_iters: int = 10):
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
             wsb = q.pg_qgemm_workspace_bytes(n, k, m)
             ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device="cuda")
-            for _ in range(2):
+            for _ in range(3):
                 q.pg_qgemm_ex(cd, sc, n, k, xr, m, y, ws, wsb)
             torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(stream_iters):
-                q.pg_qgemm_ex(cd, sc, n, k, xr, m, y, ws, wsb)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = 1e3 * e0.elapsed_time(e1) / stream_iters
+            rounds = []
+            for _ in range(rounds_n):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(stream_iters):
+                    q.pg_qgemm_ex(cd, sc, n, k, xr, m, y, ws, wsb)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                rounds.append(1e3 * e0.elapsed_time(e1) / stream_iters)
+            us = float(np.median(rounds))
             flop = 2.0 * m * n * k
             tf = flop / (us * 1e-6) / 1e12
-            per[site] = {"n": n, "k": k, "us": round(us, 2), "tflops": round(tf, 1),
+            per[site] = {"n": n, "k": k, "us": round(us, 2), "us_min_max": [round(min(rounds), 2), round(max(rounds), 2)],
+                         "tflops": round(tf, 1),
                          "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "workspace_bytes": wsb}
             tot_flop += flop
             tot_us += us

@@ -377,7 +377,8 @@ int pg_rot_qgemv_table(const uint8_t* codes, const uint16_t* scales, int64_t n, 
  *   Y[r][i] = sum_blk scale[i][blk] * sum_{k in blk} level[i][k] * X[r][k]
  *   x_rot_bf16 device u16 [m][k] (bf16 bits, already rotated), y device f32
  *   [m][n] out.  Levels enter the matrix cores as exact bf16 values; each
- *   128-block's partial product is scaled in fp32. */
+ *   128-block's partial product is scaled in fp32.  For a given shape,
+ *   device and workspace size the result is the same on every call. */
 int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
              const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
 
@@ -417,10 +418,17 @@ int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, in
                      const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
 
 /* pg_qgemm_ex with its kernel and split plan given, for tests and tuning:
- *   kernel  0: the pipelined 256 x 128-tile kernel (what pg_qgemm_ex runs);
+ *   kernel  0: the library's choice (what pg_qgemm and pg_qgemm_ex run),
+ *              at present kernel 4;
  *           1: the one-buffer 128 x 128-tile kernel (never splits);
  *           2: the pipelined tile with separate producer waves (copies and
- *              decode) and consumer waves (matrix cores); same plans
+ *              decode) and consumer waves (matrix cores);
+ *           3: as 2 in 1024 threads, the block scales carried in the
+ *              running sums (no per-block partial sums: each later block
+ *              rescales the sum by a ratio of scales, one fp32 rounding
+ *              each, within nbk * 2^-24 relative of kernel 4's sums);
+ *           4: the pipelined 256 x 128-tile kernel, per-block partial sums
+ *              scaled in fp32 (levels enter the matrix cores exactly)
  *   splits  0: the library's plan; S >= 1: tiles first_split .. split S ways
  *           (tiles before it whole), S capped by the 128-blocks of k, by 8
  *           and by the workspace

@@ -29,13 +29,15 @@ def _qgemm(codes, scales, xb):
 _kernel = [None]
 
 
-@pytest.fixture(params=["auto", "1", "2", "3"])
+@pytest.fixture(params=["auto", "1", "2", "3", "4", "5"])
 def kernel(request):
     """Which product kernel runs: pg_qgemm's own, or one selected through
     pg_qgemm_tune (1: the 128x128-tile one-buffer kernel, 2: the pipelined
-    256x128-tile kernel, which pg_qgemm runs, 3: the same tile with producer
-    and consumer waves)."""
-    _kernel[0] = {"auto": None, "1": 1, "2": 0, "3": 2}[request.param]
+    256x128-tile kernel with per-block partial sums, 3: the same tile with
+    producer and consumer waves, 4: the same in 1024 threads with the block
+    scales carried in the running sums, 5: the library's choice between 2
+    and 4 through pg_qgemm_tune)."""
+    _kernel[0] = {"auto": None, "1": 1, "2": 4, "3": 2, "4": 3, "5": 0}[request.param]
     yield request.param
     _kernel[0] = None
 
@@ -86,7 +88,12 @@ def test_one_hot_column(kernel):
         xb[i, c] = 0x3F80            # bf16 1.0
     y = _qgemm(codes, scales, xb)
     for i, c in enumerate(cols):
-        assert np.array_equal(y[i].astype(np.float64), w[:, c])
+        if _kernel[0] == 3:
+            # the carried-scale kernel rescales its sums once per later block
+            # (one rounding each): within nbk * 2^-24 of the value
+            assert np.max(np.abs(y[i] - w[:, c]) / np.maximum(np.abs(w[:, c]), 1e-30)) <= (k // 128) * 2.0 ** -23
+        else:
+            assert np.array_equal(y[i].astype(np.float64), w[:, c])
     assert not y[len(cols):].any()
 
 
@@ -137,7 +144,7 @@ def test_split_k_matches_oracle(m, n, k):
 TILE_BYTES = 256 * 128 * 4
 
 
-@pytest.mark.parametrize("kern", [0, 2])
+@pytest.mark.parametrize("kern", [0, 2, 3, 4])
 @pytest.mark.parametrize("plan", ["2", "3", "8", "2:1", "3:5"])
 @pytest.mark.parametrize("m,n,k", [(77, 130, 1152), (256, 384, 512), (3, 1, 1024), (300, 1024, 2560),
                                    (513, 1030, 1152)])
@@ -219,3 +226,27 @@ def test_prompt_shapes_split_sampled_rows(m):
         rows = np.sort(rng.choice(m, 32, replace=False))
         ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb[rows]))
         assert np.max(rel_err_rows(y[rows], ref)) <= TOL, site
+
+
+def test_zero_and_wide_scales(kernel):
+    """Blocks of zero scale (first, middle, last, whole rows) and scales that
+    span eight decades within a row: every kernel matches the oracle (the
+    carried-scale kernel rescales its running sums by ratios of consecutive
+    non-zero scales and decodes zero-scale blocks as zero levels)."""
+    rng = np.random.default_rng(77)
+    m, n, k = 300, 384, 1280
+    codes = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
+    sc = rng.uniform(0.005, 0.05, (n, k // 128))
+    sc[0, 0] = 0.0
+    sc[1, 4:7] = 0.0
+    sc[2, -1] = 0.0
+    sc[3, :] = 0.0
+    sc[4, :3] = 0.0
+    sc[5] = 10.0 ** rng.uniform(-4, 4, k // 128)
+    scales = sc.astype(np.float16).view(np.uint16)
+    xb = synth.bf16_activations_bits(m, k, seed=78)
+    y = _qgemm(codes, scales, xb)
+    ref = p8f.gemm_ref(codes, scales, p8f.bf16_bits_to_float(xb))
+    assert np.all(y[:, 3] == 0.0)
+    live = [c for c in range(n) if c != 3]
+    assert np.max(rel_err_rows(y[:, live].T, ref[:, live].T)) <= TOL
