@@ -376,9 +376,13 @@ int pg_rot_qgemv_table(const uint8_t* codes, const uint16_t* scales, int64_t n, 
  * "Results": prompt reading is the mat-mat path):
  *   Y[r][i] = sum_blk scale[i][blk] * sum_{k in blk} level[i][k] * X[r][k]
  *   x_rot_bf16 device u16 [m][k] (bf16 bits, already rotated), y device f32
- *   [m][n] out.  Levels enter the matrix cores as exact bf16 values; each
- *   128-block's partial product is scaled in fp32.  For a given shape,
- *   device and workspace size the result is the same on every call. */
+ *   [m][n] out.  Levels enter the matrix cores as exact bf16 values and
+ *   the block scales are applied in fp32: to each 128-block's partial
+ *   product, or, for products with enough output tiles to fill several
+ *   rounds of the chip, by carrying the running sum from block to block
+ *   (one rescaling per later block, within nbk * 2^-24 relative of the
+ *   first).  For a given shape, device and workspace size the result is the
+ *   same on every call. */
 int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
              const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
 
@@ -418,8 +422,10 @@ int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, in
                      const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
 
 /* pg_qgemm_ex with its kernel and split plan given, for tests and tuning:
- *   kernel  0: the library's choice (what pg_qgemm and pg_qgemm_ex run),
- *              at present kernel 4;
+ *   kernel  0: the library's choice (what pg_qgemm and pg_qgemm_ex run):
+ *              kernel 5 when the product does not split and its 256 x 256
+ *              tiles need fewer rounds of workgroups (a round of them costs
+ *              1.87 rounds of 256 x 128 tiles), else kernel 4;
  *           1: the one-buffer 128 x 128-tile kernel (never splits);
  *           2: the pipelined tile with separate producer waves (copies and
  *              decode) and consumer waves (matrix cores);
@@ -428,7 +434,10 @@ int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, in
  *              rescales the sum by a ratio of scales, one fp32 rounding
  *              each, within nbk * 2^-24 relative of kernel 4's sums);
  *           4: the pipelined 256 x 128-tile kernel, per-block partial sums
- *              scaled in fp32 (levels enter the matrix cores exactly)
+ *              scaled in fp32 (levels enter the matrix cores exactly);
+ *           5: 256 x 256 tiles over the whole of K, the block scales
+ *              carried as in kernel 3 (results equal to kernel 3's); never
+ *              splits, so splits, first_split and the workspace are unused
  *   splits  0: the library's plan; S >= 1: tiles first_split .. split S ways
  *           (tiles before it whole), S capped by the 128-blocks of k, by 8
  *           and by the workspace

@@ -825,6 +825,216 @@ __global__ __launch_bounds__(1024) void k_qgemm_v4(const uint8_t* __restrict__ c
         }
 }
 
+// Wide-tile prompt product: 256 x 256 output tiles (X rows x weight rows),
+// whole K, with the decode and copies of k_qgemm_v2 and the carried block
+// scales of k_qgemm_v4.  Per 64-wide K step the tile does twice the matrix
+// work of the 256 x 128 tile for the same 32 KB of X copied into the LDS, and
+// its 128 x 64 wave tiles (4 x 2 products of 32 x 32) read 0.75 KB of
+// operands from the LDS per product instead of 1 KB.  512 threads, two waves
+// per SIMD; every thread copies four X chunks per step and decodes the code
+// dwords of weight rows tid / 4 and tid / 4 + 128.  X is copied one step
+// ahead into two buffers, codes and scales are loaded two steps ahead.  At a
+// block's first step the decoding threads also store each row's block scale
+// in the LDS, and at the next step the waves rescale their running sums by
+// s_prev / s_new before the block's products (at the end they multiply by the
+// last scale), so no second set of accumulators is held.  A zero-scale block
+// is decoded as zero levels and keeps the previous scale.  Every output is
+// summed in the order of k_qgemm_v4, so the two give equal results.
+constexpr int Q6_BN = 256;
+constexpr int Q6_WBYTES = Q6_BN * Q2_BK * 2;
+
+__global__ __launch_bounds__(512) void k_qgemm_v6(const uint8_t* __restrict__ codes,
+                                                  const uint16_t* __restrict__ scales, int n, int k,
+                                                  const uint16_t* __restrict__ x, int m,
+                                                  float* __restrict__ y, int tiles_n, int remap, int tiles) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs0[Q2_XBYTES];      // X, 256 rows x 128 B
+    __shared__ __attribute__((aligned(16))) uint8_t xs1[Q2_XBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ws0[Q6_WBYTES];      // levels, 256 rows x 128 B
+    __shared__ __attribute__((aligned(16))) uint8_t ws1[Q6_WBYTES];
+    __shared__ float scl[2][Q6_BN];                                      // row scales, by block parity
+    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(m), "s"(y), "s"(tiles_n), "s"(remap),
+                 "s"(tiles));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    int t = blockIdx.x;
+    if (remap) t = (t & 7) * (tiles >> 3) + (t >> 3);            // tiles of one XCD share X rows in L2
+    const int n0 = (t % tiles_n) * Q6_BN, m0 = (t / tiles_n) * Q2_BM;
+    const int kg = k >> 2, nbk = k >> 7;
+    const int st_end = 2 * nbk;
+
+    // X copies: copy i of wave w fills slot (4 w + i) * 64 + lane: row slot / 8, chunk position slot % 8
+    const uint16_t* xtile = x + (int64_t)m0 * k;
+    int xoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (4 * wave + i) * 64 + lane;
+        const int r = j >> 3, c = q2_chunk(r, j & 7);
+        const int gr = m0 + r < m ? r : m - 1 - m0;
+        xoff[i] = gr * k + 8 * c;
+    }
+    auto copy_x = [&](int st, uint8_t* dst) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(xtile + xoff[i] + st * Q2_BK, dst + (4 * wave + i) * 1024, 16, 0, 0);
+    };
+    // codes: dword tid % 4 of the step, weight rows tid / 4 and tid / 4 + 128 of the tile
+    const int nr0 = tid >> 2, dm = tid & 3;
+    const uint32_t* csrc[2];
+    const uint16_t* srow[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int wrow = n0 + nr0 + 128 * h < n ? n0 + nr0 + 128 * h : n - 1;
+        csrc[h] = reinterpret_cast<const uint32_t*>(codes + (int64_t)wrow * kg) + dm;
+        srow[h] = scales + (int64_t)wrow * nbk;
+    }
+    uint32_t dprev[2] = {0u, 0u};                       // this thread's dwords of the previous step
+    auto decode = [&](bool second_half, uint32_t d, uint32_t z, int h, uint8_t* wdst) {
+        const int nr = nr0 + 128 * h;
+        const uint32_t left = (uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0x111, 0xf, 0xf, true);       // lane - 1
+        const uint32_t back = (uint32_t)__builtin_amdgcn_mov_dpp((int)dprev[h], 0x103, 0xf, 0xf, true); // lane + 3
+        const uint32_t dp = dm != 0 ? left : (second_half ? back : 0u);   // nothing before a block start
+        dprev[h] = d;
+        uint32_t P[4];
+        planes_of(d, dp, P);
+        const uint32_t t0 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
+        const uint32_t u0 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
+        const uint32_t t1 = __builtin_amdgcn_perm(P[1], P[0], 0x07030602u);
+        const uint32_t u1 = __builtin_amdgcn_perm(P[3], P[2], 0x07030602u);
+        const uint32_t Q[4] = {__builtin_amdgcn_perm(u0, t0, 0x05040100u), __builtin_amdgcn_perm(u0, t0, 0x07060302u),
+                               __builtin_amdgcn_perm(u1, t1, 0x05040100u), __builtin_amdgcn_perm(u1, t1, 0x07060302u)};
+        const uint32_t keep = (z & 0x7fffu) == 0 ? 0u : ~0u;             // a zero-scale block: zero levels
+        uint32_t o[8];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t lo = __builtin_amdgcn_perm(0xE0A04080u, 0x8040A0E0u, Q[g]);
+            const uint32_t hi = __builtin_amdgcn_perm(0x4040403Fu, 0xBFC0C0C0u, Q[g]);
+            o[2 * g] = __builtin_amdgcn_perm(hi, lo, 0x05010400u) & keep;
+            o[2 * g + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u) & keep;
+        }
+        uint8_t* row = wdst + nr * 128;
+        *reinterpret_cast<uint4*>(row + 16 * q2_chunk(nr, 2 * dm)) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(row + 16 * q2_chunk(nr, 2 * dm + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+    };
+
+    // prologue: codes, scales and X of step 0, codes and scales of step 1; levels and row scales of step 0.
+    // Codes and scales of odd steps are held in cA, zA, of even steps in cB, zB.
+    uint32_t cA[2], cB[2];
+    uint16_t zA[2], zB[2];
+    {
+        uint32_t c0[2];
+        uint16_t z0[2];
+        copy_x(0, xs0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) { c0[h] = csrc[h][0]; z0[h] = srow[h][0]; }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) { cA[h] = csrc[h][4]; zA[h] = srow[h][0]; }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            decode(false, c0[h], z0[h], h, ws0);
+            if (dm == 0) scl[0][nr0 + 128 * h] = h2f(z0[h]);
+        }
+    }
+    lds_barrier();
+
+    const int wm = wave >> 2, wn = wave & 3;             // 128-row half of X, 64-row quarter of the weights
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    float scur[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) scur[j] = scl[0][64 * wn + 32 * j + (lane & 31)];
+
+    // Step st uses buffers st % 2.  Each step copies X of step st + 1 (past
+    // the end: the last step again, into the buffer nobody reads) and then
+    // loads the codes and scales of step st + 2 (clamped the same way), so
+    // that every step makes 8 requests and the wait below has a fixed count.
+    auto body = [&](auto J, int st) {
+        constexpr int j2 = decltype(J)::value;
+        constexpr bool half2 = j2 == 1;                 // second half of a 128-block
+        uint8_t* xcur = j2 == 0 ? xs0 : xs1;
+        uint8_t* xnext = j2 == 0 ? xs1 : xs0;
+        uint8_t* wcur = j2 == 0 ? ws0 : ws1;
+        uint8_t* wnext = j2 == 0 ? ws1 : ws0;
+        copy_x(st + 1 < st_end ? st + 1 : st_end - 1, xnext);
+        asm volatile("" ::: "memory");                  // the copies are issued before the loads below,
+        const int sn = st + 2 < st_end ? st + 2 : st_end - 1;
+        uint32_t* cn = j2 == 0 ? cB : cA;               // step st + 2
+        uint16_t* zn = j2 == 0 ? zB : zA;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) { cn[h] = csrc[h][4 * sn]; zn[h] = srow[h][sn >> 1]; }
+        asm volatile("" ::: "memory");                  // and these before the operand reads
+        const uint32_t* c1 = j2 == 0 ? cA : cB;         // step st + 1
+        const uint16_t* z1 = j2 == 0 ? zA : zB;
+        if (!half2 && st > 0) {                         // a block start: carry the sums into its scale
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float sn_ = scl[(st >> 1) & 1][64 * wn + 32 * j + (lane & 31)];
+                const float snew = sn_ != 0.0f ? sn_ : scur[j];
+                const float r = snew != 0.0f ? scur[j] / snew : 1.0f;
+                scur[j] = snew;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[i][j][q] *= r;
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int c = 2 * kk + (lane >> 5);
+            bf16x8 a[4], b[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 128 * wm + 32 * i + (lane & 31);
+                a[i] = *reinterpret_cast<const bf16x8*>(xcur + r * 128 + 16 * q2_chunk(r, c));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = 64 * wn + 32 * j + (lane & 31);
+                b[j] = *reinterpret_cast<const bf16x8*>(wcur + r * 128 + 16 * q2_chunk(r, c));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        // all but this step's 4 code and scale requests have landed: the X of
+        // step st + 1 and the codes and scales of step st + 1
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        if (st + 1 < st_end) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                decode(!half2, c1[h], z1[h], h, wnext);
+                // step st + 1 starts a block: its row scales, read after the barrier
+                if (half2 && dm == 0) scl[((st + 1) >> 1) & 1][nr0 + 128 * h] = h2f(z1[h]);
+            }
+        }
+        lds_barrier();                                  // level, scale and X writes and operand reads done
+    };
+    for (int st = 0; st < st_end; st += 2) {            // whole blocks: an even count of steps
+        body(std::integral_constant<int, 0>(), st);
+        body(std::integral_constant<int, 1>(), st + 1);
+    }
+    // value r of lane l of a 32x32 tile: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+            if (col >= n) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row < m) y[(int64_t)row * n + col] = acc[i][j][r] * scur[j];
+            }
+        }
+}
+
 // y += part 0 + part 1 + ... over the split tiles: thread q takes values
 // 4 (q % 8192) .. + 3 of tile block q / 8192 (tile t_full + q / 8192, 256 x
 // 128 values, row-major) from every part in part order; values outside y
@@ -929,6 +1139,7 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
                  int64_t m, float* y, void* workspace, size_t ws_bytes, pg_stream_t s, int kernel, int splits,
                  int64_t first_split) {
     const int64_t tn = (n + Q2_BN - 1) / Q2_BN, tm = (m + Q2_BM - 1) / Q2_BM, tiles = tn * tm;
+
     // the pipelined kernel is the product; kernel 1 is the plain one-buffer
     // kernel (kept as a second implementation, for tests)
     if (kernel != 1) {
@@ -938,10 +1149,25 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
         const int64_t nrem = tiles - p.t_full, grid = p.t_full + nrem * p.splits;
         if (grid > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
         const int remap = (p.t_full % 8 == 0 ? 1 : 0) | ((nrem * p.splits) % 8 == 0 ? 2 : 0);
-        // the library's choice is the pipelined kernel: timed interleaved
-        // (medians of five rounds), it is ahead of both producer/consumer
-        // kernels on every Qwen3-4B shape at m = 512 and 4096
-        if (kernel == 0) kernel = 4;
+        // The library's choice: the pipelined kernel (timed interleaved, medians
+        // of five rounds, it is ahead of both producer/consumer kernels on
+        // every Qwen3-4B shape at m = 512 and 4096), or the wide-tile kernel
+        // when the product does not split and the wide tiles need fewer
+        // rounds of workgroups: a round of them takes 1.87 times a round of
+        // the 256 x 128 tiles (Qwen3-4B gate/up product at m = 4096).
+        const int64_t tiles6 = ((n + Q6_BN - 1) / Q6_BN) * tm;
+        if (kernel == 0) {
+            const int64_t cus = compute_units();
+            const int64_t r6 = (tiles6 + cus - 1) / cus, r2 = (tiles + cus - 1) / cus;
+            kernel = p.splits == 1 && 187 * r6 < 100 * r2 ? 5 : 4;
+        }
+        if (kernel == 5) {                              // wide tiles, whole K: no split, no workspace
+            if (tiles6 > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
+            hipLaunchKernelGGL(k_qgemm_v6, dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s, codes, scales,
+                               (int)n, (int)k, x, (int)m, y, (int)((n + Q6_BN - 1) / Q6_BN),
+                               tiles6 % 8 == 0 ? 1 : 0, (int)tiles6);
+            return hip_check(hipGetLastError(), "pg_qgemm launch");
+        }
         if (kernel == 3)
             hipLaunchKernelGGL(k_qgemm_v4, dim3((unsigned)grid), dim3(1024), 0, (hipStream_t)s, codes, scales,
                                (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)tiles, (int)p.t_full, p.splits,
