@@ -1035,6 +1035,202 @@ __global__ __launch_bounds__(512) void k_qgemm_v6(const uint8_t* __restrict__ co
         }
 }
 
+// Prompt product with the weight operand decoded in registers: the 256 x 256
+// tiles, 128 x 64 wave tiles and carried block scales of k_qgemm_v6, but
+// each wave decodes the levels of its own 64 weight rows straight into the
+// matrix cores' B operands, so that only X passes through the LDS (copied
+// one step ahead, 64 KB in two buffers) and one barrier per step hands the X
+// buffers over.  Within a 64-wide K step the products take K in a permuted
+// order, the same for both operands: product kk of lane half h (lanes 32 h ..
+// 32 h + 31) covers step positions 32 h + 8 kk .. + 7, so that a lane needs
+// code dwords 2 h and 2 h + 1 of its row's step and the dword before them
+// (the trellis state), 12 bytes it loads itself two steps ahead.  The two
+// waves that share weight rows both decode them.
+__device__ __forceinline__ void levels_bf16(uint32_t d, uint32_t dp, uint32_t keep, uint32_t o[8]) {
+    uint32_t P[4];
+    planes_of(d, dp, P);
+    // byte transpose: Qg holds P of weights 4 g .. 4 g + 3
+    const uint32_t t0 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
+    const uint32_t u0 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
+    const uint32_t t1 = __builtin_amdgcn_perm(P[1], P[0], 0x07030602u);
+    const uint32_t u1 = __builtin_amdgcn_perm(P[3], P[2], 0x07030602u);
+    const uint32_t Q[4] = {__builtin_amdgcn_perm(u0, t0, 0x05040100u), __builtin_amdgcn_perm(u0, t0, 0x07060302u),
+                           __builtin_amdgcn_perm(u1, t1, 0x05040100u), __builtin_amdgcn_perm(u1, t1, 0x07060302u)};
+    // bf16 of 2 P - 7 for P = 0..7 (as in k_qgemm_v2's decode)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = __builtin_amdgcn_perm(0xE0A04080u, 0x8040A0E0u, Q[g]);
+        const uint32_t hi = __builtin_amdgcn_perm(0x4040403Fu, 0xBFC0C0C0u, Q[g]);
+        o[2 * g] = __builtin_amdgcn_perm(hi, lo, 0x05010400u) & keep;
+        o[2 * g + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u) & keep;
+    }
+}
+
+__global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ codes,
+                                                  const uint16_t* __restrict__ scales, int n, int k,
+                                                  const uint16_t* __restrict__ x, int m,
+                                                  float* __restrict__ y, int tiles_n, int remap, int tiles) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs0[Q2_XBYTES];      // X, 256 rows x 128 B
+    __shared__ __attribute__((aligned(16))) uint8_t xs1[Q2_XBYTES];
+    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(m), "s"(y), "s"(tiles_n), "s"(remap),
+                 "s"(tiles));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    int t = blockIdx.x;
+    if (remap) t = (t & 7) * (tiles >> 3) + (t >> 3);            // tiles of one XCD share X rows in L2
+    const int n0 = (t % tiles_n) * Q6_BN, m0 = (t / tiles_n) * Q2_BM;
+    const int kg = k >> 2, nbk = k >> 7;
+    const int st_end = 2 * nbk;
+    const int wm = wave >> 2, wn = wave & 3;             // 128-row half of X, 64-row quarter of the weights
+    const int hf = lane >> 5;                            // which half of each step this lane's operands hold
+
+    // X copies: copy i of wave w fills slot (4 w + i) * 64 + lane: row slot / 8, chunk position slot % 8
+    const uint16_t* xtile = x + (int64_t)m0 * k;
+    int xoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (4 * wave + i) * 64 + lane;
+        const int r = j >> 3, c = q2_chunk(r, j & 7);
+        const int gr = m0 + r < m ? r : m - 1 - m0;
+        xoff[i] = gr * k + 8 * c;
+    }
+    auto copy_x = [&](int st, uint8_t* dst) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(xtile + xoff[i] + st * Q2_BK, dst + (4 * wave + i) * 1024, 16, 0, 0);
+    };
+    // codes and scales of weight rows n0 + 64 wn + 32 j + lane % 32, j = 0, 1
+    const uint8_t* crow[2];
+    const uint16_t* srow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+        const int wrow = col < n ? col : n - 1;
+        crow[j] = codes + (int64_t)wrow * kg;
+        srow[j] = scales + (int64_t)wrow * nbk;
+    }
+    // the 12 bytes at step st: dwords 2 hf - 1 .. 2 hf + 1 of the step (dword
+    // -1 is the previous step's dword 3), or dwords 0..2 at a block start for
+    // hf = 0 (nothing before it; the first word is then not used)
+    auto load_codes = [&](int st, uint3* c, uint16_t* z) {
+        const int off = 16 * st + 8 * hf - ((hf != 0 || (st & 1) != 0) ? 4 : 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            c[j] = *reinterpret_cast<const uint3*>(crow[j] + off);
+            z[j] = srow[j][st >> 1];
+        }
+    };
+    // B operands of step st for column group j: o[0..3] product 0, o[4..7]
+    // product 1 (from dword 2 hf), p[0..3] product 2, p[4..7] product 3
+    auto decode_b = [&](int st, const uint3& c, uint16_t z, uint32_t o[8], uint32_t p[8]) {
+        const bool start = hf == 0 && (st & 1) == 0;
+        const uint32_t prev = start ? 0u : c.x;
+        const uint32_t d0 = start ? c.x : c.y;
+        const uint32_t d1 = start ? c.y : c.z;
+        const uint32_t keep = (z & 0x7fffu) == 0 ? 0u : ~0u;       // a zero-scale block: zero levels
+        levels_bf16(d0, prev, keep, o);
+        levels_bf16(d1, d0, keep, p);
+    };
+
+    // prologue: X of step 0; codes and scales of steps 0 and 1 (even steps in
+    // set A, odd steps in set B)
+    uint3 cA[2], cB[2];
+    uint16_t zA[2], zB[2];
+    copy_x(0, xs0);
+    asm volatile("" ::: "memory");
+    load_codes(0, cA, zA);
+    load_codes(1 < st_end ? 1 : 0, cB, zB);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    float scur[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) scur[j] = h2f(zA[j]);
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Step st reads X buffer st % 2 and code set st % 2.  It copies X of step
+    // st + 1 (past the end: the last step again, into the buffer nobody
+    // reads) and, once its own codes are decoded, loads the codes and scales
+    // of step st + 2 (clamped the same way) into the set it used, so every
+    // step makes 8 requests and the wait below has a fixed count.
+    auto body = [&](auto J, int st) {
+        constexpr int j2 = decltype(J)::value;
+        uint8_t* xcur = j2 == 0 ? xs0 : xs1;
+        uint8_t* xnext = j2 == 0 ? xs1 : xs0;
+        uint3* cs = j2 == 0 ? cA : cB;
+        uint16_t* zs = j2 == 0 ? zA : zB;
+        copy_x(st + 1 < st_end ? st + 1 : st_end - 1, xnext);
+        asm volatile("" ::: "memory");                  // the copies are issued before the code loads
+        // everything but these copies has landed: the codes and scales of
+        // steps st and st + 1 (those of st + 1 were requested a step ago)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        if (j2 == 0 && st > 0) {                        // a block start: carry the sums into its scale
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float s_ = h2f(zs[j]);
+                const float snew = s_ != 0.0f ? s_ : scur[j];
+                const float r = snew != 0.0f ? scur[j] / snew : 1.0f;
+                scur[j] = snew;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[i][j][q] *= r;
+            }
+        }
+        uint32_t bo[2][8], bp[2][8];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) decode_b(st, cs[j], zs[j], bo[j], bp[j]);
+        const int sn = st + 2 < st_end ? st + 2 : st_end - 1;
+        load_codes(sn, cs, zs);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int c = 4 * hf + kk;
+            bf16x8 a[4], b[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 128 * wm + 32 * i + (lane & 31);
+                a[i] = *reinterpret_cast<const bf16x8*>(xcur + r * 128 + 16 * q2_chunk(r, c));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t* src = kk < 2 ? bo[j] + 4 * kk : bp[j] + 4 * (kk - 2);
+                const uint4 v = make_uint4(src[0], src[1], src[2], src[3]);
+                b[j] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        // all but this step's 4 code and scale requests have landed: X of step st + 1
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        lds_barrier();                                  // X copies and operand reads done
+    };
+    for (int st = 0; st < st_end; st += 2) {            // whole blocks: an even count of steps
+        body(std::integral_constant<int, 0>(), st);
+        body(std::integral_constant<int, 1>(), st + 1);
+    }
+    // value r of lane l of a 32x32 tile: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+            if (col >= n) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row < m) y[(int64_t)row * n + col] = acc[i][j][r] * scur[j];
+            }
+        }
+}
+
 // y += part 0 + part 1 + ... over the split tiles: thread q takes values
 // 4 (q % 8192) .. + 3 of tile block q / 8192 (tile t_full + q / 8192, 256 x
 // 128 values, row-major) from every part in part order; values outside y
@@ -1152,14 +1348,22 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
         // The library's choice: the pipelined kernel (timed interleaved, medians
         // of five rounds, it is ahead of both producer/consumer kernels on
         // every Qwen3-4B shape at m = 512 and 4096), or the wide-tile kernel
-        // when the product does not split and the wide tiles need fewer
-        // rounds of workgroups: a round of them takes 1.87 times a round of
-        // the 256 x 128 tiles (Qwen3-4B gate/up product at m = 4096).
+        // with register-decoded operands when the product does not split and
+        // the wide tiles need fewer rounds of workgroups: a round of them
+        // takes at most 1.87 times a round of the 256 x 128 tiles (Qwen3-4B
+        // gate/up product at m = 4096).
         const int64_t tiles6 = ((n + Q6_BN - 1) / Q6_BN) * tm;
         if (kernel == 0) {
             const int64_t cus = compute_units();
             const int64_t r6 = (tiles6 + cus - 1) / cus, r2 = (tiles + cus - 1) / cus;
-            kernel = p.splits == 1 && 187 * r6 < 100 * r2 ? 5 : 4;
+            kernel = p.splits == 1 && 187 * r6 < 100 * r2 ? 6 : 4;
+        }
+        if (kernel == 6) {                              // operands decoded in registers: no split, no workspace
+            if (tiles6 > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
+            hipLaunchKernelGGL(k_qgemm_v7, dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s, codes, scales,
+                               (int)n, (int)k, x, (int)m, y, (int)((n + Q6_BN - 1) / Q6_BN),
+                               tiles6 % 8 == 0 ? 1 : 0, (int)tiles6);
+            return hip_check(hipGetLastError(), "pg_qgemm launch");
         }
         if (kernel == 5) {                              // wide tiles, whole K: no split, no workspace
             if (tiles6 > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
