@@ -109,9 +109,13 @@ def cpu_baseline(seconds: float = 12.0, cores: int = 1):
                 if time.perf_counter() - t0 >= seconds:
                     break
         dt = time.perf_counter() - t0
-        return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        gbs = done_bytes / dt / 1e9
+        return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"{mats} launch-group products of layer 0 (decode + fp64 GEMV, batch 1) in {dt:.1f} s "
-                          f"on one core; {done_bytes} coded bytes"}
+                          f"on one core; {done_bytes} coded bytes",
+                # the 36-layer stack's coded bytes per token at this rate (extrapolated from layer 0)
+                "stack_tok_per_s_extrapolated": gbs * 1e9 / (36 * sum(
+                    n * k // 4 + n * k // 64 for n, k in synth.merged_shapes(synth.qwen3_4b_shapes()).values()))}
     import multiprocessing as mp
     jobs = []
     for site in ("o", "qkv", "down", "gu"):
@@ -131,6 +135,34 @@ def cpu_baseline(seconds: float = 12.0, cores: int = 1):
     return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{rounds} passes over the layer-0 launch groups (decode + fp64 GEMV, batch 1), 256-row chunks "
                       f"over a pool of {cores} processes, in {dt:.1f} s; {done_bytes} coded bytes"}
+
+
+def cpu_qgemm(seconds: float = 6.0, m: int = 64):
+    """The oracle's prompt product (decode + fp64 matrix product) on one
+    core, on a bounded sample of the prompt workload: m rotated bf16 rows
+    against each Qwen3-4B layer-0 launch group, repeated until `seconds` have
+    passed; GFLOP/s = 2 m n k per second."""
+    import numpy as np
+
+    from oracle import p8f
+    from qgemv_amd import synth
+
+    merged = synth.random_layer_merged(0, synth.qwen3_4b_shapes())
+    xs = {s: p8f.bf16_bits_to_float(synth.bf16_activations_bits(m, merged[s][0].shape[1] * 4, seed=m))
+          for s in merged}
+    flop, mats, t0 = 0.0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for site in ("o", "qkv", "down", "gu"):
+            codes, scales = merged[site]
+            p8f.gemm_ref(codes, scales, xs[site])
+            flop += 2.0 * m * codes.shape[0] * codes.shape[1] * 4
+            mats += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": flop / dt / 1e9, "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{mats} launch-group products of layer 0 at m = {m} (decode + fp64 product) in {dt:.1f} s "
+                      f"on one core"}
 
 
 # ----------------------------------------------------------------- GPU stacks
@@ -686,6 +718,7 @@ def main():
         res["cpu_baseline"] = cpu_baseline()
         if not args.no_extra:
             res["cpu_all_cores"] = cpu_baseline(seconds=10.0, cores=host_cores())
+            res["cpu_qgemm"] = cpu_qgemm()
     print(json.dumps(res), flush=True)
 
 
