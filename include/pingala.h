@@ -423,9 +423,9 @@ int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, in
 
 /* pg_qgemm_ex with its kernel and split plan given, for tests and tuning:
  *   kernel  0: the library's choice (what pg_qgemm and pg_qgemm_ex run):
- *              kernel 6 when the product does not split and its 256 x 256
+ *              kernel 7 when the product does not split and its 256 x 256
  *              tiles need fewer rounds of workgroups (a round of them costs
- *              at most 1.87 rounds of 256 x 128 tiles), else kernel 4;
+ *              1.5-1.7 rounds of 256 x 128 tiles), else kernel 4;
  *           1: the one-buffer 128 x 128-tile kernel (never splits);
  *           2: the pipelined tile with separate producer waves (copies and
  *              decode) and consumer waves (matrix cores);
@@ -441,7 +441,9 @@ int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, in
  *           6: as 5 with each wave decoding its weight rows straight into
  *              the matrix cores' operands (only X passes through the LDS);
  *              the products take K in another order within each 64-wide
- *              step, so results differ from kernel 5's in the last bits
+ *              step, so results differ from kernel 5's in the last bits;
+ *           7: as 6 with 256 x 32 wave tiles (each weight row decoded by
+ *              one wave; results equal to kernel 6's)
  *   splits  0: the library's plan; S >= 1: tiles first_split .. split S ways
  *           (tiles before it whole), S capped by the 128-blocks of k, by 8
  *           and by the workspace

@@ -1036,16 +1036,17 @@ __global__ __launch_bounds__(512) void k_qgemm_v6(const uint8_t* __restrict__ co
 }
 
 // Prompt product with the weight operand decoded in registers: the 256 x 256
-// tiles, 128 x 64 wave tiles and carried block scales of k_qgemm_v6, but
-// each wave decodes the levels of its own 64 weight rows straight into the
-// matrix cores' B operands, so that only X passes through the LDS (copied
-// one step ahead, 64 KB in two buffers) and one barrier per step hands the X
-// buffers over.  Within a 64-wide K step the products take K in a permuted
+// tiles and carried block scales of k_qgemm_v6, but each wave decodes the
+// levels of its own weight rows straight into the matrix cores' B operands,
+// so that only X passes through the LDS (copied one step ahead, 64 KB in two
+// buffers) and one barrier per step hands the X buffers over.  Wave tiles of
+// MI x 8/MI products of 32 x 32: MI = 4 gives 128 x 64 (two waves decode each
+// weight row), MI = 8 gives 256 x 32 (each weight row decoded once, twice the
+// X operand reads; the faster of the two).  Within a 64-wide K step the products take K in a permuted
 // order, the same for both operands: product kk of lane half h (lanes 32 h ..
 // 32 h + 31) covers step positions 32 h + 8 kk .. + 7, so that a lane needs
 // code dwords 2 h and 2 h + 1 of its row's step and the dword before them
-// (the trellis state), 12 bytes it loads itself two steps ahead.  The two
-// waves that share weight rows both decode them.
+// (the trellis state), 12 bytes it loads itself two steps ahead.
 __device__ __forceinline__ void levels_bf16(uint32_t d, uint32_t dp, uint32_t keep, uint32_t o[8]) {
     uint32_t P[4];
     planes_of(d, dp, P);
@@ -1066,6 +1067,7 @@ __device__ __forceinline__ void levels_bf16(uint32_t d, uint32_t dp, uint32_t ke
     }
 }
 
+template <int MI>
 __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ codes,
                                                   const uint16_t* __restrict__ scales, int n, int k,
                                                   const uint16_t* __restrict__ x, int m,
@@ -1081,7 +1083,9 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
     const int n0 = (t % tiles_n) * Q6_BN, m0 = (t / tiles_n) * Q2_BM;
     const int kg = k >> 2, nbk = k >> 7;
     const int st_end = 2 * nbk;
-    const int wm = wave >> 2, wn = wave & 3;             // 128-row half of X, 64-row quarter of the weights
+    // wave tile: MI row tiles of 32 (X rows) by NJ column groups of 32 (weight rows)
+    constexpr int WN = MI, NJ = 8 / MI;                  // 8 / MI waves along X rows, MI along weight rows
+    const int wm = wave / WN, wn = wave % WN;
     const int hf = lane >> 5;                            // which half of each step this lane's operands hold
 
     // X copies: copy i of wave w fills slot (4 w + i) * 64 + lane: row slot / 8, chunk position slot % 8
@@ -1099,12 +1103,12 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_global_load_lds(xtile + xoff[i] + st * Q2_BK, dst + (4 * wave + i) * 1024, 16, 0, 0);
     };
-    // codes and scales of weight rows n0 + 64 wn + 32 j + lane % 32, j = 0, 1
-    const uint8_t* crow[2];
-    const uint16_t* srow[2];
+    // codes and scales of weight rows n0 + 32 (NJ wn + j) + lane % 32, j < NJ
+    const uint8_t* crow[NJ];
+    const uint16_t* srow[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+        const int col = n0 + 32 * (NJ * wn + j) + (lane & 31);
         const int wrow = col < n ? col : n - 1;
         crow[j] = codes + (int64_t)wrow * kg;
         srow[j] = scales + (int64_t)wrow * nbk;
@@ -1115,7 +1119,7 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
     auto load_codes = [&](int st, uint3* c, uint16_t* z) {
         const int off = 16 * st + 8 * hf - ((hf != 0 || (st & 1) != 0) ? 4 : 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             c[j] = *reinterpret_cast<const uint3*>(crow[j] + off);
             z[j] = srow[j][st >> 1];
         }
@@ -1134,22 +1138,22 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
 
     // prologue: X of step 0; codes and scales of steps 0 and 1 (even steps in
     // set A, odd steps in set B)
-    uint3 cA[2], cB[2];
-    uint16_t zA[2], zB[2];
+    uint3 cA[NJ], cB[NJ];
+    uint16_t zA[NJ], zB[NJ];
     copy_x(0, xs0);
     asm volatile("" ::: "memory");
     load_codes(0, cA, zA);
     load_codes(1 < st_end ? 1 : 0, cB, zB);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
-    float scur[2];
+    float scur[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) scur[j] = h2f(zA[j]);
-    f32x16 acc[4][2];
+    for (int j = 0; j < NJ; ++j) scur[j] = h2f(zA[j]);
+    f32x16 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -1171,45 +1175,45 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
         if (j2 == 0 && st > 0) {                        // a block start: carry the sums into its scale
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const float s_ = h2f(zs[j]);
                 const float snew = s_ != 0.0f ? s_ : scur[j];
                 const float r = snew != 0.0f ? scur[j] / snew : 1.0f;
                 scur[j] = snew;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int q = 0; q < 16; ++q) acc[i][j][q] *= r;
             }
         }
-        uint32_t bo[2][8], bp[2][8];
+        uint32_t bo[NJ][8], bp[NJ][8];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) decode_b(st, cs[j], zs[j], bo[j], bp[j]);
+        for (int j = 0; j < NJ; ++j) decode_b(st, cs[j], zs[j], bo[j], bp[j]);
         const int sn = st + 2 < st_end ? st + 2 : st_end - 1;
         load_codes(sn, cs, zs);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int c = 4 * hf + kk;
-            bf16x8 a[4], b[2];
+            bf16x8 a[MI], b[NJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 128 * wm + 32 * i + (lane & 31);
+            for (int i = 0; i < MI; ++i) {
+                const int r = 32 * (MI * wm + i) + (lane & 31);
                 a[i] = *reinterpret_cast<const bf16x8*>(xcur + r * 128 + 16 * q2_chunk(r, c));
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const uint32_t* src = kk < 2 ? bo[j] + 4 * kk : bp[j] + 4 * (kk - 2);
                 const uint4 v = make_uint4(src[0], src[1], src[2], src[3]);
                 b[j] = __builtin_bit_cast(bf16x8, v);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        // all but this step's 4 code and scale requests have landed: X of step st + 1
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        // all but this step's 2 NJ code and scale requests have landed: X of step st + 1
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NJ));
         lds_barrier();                                  // X copies and operand reads done
     };
     for (int st = 0; st < st_end; st += 2) {            // whole blocks: an even count of steps
@@ -1218,14 +1222,14 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
     }
     // value r of lane l of a 32x32 tile: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+        for (int j = 0; j < NJ; ++j) {
+            const int col = n0 + 32 * (NJ * wn + j) + (lane & 31);
             if (col >= n) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int row = m0 + 32 * (MI * wm + i) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (row < m) y[(int64_t)row * n + col] = acc[i][j][r] * scur[j];
             }
         }
@@ -1348,21 +1352,26 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
         // The library's choice: the pipelined kernel (timed interleaved, medians
         // of five rounds, it is ahead of both producer/consumer kernels on
         // every Qwen3-4B shape at m = 512 and 4096), or the wide-tile kernel
-        // with register-decoded operands when the product does not split and
-        // the wide tiles need fewer rounds of workgroups: a round of them
-        // takes at most 1.87 times a round of the 256 x 128 tiles (Qwen3-4B
-        // gate/up product at m = 4096).
+        // with register-decoded operands and 256 x 32 wave tiles when the
+        // product does not split and the wide tiles need fewer rounds of
+        // workgroups: a round of them takes 1.5-1.7 times a round of the
+        // 256 x 128 tiles (Qwen3-4B products at m = 4096).
         const int64_t tiles6 = ((n + Q6_BN - 1) / Q6_BN) * tm;
         if (kernel == 0) {
             const int64_t cus = compute_units();
             const int64_t r6 = (tiles6 + cus - 1) / cus, r2 = (tiles + cus - 1) / cus;
-            kernel = p.splits == 1 && 187 * r6 < 100 * r2 ? 6 : 4;
+            kernel = p.splits == 1 && 170 * r6 < 100 * r2 ? 7 : 4;
         }
-        if (kernel == 6) {                              // operands decoded in registers: no split, no workspace
+        if (kernel == 6 || kernel == 7) {               // operands decoded in registers: no split, no workspace
             if (tiles6 > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
-            hipLaunchKernelGGL(k_qgemm_v7, dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s, codes, scales,
-                               (int)n, (int)k, x, (int)m, y, (int)((n + Q6_BN - 1) / Q6_BN),
-                               tiles6 % 8 == 0 ? 1 : 0, (int)tiles6);
+            if (kernel == 6)
+                hipLaunchKernelGGL(k_qgemm_v7<4>, dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s, codes, scales,
+                                   (int)n, (int)k, x, (int)m, y, (int)((n + Q6_BN - 1) / Q6_BN),
+                                   tiles6 % 8 == 0 ? 1 : 0, (int)tiles6);
+            else
+                hipLaunchKernelGGL(k_qgemm_v7<8>, dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s, codes, scales,
+                                   (int)n, (int)k, x, (int)m, y, (int)((n + Q6_BN - 1) / Q6_BN),
+                                   tiles6 % 8 == 0 ? 1 : 0, (int)tiles6);
             return hip_check(hipGetLastError(), "pg_qgemm launch");
         }
         if (kernel == 5) {                              // wide tiles, whole K: no split, no workspace
