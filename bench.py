@@ -440,7 +440,7 @@ def run_qgemm(stream_iters: int = 10, rounds_n: int = 5):
     site_no = {"qkv": 0, "o": 1, "gu": 2, "down": 3}
     stream = torch.cuda.current_stream()
     out = {"bound": "mfma", "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16 x bf16 -> f32",
-           "kernel": "k_qgemm_v2 (+ k_qgemm_sum when split) or k_qgemm_v7<8>, the library's choice per shape (pg_qgemm_ex)", "workload": "Qwen3-4B layer-0 launch groups qkv/o/gu/down, "
+           "kernel": "k_qgemm_v7<8,4,128> (+ k_qgemm_sum when split) (pg_qgemm_ex)", "workload": "Qwen3-4B layer-0 launch groups qkv/o/gu/down, "
            "random trellis bitstreams, bf16 N(0,1) rows", "per_m": {}}
     for m in (512, 4096):
         tot_flop = tot_us = 0.0

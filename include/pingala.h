@@ -377,12 +377,11 @@ int pg_rot_qgemv_table(const uint8_t* codes, const uint16_t* scales, int64_t n, 
  *   Y[r][i] = sum_blk scale[i][blk] * sum_{k in blk} level[i][k] * X[r][k]
  *   x_rot_bf16 device u16 [m][k] (bf16 bits, already rotated), y device f32
  *   [m][n] out.  Levels enter the matrix cores as exact bf16 values and
- *   the block scales are applied in fp32: to each 128-block's partial
- *   product, or, for products with enough output tiles to fill several
- *   rounds of the chip, by carrying the running sum from block to block
- *   (one rescaling per later block, within nbk * 2^-24 relative of the
- *   first).  For a given shape, device and workspace size the result is the
- *   same on every call. */
+ *   the block scales are applied in fp32 by carrying the running sum from
+ *   block to block (acc = acc * s_prev / s_new at each block start, times
+ *   the last scale at the end: one rounding per later block, within
+ *   nbk * 2^-24 relative of per-block partial sums).  For a given shape,
+ *   device and workspace size the result is the same on every call. */
 int pg_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
              const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
 
@@ -422,10 +421,8 @@ int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, in
                      const uint16_t* x_rot_bf16, int64_t m, float* y, pg_stream_t stream);
 
 /* pg_qgemm_ex with its kernel and split plan given, for tests and tuning:
- *   kernel  0: the library's choice (what pg_qgemm and pg_qgemm_ex run):
- *              kernel 7 when the product does not split and its 256 x 256
- *              tiles need fewer rounds of workgroups (a round of them costs
- *              1.5-1.7 rounds of 256 x 128 tiles), else kernel 4;
+ *   kernel  0: the library's choice (what pg_qgemm and pg_qgemm_ex run),
+ *              at present kernel 8;
  *           1: the one-buffer 128 x 128-tile kernel (never splits);
  *           2: the pipelined tile with separate producer waves (copies and
  *              decode) and consumer waves (matrix cores);
@@ -443,7 +440,10 @@ int pg_qgemm_noalloc(const uint8_t* codes, const uint16_t* scales, int64_t n, in
  *              the products take K in another order within each 64-wide
  *              step, so results differ from kernel 5's in the last bits;
  *           7: as 6 with 256 x 32 wave tiles (each weight row decoded by
- *              one wave; results equal to kernel 6's)
+ *              one wave; results equal to kernel 6's);
+ *           8: 256 x 128 tiles of four waves with 256 x 32 wave tiles and
+ *              register-decoded operands, two workgroups per compute unit,
+ *              the split plans of kernel 4
  *   splits  0: the library's plan; S >= 1: tiles first_split .. split S ways
  *           (tiles before it whole), S capped by the 128-blocks of k, by 8
  *           and by the workspace

@@ -307,7 +307,7 @@ int pg_qgemm_tune(const uint8_t* codes, const uint16_t* scales, int64_t n, int64
     pg::clear_error();
     PG_TRY(check_nk(n, k));
     if (m < 1 || m > ((int64_t)1 << 30)) return pg::fail(PG_ERR_INVALID_ARG, "m must be >= 1 (got %lld)", (long long)m);
-    if (kernel < 0 || kernel > 7) return pg::fail(PG_ERR_INVALID_ARG, "kernel must be 0..7 (got %d)", kernel);
+    if (kernel < 0 || kernel > 8) return pg::fail(PG_ERR_INVALID_ARG, "kernel must be 0..8 (got %d)", kernel);
     if (splits < 0 || first_split < 0)
         return pg::fail(PG_ERR_INVALID_ARG, "splits and first_split must be >= 0 (got %d, %lld)", splits,
                         (long long)first_split);

@@ -1067,41 +1067,71 @@ __device__ __forceinline__ void levels_bf16(uint32_t d, uint32_t dp, uint32_t ke
     }
 }
 
-template <int MI>
-__global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ codes,
-                                                  const uint16_t* __restrict__ scales, int n, int k,
-                                                  const uint16_t* __restrict__ x, int m,
-                                                  float* __restrict__ y, int tiles_n, int remap, int tiles) {
+template <int MI, int NW, int BN>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_qgemm_v7(const uint8_t* __restrict__ codes,
+                                                      const uint16_t* __restrict__ scales, int n, int k,
+                                                      const uint16_t* __restrict__ x, int m,
+                                                      float* __restrict__ y, int tiles_n, int remap, int tiles,
+                                                      int t_full, int splits, float* __restrict__ ws) {
     __shared__ __attribute__((aligned(16))) uint8_t xs0[Q2_XBYTES];      // X, 256 rows x 128 B
     __shared__ __attribute__((aligned(16))) uint8_t xs1[Q2_XBYTES];
     asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(m), "s"(y), "s"(tiles_n), "s"(remap),
-                 "s"(tiles));
+                 "s"(tiles), "s"(t_full), "s"(splits), "s"(ws));
+    // wave tile: MI row tiles of 32 (X rows) by NJ column groups of 32 (weight rows)
+    constexpr int WM = 8 / MI, WN = NW / WM, NJ = BN / (32 * WN);
+    static_assert(WM * WN == NW && NJ * 32 * WN == BN && NJ >= 1, "wave grid");
+    constexpr int XC = 32 / NW;                          // X copies per thread and step (2048 16-byte slots)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    int t = blockIdx.x;
-    if (remap) t = (t & 7) * (tiles >> 3) + (t >> 3);            // tiles of one XCD share X rows in L2
-    const int n0 = (t % tiles_n) * Q6_BN, m0 = (t / tiles_n) * Q2_BM;
+    // tile and split as in k_qgemm_v2: tiles 0..t_full-1 whole, the others `splits` ways
+    int t, split = 0, nsplit = 1;
+    const int nrem = tiles - t_full;
+    if ((int)blockIdx.x < t_full) {
+        t = blockIdx.x;
+        if (remap & 1) t = (t & 7) * (t_full >> 3) + (t >> 3);   // tiles of one XCD share X rows in L2
+    } else {
+        int i = blockIdx.x - t_full;
+        const int cnt = gridDim.x - t_full;
+        if (remap & 2) i = (i & 7) * (cnt >> 3) + (i >> 3);
+        split = i / nrem;
+        t = t_full + (i - split * nrem);
+        nsplit = splits;
+    }
+    const int n0 = (t % tiles_n) * BN, m0 = (t / tiles_n) * Q2_BM;
     const int kg = k >> 2, nbk = k >> 7;
-    const int st_end = 2 * nbk;
-    // wave tile: MI row tiles of 32 (X rows) by NJ column groups of 32 (weight rows)
-    constexpr int WN = MI, NJ = 8 / MI;                  // 8 / MI waves along X rows, MI along weight rows
+    const int st0 = 2 * (int)((int64_t)split * nbk / nsplit);
+    const int st_end = 2 * (int)((int64_t)(split + 1) * nbk / nsplit);
+    // output: y itself, or this split's tile block of the workspace
+    float* __restrict__ out = y;
+    int64_t ld = n;
+    int rb = 0, cb = 0;
+    if (split > 0) {
+        out = ws + ((int64_t)(split - 1) * nrem + (t - t_full)) * (Q2_BM * BN);
+        ld = BN;
+        rb = m0;
+        cb = n0;
+    }
     const int wm = wave / WN, wn = wave % WN;
     const int hf = lane >> 5;                            // which half of each step this lane's operands hold
 
-    // X copies: copy i of wave w fills slot (4 w + i) * 64 + lane: row slot / 8, chunk position slot % 8
+    // X copies: copy i of wave w fills slot (XC w + i) * 64 + lane: row slot / 8, chunk position slot % 8
+    // (the copies' operands are kept free of the template parameters: a
+    // direct-to-LDS copy whose operands depend on them is not instantiated
+    // for the host side, and the launch then has no stub)
     const uint16_t* xtile = x + (int64_t)m0 * k;
-    int xoff[4];
+    int xslot = XC * wave;
+    int xoff[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = (4 * wave + i) * 64 + lane;
+    for (int i = 0; i < XC; ++i) {
+        const int j = (xslot + i) * 64 + lane;
         const int r = j >> 3, c = q2_chunk(r, j & 7);
         const int gr = m0 + r < m ? r : m - 1 - m0;
         xoff[i] = gr * k + 8 * c;
     }
     auto copy_x = [&](int st, uint8_t* dst) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(xtile + xoff[i] + st * Q2_BK, dst + (4 * wave + i) * 1024, 16, 0, 0);
+        for (int i = 0; i < XC; ++i)
+            __builtin_amdgcn_global_load_lds(xtile + xoff[i] + st * Q2_BK, dst + (xslot + i) * 1024, 16, 0, 0);
     };
     // codes and scales of weight rows n0 + 32 (NJ wn + j) + lane % 32, j < NJ
     const uint8_t* crow[NJ];
@@ -1140,10 +1170,10 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
     // set A, odd steps in set B)
     uint3 cA[NJ], cB[NJ];
     uint16_t zA[NJ], zB[NJ];
-    copy_x(0, xs0);
+    copy_x(st0, xs0);
     asm volatile("" ::: "memory");
-    load_codes(0, cA, zA);
-    load_codes(1 < st_end ? 1 : 0, cB, zB);
+    load_codes(st0, cA, zA);
+    load_codes(st0 + 1 < st_end ? st0 + 1 : st0, cB, zB);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
     float scur[NJ];
@@ -1172,8 +1202,8 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
         asm volatile("" ::: "memory");                  // the copies are issued before the code loads
         // everything but these copies has landed: the codes and scales of
         // steps st and st + 1 (those of st + 1 were requested a step ago)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-        if (j2 == 0 && st > 0) {                        // a block start: carry the sums into its scale
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(XC));
+        if (j2 == 0 && st > st0) {                      // a block start: carry the sums into its scale
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const float s_ = h2f(zs[j]);
@@ -1216,7 +1246,7 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NJ));
         lds_barrier();                                  // X copies and operand reads done
     };
-    for (int st = 0; st < st_end; st += 2) {            // whole blocks: an even count of steps
+    for (int st = st0; st < st_end; st += 2) {          // whole blocks: an even count of steps
         body(std::integral_constant<int, 0>(), st);
         body(std::integral_constant<int, 1>(), st + 1);
     }
@@ -1230,10 +1260,11 @@ __global__ __launch_bounds__(512) void k_qgemm_v7(const uint8_t* __restrict__ co
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + 32 * (MI * wm + i) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < m) y[(int64_t)row * n + col] = acc[i][j][r] * scur[j];
+                if (row < m) out[(int64_t)(row - rb) * ld + (col - cb)] = acc[i][j][r] * scur[j];
             }
         }
 }
+
 
 // y += part 0 + part 1 + ... over the split tiles: thread q takes values
 // 4 (q % 8192) .. + 3 of tile block q / 8192 (tile t_full + q / 8192, 256 x
@@ -1276,28 +1307,32 @@ __global__ __launch_bounds__(256) void k_qgemm_sum(float* __restrict__ y, const 
 
 }  // namespace
 
-// How the pipelined kernel splits K: the first t_full tiles whole, the other
-// tiles `splits` ways (splits = 1: no split, t_full = all tiles).  Chosen by a
-// cost model in microseconds fitted to kernel timings of the Qwen3-4B-shaped
-// launches at m = 512 and 4096 (split counts 1..8 forced): workgroups run in
-// rounds of one per compute unit (the kernel's LDS holds one workgroup per
-// unit); a round costs 10 us (start, pipeline fill and drain, output stores)
-// plus 2.2 us per 128-block of its workgroups; a split adds the sum launch,
-// 2 us plus S + 1 reads or writes of the split tiles' fp32 values at 5 TB/s.
-// The candidates: no split; every tile split S ways; the tiles of the full
-// rounds whole and those of the last, partial round split S ways (run after
-// the full rounds, they fill it).  A split is taken when the model gives 8%
-// or more.
+// How the 256 x 128-tile kernels split K: the first t_full tiles whole, the
+// other tiles `splits` ways (splits = 1: no split, t_full = all tiles).
+// Chosen by a cost model in microseconds fitted to k_qgemm_v2's timings on
+// the Qwen3-4B-shaped launches at m = 512 and 4096 (split counts 1..8
+// forced): workgroups run in rounds of one per compute unit; a round costs
+// 10 us (start, pipeline fill and drain, output stores) plus 2.2 us per
+// 128-block of its workgroups; a split adds the sum launch, 2 us plus S + 1
+// reads or writes of the split tiles' fp32 values at 5 TB/s.  The
+// candidates: no split; every tile split S ways; the tiles of the full rounds
+// whole and those of the last, partial round split S ways (run after the
+// full rounds, they fill it).  A split is taken when the model gives 8% or
+// more.  The 4-wave kernel (two workgroups per unit) takes the same plans:
+// timed with them it is ahead of k_qgemm_v2 on every Qwen3-4B product at
+// m = 4096 and level at m = 512, and the plans keep the workspace of every
+// Qwen3-4B product at m = 512 within the allocation-free scratch.
 QgPlan qgemm_plan(int64_t n, int64_t k, int64_t m, size_t ws_bytes) {
     const int64_t tiles = ((n + Q2_BN - 1) / Q2_BN) * ((m + Q2_BM - 1) / Q2_BM), nbk = k / 128;
     const int64_t cus = compute_units();
+    const double per_block = 2.2;
     const double tb = (double)Q2_BM * Q2_BN * 4;                   // bytes of a tile block
     const QgPlan none = {tiles, 1};
     auto fits = [&](int64_t t_full, int64_t sp) {
         return sp >= 1 && sp <= std::min<int64_t>(8, nbk) && t_full >= 0 && t_full < tiles &&
                (double)(sp - 1) * (double)(tiles - t_full) * tb <= (double)ws_bytes;
     };
-    auto rt = [](double blocks) { return 10.0 + 2.2 * blocks; };
+    auto rt = [&](double blocks) { return 10.0 + per_block * blocks; };
     auto per = [&](int64_t sp) { return (double)((nbk + sp - 1) / sp); };
     auto sum_cost = [&](int64_t nrem, int64_t sp) { return 2.0 + (double)(sp + 1) * (double)nrem * tb / 5e6; };
     const double c1 = (double)((tiles + cus - 1) / cus) * rt((double)nbk);
@@ -1340,8 +1375,8 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
                  int64_t first_split) {
     const int64_t tn = (n + Q2_BN - 1) / Q2_BN, tm = (m + Q2_BM - 1) / Q2_BM, tiles = tn * tm;
 
-    // the pipelined kernel is the product; kernel 1 is the plain one-buffer
-    // kernel (kept as a second implementation, for tests)
+    // kernel 1, the plain one-buffer kernel (a second implementation, for
+    // tests), has its own tiles; every other kernel takes a split plan
     if (kernel != 1) {
         const QgPlan p = !workspace ? QgPlan{tiles, 1}
                          : splits >= 1 ? qgemm_forced(n, k, m, ws_bytes, splits, first_split)
@@ -1349,29 +1384,22 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
         const int64_t nrem = tiles - p.t_full, grid = p.t_full + nrem * p.splits;
         if (grid > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
         const int remap = (p.t_full % 8 == 0 ? 1 : 0) | ((nrem * p.splits) % 8 == 0 ? 2 : 0);
-        // The library's choice: the pipelined kernel (timed interleaved, medians
-        // of five rounds, it is ahead of both producer/consumer kernels on
-        // every Qwen3-4B shape at m = 512 and 4096), or the wide-tile kernel
-        // with register-decoded operands and 256 x 32 wave tiles when the
-        // product does not split and the wide tiles need fewer rounds of
-        // workgroups: a round of them takes 1.5-1.7 times a round of the
-        // 256 x 128 tiles (Qwen3-4B products at m = 4096).
+        // The library's choice: the 4-wave 256 x 128-tile kernel with
+        // register-decoded operands, two workgroups per compute unit (timed
+        // interleaved with the others, medians of five rounds: ahead of
+        // k_qgemm_v2 on the Qwen3-4B layer at m = 4096 by 15%, equal at
+        // m = 512)
         const int64_t tiles6 = ((n + Q6_BN - 1) / Q6_BN) * tm;
-        if (kernel == 0) {
-            const int64_t cus = compute_units();
-            const int64_t r6 = (tiles6 + cus - 1) / cus, r2 = (tiles + cus - 1) / cus;
-            kernel = p.splits == 1 && 170 * r6 < 100 * r2 ? 7 : 4;
-        }
+        if (kernel == 0) kernel = 8;
         if (kernel == 6 || kernel == 7) {               // operands decoded in registers: no split, no workspace
             if (tiles6 > (1 << 30)) return fail(PG_ERR_UNSUPPORTED, "m too large");
+            const int tn6 = (int)((n + Q6_BN - 1) / Q6_BN), rm6 = tiles6 % 8 == 0 ? 1 : 0;
             if (kernel == 6)
-                hipLaunchKernelGGL(k_qgemm_v7<4>, dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s, codes, scales,
-                                   (int)n, (int)k, x, (int)m, y, (int)((n + Q6_BN - 1) / Q6_BN),
-                                   tiles6 % 8 == 0 ? 1 : 0, (int)tiles6);
+                k_qgemm_v7<4, 8, Q6_BN><<<dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s>>>(
+                    codes, scales, (int)n, (int)k, x, (int)m, y, tn6, rm6, (int)tiles6, (int)tiles6, 1, nullptr);
             else
-                hipLaunchKernelGGL(k_qgemm_v7<8>, dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s, codes, scales,
-                                   (int)n, (int)k, x, (int)m, y, (int)((n + Q6_BN - 1) / Q6_BN),
-                                   tiles6 % 8 == 0 ? 1 : 0, (int)tiles6);
+                k_qgemm_v7<8, 8, Q6_BN><<<dim3((unsigned)tiles6), dim3(512), 0, (hipStream_t)s>>>(
+                    codes, scales, (int)n, (int)k, x, (int)m, y, tn6, rm6, (int)tiles6, (int)tiles6, 1, nullptr);
             return hip_check(hipGetLastError(), "pg_qgemm launch");
         }
         if (kernel == 5) {                              // wide tiles, whole K: no split, no workspace
@@ -1381,7 +1409,11 @@ int launch_qgemm(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
                                tiles6 % 8 == 0 ? 1 : 0, (int)tiles6);
             return hip_check(hipGetLastError(), "pg_qgemm launch");
         }
-        if (kernel == 3)
+        if (kernel == 8)                                // 256 x 128 tiles of 4 waves, operands decoded in registers
+            k_qgemm_v7<8, 4, Q2_BN><<<dim3((unsigned)grid), dim3(256), 0, (hipStream_t)s>>>(
+                codes, scales, (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)tiles, (int)p.t_full, p.splits,
+                static_cast<float*>(workspace));
+        else if (kernel == 3)
             hipLaunchKernelGGL(k_qgemm_v4, dim3((unsigned)grid), dim3(1024), 0, (hipStream_t)s, codes, scales,
                                (int)n, (int)k, x, (int)m, y, (int)tn, remap, (int)tiles, (int)p.t_full, p.splits,
                                static_cast<float*>(workspace));

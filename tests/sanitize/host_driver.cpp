@@ -76,7 +76,7 @@ int main() {
     CHECK(pg_qgemm(p, (uint16_t*)p, 8, 256, (uint16_t*)p, 0, (float*)p, st) == PG_ERR_INVALID_ARG);
     CHECK(pg_qgemm_ex(p, (uint16_t*)p, 8, 256, (uint16_t*)(p + 16384), 4, (float*)(p + 32768), p + 256, 64, st) ==
           PG_ERR_INVALID_ARG);                                                                  // overlaps codes
-    CHECK(pg_qgemm_tune(p, (uint16_t*)p, 8, 256, (uint16_t*)p, 4, (float*)p, nullptr, 0, 8, 0, 0, st) ==
+    CHECK(pg_qgemm_tune(p, (uint16_t*)p, 8, 256, (uint16_t*)p, 4, (float*)p, nullptr, 0, 9, 0, 0, st) ==
           PG_ERR_INVALID_ARG);
     CHECK(pg_hbm_read(p, 100, (uint32_t*)(p + 4096), st) == PG_ERR_INVALID_ARG);
     CHECK(pg_hbm_read(p, 4096, (uint32_t*)(p + 64), st) == PG_ERR_INVALID_ARG);             // out inside the range

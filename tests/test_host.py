@@ -83,7 +83,7 @@ def test_codebook_tables_by_format_match_oracle():
     lambda: q.pg_qgemv_ex(1 << 20, 1 << 20, 8, 256, 1 << 20, 3, 2, 12, 1 << 24, stream=0),  # vdot+mma
     lambda: q.pg_qgemv_ex(1 << 20, 1 << 20, 8, 256, 1 << 20, 0, 2, 4, 1 << 24, stream=0),   # choice, fp32 x
     lambda: q.pg_qgemv_ex(1 << 20, 1 << 20, 8, 256, 1 << 20, 3, 2, 1, 1 << 24, stream=0),   # flags
-    lambda: q.pg_qgemm_tune(1 << 20, 1 << 20, 8, 256, 1 << 21, 4, 1 << 22, None, 0, 8, 0, 0, stream=0),   # kernel
+    lambda: q.pg_qgemm_tune(1 << 20, 1 << 20, 8, 256, 1 << 21, 4, 1 << 22, None, 0, 9, 0, 0, stream=0),   # kernel
     lambda: q.pg_qgemm_tune(1 << 20, 1 << 20, 8, 256, 1 << 21, 4, 1 << 22, None, 0, 0, -1, 0, stream=0),  # splits
     lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 256, 4, 1 << 24, stream=0),                  # flags
     lambda: q.pg_decode_ex(1 << 20, 1 << 20, 8, 200, 2, 1 << 24, stream=0),                  # k % 128
