@@ -1035,18 +1035,22 @@ __global__ __launch_bounds__(512) void k_qgemm_v6(const uint8_t* __restrict__ co
         }
 }
 
-// Prompt product with the weight operand decoded in registers: the 256 x 256
-// tiles and carried block scales of k_qgemm_v6, but each wave decodes the
-// levels of its own weight rows straight into the matrix cores' B operands,
-// so that only X passes through the LDS (copied one step ahead, 64 KB in two
-// buffers) and one barrier per step hands the X buffers over.  Wave tiles of
-// MI x 8/MI products of 32 x 32: MI = 4 gives 128 x 64 (two waves decode each
-// weight row), MI = 8 gives 256 x 32 (each weight row decoded once, twice the
-// X operand reads; the faster of the two).  Within a 64-wide K step the products take K in a permuted
-// order, the same for both operands: product kk of lane half h (lanes 32 h ..
-// 32 h + 31) covers step positions 32 h + 8 kk .. + 7, so that a lane needs
-// code dwords 2 h and 2 h + 1 of its row's step and the dword before them
-// (the trellis state), 12 bytes it loads itself two steps ahead.
+// Prompt product with the weight operand decoded in registers (k_qgemm_v7):
+// the carried block scales of k_qgemm_v4, but each wave decodes the levels of
+// its own weight rows straight into the matrix cores' B operands, so that
+// only X passes through the LDS (copied one step ahead, 64 KB in two buffers)
+// and one barrier per step hands the X buffers over.  Template parameters:
+// NW waves over a 256 x BN output tile, each wave MI x (8 / MI) products of
+// 32 x 32.  <4, 8, 256>: 128 x 64 wave tiles (two waves decode each weight
+// row); <8, 8, 256>: 256 x 32 wave tiles (each weight row decoded once, twice
+// the X operand reads); <8, 4, 128>: the same wave tiles in 4-wave
+// workgroups over k_qgemm_v2's tiles and split plans, two workgroups per
+// compute unit (the library's kernel).  Within a 64-wide K step the products
+// take K in a permuted order, the same for both operands: product kk of lane
+// half h (lanes 32 h .. 32 h + 31) covers step positions 32 h + 8 kk .. + 7,
+// so that a lane needs code dwords 2 h and 2 h + 1 of its row's step and the
+// dword before them (the trellis state), 12 bytes it loads itself two steps
+// ahead.
 __device__ __forceinline__ void levels_bf16(uint32_t d, uint32_t dp, uint32_t keep, uint32_t o[8]) {
     uint32_t P[4];
     planes_of(d, dp, P);
