@@ -418,7 +418,7 @@ def pg_qgemv_ex(codes, scales, n: int, k: int, x_rot, x_dtype: int, batch: int, 
 
 def pg_qgemm_tune(codes, scales, n: int, k: int, x_rot_bf16, m: int, y, workspace, workspace_bytes: int, kernel: int,
                   splits: int, first_split: int, stream=None) -> None:
-    """pg_qgemm_ex with its kernel (0 the library's choice, 1..5 as in
+    """pg_qgemm_ex with its kernel (0 the library's choice, 1..8 as in
     pingala.h) and split plan given."""
     _qgemm_need(codes, scales, n, k, x_rot_bf16, m, y)
     _need(workspace, workspace_bytes, "workspace")
