@@ -38,8 +38,12 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             objs.append(obj)
         for src in HIP_SOURCES:
             obj = os.path.join(tmp, src + ".o")
+            # kernel arguments preloaded into scalar registers (the first 16
+            # dwords): a launch's first instructions need not wait for the
+            # argument segment (0.4% per token on the batch-1 stack)
             cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                   "-mllvm", "-amdgpu-kernarg-preload-count=16",
                    "-Wall", "-Wno-unused-function", "-c", os.path.join(CSRC, src), "-o", obj]
             procs.append((cmd, subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True)))
             objs.append(obj)
