@@ -137,17 +137,17 @@ __host__ __device__ constexpr bool fused_loops(int RS, int BTM) {
 
 template <int XDT, int XG, int RS, int BTM, bool CARRY>
 __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ codes,
-                                                    const uint16_t* __restrict__ scales, int n, int k,
-                                                    const void* __restrict__ x, int64_t ldx,
-                                                    const uint8_t* __restrict__ sign_bits, uint32_t flags,
-                                                    int batch, float* __restrict__ y, int R, int CG, int RP,
-                                                    int BT) {
+                                                    const uint16_t* __restrict__ scales,
+                                                    const void* __restrict__ x,
+                                                    const uint8_t* __restrict__ sign_bits,
+                                                    float* __restrict__ y, int n, uint32_t kword, int ldx32,
+                                                    uint32_t shape) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    // every argument is fetched by one scalar load burst here: loads left to
-    // the point of first use each cost a full round trip, and a scalar load
-    // in flight also holds back every later wait for LDS
-    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(ldx), "s"(sign_bits), "s"(flags),
-                 "s"(batch), "s"(y), "s"(R), "s"(CG), "s"(RP), "s"(BT));
+    // 14 argument dwords, all preloaded into scalar registers (fused_arg_words)
+    const int k = (int)(kword & 0xffffu), batch = (int)((kword >> 16) & 0xfu), BT = (int)((kword >> 20) & 0xfu);
+    const uint32_t flags = ((kword >> 24) & 1u) ? (uint32_t)PG_FLAG_RMSNORM : 0u;
+    const int64_t ldx = ldx32;
+    const int R = (int)(shape & 0x7ffu), CG = (int)((shape >> 11) & 0x7fu), RP = (int)((shape >> 18) & 0x7fu);
     constexpr int nthr = 512, W = 8;                           // the launch shape is fixed
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -479,6 +479,23 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
 }
 
 
+// The arguments of k_rot_qgemv in 14 dwords, so that the hardware preloads
+// all of them into scalar registers (the build asks for preloading; the
+// argument-segment pointer takes 2 of the 16 user registers) and no wave
+// waits for a scalar load before its first requests: k (16 bits), the
+// launch's batch rows and BT (4 bits each) and the RMS flag in one word; R,
+// CG and RP (11, 7 and 7 bits) in another; ldx in 32 bits.  False when a
+// value does not fit.
+__host__ inline bool fused_arg_words(const FusedShape& S, int64_t k, int bt, int64_t ldx, uint32_t flags,
+                                     uint32_t* kword, uint32_t* shape) {
+    if (k >= 65536 || bt < 0 || bt >= 16 || S.BT >= 16 || ldx < 0 || ldx > 0x7fffffff || S.R >= 2048 ||
+        S.CG >= 128 || S.RP >= 128)
+        return false;
+    *kword = (uint32_t)k | ((uint32_t)bt << 16) | ((uint32_t)S.BT << 20) | ((flags & PG_FLAG_RMSNORM) ? 1u << 24 : 0u);
+    *shape = (uint32_t)S.R | ((uint32_t)S.CG << 11) | ((uint32_t)S.RP << 18);
+    return true;
+}
+
 template <int XDT, int XG, int RS, int BTM, bool CARRY>
 int launch_fused_t(const FusedShape& S, const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                    const void* x, int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y,
@@ -489,9 +506,12 @@ int launch_fused_t(const FusedShape& S, const uint8_t* codes, const uint16_t* sc
     for (int b0 = 0; b0 < batch; b0 += tile) {
         const int bt = batch - b0 < tile ? batch - b0 : tile;
         const void* xb = (const uint8_t*)x + (int64_t)b0 * ldx * esz;
+        uint32_t kword, shape;
+        if (!fused_arg_words(S, k, bt, ldx, flags, &kword, &shape))
+            return fail(PG_ERR_UNSUPPORTED, "pg_rot_qgemv: shape n=%lld k=%lld ldx=%lld out of the kernel's range",
+                        (long long)n, (long long)k, (long long)ldx);
         hipLaunchKernelGGL((k_rot_qgemv<XDT, XG, RS, BTM, CARRY>), grid, dim3(64 * S.W), fused_lds_bytes((int)k, esz, S),
-                           st, codes, scales, (int)n, (int)k, xb, ldx, sign_bits, flags, bt, y + (int64_t)b0 * n,
-                           S.R, S.CG, S.RP, S.BT);
+                           st, codes, scales, xb, sign_bits, y + (int64_t)b0 * n, (int)n, kword, (int)ldx, shape);
         const int rc = hip_check(hipGetLastError(), "pg_rot_qgemv launch");
         if (rc != PG_OK) return rc;
     }

@@ -22,6 +22,15 @@ struct Fused1Shape {
     int W, R, CG, RP, RS, U;
 };
 
+// R, CG, RP and U in one argument dword (11, 7, 7 and 7 bits; fused1_shape
+// keeps them in range).  With the arguments in 14 dwords, the hardware
+// preloads all of them into scalar registers (the build asks for preloading;
+// the argument-segment pointer takes 2 of the 16 user registers), so no wave
+// waits for a scalar load of its arguments before its first requests.
+__host__ inline uint32_t fused1_shape_word(const Fused1Shape& S) {
+    return (uint32_t)S.R | ((uint32_t)S.CG << 11) | ((uint32_t)S.RP << 18) | ((uint32_t)S.U << 25);
+}
+
 // PG_ERR_UNSUPPORTED (message set) when the shape does not fit the kernel
 // with at most umax rotation rounds (and the codebook table in LDS if asked)
 int fused1_shape(int64_t n, int64_t k, int umax, bool table, Fused1Shape* out);
@@ -78,17 +87,20 @@ __device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t o, int lane) {
 // (funnel shifts of the dword and its predecessor); flags PG_FLAG_CARRY_STATE
 // continues the state from the previous 64-value chunk of the row, whose
 // last code dword every lane loads itself.
+//
+// Arguments: the first 14 dwords arrive preloaded in scalar registers (see
+// fused1_shape_word), so the requests need no scalar load; only the table
+// pointer, used by TAB > 0 alone, comes after them.
 template <int XDT, int RS, int TAB, int UMAX>
 __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ codes,
-                                                     const uint16_t* __restrict__ scales, int n, int k,
+                                                     const uint16_t* __restrict__ scales,
                                                      const void* __restrict__ x,
                                                      const uint8_t* __restrict__ sign_bits,
-                                                     const uint32_t* __restrict__ table, uint32_t flags,
-                                                     float* __restrict__ y, int R, int CG, int RP, int U) {
+                                                     float* __restrict__ y, int n, int k, uint32_t flags,
+                                                     uint32_t shape, const uint32_t* __restrict__ table) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_all[];
-    // one scalar load burst for every argument (see k_rot_qgemv)
-    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(sign_bits), "s"(table), "s"(flags),
-                 "s"(y), "s"(R), "s"(CG), "s"(RP), "s"(U));
+    const int R = (int)(shape & 0x7ffu), CG = (int)((shape >> 11) & 0x7fu), RP = (int)((shape >> 18) & 0x7fu),
+              U = (int)(shape >> 25);
     uint8_t* lds = lds_all + (TAB ? F1T_TABLE_BYTES : 0);                    // the table, if any, sits first
     constexpr int W = 8;
     const int tid = threadIdx.x;
@@ -411,7 +423,7 @@ int launch_fused1_t(const Fused1Shape& S, const uint8_t* codes, const uint16_t* 
                     hipStream_t st) {
     const dim3 grid((unsigned)((n + S.R - 1) / S.R));
     hipLaunchKernelGGL((k_rot_qgemv1<XDT, RS, TAB, UMAX>), grid, dim3(64 * S.W), fused1_lds_bytes((int)k, S, TAB != 0),
-                       st, codes, scales, (int)n, (int)k, x, sign_bits, table, flags, y, S.R, S.CG, S.RP, S.U);
+                       st, codes, scales, x, sign_bits, y, (int)n, (int)k, flags, fused1_shape_word(S), table);
     return hip_check(hipGetLastError(), TAB ? "pg_rot_qgemv_table launch" : "pg_rot_qgemv launch");
 }
 

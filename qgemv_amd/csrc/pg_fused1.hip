@@ -26,6 +26,9 @@ int fused1_shape(int64_t n, int64_t k, int umax, bool table, Fused1Shape* out) {
     S.RS = (S.R + S.RP - 1) / S.RP;
     if (fused1_lds_bytes((int)k, S, table) > 160 * 1024)
         return fail(PG_ERR_UNSUPPORTED, "shape n=%lld k=%lld does not fit the batch-1 stage", (long long)n, (long long)k);
+    // the fields of fused1_shape_word (R <= 16 RP <= 1024, CG and RP <= 64, U <= 4 here)
+    if (S.R >= 2048 || S.CG >= 128 || S.RP >= 128 || S.U >= 128)
+        return fail(PG_ERR_UNSUPPORTED, "shape n=%lld k=%lld does not fit the batch-1 stage", (long long)n, (long long)k);
     *out = S;
     return PG_OK;
 }

@@ -52,13 +52,15 @@ __host__ __device__ inline RqLayout rq_layout(int k, int R, int batch) {
 // the result does not depend on timing.
 template <int XDT, int TPW>
 __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ codes,
-                                                  const uint16_t* __restrict__ scales, int n, int k,
-                                                  const void* __restrict__ x, int64_t ldx,
-                                                  const uint8_t* __restrict__ sign_bits, uint32_t flags, int batch,
-                                                  float* __restrict__ y, int R) {
+                                                  const uint16_t* __restrict__ scales,
+                                                  const void* __restrict__ x,
+                                                  const uint8_t* __restrict__ sign_bits,
+                                                  float* __restrict__ y, int n, int k, int ldx32, uint32_t bword) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    asm volatile("" ::"s"(codes), "s"(scales), "s"(n), "s"(k), "s"(x), "s"(ldx), "s"(sign_bits), "s"(flags),
-                 "s"(batch), "s"(y), "s"(R));
+    // 14 argument dwords, all preloaded into scalar registers (launch_rq_x)
+    const int R = (int)(bword & 0xffffu), batch = (int)((bword >> 16) & 0xffu);
+    const uint32_t flags = ((bword >> 24) & 1u) ? (uint32_t)PG_FLAG_RMSNORM : 0u;
+    const int64_t ldx = ldx32;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = k >> 2, nbk = k >> 7, nbk4 = (nbk + 3) & ~3, tpr = nbk4 >> 2, ngr = k >> 3;
@@ -318,8 +320,17 @@ int launch_rq_x(int tpw, const uint8_t* codes, const uint16_t* scales, int64_t n
                 int64_t ldx, const uint8_t* sign_bits, uint32_t flags, int batch, float* y, int R, size_t lds,
                 hipStream_t st) {
     const dim3 grid((unsigned)((n + R - 1) / R));
-#define PG_RQ(T) hipLaunchKernelGGL((k_rot_qmma<XDT, T>), grid, dim3(512), lds, st, codes, scales, (int)n, (int)k, x, ldx, \
-                                    sign_bits, flags, batch, y, R)
+    // R (16 bits), the batch (8) and the RMS flag in one dword, ldx in 32
+    // bits: with 14 argument dwords the hardware preloads every argument into
+    // scalar registers (the build asks for preloading; the argument-segment
+    // pointer takes 2 of the 16 user registers), so no wave waits for a
+    // scalar load before its first requests
+    if (R >= 65536 || batch > 255 || ldx < 0 || ldx > 0x7fffffff)
+        return fail(PG_ERR_UNSUPPORTED, "pg_rot_qgemv: shape n=%lld k=%lld ldx=%lld out of the kernel's range",
+                    (long long)n, (long long)k, (long long)ldx);
+    const uint32_t bword = (uint32_t)R | ((uint32_t)batch << 16) | ((flags & PG_FLAG_RMSNORM) ? 1u << 24 : 0u);
+#define PG_RQ(T) hipLaunchKernelGGL((k_rot_qmma<XDT, T>), grid, dim3(512), lds, st, codes, scales, x, sign_bits, y, \
+                                    (int)n, (int)k, (int)ldx, bword)
     switch (tpw) {
         case 1: PG_RQ(1); break;
         case 2: PG_RQ(2); break;

@@ -119,10 +119,12 @@ __device__ __forceinline__ float sq16(const uint4 w) {
     return s;
 }
 
+// (arguments in 14 dwords, the 8-byte ones first: the hardware preloads all
+// of them into scalar registers, so no wave waits for a scalar load)
 template <int IDT>
 __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, void* __restrict__ y,
-                                              int out_dt, const uint8_t* __restrict__ sign_bits, int k,
-                                              int64_t ldx, uint32_t flags, int64_t q16_stride, int vec) {
+                                              const uint8_t* __restrict__ sign_bits, int64_t ldx,
+                                              int64_t q16_stride, int out_dt, int k, uint32_t flags, int vec) {
     constexpr int in_dt = IDT;
     const int64_t row = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -586,11 +588,11 @@ int launch_fwht(const void* x, int in_dt, int64_t ldx, void* y, int out_dt, cons
     const int64_t qs = (int64_t)q16_row_bytes(k);
     hipStream_t st = (hipStream_t)s;
     if (in_dt == PG_F32)
-        hipLaunchKernelGGL(k_fwht<PG_F32>, grid, dim3(256), 0, st, x, y, out_dt, sign_bits, (int)k, ldx, flags, qs, vec);
+        hipLaunchKernelGGL(k_fwht<PG_F32>, grid, dim3(256), 0, st, x, y, sign_bits, ldx, qs, out_dt, (int)k, flags, vec);
     else if (in_dt == PG_F16)
-        hipLaunchKernelGGL(k_fwht<PG_F16>, grid, dim3(256), 0, st, x, y, out_dt, sign_bits, (int)k, ldx, flags, qs, vec);
+        hipLaunchKernelGGL(k_fwht<PG_F16>, grid, dim3(256), 0, st, x, y, sign_bits, ldx, qs, out_dt, (int)k, flags, vec);
     else
-        hipLaunchKernelGGL(k_fwht<PG_BF16>, grid, dim3(256), 0, st, x, y, out_dt, sign_bits, (int)k, ldx, flags, qs, vec);
+        hipLaunchKernelGGL(k_fwht<PG_BF16>, grid, dim3(256), 0, st, x, y, sign_bits, ldx, qs, out_dt, (int)k, flags, vec);
     return hip_check(hipGetLastError(), "pg_fwht_rotate launch");
 }
 
