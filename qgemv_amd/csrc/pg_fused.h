@@ -166,7 +166,9 @@ __global__ __launch_bounds__(512) void k_rot_qgemv(const uint8_t* __restrict__ c
     uint32_t* cprev = reinterpret_cast<uint32_t*>(wsum + (size_t)BT * W);  // [64 teams][16 row slots]: last
                                                                            // code dword of each team's chunks
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
-    const float rk = 1.0f / (float)k;                 // computed before any wait
+    float rk = 1.0f / (float)k;
+    asm volatile("" : "+v"(rk));                      // computed here, before any wait (the
+                                                      // compiler would sink it past the barrier)
     constexpr bool carry = CARRY;                      // codes of the carried-state variant
 
     // this lane's column of chunks and its rows

@@ -115,7 +115,9 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
     float* wsum = part + R * CG;                                               // [W] sums of squares
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
     const bool carry = TAB && (flags & PG_FLAG_CARRY_STATE) != 0;
-    const float rk = 1.0f / (float)k;                 // computed before any wait
+    float rk = 1.0f / (float)k;
+    asm volatile("" : "+v"(rk));                      // computed here, before any wait (the
+                                                      // compiler would sink it past the barrier)
 
     // ---- 1. requests: the lane's x values and sign words of every round,
     // then its code chunks and scales (memory operations of a wave complete
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
         for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
         mx = fmaxf(mx, xor_lane<1>(mx, lane));
         mx = fmaxf(mx, xor_lane<2>(mx, lane));
-        const float s = mx > 0.0f ? (float)Q16_MAXQ / mx : 0.0f;
+        const float s = mx > 0.0f ? (float)Q16_MAXQ * __builtin_amdgcn_rcpf(mx) : 0.0f;   // hardware reciprocal
         uint32_t bits[8];
         int qs = 0;
 #pragma unroll

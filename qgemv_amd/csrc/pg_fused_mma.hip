@@ -76,7 +76,9 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
     uint16_t* swt = reinterpret_cast<uint16_t*>(lds + Ly.swt);
     uint8_t* ctile = lds + Ly.ctile + (size_t)wave * MMA_TILE_BYTES;
     const bool norm = (flags & PG_FLAG_RMSNORM) != 0;
-    const float rk = 1.0f / (float)k;                 // computed before any wait
+    float rk = 1.0f / (float)k;
+    asm volatile("" : "+v"(rk));                      // computed here, before any wait (the
+                                                      // compiler would sink it past the barrier)
     constexpr int esz = XDT == PG_F32 ? 4 : 2;
 
     // ---- 1. requests (past the end: repeats of valid addresses)
