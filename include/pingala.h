@@ -281,7 +281,10 @@ int pg_decode_table(const uint8_t* codes, const uint16_t* scales, int64_t n, int
  *              S = sum of v^2 over the row (fp32, order unspecified),
  *              inv = rsq(fma(S, rk, 1e-6)), rk = 1/k rounded to fp32,
  *              rsq the hardware reciprocal square root (<= 1 ulp),
- *              n(v) = fp16_RNE(v * inv)   (every kernel computes this)
+ *              n(v) = fp16_RNE(v * inv)   (every kernel computes this;
+ *              some round the product to fp32 first, some convert the
+ *              exact product as one mixed-precision fma: the two differ
+ *              by one fp16 unit in rare ties)
  * x and y may not overlap.  fp32 arithmetic; fp16/bf16 outputs round to
  * nearest even. */
 int pg_fwht_rotate(const void* x, int in_dtype, void* y, int out_dtype,
