@@ -339,7 +339,8 @@ int pg_qgemv_ex(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t
  *   x        device [batch][ldx] of x_dtype (PG_F32 / PG_F16); the first k
  *            values of each row are the input (e.g. the q part of a merged
  *            q/k/v output); ldx >= k; x and every row start 16-byte
- *            aligned (ldx a multiple of 4 for PG_F32, of 8 for PG_F16)
+ *            aligned (ldx a multiple of 4 for PG_F32, of 8 for PG_F16);
+ *            ldx < 2^31 (PG_ERR_UNSUPPORTED beyond)
  *   sign_bits device u8 [k/8], 4-byte aligned
  *   y        device f32 [batch][n] out
  *   batch    1..8

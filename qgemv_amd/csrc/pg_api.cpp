@@ -252,6 +252,8 @@ int pg_rot_qgemv(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
     if (batch < 1 || batch > 8) return pg::fail(PG_ERR_INVALID_ARG, "batch must be 1..8 (got %d)", batch);
     PG_TRY(check_dtype(x_dtype, "x_dtype", false, false));
     if (ldx < k) return pg::fail(PG_ERR_INVALID_ARG, "ldx (%lld) < k (%lld)", (long long)ldx, (long long)k);
+    if (ldx > 0x7fffffffLL)   // the stage kernels take it in 32 bits (all of their arguments are preloaded)
+        return pg::fail(PG_ERR_UNSUPPORTED, "ldx (%lld) above 2^31 - 1", (long long)ldx);
     if (flags & ~(uint32_t)(PG_FLAG_RMSNORM | PG_FLAG_CARRY_STATE | PG_FLAG_KERNEL_VDOT | PG_FLAG_KERNEL_MMA))
         return pg::fail(PG_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     if ((flags & PG_FLAG_KERNEL_VDOT) && (flags & PG_FLAG_KERNEL_MMA))

@@ -119,6 +119,15 @@ def test_invalid_arguments_fail_before_launch(call):
     assert q.pg_last_error() != ""
 
 
+def test_rot_qgemv_row_stride_beyond_32_bits_is_unsupported():
+    # the stage kernels take ldx in 32 bits; validation refuses larger strides
+    # before any launch (the pointers are never dereferenced)
+    with pytest.raises(q.PgError) as ei:
+        q.pg_rot_qgemv(1 << 20, 1 << 20, 8, 256, 1 << 22, 0, 1 << 31, 1 << 20, 1, 1, 1 << 24, stream=0)
+    assert ei.value.code == q._lib.PG_ERR_UNSUPPORTED
+    assert "2^31" in q.pg_last_error()
+
+
 def test_encode_ref_equals_oracle_on_single_layer():
     w = synth.single_layer_weights()
     sb = synth.site_sign_bits(0, 0, 2048)
