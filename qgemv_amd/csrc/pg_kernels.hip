@@ -144,20 +144,21 @@ __global__ __launch_bounds__(256) void k_fwht(const void* __restrict__ x, void* 
     float inv = 1.0f;
     if ((flags & PG_FLAG_RMSNORM) && vec) {
         // the whole row's squares, rows 16-byte aligned: 16-byte vectors
-        // t + 256 u, up to 8 per thread in flight at once
+        // t + 256 u, up to 16 per thread in flight at once (one round trip
+        // for k <= 16384 at fp32; the sum runs over u in the same order)
         constexpr int per = IDT == PG_F32 ? 4 : 8;
         const int nv = k / per;
         const uint4* xv = reinterpret_cast<const uint4*>((const uint8_t*)x + xbase * (IDT == PG_F32 ? 4 : 2));
         float ss = 0.0f;
-        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 8) {
-            uint4 w[8];
+        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 16) {
+            uint4 w[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 16; ++u) {
                 const int v = v0 + 256 * u;
                 w[u] = v < nv ? xv[v] : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) ss += sq16<IDT>(w[u]);
+            for (int u = 0; u < 16; ++u) ss += sq16<IDT>(w[u]);
         }
         ss = wave_sum(ss);
         if (lane == 0) red[wave] = ss;
