@@ -362,9 +362,12 @@ template <int BS, int R>
 __global__ __launch_bounds__(512) void k_qgemv_q16(const uint8_t* __restrict__ codes,
                                                    const uint16_t* __restrict__ scales, int n, int k,
                                                    const uint8_t* __restrict__ xq, int xq_stride, int batch,
-                                                   float* __restrict__ y) {
+                                                   float* __restrict__ y, int nthr) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tid = threadIdx.x, nthr = blockDim.x;
+    // the block size as an argument (13 dwords, all preloaded into scalar
+    // registers) rather than from the dispatch's hidden arguments, which
+    // would cost a scalar load at entry
+    const int tid = threadIdx.x;
     const int W = nthr >> 6;
     const int lane = tid & 63, wave = tid >> 6;
     const int team = lane >> 3, tl = lane & 7;
@@ -608,10 +611,10 @@ int launch_q16_bs(int R, int W, const uint8_t* codes, const uint16_t* scales, in
     const size_t lds = (size_t)W * L.wave_bytes + (size_t)W * 8 * R * BS * 4;
     if (R == 2)
         hipLaunchKernelGGL((k_qgemv_q16<BS, 2>), grid, dim3(64 * W), lds, st, codes, scales, (int)n, (int)k, xq,
-                           stride, batch, y);
+                           stride, batch, y, 64 * W);
     else
         hipLaunchKernelGGL((k_qgemv_q16<BS, 1>), grid, dim3(64 * W), lds, st, codes, scales, (int)n, (int)k, xq,
-                           stride, batch, y);
+                           stride, batch, y, 64 * W);
     return hip_check(hipGetLastError(), "pg_qgemv launch");
 }
 
