@@ -90,6 +90,7 @@ __global__ __launch_bounds__(512) void k_rot_qmma(const uint8_t* __restrict__ co
     if (rowon)                                               // waves past the batch load no row
 #pragma unroll
     for (int u = 0; u < KV; ++u) {
+        if (64 * u >= ngr) continue;                         // uniform: no group of this round in the row
         const int g = lane + 64 * u, gc = g < ngr ? g : ngr - 1;
         if constexpr (XDT == PG_F32) {
             const float4 v0 = *reinterpret_cast<const float4*>(xr + 32 * gc);
