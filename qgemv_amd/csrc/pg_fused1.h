@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512) void k_rot_qgemv1(const uint8_t* __restrict__ 
     uint32_t sw[UMAX];
 #pragma unroll
     for (int u = 0; u < UMAX; ++u) {
-        if (u < U) {
+        if (u < U && 4 * (wave + W * u) < nbk) {               // uniform: a round with blocks for this wave
             const int blk = 4 * (wave + W * u) + rbb;
             const int bc = blk < nbk ? blk : nbk - 1;          // clamped: every lane issues the same loads
             const int p0 = bc * 128 + 32 * rmh + rj;             // position of (m0, g) = (0, 0)
